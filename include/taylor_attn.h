@@ -1,0 +1,152 @@
+/*
+ * taylor_attn.h -- C ABI of the Taylor-truncated causal attention library (gfx950 / MI355X).
+ *
+ * The method ("Expanding Attention: A Taylor-Series Route to Linear-Time
+ * Transformers with a Fixed Number of Recurrent States", Z. Huang,
+ * arXiv:2610.20637, Abstract): the attention kernel exp(s), s = scale * q.k,
+ * is replaced by its Taylor polynomial of n terms,
+ *
+ *     K_n(s) = sum_{m=0}^{n-1} s^m / m!,
+ *
+ * each term is factorised as an inner product of symmetric tensor powers,
+ * s^m/m! = <phi_m(scale*q), phi_m(k)>, with binom(d_k+m-1, m) monomial features
+ * phi_m(x)_alpha = x^alpha / sqrt(alpha!), and the causal history collapses into
+ * n fixed-size recurrent states
+ *
+ *     S_m = sum_j phi_m(k_j) v_j^T      (W_m x d_v)
+ *     z_m = sum_j phi_m(k_j)            (W_m)
+ *
+ * read out as  o_i = sum_m phi_m(scale*q_i)^T S_m / sum_m phi_m(scale*q_i)^T z_m
+ * (inclusive causality: token i sees keys 0..i).  Decoding updates the states
+ * with one rank-one outer product per token; states add across chunks, so
+ * prefill is a chunked computation plus a prefix scan of chunk states.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All tensors are dense row-major.  q, k: [B, H, N, d_k]; v: [B, H, N, d_v]
+ *   (decode: N = 1 and the token axis is dropped); o: [B, H, N, d_v] float32.
+ * - q, k, v have element type cfg->in_dtype (float32 or bfloat16); outputs,
+ *   states and all accumulation are float32.
+ * - Device pointers are owned by the caller.  The library never allocates,
+ *   frees or synchronises; every call only enqueues kernels on `stream`
+ *   (0 = the null stream) and returns at once.  Pointers must be 16-byte
+ *   aligned device addresses.
+ * - Every call returns a taylor_status (0 = TAYLOR_OK, negative = error).
+ *   Arguments are validated before anything is enqueued; on an error return
+ *   nothing has been enqueued (TAYLOR_ERR_HIP: a launch failed; earlier
+ *   kernels of the same call may already be queued).  No C++ exception crosses
+ *   this boundary.  There is no global mutable state; calls are re-entrant.
+ *
+ * State layout (per head, float32): the "packed" block of
+ * W*(d_v+1) values the Abstract counts (9,945 at n=3, d_k=16, d_v=64),
+ * stored as
+ *     S   : [W][d_v]  row-major, feature-major rows, rows ordered as the
+ *                     monomial table below (orders ascending, lexicographic
+ *                     coordinate tuples within an order);
+ *     z   : [W]       the normaliser column (the "+1" column of [v | 1]);
+ *     pad : zeros up to taylor_state_stride() floats (a multiple of 4, so every
+ *           head block and every S row starts 16-byte aligned).
+ * A state buffer is [B][H][stride] floats.
+ */
+#ifndef TAYLOR_ATTN_H
+#define TAYLOR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TAYLOR_OK = 0,
+  TAYLOR_ERR_INVALID_ARG = -1, /* bad pointer, size, alignment or config value */
+  TAYLOR_ERR_UNSUPPORTED = -2, /* valid config with no compiled kernel (see taylor_supported) */
+  TAYLOR_ERR_HIP = -3          /* the HIP runtime reported an error on launch */
+} taylor_status;
+
+typedef enum { TAYLOR_F32 = 0, TAYLOR_BF16 = 1 } taylor_dtype;
+
+typedef struct {
+  int n_terms;  /* n: Taylor terms, orders 0..n-1 (1..5 compiled)                         */
+  int d_k;      /* q/k head dimension (4, 8 or 16 compiled)                                */
+  int d_v;      /* v head dimension (multiple of 4; 4, 16, 32, 64, 128 compiled)           */
+  int chunk;    /* prefill chunk length C: 64 or 128; 0 selects the default for the shape */
+  float scale;  /* score scale sigma: s = scale * q.k                                      */
+  int in_dtype; /* taylor_dtype of q, k, v                                                 */
+} taylor_config;
+
+/* Human-readable name of a taylor_status; never NULL. */
+const char* taylor_status_string(int status);
+
+/* Feature width W = sum_{m<n} binom(d_k+m-1, m) (Abstract: the m-th state is
+ * binom(d+m-1, m) wide), e.g. 153 at n=3, d_k=16.  Host only.
+ * Returns TAYLOR_ERR_INVALID_ARG if n_terms < 1, d_k < 1 or W would exceed 2^31-1. */
+int taylor_feature_width(int n_terms, int d_k);
+
+/* Logical state size per head, W*(d_v+1) floats (9,945 at n=3, d_k=16, d_v=64).
+ * Host only.  Negative taylor_status if cfg is invalid. */
+int64_t taylor_state_elems(const taylor_config* cfg);
+
+/* Floats between consecutive head blocks of a state buffer: W*(d_v+1) rounded
+ * up to a multiple of 4.  Host only.  Negative taylor_status if cfg is invalid. */
+int64_t taylor_state_stride(const taylor_config* cfg);
+
+/* Export the monomial table the kernels use (host only, bit-exact):
+ *   idx_out  [W][max(n-1,1)] int32: coordinates i_1 <= ... <= i_m of each
+ *            feature, -1 padded (row 0, the constant feature, is all -1);
+ *   coef_out [W] double: 1/sqrt(alpha!) with alpha the exponent vector, computed
+ *            as 1.0/sqrt((double)prod_i alpha_i!).
+ * Rows follow the feature order: orders m = 0..n-1 ascending, lexicographic
+ * within an order.  Either output pointer may be NULL.  `cap_rows` is the
+ * capacity of the outputs in rows.  Returns W, or TAYLOR_ERR_INVALID_ARG for a
+ * bad (n, d_k) or cap_rows < W (nothing written then). */
+int taylor_monomial_table(int n_terms, int d_k, int32_t* idx_out, double* coef_out, size_t cap_rows);
+
+/* TAYLOR_OK if kernels are compiled for this config (n_terms, d_k, d_v, chunk,
+ * in_dtype); TAYLOR_ERR_UNSUPPORTED if valid but not compiled;
+ * TAYLOR_ERR_INVALID_ARG if invalid.  Host only. */
+int taylor_supported(const taylor_config* cfg);
+
+/* Bytes of device workspace taylor_attn_prefill needs for these sizes (may be 0).
+ * Host only.  Negative taylor_status if cfg or sizes are invalid. */
+int64_t taylor_prefill_workspace_bytes(const taylor_config* cfg, int B, int H, int N);
+
+/* Zero B*H state blocks (S, z and padding) -- an empty history (Abstract: the
+ * states are sums over the causal history).  `state` is [B][H][stride] floats.
+ * B*H == 0 is a no-op. */
+int taylor_state_init(float* state, int B, int H, const taylor_config* cfg, hipStream_t stream);
+
+/* Chunked causal prefill over N tokens (Abstract: states add across chunks,
+ * so prefill is chunk-local work plus a prefix scan of chunk states).
+ *   q, k, v   : [B,H,N,d_k], [B,H,N,d_k], [B,H,N,d_v] in cfg->in_dtype;
+ *   o         : [B,H,N,d_v] float32 outputs, or NULL for a state-only pass;
+ *   state     : [B,H,stride] float32, in/out.  On entry the state of the
+ *               tokens before this call (zero = empty history); on return the
+ *               state including these N tokens, so prefill(N1) followed by
+ *               prefill(N2) equals prefill(N1+N2).  NULL: start from an empty
+ *               history and discard the final state.  At least one of o and
+ *               state must be non-NULL;
+ *   workspace : device buffer of taylor_prefill_workspace_bytes(cfg, B, H, N)
+ *               bytes (NULL allowed when that is 0); its contents on entry are
+ *               ignored and on return undefined.
+ * N == 0 or B*H == 0 is a no-op.  Calls sharing a workspace must not overlap. */
+int taylor_attn_prefill(const void* q, const void* k, const void* v, float* o, float* state, void* workspace, int B,
+                        int H, int N, const taylor_config* cfg, hipStream_t stream);
+
+/* One decode step per (b, h): S += phi(k_t) [v_t | 1]^T (one rank-one update),
+ * then o_t = (phi(scale*q_t)^T S)[:d_v] / (phi(scale*q_t)^T z) -- the update comes
+ * first, so the current token attends to itself.
+ *   q, k, v : [B,H,d_k], [B,H,d_k], [B,H,d_v] in cfg->in_dtype;
+ *   o       : [B,H,d_v] float32;
+ *   state   : [B,H,stride] float32, updated in place.
+ * B*H == 0 is a no-op. */
+int taylor_attn_decode_step(const void* q, const void* k, const void* v, float* o, float* state, int B, int H,
+                            const taylor_config* cfg, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TAYLOR_ATTN_H */

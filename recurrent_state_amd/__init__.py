@@ -1,0 +1,237 @@
+"""Python binding of the Taylor-truncated causal attention library (gfx950 / MI355X).
+
+Argument marshalling only: every function below forwards to the C entry point of
+the same name in ``_lib/libtaylor_attn.so`` (declared in ``include/taylor_attn.h``)
+with raw device pointers, sizes read off the tensor shapes, and the current HIP
+stream.  All computation runs in the library's HIP kernels; nothing here does
+any of the method's arithmetic, and there is no fallback: if the library is
+missing the import of the binding functions fails loudly.
+
+PyTorch provides device memory and streams.  torch is imported before the
+library is loaded so that the library binds to the HIP runtime torch already
+loaded (they share the soname ``libamdhip64.so.7``).
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libtaylor_attn.so")
+
+TAYLOR_OK = 0
+TAYLOR_ERR_INVALID_ARG = -1
+TAYLOR_ERR_UNSUPPORTED = -2
+TAYLOR_ERR_HIP = -3
+TAYLOR_F32 = 0
+TAYLOR_BF16 = 1
+
+# Every symbol the header declares.
+EXPORTS = (
+    "taylor_status_string",
+    "taylor_feature_width",
+    "taylor_state_elems",
+    "taylor_state_stride",
+    "taylor_monomial_table",
+    "taylor_supported",
+    "taylor_prefill_workspace_bytes",
+    "taylor_state_init",
+    "taylor_attn_prefill",
+    "taylor_attn_decode_step",
+)
+
+
+class TaylorError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {taylor_status_string(status)} ({status})")
+        self.status = status
+
+
+class taylor_config(ctypes.Structure):
+    """Mirror of the C struct taylor_config."""
+
+    _fields_ = [
+        ("n_terms", ctypes.c_int),
+        ("d_k", ctypes.c_int),
+        ("d_v", ctypes.c_int),
+        ("chunk", ctypes.c_int),
+        ("scale", ctypes.c_float),
+        ("in_dtype", ctypes.c_int),
+    ]
+
+    def __repr__(self):
+        return (f"taylor_config(n_terms={self.n_terms}, d_k={self.d_k}, d_v={self.d_v}, chunk={self.chunk}, "
+                f"scale={self.scale}, in_dtype={self.in_dtype})")
+
+
+def config(n_terms, d_k, d_v, chunk=0, scale=1.0, in_dtype=TAYLOR_F32):
+    if not isinstance(in_dtype, int):
+        in_dtype = dtype_code(in_dtype)
+    return taylor_config(n_terms, d_k, d_v, chunk, scale, in_dtype)
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (loaded on first use; raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (loads the HIP runtime the library must share)
+
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m recurrent_state_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    i, i64, p, f = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    cfgp = ctypes.POINTER(taylor_config)
+    sig = {
+        "taylor_status_string": (ctypes.c_char_p, [i]),
+        "taylor_feature_width": (i, [i, i]),
+        "taylor_state_elems": (i64, [cfgp]),
+        "taylor_state_stride": (i64, [cfgp]),
+        "taylor_monomial_table": (i, [i, i, p, p, ctypes.c_size_t]),
+        "taylor_supported": (i, [cfgp]),
+        "taylor_prefill_workspace_bytes": (i64, [cfgp, i, i, i]),
+        "taylor_state_init": (i, [p, i, i, cfgp, p]),
+        "taylor_attn_prefill": (i, [p, p, p, p, p, p, i, i, i, cfgp, p]),
+        "taylor_attn_decode_step": (i, [p, p, p, p, p, i, i, cfgp, p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(rc, what):
+    if rc != TAYLOR_OK:
+        raise TaylorError(rc, what)
+    return rc
+
+
+def dtype_code(dtype):
+    import torch
+
+    if dtype == torch.float32:
+        return TAYLOR_F32
+    if dtype == torch.bfloat16:
+        return TAYLOR_BF16
+    raise TypeError(f"unsupported input dtype {dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    import torch
+
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+# ---- host-only queries --------------------------------------------------------------------------
+
+
+def taylor_status_string(status):
+    return lib().taylor_status_string(int(status)).decode()
+
+
+def taylor_feature_width(n_terms, d_k):
+    return _check_nonneg(lib().taylor_feature_width(n_terms, d_k), "taylor_feature_width")
+
+
+def _check_nonneg(v, what):
+    if v < 0:
+        raise TaylorError(int(v), what)
+    return int(v)
+
+
+def taylor_state_elems(cfg):
+    return _check_nonneg(lib().taylor_state_elems(ctypes.byref(cfg)), "taylor_state_elems")
+
+
+def taylor_state_stride(cfg):
+    return _check_nonneg(lib().taylor_state_stride(ctypes.byref(cfg)), "taylor_state_stride")
+
+
+def taylor_monomial_table(n_terms, d_k):
+    """(idx int32 [W, max(n-1,1)], coef float64 [W]) exactly as the library exports them."""
+    import numpy as np
+
+    W = taylor_feature_width(n_terms, d_k)
+    width = max(n_terms - 1, 1)
+    idx = np.empty((W, width), dtype=np.int32)
+    coef = np.empty(W, dtype=np.float64)
+    rc = lib().taylor_monomial_table(n_terms, d_k, idx.ctypes.data, coef.ctypes.data, W)
+    _check_nonneg(rc, "taylor_monomial_table")
+    return idx, coef
+
+
+def taylor_supported(cfg):
+    return lib().taylor_supported(ctypes.byref(cfg))
+
+
+def taylor_prefill_workspace_bytes(cfg, B, H, N):
+    return _check_nonneg(lib().taylor_prefill_workspace_bytes(ctypes.byref(cfg), B, H, N),
+                         "taylor_prefill_workspace_bytes")
+
+
+# ---- device entry points ------------------------------------------------------------------------
+
+
+def taylor_state_init(state, cfg, stream=None):
+    """Zero a [B, H, stride] float32 state tensor (an empty history)."""
+    B, H = state.shape[:2]
+    _check(lib().taylor_state_init(_ptr(state), B, H, ctypes.byref(cfg), _stream(stream, state.device)),
+           "taylor_state_init")
+
+
+def taylor_attn_prefill(q, k, v, o, state, workspace, cfg, stream=None):
+    """Causal prefill over [B, H, N, d] inputs; o [B, H, N, d_v] float32 or None; state in/out or None."""
+    B, H, N = k.shape[:3]
+    rc = lib().taylor_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), _ptr(workspace), B, H, N,
+                                   ctypes.byref(cfg), _stream(stream, k.device))
+    _check(rc, "taylor_attn_prefill")
+
+
+def taylor_attn_decode_step(q, k, v, o, state, cfg, stream=None):
+    """One decode step over [B, H, d] inputs; o [B, H, d_v] float32; state updated in place."""
+    B, H = k.shape[:2]
+    rc = lib().taylor_attn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), B, H,
+                                       ctypes.byref(cfg), _stream(stream, k.device))
+    _check(rc, "taylor_attn_decode_step")
+
+
+# ---- allocation helpers (torch owns the memory) -------------------------------------------------
+
+
+def new_state(B, H, cfg, device, stream=None):
+    """A zeroed [B, H, stride] float32 state tensor on ``device``."""
+    import torch
+
+    st = torch.empty((B, H, taylor_state_stride(cfg)), dtype=torch.float32, device=device)
+    taylor_state_init(st, cfg, stream)
+    return st
+
+
+def new_workspace(cfg, B, H, N, device):
+    """A workspace tensor of taylor_prefill_workspace_bytes() bytes (None when no workspace is needed)."""
+    import torch
+
+    n = taylor_prefill_workspace_bytes(cfg, B, H, N)
+    if n == 0:
+        return None
+    return torch.empty(((n + 15) // 16 * 16,), dtype=torch.uint8, device=device)
+
+
+def state_views(state, cfg):
+    """Views (S [B, H, W, d_v], z [B, H, W]) of a [B, H, stride] state tensor."""
+    W = taylor_feature_width(cfg.n_terms, cfg.d_k)
+    S = state[..., : W * cfg.d_v].unflatten(-1, (W, cfg.d_v))
+    z = state[..., W * cfg.d_v : W * (cfg.d_v + 1)]
+    return S, z

@@ -1,0 +1,218 @@
+// C ABI of the Taylor-attention library: validation, sizing, table export and dispatch.
+//
+// Everything here is host logic.  Validation happens before any HIP call, so
+// an invalid call returns its status without touching the device (and without
+// needing one).  The library keeps no mutable global state and never
+// allocates, frees or synchronises device memory.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/taylor_attn.h"
+#include "common.hpp"
+#include "launch.hpp"
+#include "prefill_mfma.hpp"
+
+namespace {
+
+using taylor::Shape;
+
+constexpr int kDefaultChunk = 64;
+constexpr long long kMaxGridY = 65535;  // heads are the second grid dimension
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates a config and fills `s`; returns a taylor_status.
+int check_config(const taylor_config* cfg, Shape* s) {
+  if (!cfg) return TAYLOR_ERR_INVALID_ARG;
+  if (cfg->n_terms < 1 || cfg->d_k < 1 || cfg->d_v < 1) return TAYLOR_ERR_INVALID_ARG;
+  if (cfg->in_dtype != TAYLOR_F32 && cfg->in_dtype != TAYLOR_BF16) return TAYLOR_ERR_INVALID_ARG;
+  if (cfg->chunk < 0) return TAYLOR_ERR_INVALID_ARG;
+  if (!std::isfinite(cfg->scale)) return TAYLOR_ERR_INVALID_ARG;
+  if (cfg->n_terms > taylor::kMaxTerms) return TAYLOR_ERR_UNSUPPORTED;
+  if (cfg->d_k > 4096 || cfg->d_v > 65536) return TAYLOR_ERR_INVALID_ARG;
+  const long long W = taylor::feature_width_ll(cfg->n_terms, cfg->d_k);
+  if (W <= 0 || W > 0x7fffffffLL) return TAYLOR_ERR_INVALID_ARG;
+  if (cfg->d_v % 4 != 0) return TAYLOR_ERR_UNSUPPORTED;
+  if (s) {
+    s->nt = cfg->n_terms;
+    s->dk = cfg->d_k;
+    s->dv = cfg->d_v;
+    s->dtype = cfg->in_dtype;
+    s->scale = cfg->scale;
+    s->W = W;
+    s->stride = (W * (cfg->d_v + 1) + 3) / 4 * 4;
+  }
+  return TAYLOR_OK;
+}
+
+int chunk_of(const taylor_config* cfg) { return cfg->chunk == 0 ? kDefaultChunk : cfg->chunk; }
+
+enum class Path { None, Generic, Mfma };
+
+Path prefill_path(const Shape& s, int C) {
+  if (taylor::prefill_mfma_has(s.nt, s.dk, s.dv, C)) return Path::Mfma;
+  if (taylor::prefill_generic_has(s.nt, s.dk, s.dv, C)) return Path::Generic;
+  return Path::None;
+}
+
+int supported(const taylor_config* cfg, const Shape& s) {
+  const int C = chunk_of(cfg);
+  if (C != 64 && C != 128) return TAYLOR_ERR_UNSUPPORTED;
+  if (!taylor::decode_has(s.nt, s.dk, s.dv)) return TAYLOR_ERR_UNSUPPORTED;
+  if (prefill_path(s, C) == Path::None) return TAYLOR_ERR_UNSUPPORTED;
+  return TAYLOR_OK;
+}
+
+int check_sizes(int B, int H, int N) {
+  if (B < 0 || H < 0 || N < 0) return TAYLOR_ERR_INVALID_ARG;
+  if ((long long)B * H > kMaxGridY) return TAYLOR_ERR_UNSUPPORTED;
+  return TAYLOR_OK;
+}
+
+int64_t ws_bytes(const Shape& s, int C, int BH, int N) {
+  if (BH == 0 || N == 0) return 0;
+  switch (prefill_path(s, C)) {
+    case Path::Mfma: return taylor::prefill_mfma_ws_bytes(s, BH, N, C);
+    case Path::Generic: return taylor::prefill_generic_ws_bytes(s, BH, N, C);
+    default: return TAYLOR_ERR_UNSUPPORTED;
+  }
+}
+
+int map_launch(int rc) { return rc == 0 ? TAYLOR_OK : rc == -2 ? TAYLOR_ERR_UNSUPPORTED : TAYLOR_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* taylor_status_string(int status) {
+  switch (status) {
+    case TAYLOR_OK: return "TAYLOR_OK";
+    case TAYLOR_ERR_INVALID_ARG: return "TAYLOR_ERR_INVALID_ARG: invalid argument";
+    case TAYLOR_ERR_UNSUPPORTED: return "TAYLOR_ERR_UNSUPPORTED: no kernel compiled for this configuration";
+    case TAYLOR_ERR_HIP: return "TAYLOR_ERR_HIP: HIP runtime error";
+  }
+  return "unknown taylor_status";
+}
+
+int taylor_feature_width(int n_terms, int d_k) {
+  if (n_terms < 1 || d_k < 1 || d_k > 4096 || n_terms > 64) return TAYLOR_ERR_INVALID_ARG;
+  long long w = 0;
+  for (int m = 0; m < n_terms; ++m) {
+    w += taylor::binom(d_k + m - 1, m);
+    if (w > 0x7fffffffLL || w <= 0) return TAYLOR_ERR_INVALID_ARG;
+  }
+  return (int)w;
+}
+
+int64_t taylor_state_elems(const taylor_config* cfg) {
+  Shape s;
+  const int rc = check_config(cfg, &s);
+  return rc != TAYLOR_OK ? rc : s.W * (cfg->d_v + 1);
+}
+
+int64_t taylor_state_stride(const taylor_config* cfg) {
+  Shape s;
+  const int rc = check_config(cfg, &s);
+  return rc != TAYLOR_OK ? rc : s.stride;
+}
+
+int taylor_monomial_table(int n_terms, int d_k, int32_t* idx_out, double* coef_out, size_t cap_rows) {
+  if (n_terms < 1 || n_terms > taylor::kMaxTerms) return TAYLOR_ERR_INVALID_ARG;
+  const int W = taylor_feature_width(n_terms, d_k);
+  if (W < 0) return W;
+  if (cap_rows < (size_t)W) return TAYLOR_ERR_INVALID_ARG;
+  const int width = n_terms - 1 > 1 ? n_terms - 1 : 1;
+  taylor::for_each_monomial(n_terms, d_k, [&](int a, int m, const int* t, int af) {
+    if (idx_out)
+      for (int p = 0; p < width; ++p) idx_out[(size_t)a * width + p] = p < m ? t[p] : -1;
+    if (coef_out) coef_out[a] = 1.0 / std::sqrt((double)af);
+  });
+  return W;
+}
+
+int taylor_supported(const taylor_config* cfg) {
+  Shape s;
+  const int rc = check_config(cfg, &s);
+  return rc != TAYLOR_OK ? rc : supported(cfg, s);
+}
+
+int64_t taylor_prefill_workspace_bytes(const taylor_config* cfg, int B, int H, int N) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if ((rc = supported(cfg, s)) != TAYLOR_OK) return rc;
+  if ((rc = check_sizes(B, H, N)) != TAYLOR_OK) return rc;
+  return ws_bytes(s, chunk_of(cfg), B * H, N);
+}
+
+int taylor_state_init(float* state, int B, int H, const taylor_config* cfg, hipStream_t stream) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if ((rc = check_sizes(B, H, 0)) != TAYLOR_OK) return rc;
+  if ((long long)B * H == 0) return TAYLOR_OK;
+  if (!state || !aligned16(state)) return TAYLOR_ERR_INVALID_ARG;
+  return map_launch(taylor::state_zero_launch(state, (long long)B * H * s.stride, stream));
+}
+
+int taylor_attn_prefill(const void* q, const void* k, const void* v, float* o, float* state, void* workspace, int B,
+                        int H, int N, const taylor_config* cfg, hipStream_t stream) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if ((rc = supported(cfg, s)) != TAYLOR_OK) return rc;
+  if ((rc = check_sizes(B, H, N)) != TAYLOR_OK) return rc;
+  if (!o && !state) return TAYLOR_ERR_INVALID_ARG;
+  const int BH = B * H;
+  if (BH == 0 || N == 0) return TAYLOR_OK;
+  if (!k || !v || !aligned16(k) || !aligned16(v)) return TAYLOR_ERR_INVALID_ARG;
+  if (o && (!q || !aligned16(q) || !aligned16(o))) return TAYLOR_ERR_INVALID_ARG;
+  if (state && !aligned16(state)) return TAYLOR_ERR_INVALID_ARG;
+  const int C = chunk_of(cfg);
+  const int64_t need = ws_bytes(s, C, BH, N);
+  if (need < 0) return (int)need;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return TAYLOR_ERR_INVALID_ARG;
+  if ((long long)(N + C - 1) / C > 0x7fffffffLL / 256) return TAYLOR_ERR_UNSUPPORTED;
+
+  taylor::PrefillArgs a{};
+  a.s = s;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.state = state;
+  a.ws = workspace;
+  a.BH = BH;
+  a.N = N;
+  a.C = C;
+  a.stream = stream;
+  return map_launch(prefill_path(s, C) == Path::Mfma ? taylor::prefill_mfma_launch(a)
+                                                       : taylor::prefill_generic_launch(a));
+}
+
+int taylor_attn_decode_step(const void* q, const void* k, const void* v, float* o, float* state, int B, int H,
+                            const taylor_config* cfg, hipStream_t stream) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if (!taylor::decode_has(s.nt, s.dk, s.dv)) return TAYLOR_ERR_UNSUPPORTED;
+  if ((rc = check_sizes(B, H, 1)) != TAYLOR_OK) return rc;
+  const int BH = B * H;
+  if (BH == 0) return TAYLOR_OK;
+  if (!q || !k || !v || !o || !state) return TAYLOR_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state))
+    return TAYLOR_ERR_INVALID_ARG;
+  taylor::DecodeArgs a{};
+  a.s = s;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.state = state;
+  a.BH = BH;
+  a.stream = stream;
+  return map_launch(taylor::decode_launch(a));
+}
+
+}  // extern "C"

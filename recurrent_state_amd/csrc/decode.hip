@@ -1,0 +1,171 @@
+// Decode step and state initialisation (gfx950).
+//
+// "Expanding Attention" (Huang, arXiv:2610.20637), Abstract: each of the n
+// recurrent states is updated by one rank-one outer product per token, at a
+// cost independent of the context length.  Per (b, h) one decode step is
+//     S += phi(k_t) v_t^T,  z += phi(k_t)          (rank-one update)
+//     o_t = (phi(s*q_t)^T S) / (phi(s*q_t)^T z)     (readout)
+// which streams the W x (d_v+1) float32 state once: every element is read,
+// updated and written back, and the readout is folded into the same pass, so
+// the step moves 2 * 4 * W * (d_v+1) bytes per head and is bound by HBM.
+//
+// Layout per head block: S [W][d_v] row-major, then z [W], padded to a
+// multiple of 4 floats.  A workgroup owns one head.  Thread t handles the
+// float4 column group t % (d_v/4) of rows t / (d_v/4), t / (d_v/4) + 256/(d_v/4),
+// ...: a wavefront reads 64 consecutive float4s (1 KiB) per row batch, fully
+// coalesced, and each thread keeps a fixed 4-column slice of the readout
+// numerator, reduced at the end with cross-lane shuffles and one LDS pass.
+// All row loads of a batch are issued before any update, so every thread has
+// up to 12 x 16 B in flight.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace taylor {
+namespace {
+
+constexpr int kDecodeThreads = 256;
+
+template <int NT, int DK, int DV, typename T>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                                const T* __restrict__ v, float* __restrict__ o,
+                                                                float* __restrict__ state, long long stride,
+                                                                float scale) {
+  constexpr int W = Monomials<NT, DK>::W;
+  constexpr int CG = DV / 4;  // float4 column groups per S row
+  static_assert(DV % 4 == 0 && CG <= 64 && (CG & (CG - 1)) == 0, "d_v/4 must be a power of two <= 64");
+  constexpr int RSTEP = kDecodeThreads / CG;  // rows covered by the workgroup per row slot
+  constexpr int ROWS = (W + RSTEP - 1) / RSTEP;
+  constexpr int RB = ROWS < 12 ? ROWS : 12;  // rows held in registers per batch
+  constexpr int NWAVE = kDecodeThreads / 64;
+
+  __shared__ float s_q[DK], s_k[DK];
+  __shared__ __align__(16) float s_v[DV];
+  __shared__ float s_phik[W], s_phiq[W];
+  __shared__ float4 s_red[NWAVE][CG];
+  __shared__ float s_redz[NWAVE];
+
+  const int tid = threadIdx.x;
+  const long long h = blockIdx.x;
+  if (tid < DK) {
+    s_q[tid] = scale * to_f32(q[h * DK + tid]);
+    s_k[tid] = to_f32(k[h * DK + tid]);
+  }
+  if (tid < DV) s_v[tid] = to_f32(v[h * DV + tid]);
+  __syncthreads();
+  for (int a = tid; a < W; a += kDecodeThreads) {
+    s_phiq[a] = feature_at<NT, DK>(s_q, a);
+    s_phik[a] = feature_at<NT, DK>(s_k, a);
+  }
+  __syncthreads();
+
+  float* S = state + h * stride;
+  const int cg = tid % CG;
+  const int r0 = tid / CG;
+  const float4 vv = *reinterpret_cast<const float4*>(s_v + cg * 4);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int base = r0; base < W; base += RSTEP * RB) {
+    float4 buf[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int r = base + u * RSTEP;
+      if (r < W) buf[u] = *reinterpret_cast<const float4*>(S + (long long)r * DV + cg * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int r = base + u * RSTEP;
+      if (r < W) {
+        const float4 nv = fma4(s_phik[r], vv, buf[u]);
+        acc = fma4(s_phiq[r], nv, acc);
+        *reinterpret_cast<float4*>(S + (long long)r * DV + cg * 4) = nv;
+      }
+    }
+  }
+  float accz = 0.f;
+  float* z = S + (long long)W * DV;
+  for (int a = tid; a < W; a += kDecodeThreads) {
+    const float nz = z[a] + s_phik[a];
+    z[a] = nz;
+    accz = fmaf(s_phiq[a], nz, accz);
+  }
+
+  for (int off = CG; off < 64; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+  for (int off = 1; off < 64; off <<= 1) accz += __shfl_xor(accz, off);
+  const int lane = tid & 63, wave = tid >> 6;
+  if (lane < CG) s_red[wave][lane] = acc;
+  if (lane == 0) s_redz[wave] = accz;
+  __syncthreads();
+  if (tid < CG) {
+    float4 t = s_red[0][tid];
+    float den = s_redz[0];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) {
+      t = add4(t, s_red[w][tid]);
+      den += s_redz[w];
+    }
+    *reinterpret_cast<float4*>(o + h * DV + tid * 4) = make_float4(t.x / den, t.y / den, t.z / den, t.w / den);
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, long long n4) {
+  for (long long i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += (long long)gridDim.x * 256)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <int NT, int DK, int DV>
+int decode_run(const DecodeArgs& a) {
+  const dim3 grid(a.BH), block(kDecodeThreads);
+  if (a.s.dtype == 0)
+    decode_kernel<NT, DK, DV, float><<<grid, block, 0, a.stream>>>(
+        (const float*)a.q, (const float*)a.k, (const float*)a.v, a.o, a.state, a.s.stride, a.s.scale);
+  else
+    decode_kernel<NT, DK, DV, uint16_t><<<grid, block, 0, a.stream>>>(
+        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.state, a.s.stride, a.s.scale);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+using DecodeFn = int (*)(const DecodeArgs&);
+
+template <int DK, int DV>
+DecodeFn decode_pick(int nt) {
+  switch (nt) {
+    case 1: return decode_run<1, DK, DV>;
+    case 2: return decode_run<2, DK, DV>;
+    case 3: return decode_run<3, DK, DV>;
+    case 4: return decode_run<4, DK, DV>;
+    case 5: return decode_run<5, DK, DV>;
+  }
+  return nullptr;
+}
+
+DecodeFn decode_find(int nt, int dk, int dv) {
+  if (dk == 4 && dv == 4) return decode_pick<4, 4>(nt);
+  if (dk == 8 && dv == 32) return decode_pick<8, 32>(nt);
+  if (dk == 16 && dv == 64) return decode_pick<16, 64>(nt);
+  if (dk == 16 && dv == 128) return decode_pick<16, 128>(nt);
+  return nullptr;
+}
+
+}  // namespace
+
+bool decode_has(int nt, int dk, int dv) { return decode_find(nt, dk, dv) != nullptr; }
+
+int decode_launch(const DecodeArgs& a) {
+  DecodeFn f = decode_find(a.s.nt, a.s.dk, a.s.dv);
+  return f ? f(a) : -2;
+}
+
+int state_zero_launch(float* state, long long count, hipStream_t stream) {
+  const long long n4 = count / 4;
+  long long blocks = (n4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(reinterpret_cast<float4*>(state), n4);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // namespace taylor

@@ -1,0 +1,176 @@
+"""C-ABI checks that need no GPU: exports, host-only queries, table export, argument validation.
+
+No call here reaches a kernel launch: every call either is host-only or fails
+validation first (fake pointers are only ever passed to calls that are
+rejected for another argument), or is a documented no-op (N == 0, B*H == 0).
+"""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import recurrent_state_amd as rs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "taylor_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rs.LIB_PATH), reason="library not built")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\*?\s+\*?(taylor_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    declared = _header_functions()
+    assert len(declared) == 10
+    assert sorted(rs.EXPORTS) == declared
+    out = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(taylor_[a-z_0-9]+)$", out, re.M))
+    assert set(declared) <= exported
+    L = rs.lib()
+    for name in declared:
+        assert getattr(L, name) is not None
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3):
+        assert rs.taylor_status_string(st).startswith("TAYLOR_")
+    assert "unknown" in rs.taylor_status_string(7)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("d", [1, 2, 4, 16])
+def test_feature_width(n, d):
+    assert rs.taylor_feature_width(n, d) == sum(math.comb(d + m - 1, m) for m in range(n))
+
+
+def test_feature_width_rejects():
+    L = rs.lib()
+    assert L.taylor_feature_width(0, 16) == rs.TAYLOR_ERR_INVALID_ARG
+    assert L.taylor_feature_width(3, 0) == rs.TAYLOR_ERR_INVALID_ARG
+    assert L.taylor_feature_width(40, 4096) == rs.TAYLOR_ERR_INVALID_ARG  # overflows int
+
+
+def test_state_size_and_stride():
+    cfg = rs.config(3, 16, 64)
+    assert rs.taylor_state_elems(cfg) == 9945  # the Abstract's elements per head
+    assert rs.taylor_state_stride(cfg) == 9948
+    assert rs.taylor_state_stride(rs.config(3, 4, 4)) == 76
+    for n in range(1, 6):
+        c = rs.config(n, 16, 64)
+        assert rs.taylor_state_stride(c) % 4 == 0 and rs.taylor_state_stride(c) >= rs.taylor_state_elems(c)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("d", [1, 2, 3, 4, 8, 16])
+def test_monomial_table_bit_exact_against_oracle(n, d):
+    idx, coef = rs.taylor_monomial_table(n, d)
+    assert np.array_equal(idx, oracle.index_table(n, d))
+    ref = oracle.coef_table(n, d)
+    assert coef.dtype == np.float64
+    assert np.array_equal(coef.view(np.uint64), ref.view(np.uint64))
+
+
+def test_monomial_table_capacity_checked():
+    L = rs.lib()
+    idx = np.full((200, 2), 7, dtype=np.int32)
+    assert L.taylor_monomial_table(3, 16, idx.ctypes.data, None, 152) == rs.TAYLOR_ERR_INVALID_ARG
+    assert np.all(idx == 7)  # nothing written
+    assert L.taylor_monomial_table(3, 16, idx.ctypes.data, None, 153) == 153
+    assert L.taylor_monomial_table(6, 16, idx.ctypes.data, None, 200) == rs.TAYLOR_ERR_INVALID_ARG
+
+
+def test_supported_configs():
+    for n in range(1, 6):
+        for dt in (rs.TAYLOR_F32, rs.TAYLOR_BF16):
+            for C in (0, 64, 128):
+                assert rs.taylor_supported(rs.config(n, 16, 64, C, 1.0, dt)) == rs.TAYLOR_OK
+                assert rs.taylor_supported(rs.config(n, 4, 4, C, 1.0, dt)) == rs.TAYLOR_OK
+    assert rs.taylor_supported(rs.config(3, 16, 64, 96)) == rs.TAYLOR_ERR_UNSUPPORTED
+    assert rs.taylor_supported(rs.config(3, 16, 6)) == rs.TAYLOR_ERR_UNSUPPORTED
+    assert rs.taylor_supported(rs.config(6, 16, 64)) == rs.TAYLOR_ERR_UNSUPPORTED
+    assert rs.taylor_supported(rs.config(3, 5, 64)) == rs.TAYLOR_ERR_UNSUPPORTED
+    assert rs.taylor_supported(rs.config(0, 16, 64)) == rs.TAYLOR_ERR_INVALID_ARG
+    assert rs.taylor_supported(rs.config(3, 16, 64, -1)) == rs.TAYLOR_ERR_INVALID_ARG
+    assert rs.taylor_supported(rs.config(3, 16, 64, 0, float("nan"))) == rs.TAYLOR_ERR_INVALID_ARG
+    assert rs.taylor_supported(rs.config(3, 16, 64, 0, 1.0, 5)) == rs.TAYLOR_ERR_INVALID_ARG
+    assert rs.lib().taylor_supported(None) == rs.TAYLOR_ERR_INVALID_ARG
+
+
+def test_workspace_bytes():
+    cfg = rs.config(3, 16, 64, 64)
+    assert rs.taylor_prefill_workspace_bytes(cfg, 1, 8, 0) == 0
+    assert rs.taylor_prefill_workspace_bytes(cfg, 0, 8, 4096) == 0
+    assert rs.taylor_prefill_workspace_bytes(cfg, 1, 8, 4096) > 0
+    L = rs.lib()
+    assert L.taylor_prefill_workspace_bytes(ctypes.byref(cfg), -1, 8, 64) == rs.TAYLOR_ERR_INVALID_ARG
+    assert L.taylor_prefill_workspace_bytes(ctypes.byref(cfg), 1, 8, -5) == rs.TAYLOR_ERR_INVALID_ARG
+    assert L.taylor_prefill_workspace_bytes(ctypes.byref(cfg), 300, 300, 64) == rs.TAYLOR_ERR_UNSUPPORTED
+
+
+FAKE = 1 << 20  # an aligned address; only ever passed to calls rejected for another reason
+MIS = FAKE + 4  # misaligned
+
+
+def _prefill(q, k, v, o, st, ws, B, H, N, cfg):
+    return rs.lib().taylor_attn_prefill(q, k, v, o, st, ws, B, H, N, ctypes.byref(cfg) if cfg else None, None)
+
+
+def test_prefill_validation():
+    cfg = rs.config(3, 16, 64, 64)
+    E = rs.TAYLOR_ERR_INVALID_ARG
+    assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, None) == E
+    assert _prefill(FAKE, FAKE, FAKE, None, None, FAKE, 1, 1, 64, cfg) == E  # nothing to produce
+    assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 1, 64, cfg) == E
+    assert _prefill(FAKE, None, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, cfg) == E
+    assert _prefill(FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 1, 64, cfg) == E
+    assert _prefill(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, cfg) == E  # q needed for outputs
+    assert _prefill(MIS, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, cfg) == E
+    assert _prefill(FAKE, MIS, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, cfg) == E
+    assert _prefill(FAKE, FAKE, FAKE, MIS, FAKE, FAKE, 1, 1, 64, cfg) == E
+    assert _prefill(FAKE, FAKE, FAKE, FAKE, MIS, FAKE, 1, 1, 64, cfg) == E
+    assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, cfg) == E  # workspace required
+    assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, MIS, 1, 1, 64, cfg) == E
+    assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, rs.config(3, 16, 64, 96)) == rs.TAYLOR_ERR_UNSUPPORTED
+    assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, rs.config(7, 16, 64)) == rs.TAYLOR_ERR_UNSUPPORTED
+    # documented no-ops (no launch): N == 0, B*H == 0
+    assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 0, cfg) == rs.TAYLOR_OK
+    assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, cfg) == rs.TAYLOR_OK
+
+
+def test_decode_validation():
+    cfg = rs.config(3, 16, 64)
+    L = rs.lib()
+    E = rs.TAYLOR_ERR_INVALID_ARG
+
+    def dec(q, k, v, o, st, B, H, c=cfg):
+        return L.taylor_attn_decode_step(q, k, v, o, st, B, H, ctypes.byref(c) if c else None, None)
+
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, None) == E
+    for i in range(5):
+        args = [FAKE] * 5
+        args[i] = None
+        assert dec(*args, 1, 1) == E
+        args[i] = MIS
+        assert dec(*args, 1, 1) == E
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 1) == E
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, rs.config(3, 16, 60)) == rs.TAYLOR_ERR_UNSUPPORTED
+    assert dec(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 16) == rs.TAYLOR_OK
+
+
+def test_state_init_validation():
+    L = rs.lib()
+    cfg = rs.config(3, 16, 64)
+    assert L.taylor_state_init(None, 1, 1, ctypes.byref(cfg), None) == rs.TAYLOR_ERR_INVALID_ARG
+    assert L.taylor_state_init(MIS, 1, 1, ctypes.byref(cfg), None) == rs.TAYLOR_ERR_INVALID_ARG
+    assert L.taylor_state_init(FAKE, 1, 1, None, None) == rs.TAYLOR_ERR_INVALID_ARG
+    assert L.taylor_state_init(FAKE, -2, 1, ctypes.byref(cfg), None) == rs.TAYLOR_ERR_INVALID_ARG
+    assert L.taylor_state_init(None, 0, 3, ctypes.byref(cfg), None) == rs.TAYLOR_OK

@@ -1,0 +1,155 @@
+"""GPU parity of taylor_attn_prefill against the float64 oracle (same rounded inputs).
+
+Bars: 1e-5 relative per output row for float32 inputs, 3e-3 for bfloat16
+inputs; rows whose normaliser is ~0 (possible only for even n with raw scores)
+are skipped.  Sizes span several chunks and a ragged tail.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import recurrent_state_amd as rs
+import synth
+from gpu_util import announce, row_rel_err, run_prefill, tol_for
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _oracle(x, n, scale):
+    return oracle.batched(oracle.truncated_attention, x.q64, x.k64, x.v64, n, scale)
+
+
+def _check(x, n, scale, C, dtype, label):
+    cfg = rs.config(n, x.q.shape[-1], x.v.shape[-1], C, scale, rs.TAYLOR_BF16 if dtype == "bf16" else rs.TAYLOR_F32)
+    announce(label, f"n={n} C={C} dtype={dtype} shape={x.q.shape}/{x.v.shape} scale={scale}")
+    o, _ = run_prefill(x, cfg, DEV)
+    ref, den = _oracle(x, n, scale)
+    err, rows = row_rel_err(o.cpu().numpy(), ref, den)
+    assert rows > 0
+    assert err <= tol_for(dtype), f"{label}: rel err {err:.3e}"
+    return err
+
+
+@pytest.mark.parametrize("C", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tiny_config(C, dtype):
+    # B=1, H=1, N=256, d_k=d_v=4, n=3, unit-norm q, k.
+    x = synth.make_qkv(1, 1, 1, 256, 4, 4, dtype)
+    _check(x, 3, 1.0, C, dtype, "tiny")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_orders_d16(n, dtype):
+    x = synth.make_qkv(20 + n, 1, 2, 700, 16, 64, dtype)
+    _check(x, n, 1.0, 64, dtype, "orders")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_orders_small_heads(n):
+    x = synth.make_qkv(30 + n, 2, 3, 333, 4, 4)
+    _check(x, n, 1.0, 128, "f32", "small-heads")
+
+
+def test_d8_dv32():
+    x = synth.make_qkv(40, 1, 2, 500, 8, 32)
+    _check(x, 3, 1.0, 64, "f32", "d8-dv32")
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 129, 1000])
+@pytest.mark.parametrize("C", [64, 128])
+def test_ragged_lengths(N, C):
+    x = synth.make_qkv(41, 1, 2, N, 16, 64)
+    _check(x, 3, 1.0, C, "f32", "ragged")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_raw_scores(n):
+    # Un-normalised q, k ~ N(0,1) with scale 1/sqrt(d_k): scores leave [-1, 1].
+    x = synth.make_qkv(50 + n, 1, 2, 600, 16, 64, unit_norm=False)
+    _check(x, n, 0.25, 64, "f32", "raw")
+
+
+def test_prefill_fp32_config():
+    # B=1, H=8, N=4096, d_k=16, d_v=64, n=3, C=64, float32: every output row against the oracle.
+    x = synth.make_qkv(2, 1, 8, 4096, 16, 64)
+    err = _check(x, 3, 1.0, 64, "f32", "prefill-fp32")
+    soft = oracle.batched(oracle.softmax_attention, x.q64, x.k64, x.v64)[0]
+    ref = _oracle(x, 3, 1.0)[0]
+    print(f"rel err vs oracle {err:.2e}; truncated (n=3) vs softmax max-abs/max {np.max(np.abs(ref - soft)) / np.max(np.abs(soft)):.2e}")
+
+
+def test_resume_from_state():
+    # prefill(N1) then prefill(N2 | state) equals prefill(N1 + N2) (chunk additivity, Abstract).
+    import torch
+
+    n, N1, N2 = 3, 700, 517
+    x = synth.make_qkv(60, 1, 3, N1 + N2, 16, 64)
+    cfg = rs.config(n, 16, 64, 64)
+    announce("resume", N1, N2)
+    q, k, v = x.torch(DEV)
+    st = rs.new_state(1, 3, cfg, DEV)
+    o1 = torch.empty((1, 3, N1, 64), device=DEV)
+    o2 = torch.empty((1, 3, N2, 64), device=DEV)
+    parts = [t.contiguous() for t in (q[:, :, :N1], k[:, :, :N1], v[:, :, :N1])]
+    rs.taylor_attn_prefill(*parts, o1, st, rs.new_workspace(cfg, 1, 3, N1, DEV), cfg)
+    parts = [t.contiguous() for t in (q[:, :, N1:], k[:, :, N1:], v[:, :, N1:])]
+    rs.taylor_attn_prefill(*parts, o2, st, rs.new_workspace(cfg, 1, 3, N2, DEV), cfg)
+    ref, den = _oracle(x, n, 1.0)
+    err, _ = row_rel_err(torch.cat([o1, o2], dim=2).cpu().numpy(), ref, den)
+    assert err <= 1e-5
+    # and the final state is the state of all N1 + N2 tokens
+    S, z = rs.state_views(st, cfg)
+    for h in range(3):
+        full = oracle.state(x.k64[0, h], x.v64[0, h], n)
+        got = np.concatenate([S[0, h].cpu().numpy(), z[0, h].cpu().numpy()[:, None]], axis=1)
+        assert np.max(np.abs(got - full)) <= 1e-5 * np.max(np.abs(full))
+
+
+@pytest.mark.parametrize("n", [1, 3, 5])
+def test_state_only_pass_gives_the_state(n):
+    x = synth.make_qkv(61, 2, 2, 3000, 16, 64)
+    cfg = rs.config(n, 16, 64, 128)
+    announce("state-only", n)
+    st = rs.new_state(2, 2, cfg, DEV)
+    q, k, v = x.torch(DEV)
+    rs.taylor_attn_prefill(None, k, v, None, st, rs.new_workspace(cfg, 2, 2, 3000, DEV), cfg)
+    S, z = rs.state_views(st, cfg)
+    stride = rs.taylor_state_stride(cfg)
+    W = rs.taylor_feature_width(n, 16)
+    pad = st[..., W * 65 : stride].cpu().numpy()
+    assert np.all(pad == 0)
+    for b in range(2):
+        for h in range(2):
+            full = oracle.state(x.k64[b, h], x.v64[b, h], n)
+            got = np.concatenate([S[b, h].cpu().numpy(), z[b, h].cpu().numpy()[:, None]], axis=1)
+            assert np.max(np.abs(got - full)) <= 1e-5 * np.max(np.abs(full))
+
+
+def test_chunk_size_invariance_and_repeatability():
+    x = synth.make_qkv(62, 1, 4, 2000, 16, 64)
+    outs = {}
+    for C in (64, 128):
+        cfg = rs.config(3, 16, 64, C)
+        announce("chunk", C)
+        o1, _ = run_prefill(x, cfg, DEV)
+        o2, _ = run_prefill(x, cfg, DEV)
+        a, b = o1.cpu().numpy(), o2.cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "not bitwise repeatable"
+        outs[C] = a
+    err, _ = row_rel_err(outs[64], outs[128])
+    assert err <= 1e-5
+
+
+def test_noop_calls_leave_memory_untouched():
+    import torch
+
+    cfg = rs.config(3, 16, 64, 64)
+    st = torch.full((1, 2, rs.taylor_state_stride(cfg)), 7.0, device=DEV)
+    e = torch.empty((1, 2, 0, 16), device=DEV)
+    ev = torch.empty((1, 2, 0, 64), device=DEV)
+    rs.taylor_attn_prefill(e, e, ev, ev, st, None, cfg)
+    torch.cuda.synchronize()
+    assert bool((st == 7.0).all())
