@@ -1,0 +1,268 @@
+"""Benchmark of the Taylor-attention hot path on one MI355X.
+
+One step = one pass of the whole path:
+  * taylor_state_init + taylor_attn_prefill over one batch of B=4 x H=16 x N=8192
+    bfloat16 tokens (d_k=16, d_v=64, n=3, chunk 128), float32 outputs and final state;
+  * 1,000 taylor_attn_decode_step calls on 64 sequences x 16 heads whose float32
+    states (153 x 65 per head) were built by a state-only prefill of a seeded
+    65,536-token prefix (setup, untimed).  The 1,000 decode launches are replayed
+    from one HIP graph (captured once; inputs for all 1,000 steps are resident).
+Inputs are seeded synthetic data (synth module): unit-norm Gaussian q, k, Gaussian v.
+
+Reported: prefill tokens/s (B*N / prefill time) as `value`, decode microseconds per
+token (per decode step of all 64 sequences), each against its roofline; the oracle's
+CPU throughput on a bounded sample of the same prefill workload; and, in `roofline`,
+the dominant kernel (the decode step: 1,000 launches per step) measured with HIP
+events on the stream it runs on.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tok/s + decode µs/token (n=3,d_k=16,d_v=64), % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 matrix
+
+# Prefill workload: B=4, H=16, N=8192, bf16 inputs, fp32 states/outputs, chunk 128.
+PB, PH, PN, DK, DV, NT, PC = 4, 16, 8192, 16, 64, 3, 128
+# Decode workload: 64 sequences x 16 heads, 65,536-token prefix, 1,000 steps.
+DB, DH, DPREFIX, DSTEPS = 64, 16, 65536, 1000
+
+W = 153  # feature width at n=3, d_k=16
+STATE_BYTES = W * (DV + 1) * 4  # 39,780 B per head
+# Algorithmic bytes per decode head-step: state read + written, q, k, v read, o written (fp32).
+DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES + 4 * (DK + DK + DV + DV)
+# Algorithmic prefill per token-head: q, k, v (bf16) in, o (fp32) out.
+PREFILL_BYTES_PER_TOKEN_HEAD = 2 * (DK + DK + DV) + 4 * DV
+# Algorithmic prefill flops per token-head at C=128 (unpadded widths, causal half of each chunk):
+# chunk-state GEMM 2*W*(d_v+1) + readout GEMM 2*W*(d_v+1) + intra scores 2*d_k*(C+1)/2 + intra PV 2*(d_v+1)*(C+1)/2.
+PREFILL_FLOPS_PER_TOKEN_HEAD = 2 * W * (DV + 1) * 2 + DK * (PC + 1) + (DV + 1) * (PC + 1)
+
+DECODE_KERNEL_SOURCE = os.path.join(ROOT, "recurrent_state_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, source):
+    """Per-launch HBM bytes from committed rocprofv3 counters, or None if absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha") != _sha(source):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(x, budget_s=12.0):
+    """The float64 oracle on whole heads of the prefill workload until the budget is spent."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    heads = 0
+    t0 = time.perf_counter()
+    for b in range(PB):
+        for h in range(PH):
+            oracle.truncated_attention(x.q64[b, h], x.k64[b, h], x.v64[b, h], NT, 1.0)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_head = dt / heads
+    cores = blas_threads or len(os.sched_getaffinity(0))
+    return {
+        "value": PN / (per_head * PH),  # B*N tokens need B*H heads: (B*N) / (per_head * B*H)
+        "unit": "tok/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{heads} of {PB * PH} (b,h) slices of the prefill workload, full N={PN} each, "
+                  f"float64 direct O(N^2) oracle, {dt:.1f} s; extrapolated linearly in heads",
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "blas_threads": blas_threads,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=DSTEPS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager-decode", action="store_true", help="launch decode steps one by one (no graph)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is data-parallel "
+              f"over (batch, head); see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import recurrent_state_amd as rs
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = rs.lib()
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
+
+    # ---- prefill workload ----
+    x = synth.make_qkv(3, PB, PH, PN, DK, DV, synth.BF16)
+    pq, pk, pv = x.torch(dev)
+    pcfg = rs.config(NT, DK, DV, PC, 1.0, rs.TAYLOR_BF16)
+    po = torch.empty((PB, PH, PN, DV), dtype=torch.float32, device=dev)
+    pstate = torch.empty((PB, PH, rs.taylor_state_stride(pcfg)), dtype=torch.float32, device=dev)
+    pws = rs.new_workspace(pcfg, PB, PH, PN, dev)
+    log("prefill inputs ready")
+
+    # ---- decode workload: states from a 65,536-token prefix ----
+    dcfg = rs.config(NT, DK, DV, PC, 1.0, rs.TAYLOR_F32)
+    dstate = rs.new_state(DB, DH, dcfg, dev)
+    _, kpre, vpre = synth.device_qkv(4, DB, DH, DPREFIX, DK, DV, dev, need_q=False)
+    ws = rs.new_workspace(dcfg, DB, DH, DPREFIX, dev)
+    rs.taylor_attn_prefill(None, kpre, vpre, None, dstate, ws, dcfg)
+    torch.cuda.synchronize()
+    del kpre, vpre, ws
+    torch.cuda.empty_cache()
+    T = args.decode_steps
+    dq, dk_, dv_ = synth.device_qkv(4, T, DB * DH, 1, DK, DV, dev, salt=1)
+    dq, dk_, dv_ = (t.view(T, DB, DH, -1) for t in (dq, dk_, dv_))
+    dout = torch.empty((T, DB, DH, DV), dtype=torch.float32, device=dev)
+    log("decode states and inputs ready")
+
+    cfgp = __import__("ctypes").byref(dcfg)
+
+    def decode_all(stream_handle):
+        f = lib.taylor_attn_decode_step
+        qp, kp, vp, op, sp = dq.data_ptr(), dk_.data_ptr(), dv_.data_ptr(), dout.data_ptr(), dstate.data_ptr()
+        qs, vs = DB * DH * DK * 4, DB * DH * DV * 4
+        for t in range(T):
+            rc = f(qp + t * qs, kp + t * qs, vp + t * vs, op + t * vs, sp, DB, DH, cfgp, stream_handle)
+            if rc:
+                raise rs.TaylorError(rc, "taylor_attn_decode_step")
+
+    graph = None
+    if not args.eager_decode:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            decode_all(torch.cuda.current_stream().cuda_stream)  # warm-up outside capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decode_all(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        log("decode graph captured")
+
+    def step(evs):
+        cur = torch.cuda.current_stream()
+        evs[0].record(cur)
+        rs.taylor_state_init(pstate, pcfg)
+        rs.taylor_attn_prefill(pq, pk, pv, po, pstate, pws, pcfg)
+        evs[1].record(cur)
+        if graph is not None:
+            graph.replay()
+        else:
+            decode_all(cur.cuda_stream)
+        evs[2].record(cur)
+
+    for _ in range(args.warmup):
+        step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    step_ms = sum(e[0].elapsed_time(e[2]) for e in events) / args.steps
+    assert bool(torch.isfinite(po).all()) and bool(torch.isfinite(dout).all())
+
+    decode_launch_s = dec_ms / 1e3 / T
+    decode_bytes = DB * DH * DECODE_BYTES_PER_HEAD
+    dec_gbs = decode_bytes / decode_launch_s / 1e9
+    prefill_s = pre_ms / 1e3
+    prefill_tok_s = PB * PN / prefill_s
+    p_bytes = PB * PH * PN * PREFILL_BYTES_PER_TOKEN_HEAD
+    p_flops = PB * PH * PN * PREFILL_FLOPS_PER_TOKEN_HEAD
+    traffic = measured_traffic("decode_step", DECODE_KERNEL_SOURCE)
+
+    out = {
+        "metric": METRIC,
+        "value": prefill_tok_s,
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded unit-norm Gaussian q,k; Gaussian v)",
+        "config": {
+            "workload": f"prefill B{PB}xH{PH}xN{PN} bf16 in, fp32 state/out, C={PC}; "
+                        f"decode {DB} seq x {DH} heads, fp32 state, {DPREFIX}-token prefix, {T} steps/step",
+            "n_terms": NT, "d_k": DK, "d_v": DV, "global_batch": PB, "seq_len": PN,
+            "parallelism": "none (1 GPU)",
+        },
+        "decode_us_per_token": dec_ms * 1e3 / T,
+        "decode_tokens_per_s": DB * T / (dec_ms / 1e3),
+        "decode_launch": "hip graph of %d steps" % T if graph is not None else "eager",
+        "prefill_ms": pre_ms,
+        "prefill": {
+            "bound": "hbm", "achieved_GBs": p_bytes / prefill_s / 1e9, "peak_GBs": HBM_PEAK_GBS,
+            "frac_hbm": p_bytes / prefill_s / 1e9 / HBM_PEAK_GBS,
+            "achieved_TFLOPs": p_flops / prefill_s / 1e12, "bf16_peak_TFLOPs": BF16_PEAK_TFLOPS,
+            "frac_bf16_mfma": p_flops / prefill_s / 1e12 / BF16_PEAK_TFLOPS,
+            "alg_bytes": p_bytes, "alg_flops": p_flops,
+        },
+        "roofline": {
+            "kernel": "decode_kernel<3,16,64,float>",
+            "bound": "hbm",
+            "achieved": dec_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": dec_gbs / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "alg_bytes_per_launch": decode_bytes,
+            "avg_launch_us": decode_launch_s * 1e6,
+        },
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
