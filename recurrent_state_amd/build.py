@@ -32,7 +32,7 @@ def hipcc():
 
 def flags():
     return [
-        "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+        "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE, "-Wall", "-Wno-unused-function",
     ]

@@ -40,6 +40,12 @@ bool decode_has(int nt, int dk, int dv);
 
 int state_zero_launch(float* state, long long count, hipStream_t stream);
 
+// Exclusive prefix over `nseg` consecutive state blocks per head in `ws` (seeded with `state` when
+// non-null, else zero); the total is written to `state` when non-null.  Only the first `elems`
+// floats of each block are touched.
+int seg_scan_launch(float* ws, float* state, int BH, int nseg, long long stride, long long elems, bool write_prefix,
+                    hipStream_t stream);
+
 // Portable prefill path (any compiled (n, d_k, d_v), chunk 64 or 128), VALU float32.
 bool prefill_generic_has(int nt, int dk, int dv, int C);
 long long prefill_generic_ws_bytes(const Shape& s, int BH, int N, int C);

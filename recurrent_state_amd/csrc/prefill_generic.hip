@@ -238,6 +238,17 @@ __global__ __launch_bounds__(kThreads) void readout_kernel(const T* __restrict__
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+}  // namespace
+
+int seg_scan_launch(float* ws, float* state, int BH, int nseg, long long stride, long long elems, bool write_prefix,
+                    hipStream_t stream) {
+  seg_scan_kernel<<<dim3(cdiv(elems, kThreads), BH), dim3(kThreads), 0, stream>>>(ws, state, nseg, stride, elems,
+                                                                                  write_prefix ? 1 : 0);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+namespace {
+
 // Segments for a state-only pass: enough workgroups to fill the chip, never more than the chunks.
 int state_only_segments(int BH, int nfb, int nchunk) {
   long long want = (4096 + (long long)BH * nfb - 1) / ((long long)BH * nfb);
@@ -260,9 +271,7 @@ int generic_run(const PrefillArgs& a) {
   seg_state_kernel<NT, DK, DV, T><<<dim3(nseg_used, a.BH, nfb), dim3(kThreads), 0, a.stream>>>(
       (const T*)a.k, (const T*)a.v, ws, a.N, L, nseg_used, a.s.stride);
   if (hipGetLastError() != hipSuccess) return -3;
-  seg_scan_kernel<<<dim3(cdiv(elems, kThreads), a.BH), dim3(kThreads), 0, a.stream>>>(
-      ws, a.state, nseg_used, a.s.stride, elems, a.o != nullptr);
-  if (hipGetLastError() != hipSuccess) return -3;
+  if (seg_scan_launch(ws, a.state, a.BH, nseg_used, a.s.stride, elems, a.o != nullptr, a.stream)) return -3;
   if (a.o) {
     if (a.C == 64)
       readout_kernel<NT, DK, DV, 64, T><<<dim3(nchunk, a.BH), dim3(kThreads), 0, a.stream>>>(
