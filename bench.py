@@ -112,7 +112,22 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=DSTEPS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager-decode", action="store_true", help="launch decode steps one by one (no graph)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 3 times (scale reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is data-parallel "
               f"over (batch, head); see the sharding notes).", file=sys.stderr)

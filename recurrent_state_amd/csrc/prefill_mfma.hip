@@ -3,33 +3,37 @@
 // "Expanding Attention" (Huang, arXiv:2610.20637), Abstract: with the kernel
 // exp(s) truncated to n Taylor terms and each term factorised into symmetric
 // tensor-power features, the causal history is n additive states, so prefill
-// is chunk-local work plus a scan of chunk states.  Per chunk c of C tokens:
-//     O_c   = phi(s Q_c) S_{<c}  +  tril(K_n(s Q_c K_c^T)) V_c      (numerators)
-//     den_c = phi(s Q_c) z_{<c}  +  rowsum(tril(K_n(s Q_c K_c^T)))
-//     S    += phi(K_c)^T V_c,   z += phi(K_c)^T 1
+// is chunk-local work plus a scan of chunk states.  Per chunk c of C tokens,
+// with V1 = [V | 1] (the value columns plus the normaliser column):
+//     O_c  = phi(s Q_c) S_{<c}  +  tril(K_n(s Q_c K_c^T)) V1_c     ([numerators | denominator])
+//     S   += phi(K_c)^T V1_c                                        (state and normaliser z)
+//     o    = O_c[:, :d_v] / O_c[:, d_v]
 //
-// Work split (one workgroup = 4 wavefronts walks a segment of consecutive chunks):
-//   * The running state S_{<c} (W_p x 64 floats, W_p = W rounded up to 32) lives
-//     in MFMA accumulator registers for the whole segment.  Wave w owns value
-//     columns 16w..16w+15, so neither the state update nor the readout needs a
-//     cross-wave reduction.
-//   * Readout phi(sQ) S: the accumulator tile layout (4 consecutive feature rows
-//     per lane) is used directly as the MFMA A operand.  The k-slot order this
-//     implies is absorbed by storing phi(sQ) in LDS with the same permutation of
-//     features inside each 32-block, so S never round-trips through LDS.  For
-//     bfloat16 inputs S is split as S = hi + lo (two bfloat16 MFMAs) so that the
-//     state keeps float32 accuracy in the readout.
-//   * Intra-chunk scores s Q K^T use the 16x16x16 MFMA with the key block as rows;
-//     its accumulator layout is exactly the B-operand layout of the next MFMA
-//     (V^T times scores), so scores go through registers -> LDS once and are
-//     shared by the 4 waves.  Horner's rule for K_n and the causal mask are
+// Work split: one workgroup of 5 wavefronts walks a segment of consecutive chunks.
+//   * Waves 0..3 own value columns 16w..16w+15; wave 4 owns the normaliser
+//     column (a 16-wide tile whose first column is all ones and the rest zero),
+//     so z and every denominator come out of the same MFMAs as the numerators
+//     and no wave needs a cross-wave reduction.
+//   * The running state S_{<c} (W_p x 16 floats per wave, W_p = W rounded up to
+//     32) lives in MFMA accumulator registers for the whole segment.  Its tile
+//     layout (4 consecutive feature rows per lane) is used directly as the A
+//     operand of the readout phi(sQ) S; the k-slot order this implies is
+//     absorbed by storing phi(sQ) in LDS with the same permutation of features
+//     inside each 32-block, so S never round-trips through LDS.  For bfloat16
+//     inputs S is split as S = hi + lo (two bfloat16 MFMAs) so that the state
+//     keeps float32 accuracy in the readout.
+//   * Intra-chunk scores s Q K^T use the 16x16x16 MFMA with the key block as
+//     rows; its accumulator layout is exactly the B-operand layout of the next
+//     MFMA (V1^T times scores), so scores go through registers -> LDS once and
+//     are shared by the 5 waves.  Horner's rule for K_n and the causal mask are
 //     applied in registers.
-//   * The normaliser z and the inter-chunk denominator are float32 vector work
-//     (z is a column sum of phi(K), the denominator a dot product per token).
+//   * Chunk c+1's inputs are loaded into registers while chunk c is computed,
+//     and chunk c's outputs are stored after chunk c+1's first barrier (which is
+//     also the barrier that publishes the denominators of chunk c).
 //
 // Two launches of this kernel bracket the scan: a state-only pass writes each
-// segment's dS to the workspace, the scan turns those into exclusive prefixes,
-// and the readout pass starts each segment from its prefix.
+// segment's (S, z) increment to the workspace, the scan turns those into
+// exclusive prefixes, and the readout pass starts each segment from its prefix.
 //
 // bfloat16 inputs: q, k, v, phi and the scores enter the MFMAs as bfloat16;
 // S, z, all accumulation and the outputs are float32.  float32 inputs: every
@@ -48,7 +52,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kDK = 16, kDV = 64, kThreads = 256;
+constexpr int kDK = 16, kDV = 64;
+constexpr int kValueWaves = kDV / 16;    // waves owning 16 value columns each
+constexpr int kWaves = kValueWaves + 1;  // plus the normaliser wave
+constexpr int kThreads = 64 * kWaves;
 
 template <int NT>
 struct Geo {
@@ -57,6 +64,16 @@ struct Geo {
   static constexpr int WP = (W + 31) / 32 * 32;  // features padded to 32-wide MFMA k-blocks
   static constexpr int NAT = WP / 16;            // 16-row feature tiles of the state
   static constexpr int NKB = WP / 32;            // 32-wide feature k-blocks
+};
+
+// How the feature work of a chunk is split over the waves.
+template <int NT, bool BF16>
+struct Split {
+  static constexpr int WP = Geo<NT>::WP;
+  static constexpr int RK = ((WP + kWaves - 1) / kWaves + 7) / 8 * 8;  // phi(K)^T rows per wave
+  static constexpr int GQ = BF16 ? 8 : 4;                              // phi(sQ) slots per 16-byte store
+  static constexpr int NG = WP / GQ;                                   // stores per phi(sQ) row
+  static constexpr int RG = (NG + kWaves - 1) / kWaves;               // stores per wave
 };
 
 // Feature A of x (float32 registers), coordinates and coefficient fixed at compile time.
@@ -85,12 +102,8 @@ __host__ __device__ constexpr int slot_feature_bf16(int s) {
   const int kb = s / 32, r32 = s % 32, g = r32 / 8, r = r32 % 8;
   return 32 * kb + (r < 4 ? g * 4 + r : 16 + g * 4 + (r - 4));
 }
-template <bool BF16>
-__host__ __device__ constexpr int slot_feature(int s) {
-  return BF16 ? slot_feature_bf16(s) : s;
-}
 
-template <int NT, int CS, bool BF16>
+template <int NT, int CS, bool BF16, bool READOUT>
 struct Smem {
   using E = typename std::conditional<BF16, __bf16, float>::type;
   static constexpr int WP = Geo<NT>::WP;
@@ -99,17 +112,16 @@ struct Smem {
   static constexpr int LK = CS + PADE;       // phi(K)^T and V^T row stride
   static constexpr int NIT = CS / 16;
   static constexpr int NPAIR = NIT * (NIT + 1) / 2;
+  static constexpr int RQ = READOUT ? CS : 1;  // readout-only arrays collapse in the state pass
+  static constexpr int RP = READOUT ? NPAIR : 1;
   using ATile = typename std::conditional<BF16, bf16x4, f32x4>::type;
-  alignas(16) E q[CS][kDK];
   alignas(16) E k[CS][kDK];
   alignas(16) E vt[kDV][LK];
-  alignas(16) E phiq[CS][LQ];
   alignas(16) E phikt[WP][LK];
-  alignas(16) ATile a[NPAIR][64];  // score tiles in MFMA B-operand lane order
-  float den_intra[NPAIR][16];
-  float den_part[kThreads / CS][CS];
-  float z[2][WP];  // running normaliser, in phi(sQ) slot order, double-buffered per chunk
-  float den[CS];
+  alignas(16) E q[RQ][kDK];
+  alignas(16) E phiq[RQ][LQ];
+  alignas(16) ATile a[RP][64];  // score tiles in MFMA B-operand lane order
+  float den[RQ];
 };
 
 __device__ __forceinline__ int pair_index(int jt, int it) { return it * (it + 1) / 2 + jt; }
@@ -123,92 +135,149 @@ __device__ __forceinline__ void load_row16(const __bf16* src, float (&x)[kDK], f
   for (int d = 0; d < kDK; ++d) x[d] = scale * (float)src[d];
 }
 
-// Rows [G*R, G*R + R) of phi(K_c)^T for token j (R = W_p/4; wave G of 4).
-template <int NT, int CS, bool BF16, int G>
-__device__ __forceinline__ void phik_rows(Smem<NT, CS, BF16>& sm, int j, const float (&x)[kDK], bool valid) {
-  using S = Smem<NT, CS, BF16>;
-  constexpr int R = Geo<NT>::WP / 4;
+// This wave's rows of phi(K_c)^T for token j (zero rows for a token past the end).
+template <int NT, int CS, bool BF16, bool READOUT, int G>
+__device__ __forceinline__ void phik_rows(Smem<NT, CS, BF16, READOUT>& sm, int j, const float (&x)[kDK], bool valid) {
+  using SP = Split<NT, BF16>;
+  using E = typename Smem<NT, CS, BF16, READOUT>::E;
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    ((sm.phikt[G * R + I][j] = (typename S::E)(valid ? feat<NT, G * R + I>(x) : 0.f)), ...);
-  }(std::make_integer_sequence<int, R>{});
+    (([&] {
+       constexpr int row = G * SP::RK + I;
+       if constexpr (row < SP::WP) sm.phikt[row][j] = (E)(valid ? feat<NT, row>(x) : 0.f);
+     }()),
+     ...);
+  }(std::make_integer_sequence<int, SP::RK>{});
 }
 
-// Slots [G*R, G*R + R) of the phi(sQ) row of token i, in 8-slot groups (16-byte stores for bfloat16).
-template <int NT, int CS, bool BF16, int G>
-__device__ __forceinline__ void phiq_slots(Smem<NT, CS, BF16>& sm, int i, const float (&x)[kDK]) {
-  constexpr int R = Geo<NT>::WP / 4;
-  if constexpr (BF16) {
-    [&]<int... P>(std::integer_sequence<int, P...>) {
-      (([&] {
-         constexpr int s0 = G * R + 8 * P;
-         bf16x8 v;
-         v[0] = (__bf16)feat<NT, slot_feature_bf16(s0 + 0)>(x);
-         v[1] = (__bf16)feat<NT, slot_feature_bf16(s0 + 1)>(x);
-         v[2] = (__bf16)feat<NT, slot_feature_bf16(s0 + 2)>(x);
-         v[3] = (__bf16)feat<NT, slot_feature_bf16(s0 + 3)>(x);
-         v[4] = (__bf16)feat<NT, slot_feature_bf16(s0 + 4)>(x);
-         v[5] = (__bf16)feat<NT, slot_feature_bf16(s0 + 5)>(x);
-         v[6] = (__bf16)feat<NT, slot_feature_bf16(s0 + 6)>(x);
-         v[7] = (__bf16)feat<NT, slot_feature_bf16(s0 + 7)>(x);
-         *reinterpret_cast<bf16x8*>(&sm.phiq[i][s0]) = v;
-       }()),
-       ...);
-    }(std::make_integer_sequence<int, R / 8>{});
-  } else {
-    [&]<int... P>(std::integer_sequence<int, P...>) {
-      (([&] {
-         constexpr int s0 = G * R + 4 * P;
-         f32x4 v;
-         v[0] = feat<NT, s0 + 0>(x);
-         v[1] = feat<NT, s0 + 1>(x);
-         v[2] = feat<NT, s0 + 2>(x);
-         v[3] = feat<NT, s0 + 3>(x);
-         *reinterpret_cast<f32x4*>(&sm.phiq[i][s0]) = v;
-       }()),
-       ...);
-    }(std::make_integer_sequence<int, R / 4>{});
-  }
+// This wave's 16-byte groups of the phi(sQ) row of token i.
+template <int NT, int CS, bool BF16, bool READOUT, int G>
+__device__ __forceinline__ void phiq_groups(Smem<NT, CS, BF16, READOUT>& sm, int i, const float (&x)[kDK]) {
+  using SP = Split<NT, BF16>;
+  [&]<int... P>(std::integer_sequence<int, P...>) {
+    (([&] {
+       constexpr int grp = G * SP::RG + P;
+       if constexpr (grp < SP::NG) {
+         constexpr int s0 = grp * SP::GQ;
+         if constexpr (BF16) {
+           bf16x8 v;
+           v[0] = (__bf16)feat<NT, slot_feature_bf16(s0 + 0)>(x);
+           v[1] = (__bf16)feat<NT, slot_feature_bf16(s0 + 1)>(x);
+           v[2] = (__bf16)feat<NT, slot_feature_bf16(s0 + 2)>(x);
+           v[3] = (__bf16)feat<NT, slot_feature_bf16(s0 + 3)>(x);
+           v[4] = (__bf16)feat<NT, slot_feature_bf16(s0 + 4)>(x);
+           v[5] = (__bf16)feat<NT, slot_feature_bf16(s0 + 5)>(x);
+           v[6] = (__bf16)feat<NT, slot_feature_bf16(s0 + 6)>(x);
+           v[7] = (__bf16)feat<NT, slot_feature_bf16(s0 + 7)>(x);
+           *reinterpret_cast<bf16x8*>(&sm.phiq[i][s0]) = v;
+         } else {
+           f32x4 v;
+           v[0] = feat<NT, s0 + 0>(x);
+           v[1] = feat<NT, s0 + 1>(x);
+           v[2] = feat<NT, s0 + 2>(x);
+           v[3] = feat<NT, s0 + 3>(x);
+           *reinterpret_cast<f32x4*>(&sm.phiq[i][s0]) = v;
+         }
+       }
+     }()),
+     ...);
+  }(std::make_integer_sequence<int, SP::RG>{});
 }
 
-template <int NT, int CS, bool BF16>
-__device__ __forceinline__ void features(Smem<NT, CS, BF16>& sm, int w, int l, int nv, float scale, bool readout) {
+template <int NT, int CS, bool BF16, bool READOUT, int G>
+__device__ __forceinline__ void features_wave(Smem<NT, CS, BF16, READOUT>& sm, int l, int nv, float scale) {
 #pragma unroll
   for (int tt = 0; tt < CS / 64; ++tt) {
     const int j = l + 64 * tt;
     float x[kDK];
     load_row16(&sm.k[j][0], x, 1.0f);
-    const bool valid = j < nv;
-    switch (w) {
-      case 0: phik_rows<NT, CS, BF16, 0>(sm, j, x, valid); break;
-      case 1: phik_rows<NT, CS, BF16, 1>(sm, j, x, valid); break;
-      case 2: phik_rows<NT, CS, BF16, 2>(sm, j, x, valid); break;
-      default: phik_rows<NT, CS, BF16, 3>(sm, j, x, valid); break;
-    }
-    if (readout) {
+    phik_rows<NT, CS, BF16, READOUT, G>(sm, j, x, j < nv);
+    if constexpr (READOUT) {
       load_row16(&sm.q[j][0], x, scale);
-      switch (w) {
-        case 0: phiq_slots<NT, CS, BF16, 0>(sm, j, x); break;
-        case 1: phiq_slots<NT, CS, BF16, 1>(sm, j, x); break;
-        case 2: phiq_slots<NT, CS, BF16, 2>(sm, j, x); break;
-        default: phiq_slots<NT, CS, BF16, 3>(sm, j, x); break;
-      }
+      phiq_groups<NT, CS, BF16, READOUT, G>(sm, j, x);
     }
   }
 }
 
+template <int NT, int CS, bool BF16, bool READOUT>
+__device__ __forceinline__ void features(Smem<NT, CS, BF16, READOUT>& sm, int w, int l, int nv, float scale) {
+  static_assert(kWaves == 5, "feature split assumes 5 waves");
+  switch (w) {
+    case 0: features_wave<NT, CS, BF16, READOUT, 0>(sm, l, nv, scale); break;
+    case 1: features_wave<NT, CS, BF16, READOUT, 1>(sm, l, nv, scale); break;
+    case 2: features_wave<NT, CS, BF16, READOUT, 2>(sm, l, nv, scale); break;
+    case 3: features_wave<NT, CS, BF16, READOUT, 3>(sm, l, nv, scale); break;
+    default: features_wave<NT, CS, BF16, READOUT, 4>(sm, l, nv, scale); break;
+  }
+}
+
+// Chunk inputs in flight: each thread's 16-byte pieces of q, k and v for one chunk.
+template <int CS, bool BF16, bool READOUT>
+struct Prefetch {
+  using E = typename std::conditional<BF16, __bf16, float>::type;
+  static constexpr int EPP = 16 / sizeof(E);  // elements per 16-byte piece
+  static constexpr int PR = kDK / EPP;        // pieces per q/k row
+  static constexpr int PV = kDV / EPP;        // pieces per v row
+  static constexpr int NQK = (CS * PR + kThreads - 1) / kThreads;
+  static constexpr int NV = (CS * PV + kThreads - 1) / kThreads;
+  uint4 q[READOUT ? NQK : 1], k[NQK], v[NV];
+
+  // Issue the global loads of the chunk starting at token tok0 (nv valid tokens; the rest read as zero).
+  __device__ __forceinline__ void load(const E* qg, const E* kg, const E* vg, long long tok0, int nv, int tid) {
+#pragma unroll
+    for (int u = 0; u < NQK; ++u) {
+      const int p = tid + u * kThreads, row = p / PR, pc = p % PR;
+      const bool ok = p < CS * PR && row < nv;
+      k[u] = ok ? *reinterpret_cast<const uint4*>(kg + (tok0 + row) * kDK + pc * EPP) : make_uint4(0, 0, 0, 0);
+      if constexpr (READOUT)
+        q[u] = ok ? *reinterpret_cast<const uint4*>(qg + (tok0 + row) * kDK + pc * EPP) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int p = tid + u * kThreads, j = p % CS, pc = p / CS;
+      const bool ok = p < CS * PV && j < nv;
+      v[u] = ok ? *reinterpret_cast<const uint4*>(vg + (tok0 + j) * kDV + pc * EPP) : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // Write the pieces to LDS: q, k rows as they are, v transposed.
+  template <class SM>
+  __device__ __forceinline__ void store(SM& sm, int tid) const {
+#pragma unroll
+    for (int u = 0; u < NQK; ++u) {
+      const int p = tid + u * kThreads, row = p / PR, pc = p % PR;
+      if (p < CS * PR) {
+        *reinterpret_cast<uint4*>(&sm.k[row][pc * EPP]) = k[u];
+        if constexpr (READOUT) *reinterpret_cast<uint4*>(&sm.q[row][pc * EPP]) = q[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int p = tid + u * kThreads, j = p % CS, pc = p / CS;
+      if (p < CS * PV) {
+        union {
+          uint4 u4;
+          E e[EPP];
+        } buf;
+        buf.u4 = v[u];
+#pragma unroll
+        for (int r = 0; r < EPP; ++r) sm.vt[pc * EPP + r][j] = buf.e[r];
+      }
+    }
+  }
+};
+
 // One segment of L tokens per workgroup; grid = (segments, heads).
-// READOUT = false: accumulate the segment's dS, z and write them to its workspace slot.
+// READOUT = false: accumulate the segment's (S, z) increment and write it to its workspace slot.
 // READOUT = true : start from the exclusive prefix in the slot and write the outputs.
 template <int NT, int CS, bool BF16, bool READOUT>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
     const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv, float* __restrict__ o,
     float* __restrict__ ws, int N, int L, int nseg, long long stride, float scale) {
   using G = Geo<NT>;
-  using SM = Smem<NT, CS, BF16>;
+  using SM = Smem<NT, CS, BF16, READOUT>;
   using E = typename SM::E;
-  constexpr int W = G::W, WP = G::WP, NAT = G::NAT, NKB = G::NKB;
+  constexpr int W = G::W, NAT = G::NAT, NKB = G::NKB;
   constexpr int NIT = CS / 16;
-  constexpr int EPP = 16 / sizeof(E);  // elements per 16-byte piece
   static_assert(CS == 64 || CS == 128, "chunk of 64 or 128 tokens");
   __shared__ SM sm;
 
@@ -216,123 +285,78 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
   const E* k = reinterpret_cast<const E*>(kv);
   const E* v = reinterpret_cast<const E*>(vv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, lg = l >> 4;
+  const bool zw = w == kValueWaves;  // the normaliser wave
+  const int col = 16 * w + l16;      // value column of this lane (value waves)
   const int seg = blockIdx.x;
   const long long bh = blockIdx.y;
   const int t_begin = seg * L, t_end = min(N, t_begin + L);
   const long long hbase = bh * (long long)N;
   float* slot = ws + (bh * nseg + seg) * stride;
 
-  // Running state: Srun[t][r] = S[16t + 4lg + r][16w + l16].
+  Prefetch<CS, BF16, READOUT> pf;
+  pf.load(q, k, v, hbase + t_begin, min(CS, t_end - t_begin), tid);
+
+  // Running state: Srun[t][r] = S1[16t + 4lg + r][column l16 of this wave's tile], where the
+  // normaliser wave's tile is [z | 0 ... 0].
   f32x4 Srun[NAT];
 #pragma unroll
   for (int t = 0; t < NAT; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int a = 16 * t + 4 * lg + r;
-      Srun[t][r] = (READOUT && a < W) ? slot[(long long)a * kDV + 16 * w + l16] : 0.f;
+      float x = 0.f;
+      if (READOUT && a < W) {
+        if (!zw) x = slot[(long long)a * kDV + col];
+        else if (l16 == 0) x = slot[(long long)W * kDV + a];
+      }
+      Srun[t][r] = x;
     }
-  for (int s = tid; s < WP; s += kThreads) {
-    const int a = slot_feature<BF16>(s);
-    sm.z[0][s] = (READOUT && a < W) ? slot[(long long)W * kDV + a] : 0.f;
-  }
-  int zb = 0;
 
-  // bfloat16 readout operands: S = hi + lo, in the A-operand k-slot order.
-  bf16x8 Shi[BF16 && READOUT ? NKB : 1], Slo[BF16 && READOUT ? NKB : 1];
-  auto split_state = [&]() {
-    if constexpr (BF16 && READOUT) {
+  // The normaliser wave's ones column as MFMA operands (rows/columns other than the first are zero).
+  const float one = (zw && l16 == 0) ? 1.f : 0.f;
+  bf16x8 ones8;
+  bf16x4 ones4;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+  for (int r = 0; r < 8; ++r) ones8[r] = (__bf16)one;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float x = r < 4 ? Srun[2 * kb][r] : Srun[2 * kb + 1][r - 4];
-          const __bf16 hi = (__bf16)x;
-          Shi[kb][r] = hi;
-          Slo[kb][r] = (__bf16)(x - (float)hi);
+  for (int r = 0; r < 4; ++r) ones4[r] = (__bf16)one;
+
+  f32x4 O[READOUT ? NIT : 1];
+  long long out_tok0 = -1;  // first token of the chunk whose outputs are pending
+  int out_nv = 0;
+  auto store_outputs = [&]() {
+    if constexpr (READOUT) {
+      if (out_tok0 >= 0 && !zw) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int i = 16 * it + l16;
+          if (i < out_nv) {
+            const float inv = __builtin_amdgcn_rcpf(sm.den[i]);
+            const f32x4 r = O[it];
+            *reinterpret_cast<f32x4*>(o + (out_tok0 + i) * kDV + 16 * w + 4 * lg) =
+                f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
+          }
         }
+      }
     }
   };
-  split_state();
 
   for (int c0 = t_begin; c0 < t_end; c0 += CS) {
     const int nv = min(CS, t_end - c0);
     const long long tok0 = hbase + c0;
 
-    // ---- A1: chunk inputs to LDS (q, k rows as is; v transposed) ----
-    {
-      constexpr int PR = kDK / EPP;  // 16-byte pieces per q/k row
-      for (int p = tid; p < CS * PR; p += kThreads) {
-        const int row = p / PR, pc = p % PR;
-        uint4 zq = make_uint4(0, 0, 0, 0), zk = zq;
-        if (row < nv) {
-          zk = *reinterpret_cast<const uint4*>(k + (tok0 + row) * kDK + pc * EPP);
-          if (READOUT) zq = *reinterpret_cast<const uint4*>(q + (tok0 + row) * kDK + pc * EPP);
-        }
-        *reinterpret_cast<uint4*>(&sm.k[row][pc * EPP]) = zk;
-        if (READOUT) *reinterpret_cast<uint4*>(&sm.q[row][pc * EPP]) = zq;
-      }
-      constexpr int PV = kDV / EPP;  // 16-byte pieces per v row
-      for (int p = tid; p < CS * PV; p += kThreads) {
-        const int j = p % CS, pc = p / CS;
-        union {
-          uint4 u;
-          E e[EPP];
-        } buf;
-        buf.u = make_uint4(0, 0, 0, 0);
-        if (j < nv) buf.u = *reinterpret_cast<const uint4*>(v + (tok0 + j) * kDV + pc * EPP);
-#pragma unroll
-        for (int r = 0; r < EPP; ++r) sm.vt[pc * EPP + r][j] = buf.e[r];
-      }
-    }
+    // ---- A: previous chunk's outputs; this chunk's inputs to LDS; next chunk's loads issued ----
+    __syncthreads();  // previous chunk done with LDS; its denominators visible
+    store_outputs();
+    pf.store(sm, tid);
+    if (c0 + CS < t_end) pf.load(q, k, v, tok0 + CS, min(CS, t_end - c0 - CS), tid);
+    __syncthreads();
+    features<NT, CS, BF16, READOUT>(sm, w, l, nv, scale);
     __syncthreads();
 
-    // ---- A2: features phi(K_c)^T (and phi(sQ_c)) ----
-    features<NT, CS, BF16>(sm, w, l, nv, scale, READOUT);
-    __syncthreads();
-
-    // ---- B: normaliser, inter denominators, scores, readout ----
-    if (tid < WP) {
-      const int a = slot_feature<BF16>(tid);
-      float acc = 0.f;
-      if constexpr (BF16) {
-#pragma unroll
-        for (int j = 0; j < CS; j += 8) {
-          const bf16x8 x = *reinterpret_cast<const bf16x8*>(&sm.phikt[a][j]);
-#pragma unroll
-          for (int r = 0; r < 8; ++r) acc += (float)x[r];
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < CS; j += 4) {
-          const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.phikt[a][j]);
-          acc += (x[0] + x[1]) + (x[2] + x[3]);
-        }
-      }
-      sm.z[zb ^ 1][tid] = sm.z[zb][tid] + acc;
-    }
-
-    f32x4 O[READOUT ? NIT : 1];
+    // ---- B: scores, readout with S_{<c}, state update ----
     if constexpr (READOUT) {
-      // inter-chunk denominators: phi(sq_i) . z_{<c}, split over kThreads/CS parts
-      {
-        constexpr int P = kThreads / CS, SPP = WP / P;
-        const int i = tid % CS, part = tid / CS;
-        float acc = 0.f;
-        for (int s = part * SPP; s < (part + 1) * SPP; s += EPP) {
-          if constexpr (BF16) {
-            const bf16x8 x = *reinterpret_cast<const bf16x8*>(&sm.phiq[i][s]);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) acc = fmaf((float)x[r], sm.z[zb][s + r], acc);
-          } else {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.phiq[i][s]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc = fmaf(x[r], sm.z[zb][s + r], acc);
-          }
-        }
-        sm.den_part[part][i] = acc;
-      }
-      // intra-chunk scores for the (key tile jt <= query tile it) pairs of this wave
-      for (int p = w; p < SM::NPAIR; p += 4) {
+      for (int p = w; p < SM::NPAIR; p += kWaves) {
         int it = 0;
         while ((it + 1) * (it + 2) / 2 <= p) ++it;
         const int jt = p - it * (it + 1) / 2;
@@ -350,81 +374,54 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
         }
         // sc[r] = k_j . q_i with j = 16jt + 4lg + r, i = 16it + l16
         typename SM::ATile tile;
-        float dsum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
-          float wgt = j <= i ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
-          if constexpr (BF16) {
+          const float wgt = j <= i ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
+          if constexpr (BF16)
             tile[r] = (__bf16)wgt;
-            dsum += (float)tile[r];
-          } else {
+          else
             tile[r] = wgt;
-            dsum += wgt;
-          }
         }
         sm.a[p][l] = tile;
-        dsum += __shfl_xor(dsum, 16);
-        dsum += __shfl_xor(dsum, 32);
-        if (lg == 0) sm.den_intra[p][l16] = dsum;
       }
-      // readout: O[it][r] = (phi(sQ) S)[token 16it + l16][column 16w + 4lg + r]
+      // readout: O[it][r] = (phi(sQ) S1_{<c})[token 16it + l16][tile column 4lg + r]
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BF16) {
+      for (int it = 0; it < NIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF16) {
+        // S = hi + lo in bfloat16, taken in the A-operand k-slot order one 32-feature block at a time
 #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[16 * it + l16][32 * kb + 8 * lg]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Shi[kb], bq, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Slo[kb], bq, acc, 0, 0, 0);
+        for (int kb = 0; kb < NKB; ++kb) {
+          bf16x8 hi, lo;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const float x = r < 4 ? Srun[2 * kb][r] : Srun[2 * kb + 1][r - 4];
+            hi[r] = (__bf16)x;
+            lo[r] = (__bf16)(x - (float)hi[r]);
           }
-        } else {
 #pragma unroll
-          for (int t = 0; t < NAT; ++t) {
+          for (int it = 0; it < NIT; ++it) {
+            const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[16 * it + l16][32 * kb + 8 * lg]);
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, O[it], 0, 0, 0);
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, O[it], 0, 0, 0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < NAT; ++t)
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
             const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[16 * it + l16][16 * t + 4 * lg]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], acc, 0, 0, 0);
+            for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], O[it], 0, 0, 0);
           }
-        }
-        O[it] = acc;
       }
     }
-    __syncthreads();
-
-    // ---- C: denominators, intra-chunk PV, state update ----
-    if constexpr (READOUT) {
-      if (tid < CS) {
-        const int i = tid, it = i / 16;
-        float d = 0.f;
-#pragma unroll
-        for (int part = 0; part < kThreads / CS; ++part) d += sm.den_part[part][i];
-        for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[pair_index(jt, it)][i % 16];
-        sm.den[i] = d;
-      }
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        for (int jt = 0; jt <= it; ++jt) {
-          const int p = pair_index(jt, it);
-          if constexpr (BF16) {
-            const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.vt[16 * w + l16][16 * jt + 4 * lg]);
-            const bf16x4 bv = sm.a[p][l];
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
-                                                              __builtin_bit_cast(i16x4, bv), O[it], 0, 0, 0);
-          } else {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.vt[16 * w + l16][16 * jt + 4 * lg]);
-            const f32x4 bv = sm.a[p][l];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bv[r], O[it], 0, 0, 0);
-          }
-        }
-      }
-    }
-    // state update: Srun[t] += phi(K)^T[16t.., chunk] V[chunk, 16w..]
+    // state update (after the readout used S_{<c}): Srun[t] += phi(K)^T[16t.., chunk] V1[chunk, tile]
     if constexpr (BF16) {
 #pragma unroll
       for (int jb = 0; jb < CS / 32; ++jb) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[16 * w + l16][32 * jb + 8 * lg]);
+        const bf16x8 bv = zw ? ones8 : *reinterpret_cast<const bf16x8*>(&sm.vt[col][32 * jb + 8 * lg]);
 #pragma unroll
         for (int t = 0; t < NAT; ++t) {
           const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.phikt[16 * t + l16][32 * jb + 8 * lg]);
@@ -434,7 +431,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
     } else {
 #pragma unroll
       for (int jb = 0; jb < CS / 16; ++jb) {
-        const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.vt[16 * w + l16][16 * jb + 4 * lg]);
+        const f32x4 bv = zw ? f32x4{one, one, one, one}
+                            : *reinterpret_cast<const f32x4*>(&sm.vt[col][16 * jb + 4 * lg]);
 #pragma unroll
         for (int t = 0; t < NAT; ++t) {
           const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[16 * t + l16][16 * jb + 4 * lg]);
@@ -443,37 +441,47 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
         }
       }
     }
-    __syncthreads();
-
-    // ---- D: outputs, next readout operands ----
     if constexpr (READOUT) {
+      __syncthreads();  // score tiles visible
+      // ---- C: intra-chunk PV (V1^T times scores); the normaliser wave publishes the denominators ----
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
-        const int i = 16 * it + l16;
-        if (i < nv) {
-          const float d = sm.den[i];
-          f32x4 r = O[it];
-          *reinterpret_cast<f32x4*>(o + (tok0 + i) * kDV + 16 * w + 4 * lg) =
-              f32x4{r[0] / d, r[1] / d, r[2] / d, r[3] / d};
+        for (int jt = 0; jt <= it; ++jt) {
+          const int p = pair_index(jt, it);
+          if constexpr (BF16) {
+            const bf16x4 av = zw ? ones4 : *reinterpret_cast<const bf16x4*>(&sm.vt[col][16 * jt + 4 * lg]);
+            const bf16x4 bv = sm.a[p][l];
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
+                                                              __builtin_bit_cast(i16x4, bv), O[it], 0, 0, 0);
+          } else {
+            const f32x4 av = zw ? f32x4{one, one, one, one}
+                                : *reinterpret_cast<const f32x4*>(&sm.vt[col][16 * jt + 4 * lg]);
+            const f32x4 bv = sm.a[p][l];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bv[r], O[it], 0, 0, 0);
+          }
         }
+        if (zw && lg == 0) sm.den[16 * it + l16] = O[it][0];
       }
-      split_state();
+      out_tok0 = tok0;
+      out_nv = nv;
     }
-    zb ^= 1;
   }
 
-  if constexpr (!READOUT) {
+  if constexpr (READOUT) {
+    __syncthreads();
+    store_outputs();
+  } else {
 #pragma unroll
     for (int t = 0; t < NAT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int a = 16 * t + 4 * lg + r;
-        if (a < W) slot[(long long)a * kDV + 16 * w + l16] = Srun[t][r];
+        if (a < W) {
+          if (!zw) slot[(long long)a * kDV + col] = Srun[t][r];
+          else if (l16 == 0) slot[(long long)W * kDV + a] = Srun[t][r];
+        }
       }
-    if (tid < WP) {
-      const int a = slot_feature<BF16>(tid);
-      if (a < W) slot[(long long)W * kDV + a] = sm.z[zb][tid];
-    }
   }
 }
 
@@ -508,9 +516,8 @@ int run(const PrefillArgs& a) {
   return 0;
 }
 
-// This path walks 64-token chunks whatever the configured chunk (64 or 128): a 128-token chunk
-// needs more registers than a wavefront has for the readout (the outputs do not depend on the
-// chunk length beyond rounding), and 64 keeps two workgroups per CU for bfloat16 inputs.
+// This path walks 64-token chunks whatever the configured chunk (64 or 128); the outputs do not
+// depend on the chunk length beyond rounding.
 constexpr int kChunk = 64;
 
 template <int NT>
@@ -525,10 +532,9 @@ bool prefill_mfma_has(int nt, int dk, int dv, int C) {
 }
 
 long long prefill_mfma_ws_bytes(const Shape& s, int BH, int N, int C) {
-  const int CS = kChunk;
-  const int nchunk = cdiv(N, CS);
+  const int nchunk = cdiv(N, kChunk);
   const int nseg0 = n_segments(BH, nchunk);
-  const int L = cdiv(nchunk, nseg0) * CS;
+  const int L = cdiv(nchunk, nseg0) * kChunk;
   return (long long)BH * cdiv(N, L) * s.stride * 4;
 }
 
