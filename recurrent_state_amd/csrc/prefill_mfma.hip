@@ -49,6 +49,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -135,7 +136,8 @@ __device__ __forceinline__ void load_row16(const __bf16* src, float (&x)[kDK], f
   for (int d = 0; d < kDK; ++d) x[d] = scale * (float)src[d];
 }
 
-// This wave's rows of phi(K_c)^T for token j (zero rows for a token past the end).
+// This wave's rows of phi(K_c)^T for token j.  A token past the end has a zero k row, so all its
+// features are zero except the constant one.
 template <int NT, int CS, bool BF16, bool READOUT, int G>
 __device__ __forceinline__ void phik_rows(Smem<NT, CS, BF16, READOUT>& sm, int j, const float (&x)[kDK], bool valid) {
   using SP = Split<NT, BF16>;
@@ -143,7 +145,10 @@ __device__ __forceinline__ void phik_rows(Smem<NT, CS, BF16, READOUT>& sm, int j
   [&]<int... I>(std::integer_sequence<int, I...>) {
     (([&] {
        constexpr int row = G * SP::RK + I;
-       if constexpr (row < SP::WP) sm.phikt[row][j] = (E)(valid ? feat<NT, row>(x) : 0.f);
+       if constexpr (row == 0)
+         sm.phikt[row][j] = (E)(valid ? 1.f : 0.f);
+       else if constexpr (row < SP::WP)
+         sm.phikt[row][j] = (E)feat<NT, row>(x);
      }()),
      ...);
   }(std::make_integer_sequence<int, SP::RK>{});
@@ -485,20 +490,416 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Pipelined bfloat16 prefill: 8 wavefronts per workgroup, one barrier per chunk.
+//
+// Waves 0..3 ("consumers") own value columns 16w..16w+15 and run the MFMAs of chunk c:
+// the readout phi(sQ_c) S_{<c} (state kept in accumulator registers, split hi + lo), the
+// intra-chunk product V^T tril(K_n(s K Q^T)), the state update phi(K_c)^T V_c, and the
+// output division.  Waves 4..7 ("producers") meanwhile prepare chunk c+1 in the other half
+// of a double-buffered LDS area: phi(K)^T rows, phi(sQ) rows (slot-permuted), V^T, the
+// intra-chunk score tiles (16x16x16 MFMA + Horner + causal mask) and the two denominator
+// parts: phi(sq_i) . z_{<c+1} (z kept in LDS, each producer owning a quarter of the
+// features) and the row sums of the score tiles.  Producers read their inputs straight
+// from global memory, issued a whole chunk ahead.  The single barrier per chunk both hands
+// buffer c+1 to the consumers and returns buffer c to the producers.  The feature work per
+// token (vector ALU) and the LDS traffic of the operands bound this kernel; the matrix work
+// is a fraction of it.
+// ------------------------------------------------------------------------------------------------
+constexpr int kPipeConsumers = 4;  // one per 16 value columns
+constexpr int kPipeProducers = 4;
+constexpr int kPipeThreads = 64 * (kPipeConsumers + kPipeProducers);
+constexpr int kPipeChunk = 64;
+
+template <int NT, bool READOUT>
+struct PipeSmem {
+  static constexpr int WP = Geo<NT>::WP;
+  static constexpr int LQ = WP + 8;           // phi(sQ) row stride (bf16)
+  static constexpr int LK = kPipeChunk + 8;   // phi(K)^T and V^T row stride (bf16)
+  static constexpr int NPAIR = 10;            // (key tile <= query tile) pairs of a 64-token chunk
+  static constexpr int RQ = READOUT ? kPipeChunk : 1;
+  static constexpr int RP = READOUT ? NPAIR : 1;
+  alignas(16) __bf16 vt[2][kDV][LK];
+  alignas(16) __bf16 phikt[2][WP][LK];
+  alignas(16) __bf16 phiq[2][RQ][LQ];
+  alignas(16) bf16x4 a[2][RP][64];
+  float den_part[2][kPipeProducers][RQ];
+  float den_intra[2][RP][16];
+  float z[2][WP];  // z_{<c} for chunk parity c & 1, natural feature order
+};
+
+// Producer split: producer g owns phi(K)^T rows [g*RK, g*RK + RK) and phi(sQ) 8-slot groups
+// [g*RG, g*RG + RG) (clipped to the padded width); it also keeps z for its rows, writes value
+// columns [g*VC, g*VC + VC) of V^T and computes score tiles g, g + kPipeProducers.
+template <int NT>
+struct PipeSplit {
+  static constexpr int WP = Geo<NT>::WP;
+  static constexpr int RK = ((WP + kPipeProducers - 1) / kPipeProducers + 1) / 2 * 2;
+  static constexpr int NG = WP / 8;
+  static constexpr int RG = (NG + kPipeProducers - 1) / kPipeProducers;
+  static constexpr int VC = kDV / kPipeProducers;
+  static constexpr int NS = (10 + kPipeProducers - 1) / kPipeProducers;  // score tiles per producer
+};
+
+// A token past the end has a zero k row, so all its features are zero except the constant one.
+template <int NT, bool READOUT, int G>
+__device__ __forceinline__ void pipe_phik_rows(PipeSmem<NT, READOUT>& sm, int b, int j, const float (&x)[kDK],
+                                               bool valid) {
+  using SP = PipeSplit<NT>;
+  static_assert(SP::RK % 2 == 0, "rows are written in pairs");
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (([&] {
+       constexpr int r0 = G * SP::RK + 2 * I, r1 = r0 + 1;
+       if constexpr (r0 < SP::WP) {
+         float f0;
+         if constexpr (r0 == 0)
+           f0 = valid ? 1.f : 0.f;
+         else
+           f0 = feat<NT, r0>(x);
+         const bf16x2 pr = {(__bf16)f0, (__bf16)feat<NT, r1>(x)};
+         const uint32_t u = __builtin_bit_cast(uint32_t, pr);
+         *reinterpret_cast<uint16_t*>(&sm.phikt[b][r0][j]) = (uint16_t)u;
+         *reinterpret_cast<uint16_t*>(&sm.phikt[b][r1][j]) = (uint16_t)(u >> 16);
+       }
+     }()),
+     ...);
+  }(std::make_integer_sequence<int, SP::RK / 2>{});
+}
+
+// Writes this wave's phi(sQ) groups of token j and returns their part of phi(sq_j) . z.
+template <int NT, bool READOUT, int G>
+__device__ __forceinline__ float pipe_phiq_groups(PipeSmem<NT, READOUT>& sm, int b, int zb, int j,
+                                                  const float (&x)[kDK]) {
+  using SP = PipeSplit<NT>;
+  float acc = 0.f;
+  [&]<int... P>(std::integer_sequence<int, P...>) {
+    (([&] {
+       constexpr int grp = G * SP::RG + P;
+       if constexpr (grp < SP::NG) {
+         constexpr int s0 = grp * 8;
+         bf16x8 v;
+         [&]<int... R>(std::integer_sequence<int, R...>) {
+           ((v[R] = (__bf16)feat<NT, slot_feature_bf16(s0 + R)>(x)), ...);
+           ((acc = fmaf((float)v[R], sm.z[zb][slot_feature_bf16(s0 + R)], acc)), ...);
+         }(std::make_integer_sequence<int, 8>{});
+         *reinterpret_cast<bf16x8*>(&sm.phiq[b][j][s0]) = v;
+       }
+     }()),
+     ...);
+  }(std::make_integer_sequence<int, SP::RG>{});
+  return acc;
+}
+
+// A producer's inputs for one chunk, loaded one chunk ahead (lane = token j of the chunk).
+template <bool READOUT>
+struct PipeIn {
+  static constexpr int NS = (10 + kPipeProducers - 1) / kPipeProducers;
+  static constexpr int NVP = kDV / kPipeProducers / 8;  // 16-byte pieces of v per producer lane
+  static_assert(NVP * 8 * kPipeProducers == kDV, "value columns split evenly over producers");
+  uint4 k[2], q[READOUT ? 2 : 1], v[NVP];
+  uint2 sk[READOUT ? NS : 1], sq[READOUT ? NS : 1];  // score MFMA operands of this producer's tiles
+
+  // Tokens past the end read the chunk's first row (always valid) and are then zeroed, so every
+  // load is an unconditional global load.
+  __device__ __forceinline__ void load(const __bf16* qg, const __bf16* kg, const __bf16* vg, long long tok0, int nv,
+                                       int g, int l) {
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    const bool ok = l < nv;
+    const long long row = tok0 + (ok ? l : 0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint4 tk = *reinterpret_cast<const uint4*>(kg + row * kDK + 8 * u);
+      k[u] = ok ? tk : z4;
+      if constexpr (READOUT) {
+        const uint4 tq = *reinterpret_cast<const uint4*>(qg + row * kDK + 8 * u);
+        q[u] = ok ? tq : z4;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NVP; ++u) {
+      const uint4 tv = *reinterpret_cast<const uint4*>(vg + row * kDV + 8 * (NVP * g + u));
+      v[u] = ok ? tv : z4;
+    }
+    if constexpr (READOUT) {
+      const int l16 = l & 15, lg = l >> 4;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int p = g + kPipeProducers * s;
+        int it = 0;
+        while ((it + 1) * (it + 2) / 2 <= p) ++it;
+        const int jt = p - it * (it + 1) / 2;
+        const int rk = 16 * jt + l16, rq = 16 * it + l16;
+        const bool okk = p < 10 && rk < nv, okq = p < 10 && rq < nv;
+        const uint2 tk = *reinterpret_cast<const uint2*>(kg + (tok0 + (okk ? rk : 0)) * kDK + 4 * lg);
+        const uint2 tq = *reinterpret_cast<const uint2*>(qg + (tok0 + (okq ? rq : 0)) * kDK + 4 * lg);
+        sk[s] = okk ? tk : make_uint2(0, 0);
+        sq[s] = okq ? tq : make_uint2(0, 0);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void unpack_row16(const uint4 (&r)[2], float (&x)[kDK], float scale) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint32_t w[4] = {r[u].x, r[u].y, r[u].z, r[u].w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      x[8 * u + 2 * h] = scale * __uint_as_float(w[h] << 16);
+      x[8 * u + 2 * h + 1] = scale * __uint_as_float(w[h] & 0xffff0000u);
+    }
+  }
+}
+
+// Producer wave G prepares chunk data in buffer b (chunk parity), with z_{<chunk} in z[b].
+template <int NT, bool READOUT, int G>
+__device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const PipeIn<READOUT>& in, int b, int l,
+                                             int nv, float scale) {
+  using SP = PipeSplit<NT>;
+  constexpr int WP = Geo<NT>::WP;
+  const int l16 = l & 15, lg = l >> 4;
+  {
+    float x[kDK];
+    unpack_row16(in.k, x, 1.0f);
+    pipe_phik_rows<NT, READOUT, G>(sm, b, l, x, l < nv);
+  }
+  if constexpr (READOUT) {
+    float x[kDK];
+    unpack_row16(in.q, x, scale);
+    sm.den_part[b][G][l] = pipe_phiq_groups<NT, READOUT, G>(sm, b, b, l, x);
+  }
+  // V^T: this producer's value columns of token l
+#pragma unroll
+  for (int u = 0; u < PipeIn<READOUT>::NVP; ++u) {
+    const uint32_t w[4] = {in.v[u].x, in.v[u].y, in.v[u].z, in.v[u].w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      sm.vt[b][SP::VC * G + 8 * u + 2 * h][l] = __builtin_bit_cast(__bf16, (uint16_t)(w[h] & 0xffffu));
+      sm.vt[b][SP::VC * G + 8 * u + 2 * h + 1][l] = __builtin_bit_cast(__bf16, (uint16_t)(w[h] >> 16));
+    }
+  }
+  if constexpr (READOUT) {
+    // intra-chunk score tiles of this wave's pairs, and their row sums (denominator part)
+#pragma unroll
+    for (int s = 0; s < SP::NS; ++s) {
+      const int p = G + kPipeProducers * s;
+      if (p < 10) {
+        int it = 0;
+        while ((it + 1) * (it + 2) / 2 <= p) ++it;
+        const int jt = p - it * (it + 1) / 2;
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, in.sk[s]),
+                                                       __builtin_bit_cast(i16x4, in.sq[s]), sc, 0, 0, 0);
+        bf16x4 tile;
+        float dsum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
+          tile[r] = (__bf16)(j <= i ? taylor_kernel<NT>(scale * sc[r]) : 0.f);
+          dsum += (float)tile[r];
+        }
+        sm.a[b][p][l] = tile;
+        dsum += __shfl_xor(dsum, 16);
+        dsum += __shfl_xor(dsum, 32);
+        if (lg == 0) sm.den_intra[b][p][l16] = dsum;
+      }
+    }
+  }
+  // z_{<next} = z_{<this} + column sums of this wave's phi(K)^T rows (read back from LDS: the
+  // rows were written by this same wave above, and a wave's LDS accesses complete in order)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int row = G * SP::RK + l;
+  if (l < SP::RK && row < WP) {
+    float acc = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int t = 0; t < kPipeChunk; t += 8) {
+      const bf16x8 x8 = *reinterpret_cast<const bf16x8*>(&sm.phikt[b][row][t]);
+#pragma unroll
+      for (int h = 0; h < 4; ++h) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x8[2 * h], x8[2 * h + 1]}, ones, acc, false);
+    }
+    sm.z[b ^ 1][row] = sm.z[b][row] + acc;
+  }
+}
+
+template <int NT, bool READOUT>
+__device__ __forceinline__ void pipe_produce_wave(PipeSmem<NT, READOUT>& sm, const PipeIn<READOUT>& in, int g, int b,
+                                                  int l, int nv, float scale) {
+  static_assert(kPipeProducers <= 8, "dispatch below lists up to 8 producers");
+  switch (g) {
+    case 0: pipe_produce<NT, READOUT, 0>(sm, in, b, l, nv, scale); break;
+    case 1: pipe_produce<NT, READOUT, 1>(sm, in, b, l, nv, scale); break;
+    case 2: pipe_produce<NT, READOUT, 2>(sm, in, b, l, nv, scale); break;
+    case 3: pipe_produce<NT, READOUT, 3>(sm, in, b, l, nv, scale); break;
+    default:
+      if constexpr (kPipeProducers > 4) {
+        switch (g) {
+          case 4: pipe_produce<NT, READOUT, 4>(sm, in, b, l, nv, scale); break;
+          case 5: pipe_produce<NT, READOUT, 5>(sm, in, b, l, nv, scale); break;
+          case 6: pipe_produce<NT, READOUT, 6>(sm, in, b, l, nv, scale); break;
+          default: pipe_produce<NT, READOUT, 7>(sm, in, b, l, nv, scale); break;
+        }
+      }
+      break;
+  }
+}
+
+template <int NT, bool READOUT>
+__global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16* __restrict__ q,
+                                                                    const __bf16* __restrict__ k,
+                                                                    const __bf16* __restrict__ v,
+                                                                    float* __restrict__ o, float* __restrict__ ws,
+                                                                    int N, int L, int nseg, long long stride,
+                                                                    float scale) {
+  using G = Geo<NT>;
+  using SM = PipeSmem<NT, READOUT>;
+  using SP = PipeSplit<NT>;
+  constexpr int W = G::W, WP = G::WP, NAT = G::NAT, NKB = G::NKB;
+  constexpr int CS = kPipeChunk, NIT = CS / 16;
+  __shared__ SM sm;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, lg = l >> 4;
+  const bool producer = w >= kPipeConsumers;
+  const int g = w - kPipeConsumers;
+  const int seg = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int t_begin = seg * L, t_end = min(N, t_begin + L);
+  const int nch = (t_end - t_begin + CS - 1) / CS;
+  const long long hbase = bh * (long long)N;
+  float* slot = ws + (bh * nseg + seg) * stride;
+  auto chunk_nv = [&](int c) { return min(CS, t_end - (t_begin + c * CS)); };
+
+  // consumers: running state tile; producers: z prefix of their rows, chunk 0 inputs
+  f32x4 Srun[NAT];
+  PipeIn<READOUT> in;
+  if (!producer) {
+#pragma unroll
+    for (int t = 0; t < NAT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int a = 16 * t + 4 * lg + r;
+        Srun[t][r] = (READOUT && a < W) ? slot[(long long)a * kDV + 16 * w + l16] : 0.f;
+      }
+  } else {
+    const int row = g * SP::RK + l;
+    if (l < SP::RK && row < WP) sm.z[0][row] = (READOUT && row < W) ? slot[(long long)W * kDV + row] : 0.f;
+    in.load(q, k, v, hbase + t_begin, chunk_nv(0), g, l);
+  }
+  __syncthreads();  // z prefix visible to every producer
+  if (producer) {
+    pipe_produce_wave<NT, READOUT>(sm, in, g, 0, l, chunk_nv(0), scale);
+    if (nch > 1) in.load(q, k, v, hbase + t_begin + CS, chunk_nv(1), g, l);
+  }
+  __syncthreads();
+
+  for (int c = 0; c < nch; ++c) {
+    const int b = c & 1;
+    if (!producer) {
+      const int nv = chunk_nv(c);
+      const long long tok0 = hbase + t_begin + c * CS;
+      f32x4 O[READOUT ? NIT : 1];
+      if constexpr (READOUT) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // readout with S_{<c} = hi + lo, one 32-feature k-block at a time
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          bf16x8 hi, lo;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            const float x = r < 4 ? Srun[2 * kb][r] : Srun[2 * kb + 1][r - 4];
+            hi[r] = (__bf16)x;
+            lo[r] = (__bf16)(x - (float)hi[r]);
+          }
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
+            const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[b][16 * it + l16][32 * kb + 8 * lg]);
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, O[it], 0, 0, 0);
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, O[it], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight (register budget)
+        }
+        // intra-chunk V^T x scores
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+          for (int jt = 0; jt <= it; ++jt) {
+            const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.vt[b][16 * w + l16][16 * jt + 4 * lg]);
+            const bf16x4 bv = sm.a[b][pair_index(jt, it)][l];
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
+                                                              __builtin_bit_cast(i16x4, bv), O[it], 0, 0, 0);
+          }
+      }
+      // state update
+#pragma unroll
+      for (int jb = 0; jb < CS / 32; ++jb) {
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[b][16 * w + l16][32 * jb + 8 * lg]);
+#pragma unroll
+        for (int t = 0; t < NAT; ++t) {
+          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.phikt[b][16 * t + l16][32 * jb + 8 * lg]);
+          Srun[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bv, Srun[t], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (READOUT) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int i = 16 * it + l16;
+          float d = 0.f;
+#pragma unroll
+          for (int pp = 0; pp < kPipeProducers; ++pp) d += sm.den_part[b][pp][i];
+#pragma unroll
+          for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][pair_index(jt, it)][l16];
+          if (i < nv) {
+            const float inv = __builtin_amdgcn_rcpf(d);
+            const f32x4 r = O[it];
+            *reinterpret_cast<f32x4*>(o + (tok0 + i) * kDV + 16 * w + 4 * lg) =
+                f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
+          }
+        }
+      }
+    } else if (c + 1 < nch) {
+      // issue chunk c+2's loads before computing chunk c+1, so they have a whole iteration to land
+      const PipeIn<READOUT> cur = in;
+      if (c + 2 < nch) in.load(q, k, v, hbase + t_begin + (c + 2) * CS, chunk_nv(c + 2), g, l);
+      pipe_produce_wave<NT, READOUT>(sm, cur, g, b ^ 1, l, chunk_nv(c + 1), scale);
+    }
+    __syncthreads();
+  }
+
+  if constexpr (!READOUT) {
+    if (!producer) {
+#pragma unroll
+      for (int t = 0; t < NAT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int a = 16 * t + 4 * lg + r;
+          if (a < W) slot[(long long)a * kDV + 16 * w + l16] = Srun[t][r];
+        }
+    } else {
+      const int row = g * SP::RK + l;
+      if (l < SP::RK && row < W) slot[(long long)W * kDV + row] = sm.z[nch & 1][row];
+    }
+  }
+}
+
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Segments per head: enough workgroups to cover the chip about twice, never more than the chunks.
-int n_segments(int BH, int nchunk) {
-  long long want = (512 + BH - 1) / BH;
+// Segments per head: about `target` workgroups in total, never more than the chunks.
+int n_segments(int BH, int nchunk, int target) {
+  long long want = (target + BH - 1) / BH;
   if (want < 1) want = 1;
   if (want > nchunk) want = nchunk;
   return (int)want;
 }
 
+constexpr int kSegTarget = 512;
+
 template <int NT, int CS, bool BF16>
 int run(const PrefillArgs& a) {
   const int nchunk = cdiv(a.N, CS);
-  const int nseg0 = n_segments(a.BH, nchunk);
+  const int nseg0 = n_segments(a.BH, nchunk, kSegTarget);
   const int L = cdiv(nchunk, nseg0) * CS;
   const int nseg = cdiv(a.N, L);
   float* ws = (float*)a.ws;
@@ -516,13 +917,41 @@ int run(const PrefillArgs& a) {
   return 0;
 }
 
-// This path walks 64-token chunks whatever the configured chunk (64 or 128); the outputs do not
+// The pipelined bfloat16 kernel keeps one workgroup per CU (double-buffered LDS); the float32
+// kernel fits two.
+constexpr int kSegTargetPipe = 256;
+
+template <int NT>
+int run_pipe(const PrefillArgs& a) {
+  const int nchunk = cdiv(a.N, kPipeChunk);
+  const int nseg0 = n_segments(a.BH, nchunk, kSegTargetPipe);
+  const int L = cdiv(nchunk, nseg0) * kPipeChunk;
+  const int nseg = cdiv(a.N, L);
+  float* ws = (float*)a.ws;
+  const long long elems = Geo<NT>::W * (long long)(kDV + 1);
+  const dim3 grid(nseg, a.BH), block(kPipeThreads);
+  const __bf16* q = (const __bf16*)a.q;
+  const __bf16* k = (const __bf16*)a.k;
+  const __bf16* v = (const __bf16*)a.v;
+  prefill_pipe_kernel<NT, false><<<grid, block, 0, a.stream>>>(q, k, v, nullptr, ws, a.N, L, nseg, a.s.stride,
+                                                              a.s.scale);
+  if (hipGetLastError() != hipSuccess) return -3;
+  if (seg_scan_launch(ws, a.state, a.BH, nseg, a.s.stride, elems, a.o != nullptr, a.stream)) return -3;
+  if (a.o) {
+    prefill_pipe_kernel<NT, true><<<grid, block, 0, a.stream>>>(q, k, v, a.o, ws, a.N, L, nseg, a.s.stride,
+                                                               a.s.scale);
+    if (hipGetLastError() != hipSuccess) return -3;
+  }
+  return 0;
+}
+
+// Both paths walk 64-token chunks whatever the configured chunk (64 or 128); the outputs do not
 // depend on the chunk length beyond rounding.
 constexpr int kChunk = 64;
 
 template <int NT>
 int run_dtype(const PrefillArgs& a) {
-  return a.s.dtype == 1 ? run<NT, kChunk, true>(a) : run<NT, kChunk, false>(a);
+  return a.s.dtype == 1 ? run_pipe<NT>(a) : run<NT, kChunk, false>(a);
 }
 
 }  // namespace
@@ -533,7 +962,7 @@ bool prefill_mfma_has(int nt, int dk, int dv, int C) {
 
 long long prefill_mfma_ws_bytes(const Shape& s, int BH, int N, int C) {
   const int nchunk = cdiv(N, kChunk);
-  const int nseg0 = n_segments(BH, nchunk);
+  const int nseg0 = n_segments(BH, nchunk, s.dtype == 1 ? kSegTargetPipe : kSegTarget);
   const int L = cdiv(nchunk, nseg0) * kChunk;
   return (long long)BH * cdiv(N, L) * s.stride * 4;
 }
