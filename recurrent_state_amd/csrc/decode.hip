@@ -16,7 +16,8 @@
 // coalesced, and each thread keeps a fixed 4-column slice of the readout
 // numerator, reduced at the end with cross-lane shuffles and one LDS pass.
 // All row loads of a batch are issued before any update, so every thread has
-// up to 12 x 16 B in flight.
+// up to 12 x 16 B in flight; the first batch is requested before the features
+// are formed.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -46,6 +47,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
 
   const int tid = threadIdx.x;
   const long long h = blockIdx.x;
+  float* S = state + h * stride;
+  float* z = S + (long long)W * DV;
+  const int cg = tid % CG;
+  const int r0 = tid / CG;
+
+  // The first batch of state rows (and z) is requested before anything else, so the state
+  // stream is already in flight while q, k, v arrive and the features are formed.
+  float4 buf[RB];
+#pragma unroll
+  for (int u = 0; u < RB; ++u) {
+    const int r = r0 + u * RSTEP;
+    if (r < W) buf[u] = *reinterpret_cast<const float4*>(S + (long long)r * DV + cg * 4);
+  }
+  const float z0 = tid < W ? z[tid] : 0.f;
+
   if (tid < DK) {
     s_q[tid] = scale * to_f32(q[h * DK + tid]);
     s_k[tid] = to_f32(k[h * DK + tid]);
@@ -58,17 +74,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
   }
   __syncthreads();
 
-  float* S = state + h * stride;
-  const int cg = tid % CG;
-  const int r0 = tid / CG;
   const float4 vv = *reinterpret_cast<const float4*>(s_v + cg * 4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int base = r0; base < W; base += RSTEP * RB) {
-    float4 buf[RB];
+    if (base != r0) {
 #pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int r = base + u * RSTEP;
-      if (r < W) buf[u] = *reinterpret_cast<const float4*>(S + (long long)r * DV + cg * 4);
+      for (int u = 0; u < RB; ++u) {
+        const int r = base + u * RSTEP;
+        if (r < W) buf[u] = *reinterpret_cast<const float4*>(S + (long long)r * DV + cg * 4);
+      }
     }
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
@@ -81,8 +95,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
     }
   }
   float accz = 0.f;
-  float* z = S + (long long)W * DV;
-  for (int a = tid; a < W; a += kDecodeThreads) {
+  if (tid < W) {
+    const float nz = z0 + s_phik[tid];
+    z[tid] = nz;
+    accz = s_phiq[tid] * nz;
+  }
+  for (int a = tid + kDecodeThreads; a < W; a += kDecodeThreads) {
     const float nz = z[a] + s_phik[a];
     z[a] = nz;
     accz = fmaf(s_phiq[a], nz, accz);
