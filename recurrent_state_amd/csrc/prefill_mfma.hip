@@ -498,8 +498,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
 // intra-chunk product V^T tril(K_n(s K Q^T)), the state update phi(K_c)^T V_c, and the
 // output division.  Waves 4..7 ("producers") meanwhile prepare chunk c+1 in the other half
 // of a double-buffered LDS area: phi(K)^T rows, phi(sQ) rows (slot-permuted), V^T, the
-// intra-chunk score tiles (16x16x16 MFMA + Horner + causal mask) and the two denominator
-// parts: phi(sq_i) . z_{<c+1} (z kept in LDS, each producer owning a quarter of the
+// intra-chunk score tiles (16x16x16 MFMA + Horner + causal mask, stored as bfloat16 hi + lo
+// so the intra-chunk weights keep float32 accuracy) and the two denominator parts: phi(sq_i) . z_{<c+1} (z kept in LDS, each producer owning a quarter of the
 // features) and the row sums of the score tiles.  Producers read their inputs straight
 // from global memory, issued a whole chunk ahead.  The single barrier per chunk both hands
 // buffer c+1 to the consumers and returns buffer c to the producers.  The feature work per
@@ -522,7 +522,8 @@ struct PipeSmem {
   alignas(16) __bf16 vt[2][kDV][LK];
   alignas(16) __bf16 phikt[2][WP][LK];
   alignas(16) __bf16 phiq[2][RQ][LQ];
-  alignas(16) bf16x4 a[2][RP][64];
+  alignas(16) bf16x4 a[2][RP][64];    // score tiles, high bfloat16 part
+  alignas(16) bf16x4 alo[2][RP][64];  // score tiles, low part (w - hi), so hi + lo keeps float32 accuracy
   float den_part[2][kPipeProducers][RQ];
   float den_intra[2][RP][16];
   float z[2][WP];  // z_{<c} for chunk parity c & 1, natural feature order
@@ -690,15 +691,18 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
         sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, in.sk[s]),
                                                        __builtin_bit_cast(i16x4, in.sq[s]), sc, 0, 0, 0);
-        bf16x4 tile;
+        bf16x4 hi, lo;
         float dsum = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
-          tile[r] = (__bf16)(j <= i ? taylor_kernel<NT>(scale * sc[r]) : 0.f);
-          dsum += (float)tile[r];
+          const float wgt = j <= i ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
+          hi[r] = (__bf16)wgt;
+          lo[r] = (__bf16)(wgt - (float)hi[r]);
+          dsum += wgt;
         }
-        sm.a[b][p][l] = tile;
+        sm.a[b][p][l] = hi;
+        sm.alo[b][p][l] = lo;
         dsum += __shfl_xor(dsum, 16);
         dsum += __shfl_xor(dsum, 32);
         if (lg == 0) sm.den_intra[b][p][l16] = dsum;
@@ -826,9 +830,12 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
 #pragma unroll
           for (int jt = 0; jt <= it; ++jt) {
             const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.vt[b][16 * w + l16][16 * jt + 4 * lg]);
-            const bf16x4 bv = sm.a[b][pair_index(jt, it)][l];
+            const bf16x4 bh = sm.a[b][pair_index(jt, it)][l];
+            const bf16x4 bl = sm.alo[b][pair_index(jt, it)][l];
             O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
-                                                              __builtin_bit_cast(i16x4, bv), O[it], 0, 0, 0);
+                                                              __builtin_bit_cast(i16x4, bh), O[it], 0, 0, 0);
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
+                                                              __builtin_bit_cast(i16x4, bl), O[it], 0, 0, 0);
           }
       }
       // state update
