@@ -215,6 +215,12 @@ __device__ __forceinline__ void features(Smem<NT, CS, BF16, READOUT>& sm, int w,
   }
 }
 
+// x where ok holds, else zero, selected word by word (a select of the whole vector would take the
+// operands' addresses and move them to scratch memory).
+__device__ __forceinline__ uint4 keep_if(bool ok, uint4 x) {
+  return make_uint4(ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u);
+}
+
 // Chunk inputs in flight: each thread's 16-byte pieces of q, k and v for one chunk.
 template <int CS, bool BF16, bool READOUT>
 struct Prefetch {
@@ -226,33 +232,37 @@ struct Prefetch {
   static constexpr int NV = (CS * PV + kThreads - 1) / kThreads;
   uint4 q[READOUT ? NQK : 1], k[NQK], v[NV];
 
-  // Issue the global loads of the chunk starting at token tok0 (nv valid tokens; the rest read as zero).
-  __device__ __forceinline__ void load(const E* qg, const E* kg, const E* vg, long long tok0, int nv, int tid) {
+  int nv = 0;  // valid tokens of the chunk in flight
+
+  // Issue the global loads of the chunk starting at token tok0 (nv valid tokens).  Tokens past the
+  // end read the chunk's first row, and the loaded values are not touched before store(), so the
+  // loads stay in flight while the current chunk is computed.
+  __device__ __forceinline__ void load(const E* qg, const E* kg, const E* vg, long long tok0, int nv_, int tid) {
+    nv = nv_;
 #pragma unroll
     for (int u = 0; u < NQK; ++u) {
       const int p = tid + u * kThreads, row = p / PR, pc = p % PR;
-      const bool ok = p < CS * PR && row < nv;
-      k[u] = ok ? *reinterpret_cast<const uint4*>(kg + (tok0 + row) * kDK + pc * EPP) : make_uint4(0, 0, 0, 0);
-      if constexpr (READOUT)
-        q[u] = ok ? *reinterpret_cast<const uint4*>(qg + (tok0 + row) * kDK + pc * EPP) : make_uint4(0, 0, 0, 0);
+      const long long r = tok0 + (p < CS * PR && row < nv ? row : 0);
+      k[u] = *reinterpret_cast<const uint4*>(kg + r * kDK + pc * EPP);
+      if constexpr (READOUT) q[u] = *reinterpret_cast<const uint4*>(qg + r * kDK + pc * EPP);
     }
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int p = tid + u * kThreads, j = p % CS, pc = p / CS;
-      const bool ok = p < CS * PV && j < nv;
-      v[u] = ok ? *reinterpret_cast<const uint4*>(vg + (tok0 + j) * kDV + pc * EPP) : make_uint4(0, 0, 0, 0);
+      const long long r = tok0 + (p < CS * PV && j < nv ? j : 0);
+      v[u] = *reinterpret_cast<const uint4*>(vg + r * kDV + pc * EPP);
     }
   }
 
-  // Write the pieces to LDS: q, k rows as they are, v transposed.
+  // Write the pieces to LDS: q, k rows as they are, v transposed; tokens past the end as zeros.
   template <class SM>
   __device__ __forceinline__ void store(SM& sm, int tid) const {
 #pragma unroll
     for (int u = 0; u < NQK; ++u) {
       const int p = tid + u * kThreads, row = p / PR, pc = p % PR;
       if (p < CS * PR) {
-        *reinterpret_cast<uint4*>(&sm.k[row][pc * EPP]) = k[u];
-        if constexpr (READOUT) *reinterpret_cast<uint4*>(&sm.q[row][pc * EPP]) = q[u];
+        *reinterpret_cast<uint4*>(&sm.k[row][pc * EPP]) = keep_if(row < nv, k[u]);
+        if constexpr (READOUT) *reinterpret_cast<uint4*>(&sm.q[row][pc * EPP]) = keep_if(row < nv, q[u]);
       }
     }
 #pragma unroll
@@ -263,7 +273,7 @@ struct Prefetch {
           uint4 u4;
           E e[EPP];
         } buf;
-        buf.u4 = v[u];
+        buf.u4 = keep_if(j < nv, v[u]);
 #pragma unroll
         for (int r = 0; r < EPP; ++r) sm.vt[pc * EPP + r][j] = buf.e[r];
       }
@@ -600,27 +610,20 @@ struct PipeIn {
   uint4 k[2], q[READOUT ? 2 : 1], v[NVP];
   uint2 sk[READOUT ? NS : 1], sq[READOUT ? NS : 1];  // score MFMA operands of this producer's tiles
 
-  // Tokens past the end read the chunk's first row (always valid) and are then zeroed, so every
-  // load is an unconditional global load.
+  // Tokens past the end read the chunk's first row (always valid), so every load is an
+  // unconditional global load whose result is not touched until it is used a chunk later.  Only
+  // k needs masking (its features enter S and z) and that happens at unpack time; q, v and the
+  // score operands of such tokens never reach a stored output (causal mask, output guard).
   __device__ __forceinline__ void load(const __bf16* qg, const __bf16* kg, const __bf16* vg, long long tok0, int nv,
                                        int g, int l) {
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
-    const bool ok = l < nv;
-    const long long row = tok0 + (ok ? l : 0);
+    const long long row = tok0 + (l < nv ? l : 0);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const uint4 tk = *reinterpret_cast<const uint4*>(kg + row * kDK + 8 * u);
-      k[u] = ok ? tk : z4;
-      if constexpr (READOUT) {
-        const uint4 tq = *reinterpret_cast<const uint4*>(qg + row * kDK + 8 * u);
-        q[u] = ok ? tq : z4;
-      }
+      k[u] = *reinterpret_cast<const uint4*>(kg + row * kDK + 8 * u);
+      if constexpr (READOUT) q[u] = *reinterpret_cast<const uint4*>(qg + row * kDK + 8 * u);
     }
 #pragma unroll
-    for (int u = 0; u < NVP; ++u) {
-      const uint4 tv = *reinterpret_cast<const uint4*>(vg + row * kDV + 8 * (NVP * g + u));
-      v[u] = ok ? tv : z4;
-    }
+    for (int u = 0; u < NVP; ++u) v[u] = *reinterpret_cast<const uint4*>(vg + row * kDV + 8 * (NVP * g + u));
     if constexpr (READOUT) {
       const int l16 = l & 15, lg = l >> 4;
 #pragma unroll
@@ -630,11 +633,8 @@ struct PipeIn {
         while ((it + 1) * (it + 2) / 2 <= p) ++it;
         const int jt = p - it * (it + 1) / 2;
         const int rk = 16 * jt + l16, rq = 16 * it + l16;
-        const bool okk = p < 10 && rk < nv, okq = p < 10 && rq < nv;
-        const uint2 tk = *reinterpret_cast<const uint2*>(kg + (tok0 + (okk ? rk : 0)) * kDK + 4 * lg);
-        const uint2 tq = *reinterpret_cast<const uint2*>(qg + (tok0 + (okq ? rq : 0)) * kDK + 4 * lg);
-        sk[s] = okk ? tk : make_uint2(0, 0);
-        sq[s] = okq ? tq : make_uint2(0, 0);
+        sk[s] = *reinterpret_cast<const uint2*>(kg + (tok0 + (p < 10 && rk < nv ? rk : 0)) * kDK + 4 * lg);
+        sq[s] = *reinterpret_cast<const uint2*>(qg + (tok0 + (p < 10 && rq < nv ? rq : 0)) * kDK + 4 * lg);
       }
     }
   }
@@ -661,7 +661,7 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
   const int l16 = l & 15, lg = l >> 4;
   {
     float x[kDK];
-    unpack_row16(in.k, x, 1.0f);
+    unpack_row16(in.k, x, l < nv ? 1.0f : 0.0f);  // a token past the end has a zero k row
     pipe_phik_rows<NT, READOUT, G>(sm, b, l, x, l < nv);
   }
   if constexpr (READOUT) {
@@ -763,7 +763,10 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
   constexpr int CS = kPipeChunk, NIT = CS / 16;
   __shared__ SM sm;
 
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, lg = l >> 4;
+  // The role is taken from a wave-uniform scalar so each wave runs only its own loop; both loops
+  // execute exactly 2 + nch barriers.
+  const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool producer = w >= kPipeConsumers;
   const int g = w - kPipeConsumers;
   const int seg = blockIdx.x;
@@ -773,121 +776,126 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
   const long long hbase = bh * (long long)N;
   float* slot = ws + (bh * nseg + seg) * stride;
   auto chunk_nv = [&](int c) { return min(CS, t_end - (t_begin + c * CS)); };
+  auto chunk_tok0 = [&](int c) { return hbase + t_begin + (long long)c * CS; };
 
-  // consumers: running state tile; producers: z prefix of their rows, chunk 0 inputs
-  f32x4 Srun[NAT];
-  PipeIn<READOUT> in;
-  if (!producer) {
-#pragma unroll
-    for (int t = 0; t < NAT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int a = 16 * t + 4 * lg + r;
-        Srun[t][r] = (READOUT && a < W) ? slot[(long long)a * kDV + 16 * w + l16] : 0.f;
-      }
-  } else {
+  if (producer) {
+    // z prefix of this producer's rows; inputs of chunk 0 (a) and chunk 1 (b)
     const int row = g * SP::RK + l;
     if (l < SP::RK && row < WP) sm.z[0][row] = (READOUT && row < W) ? slot[(long long)W * kDV + row] : 0.f;
-    in.load(q, k, v, hbase + t_begin, chunk_nv(0), g, l);
+    PipeIn<READOUT> pa, pb;
+    pa.load(q, k, v, chunk_tok0(0), chunk_nv(0), g, l);
+    __syncthreads();  // z prefix visible to every producer
+    if (nch > 1) pb.load(q, k, v, chunk_tok0(1), chunk_nv(1), g, l);
+    pipe_produce_wave<NT, READOUT>(sm, pa, g, 0, l, chunk_nv(0), scale);
+    __syncthreads();  // chunk 0 ready
+    // Iteration c prepares chunk c+1 while the consumers work on chunk c.  The two input sets
+    // alternate (no register copies), and each chunk's loads are issued two chunks ahead of use.
+    for (int c = 0; c < nch; c += 2) {
+      if (c + 2 < nch) pa.load(q, k, v, chunk_tok0(c + 2), chunk_nv(c + 2), g, l);
+      if (c + 1 < nch) pipe_produce_wave<NT, READOUT>(sm, pb, g, (c + 1) & 1, l, chunk_nv(c + 1), scale);
+      __syncthreads();
+      if (c + 1 < nch) {
+        if (c + 3 < nch) pb.load(q, k, v, chunk_tok0(c + 3), chunk_nv(c + 3), g, l);
+        if (c + 2 < nch) pipe_produce_wave<NT, READOUT>(sm, pa, g, c & 1, l, chunk_nv(c + 2), scale);
+        __syncthreads();
+      }
+    }
+    if constexpr (!READOUT) {
+      if (l < SP::RK && row < W) slot[(long long)W * kDV + row] = sm.z[nch & 1][row];
+    }
+    return;
   }
-  __syncthreads();  // z prefix visible to every producer
-  if (producer) {
-    pipe_produce_wave<NT, READOUT>(sm, in, g, 0, l, chunk_nv(0), scale);
-    if (nch > 1) in.load(q, k, v, hbase + t_begin + CS, chunk_nv(1), g, l);
-  }
-  __syncthreads();
 
+  // ---- consumers: wave w owns value columns 16w..16w+15 ----
+  f32x4 Srun[NAT];
+#pragma unroll
+  for (int t = 0; t < NAT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int a = 16 * t + 4 * lg + r;
+      Srun[t][r] = (READOUT && a < W) ? slot[(long long)a * kDV + 16 * w + l16] : 0.f;
+    }
+  __syncthreads();
+  __syncthreads();
   for (int c = 0; c < nch; ++c) {
     const int b = c & 1;
-    if (!producer) {
-      const int nv = chunk_nv(c);
-      const long long tok0 = hbase + t_begin + c * CS;
-      f32x4 O[READOUT ? NIT : 1];
-      if constexpr (READOUT) {
+    const int nv = chunk_nv(c);
+    const long long tok0 = chunk_tok0(c);
+    f32x4 O[READOUT ? NIT : 1];
+    if constexpr (READOUT) {
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // readout with S_{<c} = hi + lo, one 32-feature k-block at a time
+      for (int it = 0; it < NIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // readout with S_{<c} = hi + lo, one 32-feature k-block at a time
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          bf16x8 hi, lo;
+      for (int kb = 0; kb < NKB; ++kb) {
+        bf16x8 hi, lo;
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const float x = r < 4 ? Srun[2 * kb][r] : Srun[2 * kb + 1][r - 4];
-            hi[r] = (__bf16)x;
-            lo[r] = (__bf16)(x - (float)hi[r]);
-          }
-#pragma unroll
-          for (int it = 0; it < NIT; ++it) {
-            const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[b][16 * it + l16][32 * kb + 8 * lg]);
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, O[it], 0, 0, 0);
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, O[it], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight (register budget)
+        for (int r = 0; r < 8; ++r) {
+          const float x = r < 4 ? Srun[2 * kb][r] : Srun[2 * kb + 1][r - 4];
+          hi[r] = (__bf16)x;
+          lo[r] = (__bf16)(x - (float)hi[r]);
         }
-        // intra-chunk V^T x scores
-#pragma unroll
-        for (int it = 0; it < NIT; ++it)
-#pragma unroll
-          for (int jt = 0; jt <= it; ++jt) {
-            const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.vt[b][16 * w + l16][16 * jt + 4 * lg]);
-            const bf16x4 bh = sm.a[b][pair_index(jt, it)][l];
-            const bf16x4 bl = sm.alo[b][pair_index(jt, it)][l];
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
-                                                              __builtin_bit_cast(i16x4, bh), O[it], 0, 0, 0);
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
-                                                              __builtin_bit_cast(i16x4, bl), O[it], 0, 0, 0);
-          }
-      }
-      // state update
-#pragma unroll
-      for (int jb = 0; jb < CS / 32; ++jb) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[b][16 * w + l16][32 * jb + 8 * lg]);
-#pragma unroll
-        for (int t = 0; t < NAT; ++t) {
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.phikt[b][16 * t + l16][32 * jb + 8 * lg]);
-          Srun[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bv, Srun[t], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (READOUT) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-          const int i = 16 * it + l16;
-          float d = 0.f;
+          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[b][16 * it + l16][32 * kb + 8 * lg]);
+          O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, O[it], 0, 0, 0);
+          O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, O[it], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight (register budget)
+      }
+      // intra-chunk V^T x scores (weights as hi + lo)
 #pragma unroll
-          for (int pp = 0; pp < kPipeProducers; ++pp) d += sm.den_part[b][pp][i];
+      for (int it = 0; it < NIT; ++it)
 #pragma unroll
-          for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][pair_index(jt, it)][l16];
-          if (i < nv) {
-            const float inv = __builtin_amdgcn_rcpf(d);
-            const f32x4 r = O[it];
-            *reinterpret_cast<f32x4*>(o + (tok0 + i) * kDV + 16 * w + 4 * lg) =
-                f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
-          }
+        for (int jt = 0; jt <= it; ++jt) {
+          const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.vt[b][16 * w + l16][16 * jt + 4 * lg]);
+          const bf16x4 bh = sm.a[b][pair_index(jt, it)][l];
+          const bf16x4 bl = sm.alo[b][pair_index(jt, it)][l];
+          O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
+                                                            __builtin_bit_cast(i16x4, bh), O[it], 0, 0, 0);
+          O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
+                                                            __builtin_bit_cast(i16x4, bl), O[it], 0, 0, 0);
+        }
+    }
+    // state update
+#pragma unroll
+    for (int jb = 0; jb < CS / 32; ++jb) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[b][16 * w + l16][32 * jb + 8 * lg]);
+#pragma unroll
+      for (int t = 0; t < NAT; ++t) {
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.phikt[b][16 * t + l16][32 * jb + 8 * lg]);
+        Srun[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bv, Srun[t], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (READOUT) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int i = 16 * it + l16;
+        float d = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < kPipeProducers; ++pp) d += sm.den_part[b][pp][i];
+#pragma unroll
+        for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][pair_index(jt, it)][l16];
+        if (i < nv) {
+          const float inv = __builtin_amdgcn_rcpf(d);
+          const f32x4 r = O[it];
+          *reinterpret_cast<f32x4*>(o + (tok0 + i) * kDV + 16 * w + 4 * lg) =
+              f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
         }
       }
-    } else if (c + 1 < nch) {
-      // issue chunk c+2's loads before computing chunk c+1, so they have a whole iteration to land
-      const PipeIn<READOUT> cur = in;
-      if (c + 2 < nch) in.load(q, k, v, hbase + t_begin + (c + 2) * CS, chunk_nv(c + 2), g, l);
-      pipe_produce_wave<NT, READOUT>(sm, cur, g, b ^ 1, l, chunk_nv(c + 1), scale);
     }
     __syncthreads();
   }
 
   if constexpr (!READOUT) {
-    if (!producer) {
 #pragma unroll
-      for (int t = 0; t < NAT; ++t)
+    for (int t = 0; t < NAT; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int a = 16 * t + 4 * lg + r;
-          if (a < W) slot[(long long)a * kDV + 16 * w + l16] = Srun[t][r];
-        }
-    } else {
-      const int row = g * SP::RK + l;
-      if (l < SP::RK && row < W) slot[(long long)W * kDV + row] = sm.z[nch & 1][row];
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int a = 16 * t + 4 * lg + r;
+        if (a < W) slot[(long long)a * kDV + 16 * w + l16] = Srun[t][r];
+      }
   }
 }
 
