@@ -509,8 +509,9 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
 // output division.  Waves 4..7 ("producers") meanwhile prepare chunk c+1 in the other half
 // of a double-buffered LDS area: phi(K)^T rows, phi(sQ) rows (slot-permuted), V^T, the
 // intra-chunk score tiles (16x16x16 MFMA + Horner + causal mask, stored as bfloat16 hi + lo
-// so the intra-chunk weights keep float32 accuracy) and the two denominator parts: phi(sq_i) . z_{<c+1} (z kept in LDS, each producer owning a quarter of the
-// features) and the row sums of the score tiles.  Producers read their inputs straight
+// so the intra-chunk weights keep float32 accuracy) and the two denominator parts:
+// phi(sq_i) . z_{<c+1} (z kept in LDS, each producer owning a quarter of the features) and
+// the row sums of the score tiles.  Producers read their inputs straight
 // from global memory, issued a whole chunk ahead.  The single barrier per chunk both hands
 // buffer c+1 to the consumers and returns buffer c to the producers.  The feature work per
 // token (vector ALU) and the LDS traffic of the operands bound this kernel; the matrix work
@@ -520,15 +521,15 @@ constexpr int kPipeConsumers = 4;  // one per 16 value columns
 constexpr int kPipeProducers = 4;
 constexpr int kPipeThreads = 64 * (kPipeConsumers + kPipeProducers);
 constexpr int kPipeChunk = 64;
+constexpr int kPipePairs = 10;  // (key tile <= query tile) pairs of 16-token tiles in a chunk
 
 template <int NT, bool READOUT>
 struct PipeSmem {
   static constexpr int WP = Geo<NT>::WP;
   static constexpr int LQ = WP + 8;           // phi(sQ) row stride (bf16)
   static constexpr int LK = kPipeChunk + 8;   // phi(K)^T and V^T row stride (bf16)
-  static constexpr int NPAIR = 10;            // (key tile <= query tile) pairs of a 64-token chunk
   static constexpr int RQ = READOUT ? kPipeChunk : 1;
-  static constexpr int RP = READOUT ? NPAIR : 1;
+  static constexpr int RP = READOUT ? kPipePairs : 1;
   alignas(16) __bf16 vt[2][kDV][LK];
   alignas(16) __bf16 phikt[2][WP][LK];
   alignas(16) __bf16 phiq[2][RQ][LQ];
@@ -541,7 +542,7 @@ struct PipeSmem {
 
 // Producer split: producer g owns phi(K)^T rows [g*RK, g*RK + RK) and phi(sQ) 8-slot groups
 // [g*RG, g*RG + RG) (clipped to the padded width); it also keeps z for its rows, writes value
-// columns [g*VC, g*VC + VC) of V^T and computes score tiles g, g + kPipeProducers.
+// columns [g*VC, g*VC + VC) of V^T and computes score tiles g, g + kPipeProducers, ...
 template <int NT>
 struct PipeSplit {
   static constexpr int WP = Geo<NT>::WP;
@@ -549,7 +550,6 @@ struct PipeSplit {
   static constexpr int NG = WP / 8;
   static constexpr int RG = (NG + kPipeProducers - 1) / kPipeProducers;
   static constexpr int VC = kDV / kPipeProducers;
-  static constexpr int NS = (10 + kPipeProducers - 1) / kPipeProducers;  // score tiles per producer
 };
 
 // A token past the end has a zero k row, so all its features are zero except the constant one.
@@ -601,21 +601,35 @@ __device__ __forceinline__ float pipe_phiq_groups(PipeSmem<NT, READOUT>& sm, int
   return acc;
 }
 
-// A producer's inputs for one chunk, loaded one chunk ahead (lane = token j of the chunk).
-template <bool READOUT>
+// Query tile and key tile of intra-chunk score pair p (pairs ordered by query tile, then key tile).
+constexpr int pair_it(int p) {
+  int it = 0;
+  while ((it + 1) * (it + 2) / 2 <= p) ++it;
+  return it;
+}
+constexpr int pair_jt(int p) { return p - pair_it(p) * (pair_it(p) + 1) / 2; }
+
+// Score pairs of producer G: G, G + kPipeProducers, ...
+template <int G>
+constexpr int producer_pairs() {
+  return G < kPipePairs ? (kPipePairs - G + kPipeProducers - 1) / kPipeProducers : 0;
+}
+
+// Producer G's inputs for one chunk, loaded a chunk ahead of use (lane = token j of the chunk).
+template <bool READOUT, int G>
 struct PipeIn {
-  static constexpr int NS = (10 + kPipeProducers - 1) / kPipeProducers;
+  static constexpr int NS = READOUT ? producer_pairs<G>() : 0;
   static constexpr int NVP = kDV / kPipeProducers / 8;  // 16-byte pieces of v per producer lane
   static_assert(NVP * 8 * kPipeProducers == kDV, "value columns split evenly over producers");
   uint4 k[2], q[READOUT ? 2 : 1], v[NVP];
-  uint2 sk[READOUT ? NS : 1], sq[READOUT ? NS : 1];  // score MFMA operands of this producer's tiles
+  uint2 sk[NS > 0 ? NS : 1], sq[NS > 0 ? NS : 1];  // score MFMA operands of this producer's tiles
 
   // Tokens past the end read the chunk's first row (always valid), so every load is an
   // unconditional global load whose result is not touched until it is used a chunk later.  Only
   // k needs masking (its features enter S and z) and that happens at unpack time; q, v and the
   // score operands of such tokens never reach a stored output (causal mask, output guard).
   __device__ __forceinline__ void load(const __bf16* qg, const __bf16* kg, const __bf16* vg, long long tok0, int nv,
-                                       int g, int l) {
+                                       int l) {
     const long long row = tok0 + (l < nv ? l : 0);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -623,20 +637,17 @@ struct PipeIn {
       if constexpr (READOUT) q[u] = *reinterpret_cast<const uint4*>(qg + row * kDK + 8 * u);
     }
 #pragma unroll
-    for (int u = 0; u < NVP; ++u) v[u] = *reinterpret_cast<const uint4*>(vg + row * kDV + 8 * (NVP * g + u));
-    if constexpr (READOUT) {
-      const int l16 = l & 15, lg = l >> 4;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const int p = g + kPipeProducers * s;
-        int it = 0;
-        while ((it + 1) * (it + 2) / 2 <= p) ++it;
-        const int jt = p - it * (it + 1) / 2;
-        const int rk = 16 * jt + l16, rq = 16 * it + l16;
-        sk[s] = *reinterpret_cast<const uint2*>(kg + (tok0 + (p < 10 && rk < nv ? rk : 0)) * kDK + 4 * lg);
-        sq[s] = *reinterpret_cast<const uint2*>(qg + (tok0 + (p < 10 && rq < nv ? rq : 0)) * kDK + 4 * lg);
-      }
-    }
+    for (int u = 0; u < NVP; ++u) v[u] = *reinterpret_cast<const uint4*>(vg + row * kDV + 8 * (NVP * G + u));
+    const int l16 = l & 15, lg = l >> 4;
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      (([&] {
+         constexpr int p = G + kPipeProducers * S;
+         const int rk = 16 * pair_jt(p) + l16, rq = 16 * pair_it(p) + l16;
+         sk[S] = *reinterpret_cast<const uint2*>(kg + (tok0 + (rk < nv ? rk : 0)) * kDK + 4 * lg);
+         sq[S] = *reinterpret_cast<const uint2*>(qg + (tok0 + (rq < nv ? rq : 0)) * kDK + 4 * lg);
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, NS>{});
   }
 };
 
@@ -654,7 +665,7 @@ __device__ __forceinline__ void unpack_row16(const uint4 (&r)[2], float (&x)[kDK
 
 // Producer wave G prepares chunk data in buffer b (chunk parity), with z_{<chunk} in z[b].
 template <int NT, bool READOUT, int G>
-__device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const PipeIn<READOUT>& in, int b, int l,
+__device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const PipeIn<READOUT, G>& in, int b, int l,
                                              int nv, float scale) {
   using SP = PipeSplit<NT>;
   constexpr int WP = Geo<NT>::WP;
@@ -671,7 +682,7 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
   }
   // V^T: this producer's value columns of token l
 #pragma unroll
-  for (int u = 0; u < PipeIn<READOUT>::NVP; ++u) {
+  for (int u = 0; u < PipeIn<READOUT, G>::NVP; ++u) {
     const uint32_t w[4] = {in.v[u].x, in.v[u].y, in.v[u].z, in.v[u].w};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -681,33 +692,30 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
   }
   if constexpr (READOUT) {
     // intra-chunk score tiles of this wave's pairs, and their row sums (denominator part)
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      (([&] {
+         constexpr int p = G + kPipeProducers * S, it = pair_it(p), jt = pair_jt(p);
+         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+         sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, in.sk[S]),
+                                                        __builtin_bit_cast(i16x4, in.sq[S]), sc, 0, 0, 0);
+         bf16x4 hi, lo;
+         float dsum = 0.f;
 #pragma unroll
-    for (int s = 0; s < SP::NS; ++s) {
-      const int p = G + kPipeProducers * s;
-      if (p < 10) {
-        int it = 0;
-        while ((it + 1) * (it + 2) / 2 <= p) ++it;
-        const int jt = p - it * (it + 1) / 2;
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-        sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, in.sk[s]),
-                                                       __builtin_bit_cast(i16x4, in.sq[s]), sc, 0, 0, 0);
-        bf16x4 hi, lo;
-        float dsum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
-          const float wgt = j <= i ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
-          hi[r] = (__bf16)wgt;
-          lo[r] = (__bf16)(wgt - (float)hi[r]);
-          dsum += wgt;
-        }
-        sm.a[b][p][l] = hi;
-        sm.alo[b][p][l] = lo;
-        dsum += __shfl_xor(dsum, 16);
-        dsum += __shfl_xor(dsum, 32);
-        if (lg == 0) sm.den_intra[b][p][l16] = dsum;
-      }
-    }
+         for (int r = 0; r < 4; ++r) {
+           const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
+           const float wgt = (jt < it || j <= i) ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
+           hi[r] = (__bf16)wgt;
+           lo[r] = (__bf16)(wgt - (float)hi[r]);
+           dsum += wgt;
+         }
+         sm.a[b][p][l] = hi;
+         sm.alo[b][p][l] = lo;
+         dsum += __shfl_xor(dsum, 16);
+         dsum += __shfl_xor(dsum, 32);
+         if (lg == 0) sm.den_intra[b][p][l16] = dsum;
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, PipeIn<READOUT, G>::NS>{});
   }
   // z_{<next} = z_{<this} + column sums of this wave's phi(K)^T rows (read back from LDS: the
   // rows were written by this same wave above, and a wave's LDS accesses complete in order)
@@ -727,25 +735,48 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
   }
 }
 
-template <int NT, bool READOUT>
-__device__ __forceinline__ void pipe_produce_wave(PipeSmem<NT, READOUT>& sm, const PipeIn<READOUT>& in, int g, int b,
-                                                  int l, int nv, float scale) {
-  static_assert(kPipeProducers <= 8, "dispatch below lists up to 8 producers");
-  switch (g) {
-    case 0: pipe_produce<NT, READOUT, 0>(sm, in, b, l, nv, scale); break;
-    case 1: pipe_produce<NT, READOUT, 1>(sm, in, b, l, nv, scale); break;
-    case 2: pipe_produce<NT, READOUT, 2>(sm, in, b, l, nv, scale); break;
-    case 3: pipe_produce<NT, READOUT, 3>(sm, in, b, l, nv, scale); break;
-    default:
-      if constexpr (kPipeProducers > 4) {
-        switch (g) {
-          case 4: pipe_produce<NT, READOUT, 4>(sm, in, b, l, nv, scale); break;
-          case 5: pipe_produce<NT, READOUT, 5>(sm, in, b, l, nv, scale); break;
-          case 6: pipe_produce<NT, READOUT, 6>(sm, in, b, l, nv, scale); break;
-          default: pipe_produce<NT, READOUT, 7>(sm, in, b, l, nv, scale); break;
-        }
-      }
-      break;
+// Producer G over one segment of nch chunks.  Phase c (consumers on chunk c) prepares chunk c+1
+// in buffer (c+1) & 1 and issues the loads of chunk c+2; the two register sets a and b alternate
+// so no loaded value is copied.  The steady-state loop has no conditional load or produce (every
+// load issued in it is consumed in it), so the compiler's memory-counter waits stay exact; the
+// last one to three phases are peeled.  Executes exactly 2 + nch barriers.
+template <int NT, bool READOUT, int G>
+__device__ __forceinline__ void pipe_producer(PipeSmem<NT, READOUT>& sm, const __bf16* q, const __bf16* k,
+                                              const __bf16* v, float* slot, long long tok_base, int n_tok, int nch,
+                                              int l, float scale) {
+  using SP = PipeSplit<NT>;
+  constexpr int W = Geo<NT>::W, WP = Geo<NT>::WP, CS = kPipeChunk;
+  auto nv_of = [&](int c) { return min(CS, n_tok - c * CS); };
+  auto tok_of = [&](int c) { return tok_base + (long long)c * CS; };
+  // z prefix of this producer's rows
+  const int row = G * SP::RK + l;
+  if (l < SP::RK && row < WP) sm.z[0][row] = (READOUT && row < W) ? slot[(long long)W * kDV + row] : 0.f;
+  PipeIn<READOUT, G> pa, pb;
+  pa.load(q, k, v, tok_of(0), nv_of(0), l);
+  __syncthreads();  // z prefix visible to every producer
+  if (nch > 1) pb.load(q, k, v, tok_of(1), nv_of(1), l);
+  pipe_produce<NT, READOUT, G>(sm, pa, 0, l, nv_of(0), scale);
+  __syncthreads();  // chunk 0 ready
+  int c = 0;
+  for (; c + 3 < nch; c += 2) {
+    pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l);
+    pipe_produce<NT, READOUT, G>(sm, pb, (c + 1) & 1, l, nv_of(c + 1), scale);
+    __syncthreads();
+    pb.load(q, k, v, tok_of(c + 3), nv_of(c + 3), l);
+    pipe_produce<NT, READOUT, G>(sm, pa, c & 1, l, nv_of(c + 2), scale);
+    __syncthreads();
+  }
+  // nch - c phases remain (1 to 3); chunks c+1 and c+2 may still need preparing
+  if (c + 2 < nch) pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l);
+  if (c + 1 < nch) pipe_produce<NT, READOUT, G>(sm, pb, (c + 1) & 1, l, nv_of(c + 1), scale);
+  __syncthreads();
+  if (c + 1 < nch) {
+    if (c + 2 < nch) pipe_produce<NT, READOUT, G>(sm, pa, c & 1, l, nv_of(c + 2), scale);
+    __syncthreads();
+    if (c + 2 < nch) __syncthreads();
+  }
+  if constexpr (!READOUT) {
+    if (l < SP::RK && row < W) slot[(long long)W * kDV + row] = sm.z[nch & 1][row];
   }
 }
 
@@ -758,8 +789,7 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
                                                                     float scale) {
   using G = Geo<NT>;
   using SM = PipeSmem<NT, READOUT>;
-  using SP = PipeSplit<NT>;
-  constexpr int W = G::W, WP = G::WP, NAT = G::NAT, NKB = G::NKB;
+  constexpr int W = G::W, NAT = G::NAT, NKB = G::NKB;
   constexpr int CS = kPipeChunk, NIT = CS / 16;
   __shared__ SM sm;
 
@@ -779,30 +809,26 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
   auto chunk_tok0 = [&](int c) { return hbase + t_begin + (long long)c * CS; };
 
   if (producer) {
-    // z prefix of this producer's rows; inputs of chunk 0 (a) and chunk 1 (b)
-    const int row = g * SP::RK + l;
-    if (l < SP::RK && row < WP) sm.z[0][row] = (READOUT && row < W) ? slot[(long long)W * kDV + row] : 0.f;
-    PipeIn<READOUT> pa, pb;
-    pa.load(q, k, v, chunk_tok0(0), chunk_nv(0), g, l);
-    __syncthreads();  // z prefix visible to every producer
-    if (nch > 1) pb.load(q, k, v, chunk_tok0(1), chunk_nv(1), g, l);
-    pipe_produce_wave<NT, READOUT>(sm, pa, g, 0, l, chunk_nv(0), scale);
-    __syncthreads();  // chunk 0 ready
-    // Iteration c prepares chunk c+1 while the consumers work on chunk c.  The two input sets
-    // alternate (no register copies), and each chunk's loads are issued two chunks ahead of use.
-    for (int c = 0; c < nch; c += 2) {
-      if (c + 2 < nch) pa.load(q, k, v, chunk_tok0(c + 2), chunk_nv(c + 2), g, l);
-      if (c + 1 < nch) pipe_produce_wave<NT, READOUT>(sm, pb, g, (c + 1) & 1, l, chunk_nv(c + 1), scale);
-      __syncthreads();
-      if (c + 1 < nch) {
-        if (c + 3 < nch) pb.load(q, k, v, chunk_tok0(c + 3), chunk_nv(c + 3), g, l);
-        if (c + 2 < nch) pipe_produce_wave<NT, READOUT>(sm, pa, g, c & 1, l, chunk_nv(c + 2), scale);
-        __syncthreads();
-      }
+    static_assert(kPipeProducers <= 8, "dispatch below lists up to 8 producers");
+    const long long tok_base = hbase + t_begin;
+    const int n_tok = t_end - t_begin;
+#define TAYLOR_PRODUCER(G_)                                                                           \
+  case G_:                                                                                          \
+    if constexpr (G_ < kPipeProducers)                                                              \
+      pipe_producer<NT, READOUT, G_>(sm, q, k, v, slot, tok_base, n_tok, nch, l, scale);            \
+    break;
+    switch (g) {
+      TAYLOR_PRODUCER(0)
+      TAYLOR_PRODUCER(1)
+      TAYLOR_PRODUCER(2)
+      TAYLOR_PRODUCER(3)
+      TAYLOR_PRODUCER(4)
+      TAYLOR_PRODUCER(5)
+      TAYLOR_PRODUCER(6)
+      TAYLOR_PRODUCER(7)
+      default: break;
     }
-    if constexpr (!READOUT) {
-      if (l < SP::RK && row < W) slot[(long long)W * kDV + row] = sm.z[nch & 1][row];
-    }
+#undef TAYLOR_PRODUCER
     return;
   }
 
