@@ -51,6 +51,18 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bfloat16 (nearest even) by one conversion instruction.
+__device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, bf16x2); }
+
+// Splits x = (a, b) into bfloat16 pairs hi = bf16(x), lo = bf16(x - hi), so hi + lo carries x to
+// about 16 significant bits.
+__device__ __forceinline__ void split_bf16x2(float a, float b, bf16x2& hi, bf16x2& lo) {
+  hi = to_bf16x2(a, b);
+  const uint32_t u = __builtin_bit_cast(uint32_t, hi);
+  lo = to_bf16x2(a - __uint_as_float(u << 16), b - __uint_as_float(u & 0xffff0000u));
+}
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDK = 16, kDV = 64;
@@ -567,7 +579,7 @@ __device__ __forceinline__ void pipe_phik_rows(PipeSmem<NT, READOUT>& sm, int b,
            f0 = valid ? 1.f : 0.f;
          else
            f0 = feat<NT, r0>(x);
-         const bf16x2 pr = {(__bf16)f0, (__bf16)feat<NT, r1>(x)};
+         const bf16x2 pr = to_bf16x2(f0, feat<NT, r1>(x));
          const uint32_t u = __builtin_bit_cast(uint32_t, pr);
          *reinterpret_cast<uint16_t*>(&sm.phikt[b][r0][j]) = (uint16_t)u;
          *reinterpret_cast<uint16_t*>(&sm.phikt[b][r1][j]) = (uint16_t)(u >> 16);
@@ -588,12 +600,15 @@ __device__ __forceinline__ float pipe_phiq_groups(PipeSmem<NT, READOUT>& sm, int
        constexpr int grp = G * SP::RG + P;
        if constexpr (grp < SP::NG) {
          constexpr int s0 = grp * 8;
-         bf16x8 v;
+         uint32_t v[4];
          [&]<int... R>(std::integer_sequence<int, R...>) {
-           ((v[R] = (__bf16)feat<NT, slot_feature_bf16(s0 + R)>(x)), ...);
-           ((acc = fmaf((float)v[R], sm.z[zb][slot_feature_bf16(s0 + R)], acc)), ...);
-         }(std::make_integer_sequence<int, 8>{});
-         *reinterpret_cast<bf16x8*>(&sm.phiq[b][j][s0]) = v;
+           ((v[R] = __builtin_bit_cast(uint32_t, to_bf16x2(feat<NT, slot_feature_bf16(s0 + 2 * R)>(x),
+                                                            feat<NT, slot_feature_bf16(s0 + 2 * R + 1)>(x)))),
+            ...);
+           ((acc = fmaf(__uint_as_float(v[R] << 16), sm.z[zb][slot_feature_bf16(s0 + 2 * R)], acc)), ...);
+           ((acc = fmaf(__uint_as_float(v[R] & 0xffff0000u), sm.z[zb][slot_feature_bf16(s0 + 2 * R + 1)], acc)), ...);
+         }(std::make_integer_sequence<int, 4>{});
+         *reinterpret_cast<uint4*>(&sm.phiq[b][j][s0]) = make_uint4(v[0], v[1], v[2], v[3]);
        }
      }()),
      ...);
@@ -672,8 +687,10 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
   const int l16 = l & 15, lg = l >> 4;
   {
     float x[kDK];
-    unpack_row16(in.k, x, l < nv ? 1.0f : 0.0f);  // a token past the end has a zero k row
-    pipe_phik_rows<NT, READOUT, G>(sm, b, l, x, l < nv);
+    const bool valid = l < nv;  // a token past the end has a zero k row
+    const uint4 kr[2] = {keep_if(valid, in.k[0]), keep_if(valid, in.k[1])};
+    unpack_row16(kr, x, 1.0f);
+    pipe_phik_rows<NT, READOUT, G>(sm, b, l, x, valid);
   }
   if constexpr (READOUT) {
     float x[kDK];
@@ -698,21 +715,24 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
          f32x4 sc = {0.f, 0.f, 0.f, 0.f};
          sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, in.sk[S]),
                                                         __builtin_bit_cast(i16x4, in.sq[S]), sc, 0, 0, 0);
-         bf16x4 hi, lo;
-         float dsum = 0.f;
+         float wgt[4];
 #pragma unroll
          for (int r = 0; r < 4; ++r) {
            const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
-           const float wgt = (jt < it || j <= i) ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
-           hi[r] = (__bf16)wgt;
-           lo[r] = (__bf16)(wgt - (float)hi[r]);
-           dsum += wgt;
+           wgt[r] = (jt < it || j <= i) ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
          }
+         bf16x2 h0, l0, h1, l1;
+         split_bf16x2(wgt[0], wgt[1], h0, l0);
+         split_bf16x2(wgt[2], wgt[3], h1, l1);
+         const bf16x4 hi = {h0[0], h0[1], h1[0], h1[1]}, lo = {l0[0], l0[1], l1[0], l1[1]};
          sm.a[b][p][l] = hi;
          sm.alo[b][p][l] = lo;
-         dsum += __shfl_xor(dsum, 16);
-         dsum += __shfl_xor(dsum, 32);
-         if (lg == 0) sm.den_intra[b][p][l16] = dsum;
+         // column sums over the 16 key rows, as ones^T (hi + lo): every row of the product holds them
+         const i16x4 ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
+         f32x4 cs = {0.f, 0.f, 0.f, 0.f};
+         cs = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_bit_cast(i16x4, hi), cs, 0, 0, 0);
+         cs = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_bit_cast(i16x4, lo), cs, 0, 0, 0);
+         if (lg == 0) sm.den_intra[b][p][l16] = cs[0];
        }()),
        ...);
     }(std::make_integer_sequence<int, PipeIn<READOUT, G>::NS>{});
@@ -854,13 +874,14 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
       // readout with S_{<c} = hi + lo, one 32-feature k-block at a time
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        bf16x8 hi, lo;
+        bf16x2 h[4], lw[4];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float x = r < 4 ? Srun[2 * kb][r] : Srun[2 * kb + 1][r - 4];
-          hi[r] = (__bf16)x;
-          lo[r] = (__bf16)(x - (float)hi[r]);
+        for (int r = 0; r < 4; ++r) {
+          const f32x4& src = Srun[2 * kb + (r >> 1)];
+          split_bf16x2(src[2 * (r & 1)], src[2 * (r & 1) + 1], h[r], lw[r]);
         }
+        const bf16x8 hi = {h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+        const bf16x8 lo = {lw[0][0], lw[0][1], lw[1][0], lw[1][1], lw[2][0], lw[2][1], lw[3][0], lw[3][1]};
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[b][16 * it + l16][32 * kb + 8 * lg]);
