@@ -81,14 +81,17 @@ def test_prefill_fp32_config():
     print(f"rel err vs oracle {err:.2e}; truncated (n=3) vs softmax max-abs/max {np.max(np.abs(ref - soft)) / np.max(np.abs(soft)):.2e}")
 
 
-def test_resume_from_state():
-    # prefill(N1) then prefill(N2 | state) equals prefill(N1 + N2) (chunk additivity, Abstract).
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N1,N2", [(700, 517), (700, 50), (64, 1000)])
+def test_resume_from_state(dtype, N1, N2):
+    # prefill(N1) then prefill(N2 | state) equals prefill(N1 + N2) (chunk additivity, Abstract);
+    # N2 = 50 is a single chunk (one segment), the others span several segments.
     import torch
 
-    n, N1, N2 = 3, 700, 517
-    x = synth.make_qkv(60, 1, 3, N1 + N2, 16, 64)
-    cfg = rs.config(n, 16, 64, 64)
-    announce("resume", N1, N2)
+    n = 3
+    x = synth.make_qkv(60, 1, 3, N1 + N2, 16, 64, dtype)
+    cfg = rs.config(n, 16, 64, 64, 1.0, rs.TAYLOR_BF16 if dtype == "bf16" else rs.TAYLOR_F32)
+    announce("resume", dtype, N1, N2)
     q, k, v = x.torch(DEV)
     st = rs.new_state(1, 3, cfg, DEV)
     o1 = torch.empty((1, 3, N1, 64), device=DEV)
@@ -99,13 +102,33 @@ def test_resume_from_state():
     rs.taylor_attn_prefill(*parts, o2, st, rs.new_workspace(cfg, 1, 3, N2, DEV), cfg)
     ref, den = _oracle(x, n, 1.0)
     err, _ = row_rel_err(torch.cat([o1, o2], dim=2).cpu().numpy(), ref, den)
-    assert err <= 1e-5
-    # and the final state is the state of all N1 + N2 tokens
+    assert err <= tol_for(dtype), err
+    # and the final state is the state of all N1 + N2 tokens.  With bfloat16 inputs the kernel
+    # rounds each phi(k_j) to bfloat16 (relative 2^-9) before the state product, so entry (f, c)
+    # may be off by up to 2^-9 sum_j |phi_f(k_j) v_jc|; the bar allows twice that.
     S, z = rs.state_views(st, cfg)
     for h in range(3):
         full = oracle.state(x.k64[0, h], x.v64[0, h], n)
         got = np.concatenate([S[0, h].cpu().numpy(), z[0, h].cpu().numpy()[:, None]], axis=1)
-        assert np.max(np.abs(got - full)) <= 1e-5 * np.max(np.abs(full))
+        if dtype == "bf16":
+            bound = 2.0**-8 * oracle.state(np.abs(x.k64[0, h]), np.abs(x.v64[0, h]), n)
+            assert np.all(np.abs(got - full) <= bound + 1e-6 * np.max(np.abs(full)))
+        else:
+            assert np.max(np.abs(got - full)) <= 1e-5 * np.max(np.abs(full))
+
+
+def test_outputs_without_state_buffer():
+    # state = NULL: empty history, final state discarded; outputs as with a zeroed state.
+    x = synth.make_qkv(62, 1, 2, 900, 16, 64, "bf16")
+    cfg = rs.config(3, 16, 64, 64, 1.0, rs.TAYLOR_BF16)
+    announce("no-state", 900)
+    import torch
+
+    q, k, v = x.torch(DEV)
+    o = torch.empty((1, 2, 900, 64), device=DEV)
+    rs.taylor_attn_prefill(q, k, v, o, None, rs.new_workspace(cfg, 1, 2, 900, DEV), cfg)
+    o2, _ = run_prefill(x, cfg, DEV, state=rs.new_state(1, 2, cfg, DEV))
+    assert torch.equal(o, o2)
 
 
 @pytest.mark.parametrize("n", [1, 3, 5])
