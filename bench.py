@@ -104,6 +104,62 @@ def cpu_baseline(x, budget_s=12.0):
     }
 
 
+def big_decode(rs, synth, torch, dev, seqs=512, steps=100, reps=3, eager=False):
+    """Decode with a state set larger than the 256 MB last-level cache (512 sequences x 16 heads:
+    326 MB of float32 state), so every step streams the states from HBM.  States come from a
+    state-only prefill of a 256-token seeded prefix (the per-step cost does not depend on the
+    history length); the steps are replayed from one HIP graph (launched one by one with `eager`).
+    Returns a dict for the JSON line."""
+    import ctypes
+
+    cfg = rs.config(NT, DK, DV, PC, 1.0, rs.TAYLOR_F32)
+    st = rs.new_state(seqs, DH, cfg, dev)
+    _, kp, vp = synth.device_qkv(6, seqs, DH, 256, DK, DV, dev, need_q=False)
+    rs.taylor_attn_prefill(None, kp, vp, None, st, rs.new_workspace(cfg, seqs, DH, 256, dev), cfg)
+    del kp, vp
+    q, k, v = synth.device_qkv(6, steps, seqs * DH, 1, DK, DV, dev, salt=1)
+    o = torch.empty((steps, seqs * DH, DV), dtype=torch.float32, device=dev)
+    f = rs.lib().taylor_attn_decode_step
+    cp = ctypes.byref(cfg)
+
+    def run(stream_handle):
+        for t in range(steps):
+            rc = f(q[t].data_ptr(), k[t].data_ptr(), v[t].data_ptr(), o[t].data_ptr(), st.data_ptr(), seqs, DH, cp,
+                   stream_handle)
+            if rc:
+                raise rs.TaylorError(rc, "taylor_attn_decode_step")
+
+    g = None
+    if not eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(torch.cuda.current_stream().cuda_stream)
+    else:
+        run(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        if g is not None:
+            g.replay()
+        else:
+            run(torch.cuda.current_stream().cuda_stream)
+    e1.record()
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all())
+    us = e0.elapsed_time(e1) * 1e3 / (reps * steps)
+    nbytes = seqs * DH * DECODE_BYTES_PER_HEAD
+    return {"sequences": seqs, "heads": DH, "state_MB": seqs * DH * STATE_BYTES / 1e6, "steps": steps * reps,
+            "launch": "eager" if eager else "hip graph of %d steps" % steps,
+            "us_per_step": us, "achieved_GBs": nbytes / us / 1e3, "frac_hbm": nbytes / us / 1e3 / HBM_PEAK_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +168,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=DSTEPS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager-decode", action="store_true", help="launch decode steps one by one (no graph)")
+    ap.add_argument("--no-big-decode", action="store_true",
+                    help="skip the secondary decode run whose states exceed the last-level cache")
+    ap.add_argument("--big-decode-steps", type=int, default=100)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (scale reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -273,6 +332,12 @@ def main():
         },
         "wall_s_timed": wall,
     }
+    if not args.no_big_decode:
+        log("decode with states above the last-level cache")
+        del dq, dk_, dv_, dout, graph
+        torch.cuda.empty_cache()
+        out["decode_llc_defeating"] = big_decode(rs, synth, torch, dev, steps=args.big_decode_steps,
+                                                 eager=args.eager_decode)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(x)
