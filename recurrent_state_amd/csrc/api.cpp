@@ -12,6 +12,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "prefill_mfma.hpp"
+#include "prefill_wide.hpp"
 
 namespace {
 
@@ -48,10 +49,11 @@ int check_config(const taylor_config* cfg, Shape* s) {
 
 int chunk_of(const taylor_config* cfg) { return cfg->chunk == 0 ? kDefaultChunk : cfg->chunk; }
 
-enum class Path { None, Generic, Mfma };
+enum class Path { None, Generic, Mfma, Wide };
 
 Path prefill_path(const Shape& s, int C) {
   if (taylor::prefill_mfma_has(s.nt, s.dk, s.dv, C)) return Path::Mfma;
+  if (taylor::prefill_wide_has(s.nt, s.dk, s.dv)) return Path::Wide;
   if (taylor::prefill_generic_has(s.nt, s.dk, s.dv, C)) return Path::Generic;
   return Path::None;
 }
@@ -74,6 +76,7 @@ int64_t ws_bytes(const Shape& s, int C, int BH, int N) {
   if (BH == 0 || N == 0) return 0;
   switch (prefill_path(s, C)) {
     case Path::Mfma: return taylor::prefill_mfma_ws_bytes(s, BH, N, C);
+    case Path::Wide: return taylor::prefill_wide_ws_bytes(s, BH, N);
     case Path::Generic: return taylor::prefill_generic_ws_bytes(s, BH, N, C);
     default: return TAYLOR_ERR_UNSUPPORTED;
   }
@@ -187,8 +190,11 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, float* o, f
   a.N = N;
   a.C = C;
   a.stream = stream;
-  return map_launch(prefill_path(s, C) == Path::Mfma ? taylor::prefill_mfma_launch(a)
-                                                       : taylor::prefill_generic_launch(a));
+  switch (prefill_path(s, C)) {
+    case Path::Mfma: return map_launch(taylor::prefill_mfma_launch(a));
+    case Path::Wide: return map_launch(taylor::prefill_wide_launch(a));
+    default: return map_launch(taylor::prefill_generic_launch(a));
+  }
 }
 
 int taylor_attn_decode_step(const void* q, const void* k, const void* v, float* o, float* state, int B, int H,

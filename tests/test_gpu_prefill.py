@@ -117,6 +117,35 @@ def test_resume_from_state(dtype, N1, N2):
             assert np.max(np.abs(got - full)) <= 1e-5 * np.max(np.abs(full))
 
 
+@pytest.mark.parametrize("n", [4, 5])
+def test_resume_from_state_wide(n):
+    # n = 4, 5 run in 128-feature blocks.  With 8 heads, n = 5 has enough (head, block) pairs for one
+    # segment (the readout pass starts from the incoming state and writes the final state itself);
+    # n = 4 uses several segments (state pass + scan).
+    import torch
+
+    N1, N2, H = 300, 233, 8
+    x = synth.make_qkv(63, 1, H, N1 + N2, 16, 64)
+    cfg = rs.config(n, 16, 64, 64)
+    announce("resume-wide", n, N1, N2)
+    q, k, v = x.torch(DEV)
+    st = rs.new_state(1, H, cfg, DEV)
+    outs = []
+    for lo, hi in ((0, N1), (N1, N1 + N2)):
+        parts = [t[:, :, lo:hi].contiguous() for t in (q, k, v)]
+        o = torch.empty((1, H, hi - lo, 64), device=DEV)
+        rs.taylor_attn_prefill(*parts, o, st, rs.new_workspace(cfg, 1, H, hi - lo, DEV), cfg)
+        outs.append(o)
+    ref, den = _oracle(x, n, 1.0)
+    err, _ = row_rel_err(torch.cat(outs, dim=2).cpu().numpy(), ref, den)
+    assert err <= 1e-5, err
+    S, z = rs.state_views(st, cfg)
+    for h in (0, H - 1):
+        full = oracle.state(x.k64[0, h], x.v64[0, h], n)
+        got = np.concatenate([S[0, h].cpu().numpy(), z[0, h].cpu().numpy()[:, None]], axis=1)
+        assert np.max(np.abs(got - full)) <= 1e-5 * np.max(np.abs(full))
+
+
 def test_outputs_without_state_buffer():
     # state = NULL: empty history, final state discarded; outputs as with a zeroed state.
     x = synth.make_qkv(62, 1, 2, 900, 16, 64, "bf16")
