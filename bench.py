@@ -160,6 +160,38 @@ def big_decode(rs, synth, torch, dev, seqs=512, steps=100, reps=3, eager=False):
             "us_per_step": us, "achieved_GBs": nbytes / us / 1e3, "frac_hbm": nbytes / us / 1e3 / HBM_PEAK_GBS}
 
 
+def order_sweep(rs, synth, torch, dev, reps=3):
+    """Prefill at the order-sweep shape (B=1, H=16, N=16,384, float32, chunk 64) for n = 1..5, timed with
+    HIP events (state init + prefill, as in the main step).  Algorithmic flops per token-head:
+    2*W*65 (state update) + 2*W*65 (readout) + intra-chunk scores 2*d_k*(C+1)/2 + PV 2*65*(C+1)/2."""
+    B, H, N, C = 1, 16, 16384, 64
+    x = synth.make_qkv(5, B, H, N, DK, DV, synth.F32)
+    q, k, v = x.torch(dev)
+    o = torch.empty((B, H, N, DV), dtype=torch.float32, device=dev)
+    res = {}
+    for n in range(1, 6):
+        cfg = rs.config(n, DK, DV, C, 1.0, rs.TAYLOR_F32)
+        st = torch.empty((B, H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
+        ws = rs.new_workspace(cfg, B, H, N, dev)
+        rs.taylor_state_init(st, cfg)
+        rs.taylor_attn_prefill(q, k, v, o, st, ws, cfg)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            rs.taylor_state_init(st, cfg)
+            rs.taylor_attn_prefill(q, k, v, o, st, ws, cfg)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        W = rs.taylor_feature_width(n, DK)
+        flops = B * H * N * (4 * W * (DV + 1) + DK * (C + 1) + (DV + 1) * (C + 1))
+        res[f"n{n}"] = {"W": W, "us": us, "tok_s": B * N / us * 1e6, "TFLOPs": flops / us / 1e6,
+                        "frac_fp32_mfma": flops / us / 1e6 / FP32_PEAK_TFLOPS}
+        del ws, st
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +203,7 @@ def main():
     ap.add_argument("--no-big-decode", action="store_true",
                     help="skip the secondary decode run whose states exceed the last-level cache")
     ap.add_argument("--big-decode-steps", type=int, default=100)
+    ap.add_argument("--no-order-sweep", action="store_true", help="skip the n = 1..5 float32 prefill timings")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (scale reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -338,6 +371,9 @@ def main():
         torch.cuda.empty_cache()
         out["decode_llc_defeating"] = big_decode(rs, synth, torch, dev, steps=args.big_decode_steps,
                                                  eager=args.eager_decode)
+    if not args.no_order_sweep:
+        log("order sweep n = 1..5 (float32 prefill, B1 H16 N16384)")
+        out["order_sweep_prefill_f32_B1xH16xN16384"] = order_sweep(rs, synth, torch, dev)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(x)

@@ -956,7 +956,7 @@ int n_segments(int BH, int nchunk, int target) {
   return (int)want;
 }
 
-constexpr int kSegTarget = 512;
+constexpr int kSegTarget = 256;
 
 template <int NT, int CS, bool BF16>
 int run(const PrefillArgs& a) {
