@@ -8,16 +8,20 @@
 // At n = 4, 5 the state (W x 65 floats per head, up to 1.26 MB) fits neither registers nor LDS.  But
 // each feature row of S evolves on its own (S_f += phi_f(K_c)^T V1_c involves only features f), and the
 // readout phi(sQ) S_{<c} = sum_f phi_f(sQ) S_{f,<c} is a sum over feature blocks f.  So the work is split
-// over (segment, head, block of 128 features):
-//   * a workgroup of 4 wavefronts walks the chunks of its segment for one feature block; wave w keeps
-//     value columns 16w..16w+15 of the block's state slice in MFMA accumulator registers and the block's
-//     z lives in LDS;
-//   * per chunk all four waves expand the block's features of the chunk's k and sq rows into LDS (one
-//     token per lane, 32 features per wave, coordinates fixed at compile time per block), then each wave
-//     runs the float32 16x16x4 MFMAs of its columns: readout with S_{<c}, then the state update;
-//   * the block's partial numerators phi_f(sQ) S_{f,<c} and partial denominators phi_f(sQ) z_{f,<c} go
-//     to a workspace; block 0 also adds the intra-chunk term; a reduction kernel sums the blocks in
-//     order and divides.
+// over (segment, head, block of FB features; FB = 64 at n = 4, 128 at n = 5), one workgroup of 8
+// wavefronts each:
+//   * waves 0..3 ("consumers") own value columns 16w..16w+15 of the block's state slice, kept in MFMA
+//     accumulator registers, and run only float32 16x16x4 MFMAs on chunk c: the readout with S_{<c}, the
+//     intra-chunk PV (block 0), the state update;
+//   * waves 4..7 ("producers") meanwhile prepare chunk c+1 in the other half of a double-buffered LDS
+//     area: producer g expands features g*FB/4 .. of the block for the chunk's 32 tokens (lanes 0..31
+//     from k into phi(K)^T, lanes 32..63 from sq into phi(sQ), the same compile-time code on both
+//     halves), writes its V^T columns, its part of the denominators phi_f(sq) . z_{f,<c} and updates the
+//     block's z rows it owns; for block 0 producers 0..2 also build the three intra-chunk score tiles and
+//     their column sums.  Their inputs are global loads issued a chunk ahead, in two alternating register
+//     sets;
+//   * one barrier per chunk; each block writes partial numerators and denominators per token to a
+//     workspace and a reduction kernel sums the blocks in order and divides.
 // Segments, when (head, block) pairs alone do not fill the chip: a state pass writes each segment's
 // increment, the scan turns them into exclusive prefixes and the readout pass starts from them.  With
 // one segment the readout pass starts from the incoming state and writes the final state itself.
@@ -35,34 +39,45 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDK = 16, kDV = 64;
-constexpr int kCS = 64;          // tokens per chunk
-constexpr int kFB = 128;         // features per block
-constexpr int kSub = kFB / 4;    // features per wave in the expansion
-constexpr int kNAT = kFB / 16;   // 16-row tiles of the block's state slice
+constexpr int kCS = 32;          // tokens per chunk
+constexpr int kProd = 4;         // producer waves, FB / 4 features each
+constexpr int kCons = 4;         // consumer waves, 16 value columns each
+constexpr int kThreads = 64 * (kProd + kCons);
 constexpr int kNIT = kCS / 16;   // 16-token tiles of a chunk
-constexpr int kPairs = kNIT * (kNIT + 1) / 2;
-constexpr int kThreads = 256;
-constexpr int kLS = kCS + 4;     // phi(K)^T and V^T row stride in floats (68 = 4 mod 64 banks)
-constexpr int kLQ = kFB + 4;     // phi(sQ) row stride in floats (132 = 4 mod 64 banks)
+constexpr int kPairs = kNIT * (kNIT + 1) / 2;  // (key tile <= query tile) pairs
+constexpr int kLS = kCS + 4;     // phi(K)^T and V^T row stride in floats (36: conflict-free 16-byte reads)
+static_assert(kPairs <= kProd, "one score tile per producer");
 
+// Features per block: 64 at n = 4 (16 blocks: enough (head, block) workgroups at few heads without a
+// state pass), 128 at n = 5 (38 blocks; half the partial-output traffic of 64).
+template <int NT>
+constexpr int block_features() {
+  return NT == 4 ? 64 : 128;
+}
 template <int NT>
 constexpr int n_blocks() {
-  return (FeatureTable<NT, kDK>::W + kFB - 1) / kFB;
+  return (FeatureTable<NT, kDK>::W + block_features<NT>() - 1) / block_features<NT>();
 }
 
-template <bool READOUT>
+constexpr int pair_it(int p) {
+  int it = 0;
+  while ((it + 1) * (it + 2) / 2 <= p) ++it;
+  return it;
+}
+constexpr int pair_jt(int p) { return p - pair_it(p) * (pair_it(p) + 1) / 2; }
+
+template <bool READOUT, int FB>
 struct WideSmem {
   static constexpr int RQ = READOUT ? kCS : 1;
   static constexpr int RP = READOUT ? kPairs : 1;
-  alignas(16) float phikt[kFB][kLS];  // phi_f(k_j), feature-major
-  alignas(16) float vt[kDV][kLS];     // V^T
-  alignas(16) float phiq[RQ][kLQ];    // phi_f(s q_i), token-major
-  alignas(16) float kr[RQ][kDK];      // block 0: raw k rows (scores)
-  alignas(16) float qr[RQ][kDK];      // block 0: raw q rows
-  alignas(16) f32x4 a[RP][64];        // block 0: score tiles in MFMA B-operand lane order
-  alignas(16) float z[kFB];           // the block's z_{<c}
-  float den_part[READOUT ? 4 : 1][RQ];
-  float den_intra[RP][16];
+  static constexpr int LQ = FB + 4;      // phi(sQ) row stride in floats (4 mod 64 banks)
+  alignas(16) float phikt[2][FB][kLS];   // phi_f(k_j), feature-major
+  alignas(16) float vt[2][kDV][kLS];     // V^T
+  alignas(16) float phiq[2][RQ][LQ];     // phi_f(s q_i), token-major
+  alignas(16) f32x4 a[2][RP][64];        // block 0: score tiles in MFMA B-operand lane order
+  alignas(16) float z[FB];               // the block's z_{<c}; producer g owns rows g*FB/4 .. + FB/4
+  float den_part[2][kProd][RQ];          // phi_f(s q_i) . z_{f,<c} over each producer's features
+  float den_intra[2][RP][16];            // column sums of the score tiles
 };
 
 // Where a workgroup's starting state comes from and where its results go (see the file comment).
@@ -76,235 +91,281 @@ struct WideIO {
   int BH;
 };
 
-// One token's 16 coordinates from 64 bytes (float32) or 32 bytes (bfloat16) of registers.
-template <typename E>
-struct Row16;
-template <>
-struct Row16<float> {
-  f32x4 p[4];
+// n consecutive elements (n a multiple of 4) of one token row, widened to float32 on unpack.
+template <typename E, int NE>
+struct Piece;
+template <int NE>
+struct Piece<float, NE> {
+  f32x4 p[NE / 4];
   __device__ __forceinline__ void load(const float* src) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) p[u] = *reinterpret_cast<const f32x4*>(src + 4 * u);
+    for (int u = 0; u < NE / 4; ++u) p[u] = *reinterpret_cast<const f32x4*>(src + 4 * u);
   }
-  __device__ __forceinline__ void unpack(float (&x)[kDK], float s) const {
+  __device__ __forceinline__ float get(int i) const { return p[i / 4][i % 4]; }
+};
+template <int NE>
+struct Piece<__bf16, NE> {
+  uint32_t p[NE / 2];
+  __device__ __forceinline__ void load(const __bf16* src) {
+    if constexpr (NE % 8 == 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[4 * u + r] = s * p[u][r];
+      for (int u = 0; u < NE / 8; ++u) {
+        const uint4 t = *reinterpret_cast<const uint4*>(src + 8 * u);
+        p[4 * u] = t.x;
+        p[4 * u + 1] = t.y;
+        p[4 * u + 2] = t.z;
+        p[4 * u + 3] = t.w;
+      }
+    } else {
+      const uint2 t = *reinterpret_cast<const uint2*>(src);
+      p[0] = t.x;
+      p[1] = t.y;
+    }
+  }
+  __device__ __forceinline__ float get(int i) const {
+    return __uint_as_float(i % 2 == 0 ? p[i / 2] << 16 : p[i / 2] & 0xffff0000u);
   }
 };
-template <>
-struct Row16<__bf16> {
-  uint4 p[2];
-  __device__ __forceinline__ void load(const __bf16* src) {
-    p[0] = *reinterpret_cast<const uint4*>(src);
-    p[1] = *reinterpret_cast<const uint4*>(src + 8);
-  }
-  __device__ __forceinline__ void unpack(float (&x)[kDK], float s) const {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t w[4] = {p[u].x, p[u].y, p[u].z, p[u].w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        x[8 * u + 2 * h] = s * __uint_as_float(w[h] << 16);
-        x[8 * u + 2 * h + 1] = s * __uint_as_float(w[h] & 0xffff0000u);
-      }
+
+// One producer lane's inputs for one chunk: a k row (lanes 0..31) or a q row (lanes 32..63) of token
+// l % 32, the lane's 8 values of that token, and its score-tile operands (used by block 0 only).
+template <typename E>
+struct WideIn {
+  Piece<E, kDK> row;
+  Piece<E, 8> v;
+  Piece<E, 4> sk, sq;
+  __device__ __forceinline__ void load(const E* qg, const E* kg, const E* vg, long long tok0, int nv, int l, int g,
+                                       bool readout) {
+    const int tk = l & 31, h = l >> 5;
+    const long long r = tok0 + (tk < nv ? tk : 0);  // tokens past the end read a valid row, masked later
+    row.load((readout && h ? qg : kg) + r * kDK);
+    v.load(vg + r * kDV + 16 * g + 8 * h);
+    if (readout) {
+      const int p = g < kPairs ? g : 0;
+      const int l16 = l & 15, lg = l >> 4;
+      const int rk = 16 * pair_jt(p) + l16, rq = 16 * pair_it(p) + l16;
+      sk.load(kg + (tok0 + (rk < nv ? rk : 0)) * kDK + 4 * lg);
+      sq.load(qg + (tok0 + (rq < nv ? rq : 0)) * kDK + 4 * lg);
     }
   }
 };
 
-// Wave w's 16 value columns of one token (v row slice) from registers.
-template <typename E>
-struct Vals16 {
-  Row16<E> r;
-  __device__ __forceinline__ void load(const E* src) { r.load(src); }
-  __device__ __forceinline__ void unpack(float (&x)[16]) const { r.unpack(x, 1.0f); }
-};
-
-// The chunk inputs one lane holds in flight: k and q rows of token l, and wave w's 16 values of it.
-template <typename E, bool READOUT>
-struct WideIn {
-  Row16<E> k, q;
-  Vals16<E> v;
-  __device__ __forceinline__ void load(const E* qg, const E* kg, const E* vg, long long tok0, int nv, int l,
-                                       int w) {
-    const long long row = tok0 + (l < nv ? l : 0);  // tokens past the end read a valid row, masked later
-    k.load(kg + row * kDK);
-    if constexpr (READOUT) q.load(qg + row * kDK);
-    v.load(vg + row * kDV + 16 * w);
-  }
-};
-
-// Expansion of the block's features of token l: wave sub-block F0 .. F0 + kSub - 1 (global indices).
-template <int NT, bool READOUT, int F0>
-__device__ __forceinline__ void expand_wave(WideSmem<READOUT>& sm, int w, int l, const float (&xk)[kDK],
-                                            const float (&xq)[kDK], bool valid) {
-  constexpr int L0 = F0 % kFB;  // row of the first feature inside the block
+// Producer g's features of its FP = FB / 4 block rows for one token: lanes 0..31 from k into
+// phi(K)^T, lanes 32..63 from sq into phi(sQ) (plus their part of the denominators).  F0 = first
+// global feature.
+template <int NT, bool READOUT, int FB, int F0>
+__device__ __forceinline__ void expand_rows(WideSmem<READOUT, FB>& sm, int b, int g, int l, const float (&x)[kDK],
+                                            bool valid) {
+  constexpr int FP = FB / kProd;
+  constexpr int L0 = F0 % FB;  // first block row of this producer
+  const int tk = l & 31;
+  float f[FP];
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    ((sm.phikt[L0 + I][l] = (F0 + I == 0) ? (valid ? 1.f : 0.f) : feature_ct<NT, kDK, F0 + I>(xk)), ...);
-  }(std::make_integer_sequence<int, kSub>{});
-  if constexpr (READOUT) {
+    ((f[I] = feature_ct<NT, kDK, F0 + I>(x)), ...);
+  }(std::make_integer_sequence<int, FP>{});
+  if (l < 32) {
+    if constexpr (F0 == 0) f[0] = valid ? 1.f : 0.f;  // the constant feature of a token past the end
+#pragma unroll
+    for (int i = 0; i < FP; ++i) sm.phikt[b][L0 + i][tk] = f[i];
+  } else if constexpr (READOUT) {
     float den = 0.f;
-    [&]<int... P>(std::integer_sequence<int, P...>) {
-      (([&] {
-         const f32x4 f = {feature_ct<NT, kDK, F0 + 4 * P>(xq), feature_ct<NT, kDK, F0 + 4 * P + 1>(xq),
-                          feature_ct<NT, kDK, F0 + 4 * P + 2>(xq), feature_ct<NT, kDK, F0 + 4 * P + 3>(xq)};
-         *reinterpret_cast<f32x4*>(&sm.phiq[l][L0 + 4 * P]) = f;
-         const f32x4 zz = *reinterpret_cast<const f32x4*>(&sm.z[L0 + 4 * P]);
-         den = fmaf(f[0], zz[0], den);
-         den = fmaf(f[1], zz[1], den);
-         den = fmaf(f[2], zz[2], den);
-         den = fmaf(f[3], zz[3], den);
-       }()),
-       ...);
-    }(std::make_integer_sequence<int, kSub / 4>{});
-    sm.den_part[w][l] = den;
+#pragma unroll
+    for (int u = 0; u < FP / 4; ++u) {
+      *reinterpret_cast<f32x4*>(&sm.phiq[b][tk][L0 + 4 * u]) = f32x4{f[4 * u], f[4 * u + 1], f[4 * u + 2], f[4 * u + 3]};
+      const f32x4 zz = *reinterpret_cast<const f32x4*>(&sm.z[L0 + 4 * u]);
+      den = fmaf(f[4 * u], zz[0], den);
+      den = fmaf(f[4 * u + 1], zz[1], den);
+      den = fmaf(f[4 * u + 2], zz[2], den);
+      den = fmaf(f[4 * u + 3], zz[3], den);
+    }
+    sm.den_part[b][g][tk] = den;
   }
 }
 
-// One segment of L tokens, one feature block; grid = (segments, heads, blocks).
+// Producer g prepares the chunk in buffer b from its inputs.
+template <int NT, typename E, bool READOUT>
+__device__ __forceinline__ void wide_produce(WideSmem<READOUT, block_features<NT>()>& sm, const WideIn<E>& in, int b,
+                                             int fb, int g, int l, int nv, float scale) {
+  constexpr int NB = n_blocks<NT>(), FB = block_features<NT>(), FP = FB / kProd;
+  const int tk = l & 31, h = l >> 5, l16 = l & 15, lg = l >> 4;
+  const bool valid = tk < nv;
+  {
+    float x[kDK];
+    // k rows of tokens past the end are zero (their features vanish except the constant one)
+    const float sx = (READOUT && h) ? scale : (valid ? 1.0f : 0.0f);
+#pragma unroll
+    for (int d = 0; d < kDK; ++d) x[d] = sx * in.row.get(d);
+    dispatch_index<0, NB * kProd>(fb * kProd + g, [&](auto I) {
+      expand_rows<NT, READOUT, FB, decltype(I)::value * FP>(sm, b, g, l, x, valid);
+    });
+  }
+  // V^T: columns 16g + 8h .. + 7 of token tk
+#pragma unroll
+  for (int c = 0; c < 8; ++c) sm.vt[b][16 * g + 8 * h + c][tk] = valid ? in.v.get(c) : 0.f;
+  if constexpr (READOUT) {
+    if (fb == 0 && g < kPairs) {
+      // score tile of pair g and its column sums (16 keys per query column)
+      const int it = pair_it(g), jt = pair_jt(g);
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(in.sk.get(r), in.sq.get(r), sc, 0, 0, 0);
+      // sc[r] = k_j . q_i with j = 16jt + 4lg + r, i = 16it + l16
+      f32x4 wt;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
+        wt[r] = (jt < it || j <= i) ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
+      }
+      sm.a[b][g][l] = wt;
+      f32x4 cs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cs = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, wt[r], cs, 0, 0, 0);
+      if (lg == 0) sm.den_intra[b][g][l16] = cs[0];
+    }
+  }
+  // z_{<next} = z + row sums of this producer's phi(K)^T rows (written by this wave above; a wave's
+  // LDS accesses complete in order)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (l < FP) {
+    const int row = FP * g + l;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < kCS; j += 4) {
+      const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sm.phikt[b][row][j]);
+      acc += (x4[0] + x4[1]) + (x4[2] + x4[3]);
+    }
+    sm.z[row] += acc;
+  }
+}
+
+// One segment of L tokens, one feature block; grid = (segments, heads, blocks).  Both roles execute
+// exactly 2 + nch barriers.
 template <int NT, typename E, bool READOUT>
 __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                                 const E* __restrict__ v, WideIO io, int N, int L,
                                                                 float scale) {
   constexpr int W = FeatureTable<NT, kDK>::W;
-  constexpr int NB = n_blocks<NT>();
-  __shared__ WideSmem<READOUT> sm;
+  constexpr int FB = block_features<NT>(), FP = FB / kProd, NAT = FB / 16;
+  __shared__ WideSmem<READOUT, FB> sm;
 
   const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = 16 * w + l16;  // value column of this lane in the MFMA tiles
   const int seg = blockIdx.x, fb = blockIdx.z;
   const long long bh = blockIdx.y;
-  const int f0 = fb * kFB;
+  const int f0 = fb * FB;
   const int t_begin = seg * L, t_end = min(N, t_begin + L);
-  const long long hbase = bh * (long long)N;
-  const bool intra = READOUT && fb == 0;  // block 0 also carries the intra-chunk term
+  const int nch = (t_end - t_begin + kCS - 1) / kCS;
+  const long long tok_base = bh * (long long)N + t_begin;
+  auto nv_of = [&](int c) { return min(kCS, t_end - (t_begin + c * kCS)); };
+  auto tok_of = [&](int c) { return tok_base + (long long)c * kCS; };
 
-  // starting state of this block: rows f0 .. f0 + kFB - 1 (zero past W)
+  // starting state of this block: rows f0 .. f0 + FB - 1 (zero past W)
   const float* init = nullptr;
   if (io.nseg > 1) {
     if (READOUT) init = io.slots + (bh * io.nseg + seg) * io.stride;
   } else if (READOUT && io.state) {
     init = io.state + bh * io.stride;
   }
-  f32x4 Srun[kNAT];
+  // state pass: the segment's increment; single-segment readout: the final state
+  float* dst = nullptr;
+  if (!READOUT)
+    dst = io.slots + (bh * io.nseg + seg) * io.stride;
+  else if (io.nseg == 1 && io.state)
+    dst = io.state + bh * io.stride;
+
+  if (w >= kCons) {
+    // ---- producers ----
+    const int g = w - kCons;
+    if (l < FP) {
+      const int a = f0 + FP * g + l;
+      sm.z[FP * g + l] = (init && a < W) ? init[(long long)W * kDV + a] : 0.f;
+    }
+    WideIn<E> pa, pb;
+    pa.load(q, k, v, tok_of(0), nv_of(0), l, g, READOUT);
+    __syncthreads();
+    if (nch > 1) pb.load(q, k, v, tok_of(1), nv_of(1), l, g, READOUT);
+    wide_produce<NT, E, READOUT>(sm, pa, 0, fb, g, l, nv_of(0), scale);
+    __syncthreads();  // chunk 0 ready
+    int c = 0;
+    for (; c + 3 < nch; c += 2) {
+      pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
+      wide_produce<NT, E, READOUT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale);
+      __syncthreads();
+      pb.load(q, k, v, tok_of(c + 3), nv_of(c + 3), l, g, READOUT);
+      wide_produce<NT, E, READOUT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale);
+      __syncthreads();
+    }
+    // nch - c phases remain (1 to 3); chunks c+1 and c+2 may still need preparing
+    if (c + 2 < nch) pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
+    if (c + 1 < nch) wide_produce<NT, E, READOUT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale);
+    __syncthreads();
+    if (c + 1 < nch) {
+      if (c + 2 < nch) wide_produce<NT, E, READOUT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale);
+      __syncthreads();
+      if (c + 2 < nch) __syncthreads();
+    }
+    if (dst && l < FP) {
+      const int a = f0 + FP * g + l;
+      if (a < W) dst[(long long)W * kDV + a] = sm.z[FP * g + l];
+    }
+    return;
+  }
+
+  // ---- consumers: wave w owns value columns 16w..16w+15 ----
+  const int col = 16 * w + l16;
+  const bool intra = READOUT && fb == 0;  // block 0 also carries the intra-chunk term
+  f32x4 Srun[NAT];
 #pragma unroll
-  for (int t = 0; t < kNAT; ++t)
+  for (int t = 0; t < NAT; ++t)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int a = f0 + 16 * t + 4 * lg + r;
       Srun[t][r] = (init && a < W) ? init[(long long)a * kDV + col] : 0.f;
     }
-  if (tid < kFB) sm.z[tid] = (init && f0 + tid < W) ? init[(long long)W * kDV + f0 + tid] : 0.f;
-
-  WideIn<E, READOUT> in;
-  in.load(q, k, v, hbase + t_begin, min(kCS, t_end - t_begin), l, w);
-
-  for (int c0 = t_begin; c0 < t_end; c0 += kCS) {
-    const int nv = min(kCS, t_end - c0);
-    const long long tok0 = hbase + c0;
-    const bool valid = l < nv;
-
-    // ---- expansion of this chunk into LDS ----
-    __syncthreads();  // previous chunk's MFMAs and z update are done with LDS
-    {
-      float xk[kDK], xq[kDK];
-      in.k.unpack(xk, valid ? 1.0f : 0.0f);  // a token past the end has a zero k row
-      if constexpr (READOUT) in.q.unpack(xq, scale);
-      dispatch_index<0, NB * 4>(fb * 4 + w, [&](auto I) {
-        expand_wave<NT, READOUT, decltype(I)::value * kSub>(sm, w, l, xk, xq, valid);
-      });
-      float vv[16];
-      in.v.unpack(vv);
-#pragma unroll
-      for (int c = 0; c < 16; ++c) sm.vt[16 * w + c][l] = valid ? vv[c] : 0.f;
-      if (intra && w == 0) {
-        float xr[kDK];
-        in.q.unpack(xr, 1.0f);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          *reinterpret_cast<f32x4*>(&sm.kr[l][4 * u]) = f32x4{xk[4 * u], xk[4 * u + 1], xk[4 * u + 2], xk[4 * u + 3]};
-          *reinterpret_cast<f32x4*>(&sm.qr[l][4 * u]) = f32x4{xr[4 * u], xr[4 * u + 1], xr[4 * u + 2], xr[4 * u + 3]};
-        }
-      }
-    }
-    __syncthreads();
-    if (c0 + kCS < t_end) in.load(q, k, v, tok0 + kCS, min(kCS, t_end - c0 - kCS), l, w);
-
-    // ---- matrix work of wave w (value columns 16w..16w+15) ----
+  __syncthreads();
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int b = c & 1;
+    const int nv = nv_of(c);
+    const long long tok0 = tok_of(c);
     f32x4 O[READOUT ? kNIT : 1];
     if constexpr (READOUT) {
-      if (intra) {
-        // score tiles (key tile jt <= query tile it) of this wave's pairs, and their column sums
-        for (int p = w; p < kPairs; p += 4) {
-          int it = 0;
-          while ((it + 1) * (it + 2) / 2 <= p) ++it;
-          const int jt = p - it * (it + 1) / 2;
-          const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.kr[16 * jt + l16][4 * lg]);
-          const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.qr[16 * it + l16][4 * lg]);
-          f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bq[r], sc, 0, 0, 0);
-          // sc[r] = k_j . q_i with j = 16jt + 4lg + r, i = 16it + l16
-          f32x4 wt;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
-            wt[r] = (jt < it || j <= i) ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
-          }
-          sm.a[p][l] = wt;
-          f32x4 cs = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) cs = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, wt[r], cs, 0, 0, 0);
-          if (lg == 0) sm.den_intra[p][l16] = cs[0];  // sum over the 16 keys for query 16it + l16
-        }
-      }
-      // readout: O[it][r] = (phi_f(sQ) S_{f,<c})[token 16it + l16][column 16w + 4lg + r]
 #pragma unroll
       for (int it = 0; it < kNIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // readout: O[it][r] = (phi_f(sQ) S_{f,<c})[token 16it + l16][column 16w + 4lg + r]
 #pragma unroll
-      for (int t = 0; t < kNAT; ++t)
+      for (int t = 0; t < NAT; ++t)
 #pragma unroll
         for (int it = 0; it < kNIT; ++it) {
-          const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[16 * it + l16][16 * t + 4 * lg]);
+          const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[b][16 * it + l16][16 * t + 4 * lg]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], O[it], 0, 0, 0);
         }
-    }
-    // state update: Srun[t] += phi_f(K)^T[16t.., chunk] V[chunk, columns]
-#pragma unroll
-    for (int jb = 0; jb < kCS / 16; ++jb) {
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.vt[col][16 * jb + 4 * lg]);
-#pragma unroll
-      for (int t = 0; t < kNAT; ++t) {
-        const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[16 * t + l16][16 * jb + 4 * lg]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
-      }
-    }
-    // z_{<c+1} = z_{<c} + row sums of phi_f(K)^T (tokens past the end are zero rows)
-    if (tid < kFB) {
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < kCS; j += 4) {
-        const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sm.phikt[tid][j]);
-        acc += (x4[0] + x4[1]) + (x4[2] + x4[3]);
-      }
-      sm.z[tid] += acc;
-    }
-    if constexpr (READOUT) {
       if (intra) {
-        __syncthreads();  // every wave's score tiles and their sums are visible
 #pragma unroll
         for (int it = 0; it < kNIT; ++it)
+#pragma unroll
           for (int jt = 0; jt <= it; ++jt) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.vt[col][16 * jt + 4 * lg]);
-            const f32x4 bw = sm.a[it * (it + 1) / 2 + jt][l];
+            const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jt + 4 * lg]);
+            const f32x4 bw = sm.a[b][it * (it + 1) / 2 + jt][l];
 #pragma unroll
             for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bw[r], O[it], 0, 0, 0);
           }
       }
+    }
+    // state update: Srun[t] += phi_f(K)^T[16t.., chunk] V[chunk, columns]
+#pragma unroll
+    for (int jb = 0; jb < kCS / 16; ++jb) {
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jb + 4 * lg]);
+#pragma unroll
+      for (int t = 0; t < NAT; ++t) {
+        const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[b][16 * t + l16][16 * jb + 4 * lg]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
+      }
+    }
+    if constexpr (READOUT) {
       // partial numerators of this block (columns 16w + 4lg .. + 3 of token 16it + l16)
       float* pn = io.part_num + ((long long)fb * io.BH * N + tok0) * kDV;
 #pragma unroll
@@ -312,33 +373,28 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(const E* __restr
         const int i = 16 * it + l16;
         if (i < nv) *reinterpret_cast<f32x4*>(pn + (long long)i * kDV + 16 * w + 4 * lg) = O[it];
       }
-      // partial denominators: wave w writes tokens 16w .. 16w + 15
-      if (lg == 0) {
+      // partial denominators: consumer w < kNIT writes tokens 16w .. 16w + 15
+      if (w < kNIT && lg == 0) {
         const int i = 16 * w + l16;
-        float d = ((sm.den_part[0][i] + sm.den_part[1][i]) + sm.den_part[2][i]) + sm.den_part[3][i];
+        float d = 0.f;
+#pragma unroll
+        for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
         if (intra)
-          for (int jt = 0; jt <= w; ++jt) d += sm.den_intra[w * (w + 1) / 2 + jt][l16];
+          for (int jt = 0; jt <= w; ++jt) d += sm.den_intra[b][w * (w + 1) / 2 + jt][l16];
         if (i < nv) io.part_den[(long long)fb * io.BH * N + tok0 + i] = d;
       }
     }
+    __syncthreads();
   }
 
-  // state pass: the segment's increment; single-segment readout: the final state
-  float* dst = nullptr;
-  if (!READOUT)
-    dst = io.slots + (bh * io.nseg + seg) * io.stride;
-  else if (io.nseg == 1 && io.state)
-    dst = io.state + bh * io.stride;
   if (dst) {
 #pragma unroll
-    for (int t = 0; t < kNAT; ++t)
+    for (int t = 0; t < NAT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int a = f0 + 16 * t + 4 * lg + r;
         if (a < W) dst[(long long)a * kDV + col] = Srun[t][r];
       }
-    __syncthreads();  // the last chunk's z update is complete
-    if (tid < kFB && f0 + tid < W) dst[(long long)W * kDV + f0 + tid] = sm.z[tid];
   }
 }
 
