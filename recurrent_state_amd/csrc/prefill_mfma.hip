@@ -9,35 +9,28 @@
 //     S   += phi(K_c)^T V1_c                                        (state and normaliser z)
 //     o    = O_c[:, :d_v] / O_c[:, d_v]
 //
-// Work split: one workgroup of 5 wavefronts walks a segment of consecutive chunks.
-//   * Waves 0..3 own value columns 16w..16w+15; wave 4 owns the normaliser
-//     column (a 16-wide tile whose first column is all ones and the rest zero),
-//     so z and every denominator come out of the same MFMAs as the numerators
-//     and no wave needs a cross-wave reduction.
-//   * The running state S_{<c} (W_p x 16 floats per wave, W_p = W rounded up to
-//     32) lives in MFMA accumulator registers for the whole segment.  Its tile
-//     layout (4 consecutive feature rows per lane) is used directly as the A
-//     operand of the readout phi(sQ) S; the k-slot order this implies is
-//     absorbed by storing phi(sQ) in LDS with the same permutation of features
-//     inside each 32-block, so S never round-trips through LDS.  For bfloat16
-//     inputs S is split as S = hi + lo (two bfloat16 MFMAs) so that the state
-//     keeps float32 accuracy in the readout.
-//   * Intra-chunk scores s Q K^T use the 16x16x16 MFMA with the key block as
-//     rows; its accumulator layout is exactly the B-operand layout of the next
-//     MFMA (V1^T times scores), so scores go through registers -> LDS once and
-//     are shared by the 5 waves.  Horner's rule for K_n and the causal mask are
-//     applied in registers.
-//   * Chunk c+1's inputs are loaded into registers while chunk c is computed,
-//     and chunk c's outputs are stored after chunk c+1's first barrier (which is
-//     also the barrier that publishes the denominators of chunk c).
+// Two kernels, one per input type; both walk segments of consecutive 64-token chunks with the
+// running state S_{<c} of the segment in MFMA accumulator registers, and two launches of each
+// bracket the scan: a state-only pass writes each segment's (S, z) increment to the workspace, the
+// scan turns those into exclusive prefixes, and the readout pass starts each segment from its prefix.
 //
-// Two launches of this kernel bracket the scan: a state-only pass writes each
-// segment's (S, z) increment to the workspace, the scan turns those into
-// exclusive prefixes, and the readout pass starts each segment from its prefix.
+// float32 inputs -- prefill_mfma_kernel, one workgroup of 5 wavefronts, every MFMA 16x16x4 float32:
+//   * waves 0..3 own value columns 16w..16w+15; wave 4 owns the normaliser column (a 16-wide tile
+//     whose first column is all ones and the rest zero), so z and every denominator come out of the
+//     same MFMAs as the numerators and no wave needs a cross-wave reduction;
+//   * the accumulator tile layout of S (4 consecutive feature rows per lane) is used directly as the
+//     A operand of the readout phi(sQ) S, so S never round-trips through LDS;
+//   * intra-chunk scores s Q K^T use the MFMA with the key block as rows; its accumulator layout is
+//     exactly the B-operand layout of the next MFMA (V1^T times scores), so scores go through
+//     registers -> LDS once and are shared by the 5 waves.  Horner's rule for K_n and the causal
+//     mask are applied in registers;
+//   * chunk c+1's inputs are loaded into registers while chunk c is computed, and chunk c's outputs
+//     are stored after chunk c+1's first barrier (which also publishes chunk c's denominators).
 //
-// bfloat16 inputs: q, k, v, phi and the scores enter the MFMAs as bfloat16;
-// S, z, all accumulation and the outputs are float32.  float32 inputs: every
-// MFMA is the float32 16x16x4 one.
+// bfloat16 inputs -- prefill_pipe_kernel (further below): producer and consumer wavefronts over a
+// double-buffered LDS area; q, k, v, phi and the score weights enter bfloat16 MFMAs, S and the
+// weights split as bfloat16 hi + lo where they meet the MFMAs, all accumulation and the outputs in
+// float32.
 #include <type_traits>
 #include <utility>
 
@@ -80,11 +73,11 @@ struct Geo {
 };
 
 // How the feature work of a chunk is split over the waves.
-template <int NT, bool BF16>
+template <int NT>
 struct Split {
   static constexpr int WP = Geo<NT>::WP;
   static constexpr int RK = ((WP + kWaves - 1) / kWaves + 7) / 8 * 8;  // phi(K)^T rows per wave
-  static constexpr int GQ = BF16 ? 8 : 4;                              // phi(sQ) slots per 16-byte store
+  static constexpr int GQ = 4;                                         // phi(sQ) features per 16-byte store
   static constexpr int NG = WP / GQ;                                   // stores per phi(sQ) row
   static constexpr int RG = (NG + kWaves - 1) / kWaves;               // stores per wave
 };
@@ -116,24 +109,22 @@ __host__ __device__ constexpr int slot_feature_bf16(int s) {
   return 32 * kb + (r < 4 ? g * 4 + r : 16 + g * 4 + (r - 4));
 }
 
-template <int NT, int CS, bool BF16, bool READOUT>
+template <int NT, int CS, bool READOUT>
 struct Smem {
-  using E = typename std::conditional<BF16, __bf16, float>::type;
   static constexpr int WP = Geo<NT>::WP;
-  static constexpr int PADE = BF16 ? 8 : 4;  // row padding (elements) against LDS bank conflicts
+  static constexpr int PADE = 4;             // row padding (floats) against LDS bank conflicts
   static constexpr int LQ = WP + PADE;       // phi(sQ) row stride
   static constexpr int LK = CS + PADE;       // phi(K)^T and V^T row stride
   static constexpr int NIT = CS / 16;
   static constexpr int NPAIR = NIT * (NIT + 1) / 2;
   static constexpr int RQ = READOUT ? CS : 1;  // readout-only arrays collapse in the state pass
   static constexpr int RP = READOUT ? NPAIR : 1;
-  using ATile = typename std::conditional<BF16, bf16x4, f32x4>::type;
-  alignas(16) E k[CS][kDK];
-  alignas(16) E vt[kDV][LK];
-  alignas(16) E phikt[WP][LK];
-  alignas(16) E q[RQ][kDK];
-  alignas(16) E phiq[RQ][LQ];
-  alignas(16) ATile a[RP][64];  // score tiles in MFMA B-operand lane order
+  alignas(16) float k[CS][kDK];
+  alignas(16) float vt[kDV][LK];
+  alignas(16) float phikt[WP][LK];
+  alignas(16) float q[RQ][kDK];
+  alignas(16) float phiq[RQ][LQ];
+  alignas(16) f32x4 a[RP][64];  // score tiles in MFMA B-operand lane order
   float den[RQ];
 };
 
@@ -143,87 +134,65 @@ __device__ __forceinline__ void load_row16(const float* src, float (&x)[kDK], fl
 #pragma unroll
   for (int d = 0; d < kDK; ++d) x[d] = scale * src[d];
 }
-__device__ __forceinline__ void load_row16(const __bf16* src, float (&x)[kDK], float scale) {
-#pragma unroll
-  for (int d = 0; d < kDK; ++d) x[d] = scale * (float)src[d];
-}
 
 // This wave's rows of phi(K_c)^T for token j.  A token past the end has a zero k row, so all its
 // features are zero except the constant one.
-template <int NT, int CS, bool BF16, bool READOUT, int G>
-__device__ __forceinline__ void phik_rows(Smem<NT, CS, BF16, READOUT>& sm, int j, const float (&x)[kDK], bool valid) {
-  using SP = Split<NT, BF16>;
-  using E = typename Smem<NT, CS, BF16, READOUT>::E;
+template <int NT, int CS, bool READOUT, int G>
+__device__ __forceinline__ void phik_rows(Smem<NT, CS, READOUT>& sm, int j, const float (&x)[kDK], bool valid) {
+  using SP = Split<NT>;
   [&]<int... I>(std::integer_sequence<int, I...>) {
     (([&] {
        constexpr int row = G * SP::RK + I;
        if constexpr (row == 0)
-         sm.phikt[row][j] = (E)(valid ? 1.f : 0.f);
+         sm.phikt[row][j] = valid ? 1.f : 0.f;
        else if constexpr (row < SP::WP)
-         sm.phikt[row][j] = (E)feat<NT, row>(x);
+         sm.phikt[row][j] = feat<NT, row>(x);
      }()),
      ...);
   }(std::make_integer_sequence<int, SP::RK>{});
 }
 
 // This wave's 16-byte groups of the phi(sQ) row of token i.
-template <int NT, int CS, bool BF16, bool READOUT, int G>
-__device__ __forceinline__ void phiq_groups(Smem<NT, CS, BF16, READOUT>& sm, int i, const float (&x)[kDK]) {
-  using SP = Split<NT, BF16>;
+template <int NT, int CS, bool READOUT, int G>
+__device__ __forceinline__ void phiq_groups(Smem<NT, CS, READOUT>& sm, int i, const float (&x)[kDK]) {
+  using SP = Split<NT>;
   [&]<int... P>(std::integer_sequence<int, P...>) {
     (([&] {
        constexpr int grp = G * SP::RG + P;
        if constexpr (grp < SP::NG) {
          constexpr int s0 = grp * SP::GQ;
-         if constexpr (BF16) {
-           bf16x8 v;
-           v[0] = (__bf16)feat<NT, slot_feature_bf16(s0 + 0)>(x);
-           v[1] = (__bf16)feat<NT, slot_feature_bf16(s0 + 1)>(x);
-           v[2] = (__bf16)feat<NT, slot_feature_bf16(s0 + 2)>(x);
-           v[3] = (__bf16)feat<NT, slot_feature_bf16(s0 + 3)>(x);
-           v[4] = (__bf16)feat<NT, slot_feature_bf16(s0 + 4)>(x);
-           v[5] = (__bf16)feat<NT, slot_feature_bf16(s0 + 5)>(x);
-           v[6] = (__bf16)feat<NT, slot_feature_bf16(s0 + 6)>(x);
-           v[7] = (__bf16)feat<NT, slot_feature_bf16(s0 + 7)>(x);
-           *reinterpret_cast<bf16x8*>(&sm.phiq[i][s0]) = v;
-         } else {
-           f32x4 v;
-           v[0] = feat<NT, s0 + 0>(x);
-           v[1] = feat<NT, s0 + 1>(x);
-           v[2] = feat<NT, s0 + 2>(x);
-           v[3] = feat<NT, s0 + 3>(x);
-           *reinterpret_cast<f32x4*>(&sm.phiq[i][s0]) = v;
-         }
+         const f32x4 v = {feat<NT, s0 + 0>(x), feat<NT, s0 + 1>(x), feat<NT, s0 + 2>(x), feat<NT, s0 + 3>(x)};
+         *reinterpret_cast<f32x4*>(&sm.phiq[i][s0]) = v;
        }
      }()),
      ...);
   }(std::make_integer_sequence<int, SP::RG>{});
 }
 
-template <int NT, int CS, bool BF16, bool READOUT, int G>
-__device__ __forceinline__ void features_wave(Smem<NT, CS, BF16, READOUT>& sm, int l, int nv, float scale) {
+template <int NT, int CS, bool READOUT, int G>
+__device__ __forceinline__ void features_wave(Smem<NT, CS, READOUT>& sm, int l, int nv, float scale) {
 #pragma unroll
   for (int tt = 0; tt < CS / 64; ++tt) {
     const int j = l + 64 * tt;
     float x[kDK];
     load_row16(&sm.k[j][0], x, 1.0f);
-    phik_rows<NT, CS, BF16, READOUT, G>(sm, j, x, j < nv);
+    phik_rows<NT, CS, READOUT, G>(sm, j, x, j < nv);
     if constexpr (READOUT) {
       load_row16(&sm.q[j][0], x, scale);
-      phiq_groups<NT, CS, BF16, READOUT, G>(sm, j, x);
+      phiq_groups<NT, CS, READOUT, G>(sm, j, x);
     }
   }
 }
 
-template <int NT, int CS, bool BF16, bool READOUT>
-__device__ __forceinline__ void features(Smem<NT, CS, BF16, READOUT>& sm, int w, int l, int nv, float scale) {
+template <int NT, int CS, bool READOUT>
+__device__ __forceinline__ void features(Smem<NT, CS, READOUT>& sm, int w, int l, int nv, float scale) {
   static_assert(kWaves == 5, "feature split assumes 5 waves");
   switch (w) {
-    case 0: features_wave<NT, CS, BF16, READOUT, 0>(sm, l, nv, scale); break;
-    case 1: features_wave<NT, CS, BF16, READOUT, 1>(sm, l, nv, scale); break;
-    case 2: features_wave<NT, CS, BF16, READOUT, 2>(sm, l, nv, scale); break;
-    case 3: features_wave<NT, CS, BF16, READOUT, 3>(sm, l, nv, scale); break;
-    default: features_wave<NT, CS, BF16, READOUT, 4>(sm, l, nv, scale); break;
+    case 0: features_wave<NT, CS, READOUT, 0>(sm, l, nv, scale); break;
+    case 1: features_wave<NT, CS, READOUT, 1>(sm, l, nv, scale); break;
+    case 2: features_wave<NT, CS, READOUT, 2>(sm, l, nv, scale); break;
+    case 3: features_wave<NT, CS, READOUT, 3>(sm, l, nv, scale); break;
+    default: features_wave<NT, CS, READOUT, 4>(sm, l, nv, scale); break;
   }
 }
 
@@ -234,10 +203,10 @@ __device__ __forceinline__ uint4 keep_if(bool ok, uint4 x) {
 }
 
 // Chunk inputs in flight: each thread's 16-byte pieces of q, k and v for one chunk.
-template <int CS, bool BF16, bool READOUT>
+template <int CS, bool READOUT>
 struct Prefetch {
-  using E = typename std::conditional<BF16, __bf16, float>::type;
-  static constexpr int EPP = 16 / sizeof(E);  // elements per 16-byte piece
+  using E = float;
+  static constexpr int EPP = 4;               // elements per 16-byte piece
   static constexpr int PR = kDK / EPP;        // pieces per q/k row
   static constexpr int PV = kDV / EPP;        // pieces per v row
   static constexpr int NQK = (CS * PR + kThreads - 1) / kThreads;
@@ -296,21 +265,17 @@ struct Prefetch {
 // One segment of L tokens per workgroup; grid = (segments, heads).
 // READOUT = false: accumulate the segment's (S, z) increment and write it to its workspace slot.
 // READOUT = true : start from the exclusive prefix in the slot and write the outputs.
-template <int NT, int CS, bool BF16, bool READOUT>
+template <int NT, int CS, bool READOUT>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
-    const void* __restrict__ qv, const void* __restrict__ kv, const void* __restrict__ vv, float* __restrict__ o,
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ o,
     float* __restrict__ ws, int N, int L, int nseg, long long stride, float scale) {
   using G = Geo<NT>;
-  using SM = Smem<NT, CS, BF16, READOUT>;
-  using E = typename SM::E;
-  constexpr int W = G::W, NAT = G::NAT, NKB = G::NKB;
+  using SM = Smem<NT, CS, READOUT>;
+  constexpr int W = G::W, NAT = G::NAT;
   constexpr int NIT = CS / 16;
   static_assert(CS == 64 || CS == 128, "chunk of 64 or 128 tokens");
   __shared__ SM sm;
 
-  const E* q = reinterpret_cast<const E*>(qv);
-  const E* k = reinterpret_cast<const E*>(kv);
-  const E* v = reinterpret_cast<const E*>(vv);
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, lg = l >> 4;
   const bool zw = w == kValueWaves;  // the normaliser wave
   const int col = 16 * w + l16;      // value column of this lane (value waves)
@@ -320,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
   const long long hbase = bh * (long long)N;
   float* slot = ws + (bh * nseg + seg) * stride;
 
-  Prefetch<CS, BF16, READOUT> pf;
+  Prefetch<CS, READOUT> pf;
   pf.load(q, k, v, hbase + t_begin, min(CS, t_end - t_begin), tid);
 
   // Running state: Srun[t][r] = S1[16t + 4lg + r][column l16 of this wave's tile], where the
@@ -339,14 +304,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
       Srun[t][r] = x;
     }
 
-  // The normaliser wave's ones column as MFMA operands (rows/columns other than the first are zero).
+  // The normaliser wave's ones column as an MFMA operand (rows/columns other than the first are zero).
   const float one = (zw && l16 == 0) ? 1.f : 0.f;
-  bf16x8 ones8;
-  bf16x4 ones4;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) ones8[r] = (__bf16)one;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) ones4[r] = (__bf16)one;
 
   f32x4 O[READOUT ? NIT : 1];
   long long out_tok0 = -1;  // first token of the chunk whose outputs are pending
@@ -378,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
     pf.store(sm, tid);
     if (c0 + CS < t_end) pf.load(q, k, v, tok0 + CS, min(CS, t_end - c0 - CS), tid);
     __syncthreads();
-    features<NT, CS, BF16, READOUT>(sm, w, l, nv, scale);
+    features<NT, CS, READOUT>(sm, w, l, nv, scale);
     __syncthreads();
 
     // ---- B: scores, readout with S_{<c}, state update ----
@@ -388,84 +347,40 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
         while ((it + 1) * (it + 2) / 2 <= p) ++it;
         const int jt = p - it * (it + 1) / 2;
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (BF16) {
-          const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.k[16 * jt + l16][4 * lg]);
-          const bf16x4 bv = *reinterpret_cast<const bf16x4*>(&sm.q[16 * it + l16][4 * lg]);
-          sc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av), __builtin_bit_cast(i16x4, bv),
-                                                         sc, 0, 0, 0);
-        } else {
-          const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.k[16 * jt + l16][4 * lg]);
-          const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.q[16 * it + l16][4 * lg]);
+        const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.k[16 * jt + l16][4 * lg]);
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.q[16 * it + l16][4 * lg]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bv[r], sc, 0, 0, 0);
-        }
+        for (int r = 0; r < 4; ++r) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bv[r], sc, 0, 0, 0);
         // sc[r] = k_j . q_i with j = 16jt + 4lg + r, i = 16it + l16
-        typename SM::ATile tile;
+        f32x4 tile;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
-          const float wgt = j <= i ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
-          if constexpr (BF16)
-            tile[r] = (__bf16)wgt;
-          else
-            tile[r] = wgt;
+          tile[r] = j <= i ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
         }
         sm.a[p][l] = tile;
       }
       // readout: O[it][r] = (phi(sQ) S1_{<c})[token 16it + l16][tile column 4lg + r]
 #pragma unroll
       for (int it = 0; it < NIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (BF16) {
-        // S = hi + lo in bfloat16, taken in the A-operand k-slot order one 32-feature block at a time
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          bf16x8 hi, lo;
+      for (int t = 0; t < NAT; ++t)
 #pragma unroll
-          for (int r = 0; r < 8; ++r) {
-            const float x = r < 4 ? Srun[2 * kb][r] : Srun[2 * kb + 1][r - 4];
-            hi[r] = (__bf16)x;
-            lo[r] = (__bf16)(x - (float)hi[r]);
-          }
+        for (int it = 0; it < NIT; ++it) {
+          const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[16 * it + l16][16 * t + 4 * lg]);
 #pragma unroll
-          for (int it = 0; it < NIT; ++it) {
-            const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[16 * it + l16][32 * kb + 8 * lg]);
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, O[it], 0, 0, 0);
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, O[it], 0, 0, 0);
-          }
+          for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], O[it], 0, 0, 0);
         }
-      } else {
-#pragma unroll
-        for (int t = 0; t < NAT; ++t)
-#pragma unroll
-          for (int it = 0; it < NIT; ++it) {
-            const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[16 * it + l16][16 * t + 4 * lg]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], O[it], 0, 0, 0);
-          }
-      }
     }
     // state update (after the readout used S_{<c}): Srun[t] += phi(K)^T[16t.., chunk] V1[chunk, tile]
-    if constexpr (BF16) {
 #pragma unroll
-      for (int jb = 0; jb < CS / 32; ++jb) {
-        const bf16x8 bv = zw ? ones8 : *reinterpret_cast<const bf16x8*>(&sm.vt[col][32 * jb + 8 * lg]);
+    for (int jb = 0; jb < CS / 16; ++jb) {
+      const f32x4 bv = zw ? f32x4{one, one, one, one} : *reinterpret_cast<const f32x4*>(&sm.vt[col][16 * jb + 4 * lg]);
 #pragma unroll
-        for (int t = 0; t < NAT; ++t) {
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.phikt[16 * t + l16][32 * jb + 8 * lg]);
-          Srun[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bv, Srun[t], 0, 0, 0);
-        }
-      }
-    } else {
+      for (int t = 0; t < NAT; ++t) {
+        const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[16 * t + l16][16 * jb + 4 * lg]);
 #pragma unroll
-      for (int jb = 0; jb < CS / 16; ++jb) {
-        const f32x4 bv = zw ? f32x4{one, one, one, one}
-                            : *reinterpret_cast<const f32x4*>(&sm.vt[col][16 * jb + 4 * lg]);
-#pragma unroll
-        for (int t = 0; t < NAT; ++t) {
-          const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[16 * t + l16][16 * jb + 4 * lg]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
-        }
+        for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
       }
     }
     if constexpr (READOUT) {
@@ -475,18 +390,11 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
       for (int it = 0; it < NIT; ++it) {
         for (int jt = 0; jt <= it; ++jt) {
           const int p = pair_index(jt, it);
-          if constexpr (BF16) {
-            const bf16x4 av = zw ? ones4 : *reinterpret_cast<const bf16x4*>(&sm.vt[col][16 * jt + 4 * lg]);
-            const bf16x4 bv = sm.a[p][l];
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
-                                                              __builtin_bit_cast(i16x4, bv), O[it], 0, 0, 0);
-          } else {
-            const f32x4 av = zw ? f32x4{one, one, one, one}
-                                : *reinterpret_cast<const f32x4*>(&sm.vt[col][16 * jt + 4 * lg]);
-            const f32x4 bv = sm.a[p][l];
+          const f32x4 av = zw ? f32x4{one, one, one, one}
+                              : *reinterpret_cast<const f32x4*>(&sm.vt[col][16 * jt + 4 * lg]);
+          const f32x4 bv = sm.a[p][l];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bv[r], O[it], 0, 0, 0);
-          }
+          for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bv[r], O[it], 0, 0, 0);
         }
         if (zw && lg == 0) sm.den[16 * it + l16] = O[it][0];
       }
@@ -958,7 +866,7 @@ int n_segments(int BH, int nchunk, int target) {
 
 constexpr int kSegTarget = 256;
 
-template <int NT, int CS, bool BF16>
+template <int NT, int CS>
 int run(const PrefillArgs& a) {
   const int nchunk = cdiv(a.N, CS);
   const int nseg0 = n_segments(a.BH, nchunk, kSegTarget);
@@ -967,13 +875,16 @@ int run(const PrefillArgs& a) {
   float* ws = (float*)a.ws;
   const long long elems = Geo<NT>::W * (long long)(kDV + 1);
   const dim3 grid(nseg, a.BH), block(kThreads);
-  prefill_mfma_kernel<NT, CS, BF16, false>
-      <<<grid, block, 0, a.stream>>>(a.q, a.k, a.v, nullptr, ws, a.N, L, nseg, a.s.stride, a.s.scale);
+  const float* q = (const float*)a.q;
+  const float* k = (const float*)a.k;
+  const float* v = (const float*)a.v;
+  prefill_mfma_kernel<NT, CS, false>
+      <<<grid, block, 0, a.stream>>>(q, k, v, nullptr, ws, a.N, L, nseg, a.s.stride, a.s.scale);
   if (hipGetLastError() != hipSuccess) return -3;
   if (seg_scan_launch(ws, a.state, a.BH, nseg, a.s.stride, elems, a.o != nullptr, a.stream)) return -3;
   if (a.o) {
-    prefill_mfma_kernel<NT, CS, BF16, true>
-        <<<grid, block, 0, a.stream>>>(a.q, a.k, a.v, a.o, ws, a.N, L, nseg, a.s.stride, a.s.scale);
+    prefill_mfma_kernel<NT, CS, true>
+        <<<grid, block, 0, a.stream>>>(q, k, v, a.o, ws, a.N, L, nseg, a.s.stride, a.s.scale);
     if (hipGetLastError() != hipSuccess) return -3;
   }
   return 0;
@@ -1013,7 +924,7 @@ constexpr int kChunk = 64;
 
 template <int NT>
 int run_dtype(const PrefillArgs& a) {
-  return a.s.dtype == 1 ? run_pipe<NT>(a) : run<NT, kChunk, false>(a);
+  return a.s.dtype == 1 ? run_pipe<NT>(a) : run<NT, kChunk>(a);
 }
 
 }  // namespace
