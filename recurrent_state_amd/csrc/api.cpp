@@ -52,8 +52,8 @@ int chunk_of(const taylor_config* cfg) { return cfg->chunk == 0 ? kDefaultChunk 
 enum class Path { None, Generic, Mfma, Wide };
 
 Path prefill_path(const Shape& s, int C) {
-  if (taylor::prefill_mfma_has(s.nt, s.dk, s.dv, C)) return Path::Mfma;
-  if (taylor::prefill_wide_has(s.nt, s.dk, s.dv)) return Path::Wide;
+  if (taylor::prefill_wide_has(s.nt, s.dk, s.dv, s.dtype)) return Path::Wide;
+  if (taylor::prefill_mfma_has(s.nt, s.dk, s.dv, s.dtype)) return Path::Mfma;
   if (taylor::prefill_generic_has(s.nt, s.dk, s.dv, C)) return Path::Generic;
   return Path::None;
 }
@@ -75,7 +75,7 @@ int check_sizes(int B, int H, int N) {
 int64_t ws_bytes(const Shape& s, int C, int BH, int N) {
   if (BH == 0 || N == 0) return 0;
   switch (prefill_path(s, C)) {
-    case Path::Mfma: return taylor::prefill_mfma_ws_bytes(s, BH, N, C);
+    case Path::Mfma: return taylor::prefill_mfma_ws_bytes(s, BH, N);
     case Path::Wide: return taylor::prefill_wide_ws_bytes(s, BH, N);
     case Path::Generic: return taylor::prefill_generic_ws_bytes(s, BH, N, C);
     default: return TAYLOR_ERR_UNSUPPORTED;

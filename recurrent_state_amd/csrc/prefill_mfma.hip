@@ -1,4 +1,4 @@
-// MFMA chunked prefill for d_k = 16, d_v = 64, n = 1..3 (gfx950 matrix cores).
+// Pipelined bfloat16 chunked prefill for d_k = 16, d_v = 64, n = 1..3 (gfx950 matrix cores).
 //
 // "Expanding Attention" (Huang, arXiv:2610.20637), Abstract: with the kernel
 // exp(s) truncated to n Taylor terms and each term factorised into symmetric
@@ -9,32 +9,17 @@
 //     S   += phi(K_c)^T V1_c                                        (state and normaliser z)
 //     o    = O_c[:, :d_v] / O_c[:, d_v]
 //
-// Two kernels, one per input type; both walk segments of consecutive 64-token chunks with the
-// running state S_{<c} of the segment in MFMA accumulator registers, and two launches of each
-// bracket the scan: a state-only pass writes each segment's (S, z) increment to the workspace, the
-// scan turns those into exclusive prefixes, and the readout pass starts each segment from its prefix.
-//
-// float32 inputs -- prefill_mfma_kernel, one workgroup of 5 wavefronts, every MFMA 16x16x4 float32:
-//   * waves 0..3 own value columns 16w..16w+15; wave 4 owns the normaliser column (a 16-wide tile
-//     whose first column is all ones and the rest zero), so z and every denominator come out of the
-//     same MFMAs as the numerators and no wave needs a cross-wave reduction;
-//   * the accumulator tile layout of S (4 consecutive feature rows per lane) is used directly as the
-//     A operand of the readout phi(sQ) S, so S never round-trips through LDS;
-//   * intra-chunk scores s Q K^T use the MFMA with the key block as rows; its accumulator layout is
-//     exactly the B-operand layout of the next MFMA (V1^T times scores), so scores go through
-//     registers -> LDS once and are shared by the 5 waves.  Horner's rule for K_n and the causal
-//     mask are applied in registers;
-//   * chunk c+1's inputs are loaded into registers while chunk c is computed, and chunk c's outputs
-//     are stored after chunk c+1's first barrier (which also publishes chunk c's denominators).
-//
-// bfloat16 inputs -- prefill_pipe_kernel (further below): producer and consumer wavefronts over a
-// double-buffered LDS area; q, k, v, phi and the score weights enter bfloat16 MFMAs, S and the
-// weights split as bfloat16 hi + lo where they meet the MFMAs, all accumulation and the outputs in
-// float32.
+// One workgroup walks a segment of consecutive 64-token chunks with the running state S_{<c} of the
+// segment in MFMA accumulator registers; two launches bracket the scan: a state-only pass writes
+// each segment's (S, z) increment to the workspace, the scan turns those into exclusive prefixes,
+// and the readout pass starts each segment from its prefix.  q, k, v, phi and the score weights
+// enter bfloat16 MFMAs; S and the weights are split as bfloat16 hi + lo where they meet the MFMAs
+// (float32 accuracy for the state), and all accumulation and the outputs are float32.  (float32
+// inputs run on the feature-block kernels of prefill_wide.hip.)
 #include <type_traits>
 #include <utility>
 
-#include "common.hpp"
+#include "features.hpp"
 #include "prefill_mfma.hpp"
 
 namespace taylor {
@@ -59,47 +44,19 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, bf16x2& hi, bf16x
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDK = 16, kDV = 64;
-constexpr int kValueWaves = kDV / 16;    // waves owning 16 value columns each
-constexpr int kWaves = kValueWaves + 1;  // plus the normaliser wave
-constexpr int kThreads = 64 * kWaves;
 
 template <int NT>
 struct Geo {
-  static constexpr Monomials<NT, kDK> T{};
-  static constexpr int W = Monomials<NT, kDK>::W;
+  static constexpr int W = FeatureTable<NT, kDK>::W;
   static constexpr int WP = (W + 31) / 32 * 32;  // features padded to 32-wide MFMA k-blocks
   static constexpr int NAT = WP / 16;            // 16-row feature tiles of the state
   static constexpr int NKB = WP / 32;            // 32-wide feature k-blocks
 };
 
-// How the feature work of a chunk is split over the waves.
-template <int NT>
-struct Split {
-  static constexpr int WP = Geo<NT>::WP;
-  static constexpr int RK = ((WP + kWaves - 1) / kWaves + 7) / 8 * 8;  // phi(K)^T rows per wave
-  static constexpr int GQ = 4;                                         // phi(sQ) features per 16-byte store
-  static constexpr int NG = WP / GQ;                                   // stores per phi(sQ) row
-  static constexpr int RG = (NG + kWaves - 1) / kWaves;               // stores per wave
-};
-
 // Feature A of x (float32 registers), coordinates and coefficient fixed at compile time.
 template <int NT, int A>
 __device__ __forceinline__ float feat(const float (&x)[kDK]) {
-  if constexpr (A >= Geo<NT>::W) {
-    return 0.f;
-  } else {
-    constexpr int c0 = Geo<NT>::T.coord[A][0];
-    constexpr int c1 = Geo<NT>::T.coord[A][1];
-    constexpr int c2 = Geo<NT>::T.coord[A][2];
-    constexpr int c3 = Geo<NT>::T.coord[A][3];
-    constexpr float cf = coef_of_afact(Geo<NT>::T.afact[A]);
-    float f = cf;
-    if constexpr (c0 >= 0) f *= x[c0];
-    if constexpr (c1 >= 0) f *= x[c1];
-    if constexpr (c2 >= 0) f *= x[c2];
-    if constexpr (c3 >= 0) f *= x[c3];
-    return f;
-  }
+  return feature_ct<NT, kDK, A>(x);
 }
 
 // bfloat16 path: position s of a phi(sQ) row holds feature slot_feature(s), the k-slot order of the
@@ -109,315 +66,12 @@ __host__ __device__ constexpr int slot_feature_bf16(int s) {
   return 32 * kb + (r < 4 ? g * 4 + r : 16 + g * 4 + (r - 4));
 }
 
-template <int NT, int CS, bool READOUT>
-struct Smem {
-  static constexpr int WP = Geo<NT>::WP;
-  static constexpr int PADE = 4;             // row padding (floats) against LDS bank conflicts
-  static constexpr int LQ = WP + PADE;       // phi(sQ) row stride
-  static constexpr int LK = CS + PADE;       // phi(K)^T and V^T row stride
-  static constexpr int NIT = CS / 16;
-  static constexpr int NPAIR = NIT * (NIT + 1) / 2;
-  static constexpr int RQ = READOUT ? CS : 1;  // readout-only arrays collapse in the state pass
-  static constexpr int RP = READOUT ? NPAIR : 1;
-  alignas(16) float k[CS][kDK];
-  alignas(16) float vt[kDV][LK];
-  alignas(16) float phikt[WP][LK];
-  alignas(16) float q[RQ][kDK];
-  alignas(16) float phiq[RQ][LQ];
-  alignas(16) f32x4 a[RP][64];  // score tiles in MFMA B-operand lane order
-  float den[RQ];
-};
-
 __device__ __forceinline__ int pair_index(int jt, int it) { return it * (it + 1) / 2 + jt; }
-
-__device__ __forceinline__ void load_row16(const float* src, float (&x)[kDK], float scale) {
-#pragma unroll
-  for (int d = 0; d < kDK; ++d) x[d] = scale * src[d];
-}
-
-// This wave's rows of phi(K_c)^T for token j.  A token past the end has a zero k row, so all its
-// features are zero except the constant one.
-template <int NT, int CS, bool READOUT, int G>
-__device__ __forceinline__ void phik_rows(Smem<NT, CS, READOUT>& sm, int j, const float (&x)[kDK], bool valid) {
-  using SP = Split<NT>;
-  [&]<int... I>(std::integer_sequence<int, I...>) {
-    (([&] {
-       constexpr int row = G * SP::RK + I;
-       if constexpr (row == 0)
-         sm.phikt[row][j] = valid ? 1.f : 0.f;
-       else if constexpr (row < SP::WP)
-         sm.phikt[row][j] = feat<NT, row>(x);
-     }()),
-     ...);
-  }(std::make_integer_sequence<int, SP::RK>{});
-}
-
-// This wave's 16-byte groups of the phi(sQ) row of token i.
-template <int NT, int CS, bool READOUT, int G>
-__device__ __forceinline__ void phiq_groups(Smem<NT, CS, READOUT>& sm, int i, const float (&x)[kDK]) {
-  using SP = Split<NT>;
-  [&]<int... P>(std::integer_sequence<int, P...>) {
-    (([&] {
-       constexpr int grp = G * SP::RG + P;
-       if constexpr (grp < SP::NG) {
-         constexpr int s0 = grp * SP::GQ;
-         const f32x4 v = {feat<NT, s0 + 0>(x), feat<NT, s0 + 1>(x), feat<NT, s0 + 2>(x), feat<NT, s0 + 3>(x)};
-         *reinterpret_cast<f32x4*>(&sm.phiq[i][s0]) = v;
-       }
-     }()),
-     ...);
-  }(std::make_integer_sequence<int, SP::RG>{});
-}
-
-template <int NT, int CS, bool READOUT, int G>
-__device__ __forceinline__ void features_wave(Smem<NT, CS, READOUT>& sm, int l, int nv, float scale) {
-#pragma unroll
-  for (int tt = 0; tt < CS / 64; ++tt) {
-    const int j = l + 64 * tt;
-    float x[kDK];
-    load_row16(&sm.k[j][0], x, 1.0f);
-    phik_rows<NT, CS, READOUT, G>(sm, j, x, j < nv);
-    if constexpr (READOUT) {
-      load_row16(&sm.q[j][0], x, scale);
-      phiq_groups<NT, CS, READOUT, G>(sm, j, x);
-    }
-  }
-}
-
-template <int NT, int CS, bool READOUT>
-__device__ __forceinline__ void features(Smem<NT, CS, READOUT>& sm, int w, int l, int nv, float scale) {
-  static_assert(kWaves == 5, "feature split assumes 5 waves");
-  switch (w) {
-    case 0: features_wave<NT, CS, READOUT, 0>(sm, l, nv, scale); break;
-    case 1: features_wave<NT, CS, READOUT, 1>(sm, l, nv, scale); break;
-    case 2: features_wave<NT, CS, READOUT, 2>(sm, l, nv, scale); break;
-    case 3: features_wave<NT, CS, READOUT, 3>(sm, l, nv, scale); break;
-    default: features_wave<NT, CS, READOUT, 4>(sm, l, nv, scale); break;
-  }
-}
 
 // x where ok holds, else zero, selected word by word (a select of the whole vector would take the
 // operands' addresses and move them to scratch memory).
 __device__ __forceinline__ uint4 keep_if(bool ok, uint4 x) {
   return make_uint4(ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u);
-}
-
-// Chunk inputs in flight: each thread's 16-byte pieces of q, k and v for one chunk.
-template <int CS, bool READOUT>
-struct Prefetch {
-  using E = float;
-  static constexpr int EPP = 4;               // elements per 16-byte piece
-  static constexpr int PR = kDK / EPP;        // pieces per q/k row
-  static constexpr int PV = kDV / EPP;        // pieces per v row
-  static constexpr int NQK = (CS * PR + kThreads - 1) / kThreads;
-  static constexpr int NV = (CS * PV + kThreads - 1) / kThreads;
-  uint4 q[READOUT ? NQK : 1], k[NQK], v[NV];
-
-  int nv = 0;  // valid tokens of the chunk in flight
-
-  // Issue the global loads of the chunk starting at token tok0 (nv valid tokens).  Tokens past the
-  // end read the chunk's first row, and the loaded values are not touched before store(), so the
-  // loads stay in flight while the current chunk is computed.
-  __device__ __forceinline__ void load(const E* qg, const E* kg, const E* vg, long long tok0, int nv_, int tid) {
-    nv = nv_;
-#pragma unroll
-    for (int u = 0; u < NQK; ++u) {
-      const int p = tid + u * kThreads, row = p / PR, pc = p % PR;
-      const long long r = tok0 + (p < CS * PR && row < nv ? row : 0);
-      k[u] = *reinterpret_cast<const uint4*>(kg + r * kDK + pc * EPP);
-      if constexpr (READOUT) q[u] = *reinterpret_cast<const uint4*>(qg + r * kDK + pc * EPP);
-    }
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int p = tid + u * kThreads, j = p % CS, pc = p / CS;
-      const long long r = tok0 + (p < CS * PV && j < nv ? j : 0);
-      v[u] = *reinterpret_cast<const uint4*>(vg + r * kDV + pc * EPP);
-    }
-  }
-
-  // Write the pieces to LDS: q, k rows as they are, v transposed; tokens past the end as zeros.
-  template <class SM>
-  __device__ __forceinline__ void store(SM& sm, int tid) const {
-#pragma unroll
-    for (int u = 0; u < NQK; ++u) {
-      const int p = tid + u * kThreads, row = p / PR, pc = p % PR;
-      if (p < CS * PR) {
-        *reinterpret_cast<uint4*>(&sm.k[row][pc * EPP]) = keep_if(row < nv, k[u]);
-        if constexpr (READOUT) *reinterpret_cast<uint4*>(&sm.q[row][pc * EPP]) = keep_if(row < nv, q[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
-      const int p = tid + u * kThreads, j = p % CS, pc = p / CS;
-      if (p < CS * PV) {
-        union {
-          uint4 u4;
-          E e[EPP];
-        } buf;
-        buf.u4 = keep_if(j < nv, v[u]);
-#pragma unroll
-        for (int r = 0; r < EPP; ++r) sm.vt[pc * EPP + r][j] = buf.e[r];
-      }
-    }
-  }
-};
-
-// One segment of L tokens per workgroup; grid = (segments, heads).
-// READOUT = false: accumulate the segment's (S, z) increment and write it to its workspace slot.
-// READOUT = true : start from the exclusive prefix in the slot and write the outputs.
-template <int NT, int CS, bool READOUT>
-__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ o,
-    float* __restrict__ ws, int N, int L, int nseg, long long stride, float scale) {
-  using G = Geo<NT>;
-  using SM = Smem<NT, CS, READOUT>;
-  constexpr int W = G::W, NAT = G::NAT;
-  constexpr int NIT = CS / 16;
-  static_assert(CS == 64 || CS == 128, "chunk of 64 or 128 tokens");
-  __shared__ SM sm;
-
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, l16 = l & 15, lg = l >> 4;
-  const bool zw = w == kValueWaves;  // the normaliser wave
-  const int col = 16 * w + l16;      // value column of this lane (value waves)
-  const int seg = blockIdx.x;
-  const long long bh = blockIdx.y;
-  const int t_begin = seg * L, t_end = min(N, t_begin + L);
-  const long long hbase = bh * (long long)N;
-  float* slot = ws + (bh * nseg + seg) * stride;
-
-  Prefetch<CS, READOUT> pf;
-  pf.load(q, k, v, hbase + t_begin, min(CS, t_end - t_begin), tid);
-
-  // Running state: Srun[t][r] = S1[16t + 4lg + r][column l16 of this wave's tile], where the
-  // normaliser wave's tile is [z | 0 ... 0].
-  f32x4 Srun[NAT];
-#pragma unroll
-  for (int t = 0; t < NAT; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int a = 16 * t + 4 * lg + r;
-      float x = 0.f;
-      if (READOUT && a < W) {
-        if (!zw) x = slot[(long long)a * kDV + col];
-        else if (l16 == 0) x = slot[(long long)W * kDV + a];
-      }
-      Srun[t][r] = x;
-    }
-
-  // The normaliser wave's ones column as an MFMA operand (rows/columns other than the first are zero).
-  const float one = (zw && l16 == 0) ? 1.f : 0.f;
-
-  f32x4 O[READOUT ? NIT : 1];
-  long long out_tok0 = -1;  // first token of the chunk whose outputs are pending
-  int out_nv = 0;
-  auto store_outputs = [&]() {
-    if constexpr (READOUT) {
-      if (out_tok0 >= 0 && !zw) {
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const int i = 16 * it + l16;
-          if (i < out_nv) {
-            const float inv = __builtin_amdgcn_rcpf(sm.den[i]);
-            const f32x4 r = O[it];
-            *reinterpret_cast<f32x4*>(o + (out_tok0 + i) * kDV + 16 * w + 4 * lg) =
-                f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
-          }
-        }
-      }
-    }
-  };
-
-  for (int c0 = t_begin; c0 < t_end; c0 += CS) {
-    const int nv = min(CS, t_end - c0);
-    const long long tok0 = hbase + c0;
-
-    // ---- A: previous chunk's outputs; this chunk's inputs to LDS; next chunk's loads issued ----
-    __syncthreads();  // previous chunk done with LDS; its denominators visible
-    store_outputs();
-    pf.store(sm, tid);
-    if (c0 + CS < t_end) pf.load(q, k, v, tok0 + CS, min(CS, t_end - c0 - CS), tid);
-    __syncthreads();
-    features<NT, CS, READOUT>(sm, w, l, nv, scale);
-    __syncthreads();
-
-    // ---- B: scores, readout with S_{<c}, state update ----
-    if constexpr (READOUT) {
-      for (int p = w; p < SM::NPAIR; p += kWaves) {
-        int it = 0;
-        while ((it + 1) * (it + 2) / 2 <= p) ++it;
-        const int jt = p - it * (it + 1) / 2;
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.k[16 * jt + l16][4 * lg]);
-        const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.q[16 * it + l16][4 * lg]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bv[r], sc, 0, 0, 0);
-        // sc[r] = k_j . q_i with j = 16jt + 4lg + r, i = 16it + l16
-        f32x4 tile;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
-          tile[r] = j <= i ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
-        }
-        sm.a[p][l] = tile;
-      }
-      // readout: O[it][r] = (phi(sQ) S1_{<c})[token 16it + l16][tile column 4lg + r]
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < NAT; ++t)
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[16 * it + l16][16 * t + 4 * lg]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], O[it], 0, 0, 0);
-        }
-    }
-    // state update (after the readout used S_{<c}): Srun[t] += phi(K)^T[16t.., chunk] V1[chunk, tile]
-#pragma unroll
-    for (int jb = 0; jb < CS / 16; ++jb) {
-      const f32x4 bv = zw ? f32x4{one, one, one, one} : *reinterpret_cast<const f32x4*>(&sm.vt[col][16 * jb + 4 * lg]);
-#pragma unroll
-      for (int t = 0; t < NAT; ++t) {
-        const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[16 * t + l16][16 * jb + 4 * lg]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
-      }
-    }
-    if constexpr (READOUT) {
-      __syncthreads();  // score tiles visible
-      // ---- C: intra-chunk PV (V1^T times scores); the normaliser wave publishes the denominators ----
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        for (int jt = 0; jt <= it; ++jt) {
-          const int p = pair_index(jt, it);
-          const f32x4 av = zw ? f32x4{one, one, one, one}
-                              : *reinterpret_cast<const f32x4*>(&sm.vt[col][16 * jt + 4 * lg]);
-          const f32x4 bv = sm.a[p][l];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bv[r], O[it], 0, 0, 0);
-        }
-        if (zw && lg == 0) sm.den[16 * it + l16] = O[it][0];
-      }
-      out_tok0 = tok0;
-      out_nv = nv;
-    }
-  }
-
-  if constexpr (READOUT) {
-    __syncthreads();
-    store_outputs();
-  } else {
-#pragma unroll
-    for (int t = 0; t < NAT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int a = 16 * t + 4 * lg + r;
-        if (a < W) {
-          if (!zw) slot[(long long)a * kDV + col] = Srun[t][r];
-          else if (l16 == 0) slot[(long long)W * kDV + a] = Srun[t][r];
-        }
-      }
-  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -864,34 +518,7 @@ int n_segments(int BH, int nchunk, int target) {
   return (int)want;
 }
 
-constexpr int kSegTarget = 256;
-
-template <int NT, int CS>
-int run(const PrefillArgs& a) {
-  const int nchunk = cdiv(a.N, CS);
-  const int nseg0 = n_segments(a.BH, nchunk, kSegTarget);
-  const int L = cdiv(nchunk, nseg0) * CS;
-  const int nseg = cdiv(a.N, L);
-  float* ws = (float*)a.ws;
-  const long long elems = Geo<NT>::W * (long long)(kDV + 1);
-  const dim3 grid(nseg, a.BH), block(kThreads);
-  const float* q = (const float*)a.q;
-  const float* k = (const float*)a.k;
-  const float* v = (const float*)a.v;
-  prefill_mfma_kernel<NT, CS, false>
-      <<<grid, block, 0, a.stream>>>(q, k, v, nullptr, ws, a.N, L, nseg, a.s.stride, a.s.scale);
-  if (hipGetLastError() != hipSuccess) return -3;
-  if (seg_scan_launch(ws, a.state, a.BH, nseg, a.s.stride, elems, a.o != nullptr, a.stream)) return -3;
-  if (a.o) {
-    prefill_mfma_kernel<NT, CS, true>
-        <<<grid, block, 0, a.stream>>>(q, k, v, a.o, ws, a.N, L, nseg, a.s.stride, a.s.scale);
-    if (hipGetLastError() != hipSuccess) return -3;
-  }
-  return 0;
-}
-
-// The pipelined bfloat16 kernel keeps one workgroup per CU (double-buffered LDS); the float32
-// kernel fits two.
+// One workgroup per CU (double-buffered LDS): about 256 workgroups in total.
 constexpr int kSegTargetPipe = 256;
 
 template <int NT>
@@ -918,34 +545,24 @@ int run_pipe(const PrefillArgs& a) {
   return 0;
 }
 
-// Both paths walk 64-token chunks whatever the configured chunk (64 or 128); the outputs do not
-// depend on the chunk length beyond rounding.
-constexpr int kChunk = 64;
-
-template <int NT>
-int run_dtype(const PrefillArgs& a) {
-  return a.s.dtype == 1 ? run_pipe<NT>(a) : run<NT, kChunk>(a);
-}
-
 }  // namespace
 
-bool prefill_mfma_has(int nt, int dk, int dv, int C) {
-  return dk == kDK && dv == kDV && nt >= 1 && nt <= 3 && (C == 64 || C == 128);
-}
+// bfloat16 inputs at d_k = 16, d_v = 64, n = 1..3.  The kernel walks 64-token chunks whatever the
+// configured chunk (64 or 128); the outputs do not depend on the chunk length beyond rounding.
+bool prefill_mfma_has(int nt, int dk, int dv, int dtype) { return dk == kDK && dv == kDV && nt >= 1 && nt <= 3 && dtype == 1; }
 
-long long prefill_mfma_ws_bytes(const Shape& s, int BH, int N, int C) {
-  const int nchunk = cdiv(N, kChunk);
-  const int nseg0 = n_segments(BH, nchunk, s.dtype == 1 ? kSegTargetPipe : kSegTarget);
-  const int L = cdiv(nchunk, nseg0) * kChunk;
+long long prefill_mfma_ws_bytes(const Shape& s, int BH, int N) {
+  const int nchunk = cdiv(N, kPipeChunk);
+  const int L = cdiv(nchunk, n_segments(BH, nchunk, kSegTargetPipe)) * kPipeChunk;
   return (long long)BH * cdiv(N, L) * s.stride * 4;
 }
 
 int prefill_mfma_launch(const PrefillArgs& a) {
-  if (!prefill_mfma_has(a.s.nt, a.s.dk, a.s.dv, a.C)) return -2;
+  if (!prefill_mfma_has(a.s.nt, a.s.dk, a.s.dv, a.s.dtype)) return -2;
   switch (a.s.nt) {
-    case 1: return run_dtype<1>(a);
-    case 2: return run_dtype<2>(a);
-    default: return run_dtype<3>(a);
+    case 1: return run_pipe<1>(a);
+    case 2: return run_pipe<2>(a);
+    default: return run_pipe<3>(a);
   }
 }
 

@@ -1,12 +1,12 @@
-// MFMA prefill path (bfloat16 / float32 matrix cores on gfx950) for d_k = 16, d_v = 64.
+// Pipelined bfloat16 MFMA prefill (gfx950) for d_k = 16, d_v = 64, n = 1..3.
 #pragma once
 
 #include "launch.hpp"
 
 namespace taylor {
 
-bool prefill_mfma_has(int nt, int dk, int dv, int C);
-long long prefill_mfma_ws_bytes(const Shape& s, int BH, int N, int C);
+bool prefill_mfma_has(int nt, int dk, int dv, int dtype);
+long long prefill_mfma_ws_bytes(const Shape& s, int BH, int N);
 int prefill_mfma_launch(const PrefillArgs& a);
 
 }  // namespace taylor

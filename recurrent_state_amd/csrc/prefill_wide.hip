@@ -48,11 +48,13 @@ constexpr int kPairs = kNIT * (kNIT + 1) / 2;  // (key tile <= query tile) pairs
 constexpr int kLS = kCS + 4;     // phi(K)^T and V^T row stride in floats (36: conflict-free 16-byte reads)
 static_assert(kPairs <= kProd, "one score tile per producer");
 
-// Features per block: 64 at n = 4 (16 blocks: enough (head, block) workgroups at few heads without a
-// state pass), 128 at n = 5 (38 blocks; half the partial-output traffic of 64).
+// Features per block: one block holds all features at n <= 3 (16, 32, 160 for W = 1, 17, 153: the
+// outputs are then final and written directly); 64 at n = 4 (16 blocks: enough (head, block)
+// workgroups at few heads without a state pass); 128 at n = 5 (38 blocks; half the partial-output
+// traffic of 64).
 template <int NT>
 constexpr int block_features() {
-  return NT == 4 ? 64 : 128;
+  return NT == 1 ? 16 : NT == 2 ? 32 : NT == 3 ? 160 : NT == 4 ? 64 : 128;
 }
 template <int NT>
 constexpr int n_blocks() {
@@ -86,6 +88,7 @@ struct WideIO {
   float* state;        // nseg == 1: incoming / final state [heads][stride], or null
   float* part_num;     // [blocks][heads * N][d_v] partial numerators
   float* part_den;     // [blocks][heads * N] partial denominators
+  float* out;          // a single block: the outputs [heads * N][d_v]
   long long stride;
   int nseg;
   int BH;
@@ -365,7 +368,23 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(const E* __restr
         for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
       }
     }
-    if constexpr (READOUT) {
+    if constexpr (READOUT && n_blocks<NT>() == 1) {
+      // a single block: the outputs are final (columns 16w + 4lg .. + 3 of token 16it + l16)
+#pragma unroll
+      for (int it = 0; it < kNIT; ++it) {
+        const int i = 16 * it + l16;
+        float d = 0.f;
+#pragma unroll
+        for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
+        for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][it * (it + 1) / 2 + jt][l16];
+        if (i < nv) {
+          const float inv = 1.0f / d;
+          const f32x4 r = O[it];
+          *reinterpret_cast<f32x4*>(io.out + (tok0 + i) * kDV + 16 * w + 4 * lg) =
+              f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
+        }
+      }
+    } else if constexpr (READOUT) {
       // partial numerators of this block (columns 16w + 4lg .. + 3 of token 16it + l16)
       float* pn = io.part_num + ((long long)fb * io.BH * N + tok0) * kDV;
 #pragma unroll
@@ -441,7 +460,7 @@ WideLayout wide_layout(const Shape& s, int BH, int N, bool outputs) {
   lay.nseg = cdiv(N, lay.L);
   // slots are needed for several segments, and always for a state-only call (the scan sums them)
   lay.slot_floats = (lay.nseg > 1 || !outputs) ? (long long)BH * lay.nseg * s.stride : 0;
-  lay.part_floats = outputs ? (long long)NB * BH * N * (kDV + 1) : 0;
+  lay.part_floats = (outputs && NB > 1) ? (long long)NB * BH * N * (kDV + 1) : 0;
   return lay;
 }
 
@@ -462,15 +481,16 @@ int wide_run(const PrefillArgs& a) {
   const long long elems = FeatureTable<NT, kDK>::W * (long long)(kDV + 1);
   const dim3 grid(lay.nseg, a.BH, NB), block(kThreads);
   if (!outputs || lay.nseg > 1) {
-    const WideIO io{slots, nullptr, nullptr, nullptr, a.s.stride, lay.nseg, a.BH};
+    const WideIO io{slots, nullptr, nullptr, nullptr, nullptr, a.s.stride, lay.nseg, a.BH};
     prefill_wide_kernel<NT, E, false><<<grid, block, 0, a.stream>>>(q, k, v, io, a.N, lay.L, a.s.scale);
     if (hipGetLastError() != hipSuccess) return -3;
     if (seg_scan_launch(slots, a.state, a.BH, lay.nseg, a.s.stride, elems, outputs, a.stream)) return -3;
     if (!outputs) return 0;
   }
-  const WideIO io{slots, lay.nseg == 1 ? a.state : nullptr, part_num, part_den, a.s.stride, lay.nseg, a.BH};
+  const WideIO io{slots, lay.nseg == 1 ? a.state : nullptr, part_num, part_den, a.o, a.s.stride, lay.nseg, a.BH};
   prefill_wide_kernel<NT, E, true><<<grid, block, 0, a.stream>>>(q, k, v, io, a.N, lay.L, a.s.scale);
   if (hipGetLastError() != hipSuccess) return -3;
+  if (NB == 1) return 0;  // the outputs are final
   const long long tokens = (long long)a.BH * a.N;
   wide_reduce_kernel<<<dim3((unsigned)cdiv(tokens * 16, 256)), dim3(256), 0, a.stream>>>(part_num, part_den, a.o,
                                                                                           tokens, NB);
@@ -479,19 +499,33 @@ int wide_run(const PrefillArgs& a) {
 
 }  // namespace
 
-bool prefill_wide_has(int nt, int dk, int dv) { return dk == kDK && dv == kDV && (nt == 4 || nt == 5); }
+// n = 4, 5 for either input type; n = 1..3 for float32 inputs (bfloat16 ones have their own kernel).
+bool prefill_wide_has(int nt, int dk, int dv, int dtype) {
+  return dk == kDK && dv == kDV && (nt == 4 || nt == 5 || (nt >= 1 && nt <= 3 && dtype == 0));
+}
 
 // An upper bound over both uses (with and without outputs): the query does not know which follows.
 long long prefill_wide_ws_bytes(const Shape& s, int BH, int N) {
   auto bytes = [](const WideLayout& lay) { return (round_up(lay.slot_floats, 64) + lay.part_floats) * 4; };
-  if (s.nt == 4) return std::max(bytes(wide_layout<4>(s, BH, N, true)), bytes(wide_layout<4>(s, BH, N, false)));
-  return std::max(bytes(wide_layout<5>(s, BH, N, true)), bytes(wide_layout<5>(s, BH, N, false)));
+  auto both = [&](auto layout) { return std::max(bytes(layout(true)), bytes(layout(false))); };
+  switch (s.nt) {
+    case 1: return both([&](bool o) { return wide_layout<1>(s, BH, N, o); });
+    case 2: return both([&](bool o) { return wide_layout<2>(s, BH, N, o); });
+    case 3: return both([&](bool o) { return wide_layout<3>(s, BH, N, o); });
+    case 4: return both([&](bool o) { return wide_layout<4>(s, BH, N, o); });
+    default: return both([&](bool o) { return wide_layout<5>(s, BH, N, o); });
+  }
 }
 
 int prefill_wide_launch(const PrefillArgs& a) {
-  if (!prefill_wide_has(a.s.nt, a.s.dk, a.s.dv)) return -2;
-  if (a.s.nt == 4) return a.s.dtype == 0 ? wide_run<4, float>(a) : wide_run<4, __bf16>(a);
-  return a.s.dtype == 0 ? wide_run<5, float>(a) : wide_run<5, __bf16>(a);
+  if (!prefill_wide_has(a.s.nt, a.s.dk, a.s.dv, a.s.dtype)) return -2;
+  switch (a.s.nt) {
+    case 1: return wide_run<1, float>(a);
+    case 2: return wide_run<2, float>(a);
+    case 3: return wide_run<3, float>(a);
+    case 4: return a.s.dtype == 0 ? wide_run<4, float>(a) : wide_run<4, __bf16>(a);
+    default: return a.s.dtype == 0 ? wide_run<5, float>(a) : wide_run<5, __bf16>(a);
+  }
 }
 
 }  // namespace taylor
