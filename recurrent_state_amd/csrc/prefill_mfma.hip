@@ -127,11 +127,19 @@ struct PipeSplit {
 };
 
 // A token past the end has a zero k row, so all its features are zero except the constant one.
+// Rows are written in pairs (r0, r0+1) as whole dwords: lanes j and j^1 swap their (r0, r1) pairs
+// (a quad permutation), then the even lane stores row r0 of tokens j, j+1 and the odd lane row r1 of
+// tokens j-1, j.
 template <int NT, bool READOUT, int G>
 __device__ __forceinline__ void pipe_phik_rows(PipeSmem<NT, READOUT>& sm, int b, int j, const float (&x)[kDK],
                                                bool valid) {
   using SP = PipeSplit<NT>;
+  using SM = PipeSmem<NT, READOUT>;
   static_assert(SP::RK % 2 == 0, "rows are written in pairs");
+  const bool odd = j & 1;
+  // byte selectors of v_perm_b32(partner, own): even lane -> (own.lo, partner.lo), odd -> (partner.hi, own.hi)
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+  char* base = reinterpret_cast<char*>(&sm.phikt[b][0][0]) + (odd ? SM::LK * 2 + (j - 1) * 2 : j * 2);
   [&]<int... I>(std::integer_sequence<int, I...>) {
     (([&] {
        constexpr int r0 = G * SP::RK + 2 * I, r1 = r0 + 1;
@@ -141,10 +149,9 @@ __device__ __forceinline__ void pipe_phik_rows(PipeSmem<NT, READOUT>& sm, int b,
            f0 = valid ? 1.f : 0.f;
          else
            f0 = feat<NT, r0>(x);
-         const bf16x2 pr = to_bf16x2(f0, feat<NT, r1>(x));
-         const uint32_t u = __builtin_bit_cast(uint32_t, pr);
-         *reinterpret_cast<uint16_t*>(&sm.phikt[b][r0][j]) = (uint16_t)u;
-         *reinterpret_cast<uint16_t*>(&sm.phikt[b][r1][j]) = (uint16_t)(u >> 16);
+         const uint32_t u = __builtin_bit_cast(uint32_t, to_bf16x2(f0, feat<NT, r1>(x)));
+         const uint32_t v = (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+         *reinterpret_cast<uint32_t*>(base + r0 * SM::LK * 2) = __builtin_amdgcn_perm(v, u, sel);
        }
      }()),
      ...);
