@@ -126,20 +126,32 @@ struct PipeSplit {
   static constexpr int VC = kDV / kPipeProducers;
 };
 
+// Transposed bfloat16 tiles ([row][token], `stride` elements per row) are written two rows at a time
+// as whole dwords: lane j holds (row r, row r+1) of token j; lanes j and j^1 swap those pairs (a quad
+// permutation), then the even lane stores row r of tokens j, j+1 and the odd lane row r+1 of tokens
+// j-1, j.  `base` is the lane's byte address for row 0; a row pair adds r * stride * 2 bytes.
+struct PairStore {
+  char* base;
+  uint32_t sel;  // v_perm_b32(partner, own) bytes: even -> (own.lo, partner.lo), odd -> (partner.hi, own.hi)
+  __device__ __forceinline__ PairStore(__bf16* tile, int stride, int j) {
+    const bool odd = j & 1;
+    base = reinterpret_cast<char*>(tile) + (odd ? stride * 2 + (j - 1) * 2 : j * 2);
+    sel = odd ? 0x03020706u : 0x05040100u;
+  }
+  __device__ __forceinline__ void store(int row_bytes, uint32_t own) const {
+    const uint32_t partner = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+    *reinterpret_cast<uint32_t*>(base + row_bytes) = __builtin_amdgcn_perm(partner, own, sel);
+  }
+};
+
 // A token past the end has a zero k row, so all its features are zero except the constant one.
-// Rows are written in pairs (r0, r0+1) as whole dwords: lanes j and j^1 swap their (r0, r1) pairs
-// (a quad permutation), then the even lane stores row r0 of tokens j, j+1 and the odd lane row r1 of
-// tokens j-1, j.
 template <int NT, bool READOUT, int G>
 __device__ __forceinline__ void pipe_phik_rows(PipeSmem<NT, READOUT>& sm, int b, int j, const float (&x)[kDK],
                                                bool valid) {
   using SP = PipeSplit<NT>;
   using SM = PipeSmem<NT, READOUT>;
   static_assert(SP::RK % 2 == 0, "rows are written in pairs");
-  const bool odd = j & 1;
-  // byte selectors of v_perm_b32(partner, own): even lane -> (own.lo, partner.lo), odd -> (partner.hi, own.hi)
-  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
-  char* base = reinterpret_cast<char*>(&sm.phikt[b][0][0]) + (odd ? SM::LK * 2 + (j - 1) * 2 : j * 2);
+  const PairStore ps(&sm.phikt[b][0][0], SM::LK, j);
   [&]<int... I>(std::integer_sequence<int, I...>) {
     (([&] {
        constexpr int r0 = G * SP::RK + 2 * I, r1 = r0 + 1;
@@ -149,9 +161,7 @@ __device__ __forceinline__ void pipe_phik_rows(PipeSmem<NT, READOUT>& sm, int b,
            f0 = valid ? 1.f : 0.f;
          else
            f0 = feat<NT, r0>(x);
-         const uint32_t u = __builtin_bit_cast(uint32_t, to_bf16x2(f0, feat<NT, r1>(x)));
-         const uint32_t v = (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
-         *reinterpret_cast<uint32_t*>(base + r0 * SM::LK * 2) = __builtin_amdgcn_perm(v, u, sel);
+         ps.store(r0 * SM::LK * 2, __builtin_bit_cast(uint32_t, to_bf16x2(f0, feat<NT, r1>(x))));
        }
      }()),
      ...);
@@ -266,7 +276,8 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
     unpack_row16(in.q, x, scale);
     sm.den_part[b][G][l] = pipe_phiq_groups<NT, READOUT, G>(sm, b, b, l, x);
   }
-  // V^T: this producer's value columns of token l
+  // V^T: this producer's value columns of token l (16-bit stores: the dword pairing measured no
+  // faster here)
 #pragma unroll
   for (int u = 0; u < PipeIn<READOUT, G>::NVP; ++u) {
     const uint32_t w[4] = {in.v[u].x, in.v[u].y, in.v[u].z, in.v[u].w};
