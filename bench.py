@@ -14,6 +14,11 @@ token (per decode step of all 64 sequences), each against its roofline; the orac
 CPU throughput on a bounded sample of the same prefill workload; and, in `roofline`,
 the dominant kernel (the decode step: 1,000 launches per step) measured with HIP
 events on the stream it runs on.
+
+Secondary timings after the timed steps (each can be skipped by a flag): decode over
+512 sequences whose states exceed the last-level cache, the float32 prefill at
+n = 1..5 (B=1, H=16, N=16,384), and a ragged-batch prefill (32 prompts of seeded
+lengths 1..2,047, 16 heads, bfloat16, n = 3).
 """
 
 import argparse
@@ -192,6 +197,36 @@ def order_sweep(rs, synth, torch, dev, reps=3):
     return res
 
 
+def varlen_prefill(rs, synth, torch, dev, reps=5):
+    """Ragged-batch prefill: 32 prompts of 1..2047 seeded lengths (about the main step's 32k tokens per
+    head), 16 heads, bfloat16 inputs, n = 3, packed head-major; state init + prefill, HIP events."""
+    H, n = 16, 3
+    lens = synth.ragged_lengths(6, 32, 1, 2047)
+    x = synth.make_ragged(6, lens, H, DK, DV, synth.BF16)
+    q, k, v = x.torch(dev)
+    cu = x.torch_cu(dev)
+    T, N = sum(lens), max(lens)
+    cfg = rs.config(n, DK, DV, 0, 1.0, rs.TAYLOR_BF16)
+    o = torch.empty((H, T, DV), dtype=torch.float32, device=dev)
+    st = torch.empty((len(lens), H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
+    ws = rs.new_varlen_workspace(cfg, len(lens), H, N, T, dev)
+
+    def step():
+        rs.taylor_state_init(st, cfg)
+        rs.taylor_attn_prefill_varlen(q, k, v, o, st, ws, cu, N, cfg)
+
+    step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    return {"sequences": len(lens), "heads": H, "tokens": T, "max_len": N, "us": us, "tok_s": T / us * 1e6}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +239,7 @@ def main():
                     help="skip the secondary decode run whose states exceed the last-level cache")
     ap.add_argument("--big-decode-steps", type=int, default=100)
     ap.add_argument("--no-order-sweep", action="store_true", help="skip the n = 1..5 float32 prefill timings")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the ragged-batch prefill timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (scale reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -374,6 +410,9 @@ def main():
     if not args.no_order_sweep:
         log("order sweep n = 1..5 (float32 prefill, B1 H16 N16384)")
         out["order_sweep_prefill_f32_B1xH16xN16384"] = order_sweep(rs, synth, torch, dev)
+    if not args.no_varlen:
+        log("ragged-batch prefill (32 prompts, 16 heads, bf16)")
+        out["prefill_varlen_bf16_32seqs_H16"] = varlen_prefill(rs, synth, torch, dev)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(x)

@@ -135,6 +135,42 @@ int taylor_state_init(float* state, int B, int H, const taylor_config* cfg, hipS
 int taylor_attn_prefill(const void* q, const void* k, const void* v, float* o, float* state, void* workspace, int B,
                         int H, int N, const taylor_config* cfg, hipStream_t stream);
 
+/* Bytes of device workspace taylor_attn_prefill_varlen needs for these sizes
+ * (may be 0); it depends on the sizes only, not on the individual lengths.
+ * Host only.  Negative taylor_status if cfg or sizes are invalid;
+ * TAYLOR_ERR_UNSUPPORTED for a config without a ragged-batch kernel (below). */
+int64_t taylor_prefill_varlen_workspace_bytes(const taylor_config* cfg, int n_seqs, int H, int max_seqlen,
+                                              int64_t total_tokens);
+
+/* Causal prefill of a ragged batch: n_seqs sequences of different lengths, each
+ * its own causal history (Abstract: the states sum over a sequence's past; they
+ * are kept per sequence), packed back to back along the token axis.
+ *   q, k       : [H][T][d_k] in cfg->in_dtype, T = total_tokens; sequence b
+ *                occupies tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head;
+ *   v          : [H][T][d_v] in cfg->in_dtype;
+ *   o          : [H][T][d_v] float32, or NULL for a state-only pass;
+ *   state      : [n_seqs][H][stride] float32, in/out as in taylor_attn_prefill
+ *                (NULL: empty histories, final states discarded).  At least one
+ *                of o and state must be non-NULL;
+ *   cu_seqlens : DEVICE array of n_seqs+1 int32 offsets (4-byte aligned), read
+ *                by the kernels only: 0 = cu[0] <= cu[1] <= ... <= cu[n_seqs] = T
+ *                and every length cu[b+1]-cu[b] <= max_seqlen.  Violations are not
+ *                detected: the kernels clamp every offset into [0, T], so no access
+ *                leaves the buffers, but outputs and states are then undefined;
+ *   workspace  : taylor_prefill_varlen_workspace_bytes(cfg, n_seqs, H,
+ *                max_seqlen, T) bytes (NULL allowed when 0); contents on entry
+ *                ignored, on return undefined.
+ * Each sequence gives, up to float32 summation order, the outputs and final
+ * state that taylor_attn_prefill with B = 1 gives on it alone; an empty
+ * sequence leaves its state unchanged.  Compiled for d_k = 16, d_v = 64 (the
+ * matrix-core kernels, n = 1..5, both input types); other configs return
+ * TAYLOR_ERR_UNSUPPORTED.  T > n_seqs * max_seqlen or negative sizes:
+ * TAYLOR_ERR_INVALID_ARG.  n_seqs*H == 0 or T == 0 is a no-op.  Calls sharing a
+ * workspace must not overlap. */
+int taylor_attn_prefill_varlen(const void* q, const void* k, const void* v, float* o, float* state, void* workspace,
+                               const int32_t* cu_seqlens, int n_seqs, int H, int max_seqlen, int64_t total_tokens,
+                               const taylor_config* cfg, hipStream_t stream);
+
 /* One decode step per (b, h): S += phi(k_t) [v_t | 1]^T (one rank-one update),
  * then o_t = (phi(scale*q_t)^T S)[:d_v] / (phi(scale*q_t)^T z) -- the update comes
  * first, so the current token attends to itself.

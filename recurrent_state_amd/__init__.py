@@ -36,6 +36,8 @@ EXPORTS = (
     "taylor_prefill_workspace_bytes",
     "taylor_state_init",
     "taylor_attn_prefill",
+    "taylor_prefill_varlen_workspace_bytes",
+    "taylor_attn_prefill_varlen",
     "taylor_attn_decode_step",
 )
 
@@ -94,6 +96,8 @@ def lib():
         "taylor_prefill_workspace_bytes": (i64, [cfgp, i, i, i]),
         "taylor_state_init": (i, [p, i, i, cfgp, p]),
         "taylor_attn_prefill": (i, [p, p, p, p, p, p, i, i, i, cfgp, p]),
+        "taylor_prefill_varlen_workspace_bytes": (i64, [cfgp, i, i, i, i64]),
+        "taylor_attn_prefill_varlen": (i, [p, p, p, p, p, p, p, i, i, i, i64, cfgp, p]),
         "taylor_attn_decode_step": (i, [p, p, p, p, p, i, i, cfgp, p]),
     }
     for name, (res, args) in sig.items():
@@ -181,6 +185,12 @@ def taylor_prefill_workspace_bytes(cfg, B, H, N):
                          "taylor_prefill_workspace_bytes")
 
 
+def taylor_prefill_varlen_workspace_bytes(cfg, n_seqs, H, max_seqlen, total_tokens):
+    return _check_nonneg(
+        lib().taylor_prefill_varlen_workspace_bytes(ctypes.byref(cfg), n_seqs, H, max_seqlen, total_tokens),
+        "taylor_prefill_varlen_workspace_bytes")
+
+
 # ---- device entry points ------------------------------------------------------------------------
 
 
@@ -197,6 +207,17 @@ def taylor_attn_prefill(q, k, v, o, state, workspace, cfg, stream=None):
     rc = lib().taylor_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), _ptr(workspace), B, H, N,
                                    ctypes.byref(cfg), _stream(stream, k.device))
     _check(rc, "taylor_attn_prefill")
+
+
+def taylor_attn_prefill_varlen(q, k, v, o, state, workspace, cu_seqlens, max_seqlen, cfg, stream=None):
+    """Causal prefill of a ragged batch packed as [H, T, d]; cu_seqlens is a device int32 tensor of
+    n_seqs + 1 offsets; o [H, T, d_v] float32 or None; state [n_seqs, H, stride] in/out or None."""
+    H, T = k.shape[:2]
+    n_seqs = cu_seqlens.shape[0] - 1
+    rc = lib().taylor_attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), _ptr(workspace),
+                                          _ptr(cu_seqlens), n_seqs, H, int(max_seqlen), T, ctypes.byref(cfg),
+                                          _stream(stream, k.device))
+    _check(rc, "taylor_attn_prefill_varlen")
 
 
 def taylor_attn_decode_step(q, k, v, o, state, cfg, stream=None):
@@ -224,6 +245,16 @@ def new_workspace(cfg, B, H, N, device):
     import torch
 
     n = taylor_prefill_workspace_bytes(cfg, B, H, N)
+    if n == 0:
+        return None
+    return torch.empty(((n + 15) // 16 * 16,), dtype=torch.uint8, device=device)
+
+
+def new_varlen_workspace(cfg, n_seqs, H, max_seqlen, total_tokens, device):
+    """A workspace tensor of taylor_prefill_varlen_workspace_bytes() bytes (None when none is needed)."""
+    import torch
+
+    n = taylor_prefill_varlen_workspace_bytes(cfg, n_seqs, H, max_seqlen, total_tokens)
     if n == 0:
         return None
     return torch.empty(((n + 15) // 16 * 16,), dtype=torch.uint8, device=device)

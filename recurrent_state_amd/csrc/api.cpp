@@ -72,17 +72,65 @@ int check_sizes(int B, int H, int N) {
   return TAYLOR_OK;
 }
 
-int64_t ws_bytes(const Shape& s, int C, int BH, int N) {
-  if (BH == 0 || N == 0) return 0;
+taylor::SeqMap equal_lengths(int B, int H, int N) { return taylor::SeqMap{nullptr, 0, B, H, N, 0}; }
+
+int64_t ws_bytes(const Shape& s, int C, int BH, const taylor::SeqMap& seq) {
+  if (BH == 0 || seq.N == 0 || seq.tokens(BH) == 0) return 0;
   switch (prefill_path(s, C)) {
-    case Path::Mfma: return taylor::prefill_mfma_ws_bytes(s, BH, N);
-    case Path::Wide: return taylor::prefill_wide_ws_bytes(s, BH, N);
-    case Path::Generic: return taylor::prefill_generic_ws_bytes(s, BH, N, C);
+    case Path::Mfma: return taylor::prefill_mfma_ws_bytes(s, BH, seq);
+    case Path::Wide: return taylor::prefill_wide_ws_bytes(s, BH, seq);
+    case Path::Generic:
+      if (seq.packed) return TAYLOR_ERR_UNSUPPORTED;
+      return taylor::prefill_generic_ws_bytes(s, BH, seq.N, C);
     default: return TAYLOR_ERR_UNSUPPORTED;
   }
 }
 
+// Ragged batches: sizes, and the sequence map of a call (cu may be null for a workspace query).
+int check_varlen(int n_seqs, int H, int max_seqlen, int64_t total_tokens) {
+  int rc = check_sizes(n_seqs, H, max_seqlen);
+  if (rc != TAYLOR_OK) return rc;
+  if (total_tokens < 0 || total_tokens > (int64_t)n_seqs * max_seqlen) return TAYLOR_ERR_INVALID_ARG;
+  if (total_tokens * (int64_t)(H > 0 ? H : 1) > (int64_t(1) << 40)) return TAYLOR_ERR_UNSUPPORTED;
+  return TAYLOR_OK;
+}
+
+taylor::SeqMap packed_map(const int32_t* cu, int n_seqs, int H, int max_seqlen, int64_t total_tokens) {
+  return taylor::SeqMap{cu, 1, n_seqs, H, max_seqlen, (long long)total_tokens};
+}
+
 int map_launch(int rc) { return rc == 0 ? TAYLOR_OK : rc == -2 ? TAYLOR_ERR_UNSUPPORTED : TAYLOR_ERR_HIP; }
+
+// Shared by the equal-length and ragged prefills once sizes are checked: pointers, workspace and launch.
+int prefill_common(const Shape& s, int C, const void* q, const void* k, const void* v, float* o, float* state,
+                   void* workspace, int BH, const taylor::SeqMap& seq, hipStream_t stream) {
+  if (!k || !v || !aligned16(k) || !aligned16(v)) return TAYLOR_ERR_INVALID_ARG;
+  if (o && (!q || !aligned16(q) || !aligned16(o))) return TAYLOR_ERR_INVALID_ARG;
+  if (state && !aligned16(state)) return TAYLOR_ERR_INVALID_ARG;
+  const int64_t need = ws_bytes(s, C, BH, seq);
+  if (need < 0) return (int)need;
+  if (need > 0 && (!workspace || !aligned16(workspace))) return TAYLOR_ERR_INVALID_ARG;
+  if ((long long)(seq.N + C - 1) / C > 0x7fffffffLL / 256) return TAYLOR_ERR_UNSUPPORTED;
+
+  taylor::PrefillArgs a{};
+  a.s = s;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.state = state;
+  a.ws = workspace;
+  a.BH = BH;
+  a.N = seq.N;
+  a.C = C;
+  a.seq = seq;
+  a.stream = stream;
+  switch (prefill_path(s, C)) {
+    case Path::Mfma: return map_launch(taylor::prefill_mfma_launch(a));
+    case Path::Wide: return map_launch(taylor::prefill_wide_launch(a));
+    default: return seq.packed ? TAYLOR_ERR_UNSUPPORTED : map_launch(taylor::prefill_generic_launch(a));
+  }
+}
 
 }  // namespace
 
@@ -146,7 +194,17 @@ int64_t taylor_prefill_workspace_bytes(const taylor_config* cfg, int B, int H, i
   if (rc != TAYLOR_OK) return rc;
   if ((rc = supported(cfg, s)) != TAYLOR_OK) return rc;
   if ((rc = check_sizes(B, H, N)) != TAYLOR_OK) return rc;
-  return ws_bytes(s, chunk_of(cfg), B * H, N);
+  return ws_bytes(s, chunk_of(cfg), B * H, equal_lengths(B, H, N));
+}
+
+int64_t taylor_prefill_varlen_workspace_bytes(const taylor_config* cfg, int n_seqs, int H, int max_seqlen,
+                                              int64_t total_tokens) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if ((rc = supported(cfg, s)) != TAYLOR_OK) return rc;
+  if ((rc = check_varlen(n_seqs, H, max_seqlen, total_tokens)) != TAYLOR_OK) return rc;
+  return ws_bytes(s, chunk_of(cfg), n_seqs * H, packed_map(nullptr, n_seqs, H, max_seqlen, total_tokens));
 }
 
 int taylor_state_init(float* state, int B, int H, const taylor_config* cfg, hipStream_t stream) {
@@ -169,32 +227,23 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, float* o, f
   if (!o && !state) return TAYLOR_ERR_INVALID_ARG;
   const int BH = B * H;
   if (BH == 0 || N == 0) return TAYLOR_OK;
-  if (!k || !v || !aligned16(k) || !aligned16(v)) return TAYLOR_ERR_INVALID_ARG;
-  if (o && (!q || !aligned16(q) || !aligned16(o))) return TAYLOR_ERR_INVALID_ARG;
-  if (state && !aligned16(state)) return TAYLOR_ERR_INVALID_ARG;
-  const int C = chunk_of(cfg);
-  const int64_t need = ws_bytes(s, C, BH, N);
-  if (need < 0) return (int)need;
-  if (need > 0 && (!workspace || !aligned16(workspace))) return TAYLOR_ERR_INVALID_ARG;
-  if ((long long)(N + C - 1) / C > 0x7fffffffLL / 256) return TAYLOR_ERR_UNSUPPORTED;
+  return prefill_common(s, chunk_of(cfg), q, k, v, o, state, workspace, BH, equal_lengths(B, H, N), stream);
+}
 
-  taylor::PrefillArgs a{};
-  a.s = s;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.state = state;
-  a.ws = workspace;
-  a.BH = BH;
-  a.N = N;
-  a.C = C;
-  a.stream = stream;
-  switch (prefill_path(s, C)) {
-    case Path::Mfma: return map_launch(taylor::prefill_mfma_launch(a));
-    case Path::Wide: return map_launch(taylor::prefill_wide_launch(a));
-    default: return map_launch(taylor::prefill_generic_launch(a));
-  }
+int taylor_attn_prefill_varlen(const void* q, const void* k, const void* v, float* o, float* state, void* workspace,
+                               const int32_t* cu_seqlens, int n_seqs, int H, int max_seqlen, int64_t total_tokens,
+                               const taylor_config* cfg, hipStream_t stream) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if ((rc = supported(cfg, s)) != TAYLOR_OK) return rc;
+  if ((rc = check_varlen(n_seqs, H, max_seqlen, total_tokens)) != TAYLOR_OK) return rc;
+  if (!o && !state) return TAYLOR_ERR_INVALID_ARG;
+  const int BH = n_seqs * H;
+  if (BH == 0 || total_tokens == 0) return TAYLOR_OK;  // every sequence is empty: states unchanged
+  if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return TAYLOR_ERR_INVALID_ARG;
+  return prefill_common(s, chunk_of(cfg), q, k, v, o, state, workspace, BH,
+                        packed_map(cu_seqlens, n_seqs, H, max_seqlen, total_tokens), stream);
 }
 
 int taylor_attn_decode_step(const void* q, const void* k, const void* v, float* o, float* state, int B, int H,

@@ -100,17 +100,20 @@ __global__ __launch_bounds__(kThreads) void seg_state_kernel(const T* __restrict
   if (tid < kFB && fb0 + tid < W) out[(long long)W * DV + fb0 + tid] = accz;
 }
 
-// Exclusive prefix over the segments of each head, seeded with the incoming
-// state; the total goes back to the state.  grid = (ceil(elems/256), heads).
+// Exclusive prefix over the segments of each (sequence, head) pair, seeded with the incoming state;
+// the total goes back to the state.  grid = (ceil(elems/256), pairs).
 __global__ __launch_bounds__(kThreads) void seg_scan_kernel(float* __restrict__ ws, float* __restrict__ state,
-                                                            int nseg, long long stride, long long elems,
-                                                            int write_prefix) {
+                                                            long long nslot, long long stride, long long elems,
+                                                            int write_prefix, SeqMap seq, int L) {
   const long long e = blockIdx.x * (long long)kThreads + threadIdx.x;
   if (e >= elems) return;
   const long long bh = blockIdx.y;
+  long long first;
+  int n;
+  seq.pair_slots(bh, nslot, L, first, n);
   float run = state ? state[bh * stride + e] : 0.f;
-  float* w = ws + bh * nseg * stride + e;
-  for (int s = 0; s < nseg; ++s) {
+  float* w = ws + first * stride + e;
+  for (int s = 0; s < n; ++s) {
     const float t = w[s * stride];
     if (write_prefix) w[s * stride] = run;
     run += t;
@@ -240,10 +243,10 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
 
-int seg_scan_launch(float* ws, float* state, int BH, int nseg, long long stride, long long elems, bool write_prefix,
-                    hipStream_t stream) {
-  seg_scan_kernel<<<dim3(cdiv(elems, kThreads), BH), dim3(kThreads), 0, stream>>>(ws, state, nseg, stride, elems,
-                                                                                  write_prefix ? 1 : 0);
+int seg_scan_launch(float* ws, float* state, int BH, long long nslot, long long stride, long long elems,
+                    bool write_prefix, const SeqMap& seq, int L, hipStream_t stream) {
+  seg_scan_kernel<<<dim3(cdiv(elems, kThreads), BH), dim3(kThreads), 0, stream>>>(ws, state, nslot, stride, elems,
+                                                                                  write_prefix ? 1 : 0, seq, L);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
@@ -271,7 +274,7 @@ int generic_run(const PrefillArgs& a) {
   seg_state_kernel<NT, DK, DV, T><<<dim3(nseg_used, a.BH, nfb), dim3(kThreads), 0, a.stream>>>(
       (const T*)a.k, (const T*)a.v, ws, a.N, L, nseg_used, a.s.stride);
   if (hipGetLastError() != hipSuccess) return -3;
-  if (seg_scan_launch(ws, a.state, a.BH, nseg_used, a.s.stride, elems, a.o != nullptr, a.stream)) return -3;
+  if (seg_scan_launch(ws, a.state, a.BH, nseg_used, a.s.stride, elems, a.o != nullptr, a.seq, L, a.stream)) return -3;
   if (a.o) {
     if (a.C == 64)
       readout_kernel<NT, DK, DV, 64, T><<<dim3(nchunk, a.BH), dim3(kThreads), 0, a.stream>>>(

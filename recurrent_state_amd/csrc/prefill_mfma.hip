@@ -16,6 +16,7 @@
 // enter bfloat16 MFMAs; S and the weights are split as bfloat16 hi + lo where they meet the MFMAs
 // (float32 accuracy for the state), and all accumulation and the outputs are float32.  (float32
 // inputs run on the feature-block kernels of prefill_wide.hip.)
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -380,44 +381,38 @@ __device__ __forceinline__ void pipe_producer(PipeSmem<NT, READOUT>& sm, const _
   }
 }
 
-template <int NT, bool READOUT>
+template <int NT, bool READOUT, bool PACKED>
 __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16* __restrict__ q,
                                                                     const __bf16* __restrict__ k,
                                                                     const __bf16* __restrict__ v,
                                                                     float* __restrict__ o, float* __restrict__ ws,
-                                                                    int N, int L, int nseg, long long stride,
-                                                                    float scale) {
+                                                                    SeqMap seq, int L, long long nslot,
+                                                                    long long stride, float scale) {
   using G = Geo<NT>;
   using SM = PipeSmem<NT, READOUT>;
   constexpr int W = G::W, NAT = G::NAT, NKB = G::NKB;
   constexpr int CS = kPipeChunk, NIT = CS / 16;
   __shared__ SM sm;
 
-  // The role is taken from a wave-uniform scalar so each wave runs only its own loop; both loops
-  // execute exactly 2 + nch barriers.
+  // The role is taken from a wave-uniform scalar so each wave runs only its own loops; both roles
+  // walk the same pieces and execute exactly 2 + nch barriers per piece.  Pieces follow one
+  // another in LDS without an extra barrier: a piece's last barrier orders every read of its
+  // buffers before the next piece's first writes, and the z rows each producer rewrites at a
+  // piece's start are its own.
   const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool producer = w >= kPipeConsumers;
-  const int g = w - kPipeConsumers;
-  const int seg = blockIdx.x;
-  const long long bh = blockIdx.y;
-  const int t_begin = seg * L, t_end = min(N, t_begin + L);
-  const int nch = (t_end - t_begin + CS - 1) / CS;
-  const long long hbase = bh * (long long)N;
-  float* slot = ws + (bh * nseg + seg) * stride;
-  auto chunk_nv = [&](int c) { return min(CS, t_end - (t_begin + c * CS)); };
-  auto chunk_tok0 = [&](int c) { return hbase + t_begin + (long long)c * CS; };
-
-  if (producer) {
+  const long long bx = blockIdx.x, by = blockIdx.y;
+  if (w >= kPipeConsumers) {
     static_assert(kPipeProducers <= 8, "dispatch below lists up to 8 producers");
-    const long long tok_base = hbase + t_begin;
-    const int n_tok = t_end - t_begin;
 #define TAYLOR_PRODUCER(G_)                                                                           \
   case G_:                                                                                          \
     if constexpr (G_ < kPipeProducers)                                                              \
-      pipe_producer<NT, READOUT, G_>(sm, q, k, v, slot, tok_base, n_tok, nch, l, scale);            \
+      for_each_piece<PACKED>(seq, bx, by, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {                       \
+        pipe_producer<NT, READOUT, G_>(sm, q, k, v, ws + pc.slot * stride, pc.tok, pc.n,            \
+                                       (pc.n + CS - 1) / CS, l, scale);                             \
+      });                                                                                           \
     break;
-    switch (g) {
+    switch (w - kPipeConsumers) {
       TAYLOR_PRODUCER(0)
       TAYLOR_PRODUCER(1)
       TAYLOR_PRODUCER(2)
@@ -432,98 +427,103 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
     return;
   }
 
-  // ---- consumers: wave w owns value columns 16w..16w+15 ----
-  f32x4 Srun[NAT];
-#pragma unroll
-  for (int t = 0; t < NAT; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int a = 16 * t + 4 * lg + r;
-      Srun[t][r] = (READOUT && a < W) ? slot[(long long)a * kDV + 16 * w + l16] : 0.f;
-    }
-  __syncthreads();
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int b = c & 1;
-    const int nv = chunk_nv(c);
-    const long long tok0 = chunk_tok0(c);
-    f32x4 O[READOUT ? NIT : 1];
-    if constexpr (READOUT) {
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // readout with S_{<c} = hi + lo, one 32-feature k-block at a time
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        bf16x2 h[4], lw[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const f32x4& src = Srun[2 * kb + (r >> 1)];
-          split_bf16x2(src[2 * (r & 1)], src[2 * (r & 1) + 1], h[r], lw[r]);
-        }
-        const bf16x8 hi = {h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
-        const bf16x8 lo = {lw[0][0], lw[0][1], lw[1][0], lw[1][1], lw[2][0], lw[2][1], lw[3][0], lw[3][1]};
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[b][16 * it + l16][32 * kb + 8 * lg]);
-          O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, O[it], 0, 0, 0);
-          O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, O[it], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight (register budget)
-      }
-      // intra-chunk V^T x scores (weights as hi + lo)
-#pragma unroll
-      for (int it = 0; it < NIT; ++it)
-#pragma unroll
-        for (int jt = 0; jt <= it; ++jt) {
-          const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.vt[b][16 * w + l16][16 * jt + 4 * lg]);
-          const bf16x4 bh = sm.a[b][pair_index(jt, it)][l];
-          const bf16x4 bl = sm.alo[b][pair_index(jt, it)][l];
-          O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
-                                                            __builtin_bit_cast(i16x4, bh), O[it], 0, 0, 0);
-          O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
-                                                            __builtin_bit_cast(i16x4, bl), O[it], 0, 0, 0);
-        }
-    }
-    // state update
-#pragma unroll
-    for (int jb = 0; jb < CS / 32; ++jb) {
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[b][16 * w + l16][32 * jb + 8 * lg]);
-#pragma unroll
-      for (int t = 0; t < NAT; ++t) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.phikt[b][16 * t + l16][32 * jb + 8 * lg]);
-        Srun[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bv, Srun[t], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (READOUT) {
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int i = 16 * it + l16;
-        float d = 0.f;
-#pragma unroll
-        for (int pp = 0; pp < kPipeProducers; ++pp) d += sm.den_part[b][pp][i];
-#pragma unroll
-        for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][pair_index(jt, it)][l16];
-        if (i < nv) {
-          const float inv = __builtin_amdgcn_rcpf(d);
-          const f32x4 r = O[it];
-          *reinterpret_cast<f32x4*>(o + (tok0 + i) * kDV + 16 * w + 4 * lg) =
-              f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
-        }
-      }
-    }
-    __syncthreads();
-  }
+  for_each_piece<PACKED>(seq, bx, by, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
+    const int nch = (pc.n + CS - 1) / CS;
+    float* slot = ws + pc.slot * stride;
 
-  if constexpr (!READOUT) {
+    // ---- consumers: wave w owns value columns 16w..16w+15 ----
+    f32x4 Srun[NAT];
 #pragma unroll
     for (int t = 0; t < NAT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int a = 16 * t + 4 * lg + r;
-        if (a < W) slot[(long long)a * kDV + 16 * w + l16] = Srun[t][r];
+        Srun[t][r] = (READOUT && a < W) ? slot[(long long)a * kDV + 16 * w + l16] : 0.f;
       }
-  }
+    __syncthreads();
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      const int b = c & 1;
+      const int nv = min(CS, pc.n - c * CS);
+      const long long tok0 = pc.tok + (long long)c * CS;
+      f32x4 O[READOUT ? NIT : 1];
+      if constexpr (READOUT) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // readout with S_{<c} = hi + lo, one 32-feature k-block at a time
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          bf16x2 h[4], lw[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const f32x4& src = Srun[2 * kb + (r >> 1)];
+            split_bf16x2(src[2 * (r & 1)], src[2 * (r & 1) + 1], h[r], lw[r]);
+          }
+          const bf16x8 hi = {h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+          const bf16x8 lo = {lw[0][0], lw[0][1], lw[1][0], lw[1][1], lw[2][0], lw[2][1], lw[3][0], lw[3][1]};
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
+            const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[b][16 * it + l16][32 * kb + 8 * lg]);
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, O[it], 0, 0, 0);
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, O[it], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight (register budget)
+        }
+        // intra-chunk V^T x scores (weights as hi + lo)
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+          for (int jt = 0; jt <= it; ++jt) {
+            const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.vt[b][16 * w + l16][16 * jt + 4 * lg]);
+            const bf16x4 bh = sm.a[b][pair_index(jt, it)][l];
+            const bf16x4 bl = sm.alo[b][pair_index(jt, it)][l];
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
+                                                              __builtin_bit_cast(i16x4, bh), O[it], 0, 0, 0);
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
+                                                              __builtin_bit_cast(i16x4, bl), O[it], 0, 0, 0);
+          }
+      }
+      // state update
+#pragma unroll
+      for (int jb = 0; jb < CS / 32; ++jb) {
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[b][16 * w + l16][32 * jb + 8 * lg]);
+#pragma unroll
+        for (int t = 0; t < NAT; ++t) {
+          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.phikt[b][16 * t + l16][32 * jb + 8 * lg]);
+          Srun[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bv, Srun[t], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (READOUT) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int i = 16 * it + l16;
+          float d = 0.f;
+#pragma unroll
+          for (int pp = 0; pp < kPipeProducers; ++pp) d += sm.den_part[b][pp][i];
+#pragma unroll
+          for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][pair_index(jt, it)][l16];
+          if (i < nv) {
+            const float inv = __builtin_amdgcn_rcpf(d);
+            const f32x4 r = O[it];
+            *reinterpret_cast<f32x4*>(o + (tok0 + i) * kDV + 16 * w + 4 * lg) =
+                f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+    if constexpr (!READOUT) {
+#pragma unroll
+      for (int t = 0; t < NAT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int a = 16 * t + 4 * lg + r;
+          if (a < W) slot[(long long)a * kDV + 16 * w + l16] = Srun[t][r];
+        }
+    }
+  });
 }
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -539,25 +539,44 @@ int n_segments(int BH, int nchunk, int target) {
 // One workgroup per CU (double-buffered LDS): about 256 workgroups in total.
 constexpr int kSegTargetPipe = 256;
 
+// Piece length and slots.  Equal lengths: about kSegTargetPipe workgroups, each pair cut into
+// equal segments.  Ragged: ranges of the packed token axis of about total / kSegTargetPipe
+// token-heads each (a multiple of the chunk).
+struct PipePlan {
+  int L;            // piece (segment or range) length
+  long long nslot;  // workspace slots per row
+};
+
+PipePlan pipe_plan(int BH, const SeqMap& seq) {
+  PipePlan p;
+  if (seq.packed) {
+    const long long per = std::max<long long>(1, (seq.tokens(BH) + kSegTargetPipe - 1) / kSegTargetPipe);
+    p.L = (int)std::min<long long>((per + kPipeChunk - 1) / kPipeChunk * kPipeChunk, 1 << 30);
+  } else {
+    const int nchunk = cdiv(seq.N, kPipeChunk);
+    p.L = cdiv(nchunk, n_segments(BH, nchunk, kSegTargetPipe)) * kPipeChunk;
+  }
+  p.nslot = seq.row_slots(p.L);
+  return p;
+}
+
 template <int NT>
 int run_pipe(const PrefillArgs& a) {
-  const int nchunk = cdiv(a.N, kPipeChunk);
-  const int nseg0 = n_segments(a.BH, nchunk, kSegTargetPipe);
-  const int L = cdiv(nchunk, nseg0) * kPipeChunk;
-  const int nseg = cdiv(a.N, L);
+  const PipePlan p = pipe_plan(a.BH, a.seq);
   float* ws = (float*)a.ws;
   const long long elems = Geo<NT>::W * (long long)(kDV + 1);
-  const dim3 grid(nseg, a.BH), block(kPipeThreads);
+  const dim3 grid((unsigned)a.seq.grid_x(p.L), (unsigned)a.seq.grid_y(a.BH)), block(kPipeThreads);
   const __bf16* q = (const __bf16*)a.q;
   const __bf16* k = (const __bf16*)a.k;
   const __bf16* v = (const __bf16*)a.v;
-  prefill_pipe_kernel<NT, false><<<grid, block, 0, a.stream>>>(q, k, v, nullptr, ws, a.N, L, nseg, a.s.stride,
-                                                              a.s.scale);
+  auto state_pass = a.seq.packed ? prefill_pipe_kernel<NT, false, true> : prefill_pipe_kernel<NT, false, false>;
+  auto readout = a.seq.packed ? prefill_pipe_kernel<NT, true, true> : prefill_pipe_kernel<NT, true, false>;
+  state_pass<<<grid, block, 0, a.stream>>>(q, k, v, nullptr, ws, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
   if (hipGetLastError() != hipSuccess) return -3;
-  if (seg_scan_launch(ws, a.state, a.BH, nseg, a.s.stride, elems, a.o != nullptr, a.stream)) return -3;
+  if (seg_scan_launch(ws, a.state, a.BH, p.nslot, a.s.stride, elems, a.o != nullptr, a.seq, p.L, a.stream))
+    return -3;
   if (a.o) {
-    prefill_pipe_kernel<NT, true><<<grid, block, 0, a.stream>>>(q, k, v, a.o, ws, a.N, L, nseg, a.s.stride,
-                                                               a.s.scale);
+    readout<<<grid, block, 0, a.stream>>>(q, k, v, a.o, ws, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
     if (hipGetLastError() != hipSuccess) return -3;
   }
   return 0;
@@ -569,10 +588,9 @@ int run_pipe(const PrefillArgs& a) {
 // configured chunk (64 or 128); the outputs do not depend on the chunk length beyond rounding.
 bool prefill_mfma_has(int nt, int dk, int dv, int dtype) { return dk == kDK && dv == kDV && nt >= 1 && nt <= 3 && dtype == 1; }
 
-long long prefill_mfma_ws_bytes(const Shape& s, int BH, int N) {
-  const int nchunk = cdiv(N, kPipeChunk);
-  const int L = cdiv(nchunk, n_segments(BH, nchunk, kSegTargetPipe)) * kPipeChunk;
-  return (long long)BH * cdiv(N, L) * s.stride * 4;
+long long prefill_mfma_ws_bytes(const Shape& s, int BH, const SeqMap& seq) {
+  const PipePlan p = pipe_plan(BH, seq);
+  return seq.rows(BH) * p.nslot * s.stride * 4;
 }
 
 int prefill_mfma_launch(const PrefillArgs& a) {

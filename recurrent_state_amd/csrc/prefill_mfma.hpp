@@ -6,7 +6,7 @@
 namespace taylor {
 
 bool prefill_mfma_has(int nt, int dk, int dv, int dtype);
-long long prefill_mfma_ws_bytes(const Shape& s, int BH, int N);
+long long prefill_mfma_ws_bytes(const Shape& s, int BH, const SeqMap& seq);
 int prefill_mfma_launch(const PrefillArgs& a);
 
 }  // namespace taylor

@@ -84,14 +84,16 @@ struct WideSmem {
 
 // Where a workgroup's starting state comes from and where its results go (see the file comment).
 struct WideIO {
-  float* slots;        // nseg > 1: [heads][nseg][stride] prefixes (readout) or increments (state pass)
-  float* state;        // nseg == 1: incoming / final state [heads][stride], or null
-  float* part_num;     // [blocks][heads * N][d_v] partial numerators
-  float* part_den;     // [blocks][heads * N] partial denominators
-  float* out;          // a single block: the outputs [heads * N][d_v]
+  float* slots;        // several segments per pair: workspace slots (placed as SeqMap describes) of
+                       // prefixes (readout) or increments (state pass)
+  float* state;        // one segment per pair: incoming / final state [pairs][stride], or null
+  float* part_num;     // [blocks][token-heads][d_v] partial numerators
+  float* part_den;     // [blocks][token-heads] partial denominators
+  float* out;          // a single block: the outputs [token-heads][d_v]
   long long stride;
-  int nseg;
-  int BH;
+  long long nslot;     // slots per workspace row
+  long long tokens;    // token-heads of the call
+  int multi;           // several segments per pair (grid x > 1)
 };
 
 // n consecutive elements (n a multiple of 4) of one token row, widened to float32 on unpack.
@@ -242,179 +244,198 @@ __device__ __forceinline__ void wide_produce(WideSmem<READOUT, block_features<NT
   }
 }
 
-// One segment of L tokens, one feature block; grid = (segments, heads, blocks).  Both roles execute
-// exactly 2 + nch barriers.
-template <int NT, typename E, bool READOUT>
+// Where a piece's block starts from (init: its prefix, or the incoming state when a pair is one
+// piece; null: zero) and where its state goes (the piece's increment in the state pass; the final
+// state when a pair is one piece; null: nowhere).
+template <bool READOUT>
+__device__ __forceinline__ void piece_state(const WideIO& io, const SeqPiece& pc, const float*& init, float*& dst) {
+  init = nullptr;
+  dst = nullptr;
+  if (io.multi) {
+    if (READOUT) init = io.slots + pc.slot * io.stride;
+  } else if (READOUT && io.state) {
+    init = io.state + pc.pair * io.stride;
+  }
+  if (!READOUT)
+    dst = io.slots + pc.slot * io.stride;
+  else if (!io.multi && io.state)
+    dst = io.state + pc.pair * io.stride;
+}
+
+// The pieces of one workgroup (see SeqMap: a segment of one pair, or the pieces of one token
+// range of one head), one feature block; grid = (segments or ranges, pairs or heads, blocks).
+template <int NT, typename E, bool READOUT, bool PACKED>
 __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(const E* __restrict__ q, const E* __restrict__ k,
-                                                                const E* __restrict__ v, WideIO io, int N, int L,
-                                                                float scale) {
+                                                                const E* __restrict__ v, WideIO io, SeqMap seq,
+                                                                int L, float scale) {
   constexpr int W = FeatureTable<NT, kDK>::W;
   constexpr int FB = block_features<NT>(), FP = FB / kProd, NAT = FB / 16;
   __shared__ WideSmem<READOUT, FB> sm;
 
   const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int seg = blockIdx.x, fb = blockIdx.z;
-  const long long bh = blockIdx.y;
+  const int fb = blockIdx.z;
+  const long long bx = blockIdx.x, by = blockIdx.y;
   const int f0 = fb * FB;
-  const int t_begin = seg * L, t_end = min(N, t_begin + L);
-  const int nch = (t_end - t_begin + kCS - 1) / kCS;
-  const long long tok_base = bh * (long long)N + t_begin;
-  auto nv_of = [&](int c) { return min(kCS, t_end - (t_begin + c * kCS)); };
-  auto tok_of = [&](int c) { return tok_base + (long long)c * kCS; };
-
-  // starting state of this block: rows f0 .. f0 + FB - 1 (zero past W)
-  const float* init = nullptr;
-  if (io.nseg > 1) {
-    if (READOUT) init = io.slots + (bh * io.nseg + seg) * io.stride;
-  } else if (READOUT && io.state) {
-    init = io.state + bh * io.stride;
-  }
-  // state pass: the segment's increment; single-segment readout: the final state
-  float* dst = nullptr;
-  if (!READOUT)
-    dst = io.slots + (bh * io.nseg + seg) * io.stride;
-  else if (io.nseg == 1 && io.state)
-    dst = io.state + bh * io.stride;
-
+  // Both roles walk the same pieces and execute exactly 2 + nch barriers per piece.  Pieces follow
+  // one another in LDS without an extra barrier: a piece's last barrier orders every read of its
+  // buffers before the next piece's first writes, and each producer rewrites only its own z rows
+  // at a piece's start.
   if (w >= kCons) {
     // ---- producers ----
-    const int g = w - kCons;
-    if (l < FP) {
-      const int a = f0 + FP * g + l;
-      sm.z[FP * g + l] = (init && a < W) ? init[(long long)W * kDV + a] : 0.f;
-    }
-    WideIn<E> pa, pb;
-    pa.load(q, k, v, tok_of(0), nv_of(0), l, g, READOUT);
-    __syncthreads();
-    if (nch > 1) pb.load(q, k, v, tok_of(1), nv_of(1), l, g, READOUT);
-    wide_produce<NT, E, READOUT>(sm, pa, 0, fb, g, l, nv_of(0), scale);
-    __syncthreads();  // chunk 0 ready
-    int c = 0;
-    for (; c + 3 < nch; c += 2) {
-      pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
-      wide_produce<NT, E, READOUT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale);
+    for_each_piece<PACKED>(seq, bx, by, L, io.nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
+      const int nch = (pc.n + kCS - 1) / kCS;
+      auto nv_of = [&](int c) { return min(kCS, pc.n - c * kCS); };
+      auto tok_of = [&](int c) { return pc.tok + (long long)c * kCS; };
+      const float* init;
+      float* dst;
+      piece_state<READOUT>(io, pc, init, dst);
+      const int g = w - kCons;
+      if (l < FP) {
+        const int a = f0 + FP * g + l;
+        sm.z[FP * g + l] = (init && a < W) ? init[(long long)W * kDV + a] : 0.f;
+      }
+      WideIn<E> pa, pb;
+      pa.load(q, k, v, tok_of(0), nv_of(0), l, g, READOUT);
       __syncthreads();
-      pb.load(q, k, v, tok_of(c + 3), nv_of(c + 3), l, g, READOUT);
-      wide_produce<NT, E, READOUT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale);
+      if (nch > 1) pb.load(q, k, v, tok_of(1), nv_of(1), l, g, READOUT);
+      wide_produce<NT, E, READOUT>(sm, pa, 0, fb, g, l, nv_of(0), scale);
+      __syncthreads();  // chunk 0 ready
+      int c = 0;
+      for (; c + 3 < nch; c += 2) {
+        pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
+        wide_produce<NT, E, READOUT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale);
+        __syncthreads();
+        pb.load(q, k, v, tok_of(c + 3), nv_of(c + 3), l, g, READOUT);
+        wide_produce<NT, E, READOUT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale);
+        __syncthreads();
+      }
+      // nch - c phases remain (1 to 3); chunks c+1 and c+2 may still need preparing
+      if (c + 2 < nch) pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
+      if (c + 1 < nch) wide_produce<NT, E, READOUT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale);
       __syncthreads();
-    }
-    // nch - c phases remain (1 to 3); chunks c+1 and c+2 may still need preparing
-    if (c + 2 < nch) pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
-    if (c + 1 < nch) wide_produce<NT, E, READOUT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale);
-    __syncthreads();
-    if (c + 1 < nch) {
-      if (c + 2 < nch) wide_produce<NT, E, READOUT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale);
-      __syncthreads();
-      if (c + 2 < nch) __syncthreads();
-    }
-    if (dst && l < FP) {
-      const int a = f0 + FP * g + l;
-      if (a < W) dst[(long long)W * kDV + a] = sm.z[FP * g + l];
-    }
+      if (c + 1 < nch) {
+        if (c + 2 < nch) wide_produce<NT, E, READOUT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale);
+        __syncthreads();
+        if (c + 2 < nch) __syncthreads();
+      }
+      if (dst && l < FP) {
+        const int a = f0 + FP * g + l;
+        if (a < W) dst[(long long)W * kDV + a] = sm.z[FP * g + l];
+      }
+    });
     return;
   }
 
-  // ---- consumers: wave w owns value columns 16w..16w+15 ----
-  const int col = 16 * w + l16;
-  const bool intra = READOUT && fb == 0;  // block 0 also carries the intra-chunk term
-  f32x4 Srun[NAT];
-#pragma unroll
-  for (int t = 0; t < NAT; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int a = f0 + 16 * t + 4 * lg + r;
-      Srun[t][r] = (init && a < W) ? init[(long long)a * kDV + col] : 0.f;
-    }
-  __syncthreads();
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int b = c & 1;
-    const int nv = nv_of(c);
-    const long long tok0 = tok_of(c);
-    f32x4 O[READOUT ? kNIT : 1];
-    if constexpr (READOUT) {
-#pragma unroll
-      for (int it = 0; it < kNIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // readout: O[it][r] = (phi_f(sQ) S_{f,<c})[token 16it + l16][column 16w + 4lg + r]
-#pragma unroll
-      for (int t = 0; t < NAT; ++t)
-#pragma unroll
-        for (int it = 0; it < kNIT; ++it) {
-          const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[b][16 * it + l16][16 * t + 4 * lg]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], O[it], 0, 0, 0);
-        }
-      if (intra) {
-#pragma unroll
-        for (int it = 0; it < kNIT; ++it)
-#pragma unroll
-          for (int jt = 0; jt <= it; ++jt) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jt + 4 * lg]);
-            const f32x4 bw = sm.a[b][it * (it + 1) / 2 + jt][l];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bw[r], O[it], 0, 0, 0);
-          }
-      }
-    }
-    // state update: Srun[t] += phi_f(K)^T[16t.., chunk] V[chunk, columns]
-#pragma unroll
-    for (int jb = 0; jb < kCS / 16; ++jb) {
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jb + 4 * lg]);
-#pragma unroll
-      for (int t = 0; t < NAT; ++t) {
-        const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[b][16 * t + l16][16 * jb + 4 * lg]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
-      }
-    }
-    if constexpr (READOUT && n_blocks<NT>() == 1) {
-      // a single block: the outputs are final (columns 16w + 4lg .. + 3 of token 16it + l16)
-#pragma unroll
-      for (int it = 0; it < kNIT; ++it) {
-        const int i = 16 * it + l16;
-        float d = 0.f;
-#pragma unroll
-        for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
-        for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][it * (it + 1) / 2 + jt][l16];
-        if (i < nv) {
-          const float inv = 1.0f / d;
-          const f32x4 r = O[it];
-          *reinterpret_cast<f32x4*>(io.out + (tok0 + i) * kDV + 16 * w + 4 * lg) =
-              f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
-        }
-      }
-    } else if constexpr (READOUT) {
-      // partial numerators of this block (columns 16w + 4lg .. + 3 of token 16it + l16)
-      float* pn = io.part_num + ((long long)fb * io.BH * N + tok0) * kDV;
-#pragma unroll
-      for (int it = 0; it < kNIT; ++it) {
-        const int i = 16 * it + l16;
-        if (i < nv) *reinterpret_cast<f32x4*>(pn + (long long)i * kDV + 16 * w + 4 * lg) = O[it];
-      }
-      // partial denominators: consumer w < kNIT writes tokens 16w .. 16w + 15
-      if (w < kNIT && lg == 0) {
-        const int i = 16 * w + l16;
-        float d = 0.f;
-#pragma unroll
-        for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
-        if (intra)
-          for (int jt = 0; jt <= w; ++jt) d += sm.den_intra[b][w * (w + 1) / 2 + jt][l16];
-        if (i < nv) io.part_den[(long long)fb * io.BH * N + tok0 + i] = d;
-      }
-    }
-    __syncthreads();
-  }
+  for_each_piece<PACKED>(seq, bx, by, L, io.nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
+    const int nch = (pc.n + kCS - 1) / kCS;
+    auto nv_of = [&](int c) { return min(kCS, pc.n - c * kCS); };
+    auto tok_of = [&](int c) { return pc.tok + (long long)c * kCS; };
+    const float* init;
+    float* dst;
+    piece_state<READOUT>(io, pc, init, dst);
 
-  if (dst) {
+    // ---- consumers: wave w owns value columns 16w..16w+15 ----
+    const int col = 16 * w + l16;
+    const bool intra = READOUT && fb == 0;  // block 0 also carries the intra-chunk term
+    f32x4 Srun[NAT];
 #pragma unroll
     for (int t = 0; t < NAT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int a = f0 + 16 * t + 4 * lg + r;
-        if (a < W) dst[(long long)a * kDV + col] = Srun[t][r];
+        Srun[t][r] = (init && a < W) ? init[(long long)a * kDV + col] : 0.f;
       }
-  }
+    __syncthreads();
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      const int b = c & 1;
+      const int nv = nv_of(c);
+      const long long tok0 = tok_of(c);
+      f32x4 O[READOUT ? kNIT : 1];
+      if constexpr (READOUT) {
+#pragma unroll
+        for (int it = 0; it < kNIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // readout: O[it][r] = (phi_f(sQ) S_{f,<c})[token 16it + l16][column 16w + 4lg + r]
+#pragma unroll
+        for (int t = 0; t < NAT; ++t)
+#pragma unroll
+          for (int it = 0; it < kNIT; ++it) {
+            const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[b][16 * it + l16][16 * t + 4 * lg]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], O[it], 0, 0, 0);
+          }
+        if (intra) {
+#pragma unroll
+          for (int it = 0; it < kNIT; ++it)
+#pragma unroll
+            for (int jt = 0; jt <= it; ++jt) {
+              const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jt + 4 * lg]);
+              const f32x4 bw = sm.a[b][it * (it + 1) / 2 + jt][l];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bw[r], O[it], 0, 0, 0);
+            }
+        }
+      }
+      // state update: Srun[t] += phi_f(K)^T[16t.., chunk] V[chunk, columns]
+#pragma unroll
+      for (int jb = 0; jb < kCS / 16; ++jb) {
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jb + 4 * lg]);
+#pragma unroll
+        for (int t = 0; t < NAT; ++t) {
+          const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[b][16 * t + l16][16 * jb + 4 * lg]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
+        }
+      }
+      if constexpr (READOUT && n_blocks<NT>() == 1) {
+        // a single block: the outputs are final (columns 16w + 4lg .. + 3 of token 16it + l16)
+#pragma unroll
+        for (int it = 0; it < kNIT; ++it) {
+          const int i = 16 * it + l16;
+          float d = 0.f;
+#pragma unroll
+          for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
+          for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][it * (it + 1) / 2 + jt][l16];
+          if (i < nv) {
+            const float inv = 1.0f / d;
+            const f32x4 r = O[it];
+            *reinterpret_cast<f32x4*>(io.out + (tok0 + i) * kDV + 16 * w + 4 * lg) =
+                f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
+          }
+        }
+      } else if constexpr (READOUT) {
+        // partial numerators of this block (columns 16w + 4lg .. + 3 of token 16it + l16)
+        float* pn = io.part_num + ((long long)fb * io.tokens + tok0) * kDV;
+#pragma unroll
+        for (int it = 0; it < kNIT; ++it) {
+          const int i = 16 * it + l16;
+          if (i < nv) *reinterpret_cast<f32x4*>(pn + (long long)i * kDV + 16 * w + 4 * lg) = O[it];
+        }
+        // partial denominators: consumer w < kNIT writes tokens 16w .. 16w + 15
+        if (w < kNIT && lg == 0) {
+          const int i = 16 * w + l16;
+          float d = 0.f;
+#pragma unroll
+          for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
+          if (intra)
+            for (int jt = 0; jt <= w; ++jt) d += sm.den_intra[b][w * (w + 1) / 2 + jt][l16];
+          if (i < nv) io.part_den[(long long)fb * io.tokens + tok0 + i] = d;
+        }
+      }
+      __syncthreads();
+    }
+
+    if (dst) {
+#pragma unroll
+      for (int t = 0; t < NAT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int a = f0 + 16 * t + 4 * lg + r;
+          if (a < W) dst[(long long)a * kDV + col] = Srun[t][r];
+        }
+    }
+  });
 }
 
 // o[token][c] = sum_blocks num / sum_blocks den, blocks in order; 16 threads per token.
@@ -437,9 +458,13 @@ __global__ __launch_bounds__(256) void wide_reduce_kernel(const float* __restric
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Segments per head: enough (segment, head, block) workgroups to cover the chip once.
+// Workgroups to aim for: with outputs about one per CU (the readout kernel's LDS allows one), for a
+// state-only pass four per CU.
+long long wide_target(bool outputs) { return outputs ? 256 : 1024; }
+
+// Segments per pair (equal lengths): enough (segment, pair, block) workgroups to cover the chip once.
 int wide_segments(int BH, int nb, int nchunk, bool outputs) {
-  const long long target = outputs ? 256 : 1024;
+  const long long target = wide_target(outputs);
   long long want = (target + (long long)BH * nb - 1) / ((long long)BH * nb);
   if (want < 1) want = 1;
   if (want > nchunk) want = nchunk;
@@ -447,20 +472,28 @@ int wide_segments(int BH, int nb, int nchunk, bool outputs) {
 }
 
 struct WideLayout {
-  int nseg, L;
-  long long slot_floats, part_floats;
+  int L;  // piece (segment or range) length
+  long long gx, nslot, slot_floats, part_floats;
 };
 
 template <int NT>
-WideLayout wide_layout(const Shape& s, int BH, int N, bool outputs) {
+WideLayout wide_layout(const Shape& s, int BH, const SeqMap& seq, bool outputs) {
   constexpr int NB = n_blocks<NT>();
-  const int nchunk = cdiv(N, kCS);
   WideLayout lay;
-  lay.L = cdiv(nchunk, wide_segments(BH, NB, nchunk, outputs)) * kCS;
-  lay.nseg = cdiv(N, lay.L);
-  // slots are needed for several segments, and always for a state-only call (the scan sums them)
-  lay.slot_floats = (lay.nseg > 1 || !outputs) ? (long long)BH * lay.nseg * s.stride : 0;
-  lay.part_floats = (outputs && NB > 1) ? (long long)NB * BH * N * (kDV + 1) : 0;
+  if (seq.packed) {
+    // ragged: ranges of the packed token axis, about target workgroups over heads and blocks
+    const long long target = wide_target(outputs);
+    const long long per = std::max<long long>(1, (seq.tokens(BH) * NB + target - 1) / target);
+    lay.L = (int)std::min<long long>((per + kCS - 1) / kCS * kCS, 1 << 30);
+  } else {
+    const int nchunk = cdiv(seq.N, kCS);
+    lay.L = cdiv(nchunk, wide_segments(BH, NB, nchunk, outputs)) * kCS;
+  }
+  lay.gx = seq.grid_x(lay.L);
+  lay.nslot = seq.row_slots(lay.L);
+  // slots are needed for several pieces per pair, and always for a state-only call (the scan sums them)
+  lay.slot_floats = (lay.gx > 1 || !outputs) ? seq.rows(BH) * lay.nslot * s.stride : 0;
+  lay.part_floats = (outputs && NB > 1) ? (long long)NB * seq.tokens(BH) * (kDV + 1) : 0;
   return lay;
 }
 
@@ -470,28 +503,32 @@ template <int NT, typename E>
 int wide_run(const PrefillArgs& a) {
   constexpr int NB = n_blocks<NT>();
   const bool outputs = a.o != nullptr;
-  const WideLayout lay = wide_layout<NT>(a.s, a.BH, a.N, outputs);
+  const WideLayout lay = wide_layout<NT>(a.s, a.BH, a.seq, outputs);
+  const long long tokens = a.seq.tokens(a.BH);
   float* ws = (float*)a.ws;
   float* slots = ws;
   float* part_num = ws + round_up(lay.slot_floats, 64);
-  float* part_den = part_num + (long long)NB * a.BH * a.N * kDV;
+  float* part_den = part_num + (long long)NB * tokens * kDV;
   const E* q = (const E*)a.q;
   const E* k = (const E*)a.k;
   const E* v = (const E*)a.v;
   const long long elems = FeatureTable<NT, kDK>::W * (long long)(kDV + 1);
-  const dim3 grid(lay.nseg, a.BH, NB), block(kThreads);
-  if (!outputs || lay.nseg > 1) {
-    const WideIO io{slots, nullptr, nullptr, nullptr, nullptr, a.s.stride, lay.nseg, a.BH};
-    prefill_wide_kernel<NT, E, false><<<grid, block, 0, a.stream>>>(q, k, v, io, a.N, lay.L, a.s.scale);
+  const int multi = lay.gx > 1;
+  const dim3 grid((unsigned)lay.gx, (unsigned)a.seq.grid_y(a.BH), NB), block(kThreads);
+  if (!outputs || multi) {
+    const WideIO io{slots, nullptr, nullptr, nullptr, nullptr, a.s.stride, lay.nslot, tokens, multi};
+    auto state_pass = a.seq.packed ? prefill_wide_kernel<NT, E, false, true> : prefill_wide_kernel<NT, E, false, false>;
+    state_pass<<<grid, block, 0, a.stream>>>(q, k, v, io, a.seq, lay.L, a.s.scale);
     if (hipGetLastError() != hipSuccess) return -3;
-    if (seg_scan_launch(slots, a.state, a.BH, lay.nseg, a.s.stride, elems, outputs, a.stream)) return -3;
+    if (seg_scan_launch(slots, a.state, a.BH, lay.nslot, a.s.stride, elems, outputs, a.seq, lay.L, a.stream))
+      return -3;
     if (!outputs) return 0;
   }
-  const WideIO io{slots, lay.nseg == 1 ? a.state : nullptr, part_num, part_den, a.o, a.s.stride, lay.nseg, a.BH};
-  prefill_wide_kernel<NT, E, true><<<grid, block, 0, a.stream>>>(q, k, v, io, a.N, lay.L, a.s.scale);
+  const WideIO io{slots, multi ? nullptr : a.state, part_num, part_den, a.o, a.s.stride, lay.nslot, tokens, multi};
+  auto readout = a.seq.packed ? prefill_wide_kernel<NT, E, true, true> : prefill_wide_kernel<NT, E, true, false>;
+  readout<<<grid, block, 0, a.stream>>>(q, k, v, io, a.seq, lay.L, a.s.scale);
   if (hipGetLastError() != hipSuccess) return -3;
   if (NB == 1) return 0;  // the outputs are final
-  const long long tokens = (long long)a.BH * a.N;
   wide_reduce_kernel<<<dim3((unsigned)cdiv(tokens * 16, 256)), dim3(256), 0, a.stream>>>(part_num, part_den, a.o,
                                                                                           tokens, NB);
   return hipGetLastError() == hipSuccess ? 0 : -3;
@@ -505,15 +542,15 @@ bool prefill_wide_has(int nt, int dk, int dv, int dtype) {
 }
 
 // An upper bound over both uses (with and without outputs): the query does not know which follows.
-long long prefill_wide_ws_bytes(const Shape& s, int BH, int N) {
+long long prefill_wide_ws_bytes(const Shape& s, int BH, const SeqMap& seq) {
   auto bytes = [](const WideLayout& lay) { return (round_up(lay.slot_floats, 64) + lay.part_floats) * 4; };
   auto both = [&](auto layout) { return std::max(bytes(layout(true)), bytes(layout(false))); };
   switch (s.nt) {
-    case 1: return both([&](bool o) { return wide_layout<1>(s, BH, N, o); });
-    case 2: return both([&](bool o) { return wide_layout<2>(s, BH, N, o); });
-    case 3: return both([&](bool o) { return wide_layout<3>(s, BH, N, o); });
-    case 4: return both([&](bool o) { return wide_layout<4>(s, BH, N, o); });
-    default: return both([&](bool o) { return wide_layout<5>(s, BH, N, o); });
+    case 1: return both([&](bool o) { return wide_layout<1>(s, BH, seq, o); });
+    case 2: return both([&](bool o) { return wide_layout<2>(s, BH, seq, o); });
+    case 3: return both([&](bool o) { return wide_layout<3>(s, BH, seq, o); });
+    case 4: return both([&](bool o) { return wide_layout<4>(s, BH, seq, o); });
+    default: return both([&](bool o) { return wide_layout<5>(s, BH, seq, o); });
   }
 }
 

@@ -7,7 +7,7 @@
 namespace taylor {
 
 bool prefill_wide_has(int nt, int dk, int dv, int dtype);
-long long prefill_wide_ws_bytes(const Shape& s, int BH, int N);
+long long prefill_wide_ws_bytes(const Shape& s, int BH, const SeqMap& seq);
 int prefill_wide_launch(const PrefillArgs& a);
 
 }  // namespace taylor

@@ -135,3 +135,51 @@ def device_qkv(cfg_id, B, H, N, d_k, d_v, device, unit_norm=True, salt=0, need_q
         k[b0:b1] = unit(t) if unit_norm else t
         v[b0:b1] = torch.randn((b1 - b0, H, N, d_v), generator=g, device=device)
     return q, k, v
+
+
+def ragged_lengths(cfg_id, n_seqs, lo, hi, salt=0):
+    """Seeded sequence lengths drawn uniformly from [lo, hi] (a mix of short and long prompts)."""
+    rng = np.random.default_rng(np.random.SeedSequence([int(cfg_id), int(salt), 7]))
+    return [int(x) for x in rng.integers(lo, hi + 1, size=n_seqs)]
+
+
+class Ragged(QKV):
+    """A ragged batch packed head-major: q, k [H, T, d_k] and v [H, T, d_v] in device format (float64
+    copies q64 ...), and offsets ``cu`` [n_seqs + 1] (int32): sequence b is tokens cu[b] .. cu[b+1]-1."""
+
+    def __init__(self, q, k, v, q64, k64, v64, dtype, cu):
+        super().__init__(q, k, v, q64, k64, v64, dtype)
+        self.cu = cu
+
+    @property
+    def lengths(self):
+        return [int(b - a) for a, b in zip(self.cu[:-1], self.cu[1:])]
+
+    def seq(self, b):
+        """float64 (q, k, v) of sequence b, each [H, len_b, d]."""
+        a, e = int(self.cu[b]), int(self.cu[b + 1])
+        return self.q64[:, a:e], self.k64[:, a:e], self.v64[:, a:e]
+
+    def torch_cu(self, device):
+        import torch
+
+        return torch.from_numpy(self.cu).to(device)
+
+
+def make_ragged(cfg_id, lengths, H, d_k, d_v, dtype=F32, unit_norm=True, salt=0):
+    """Seeded ragged batch: sequence b, head h draws its rows as draw_head(cfg_id, b, h, len_b, ...)."""
+    lengths = [int(n) for n in lengths]
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    T = int(cu[-1])
+    q64 = np.empty((H, T, d_k))
+    k64 = np.empty((H, T, d_k))
+    v64 = np.empty((H, T, d_v))
+    for b, n in enumerate(lengths):
+        for h in range(H):
+            q64[h, cu[b] : cu[b + 1]], k64[h, cu[b] : cu[b + 1]], v64[h, cu[b] : cu[b + 1]] = draw_head(
+                cfg_id, b, h, n, d_k, d_v, unit_norm, salt)
+    q, q64 = round_values(q64, dtype)
+    k, k64 = round_values(k64, dtype)
+    v, v64 = round_values(v64, dtype)
+    return Ragged(q, k, v, q64, k64, v64, dtype, cu)

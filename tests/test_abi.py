@@ -30,7 +30,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     declared = _header_functions()
-    assert len(declared) == 10
+    assert len(declared) == 12
     assert sorted(rs.EXPORTS) == declared
     out = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(taylor_[a-z_0-9]+)$", out, re.M))
@@ -144,6 +144,66 @@ def test_prefill_validation():
     # documented no-ops (no launch): N == 0, B*H == 0
     assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 0, cfg) == rs.TAYLOR_OK
     assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, cfg) == rs.TAYLOR_OK
+
+
+def test_varlen_workspace_bytes():
+    cfg = rs.config(3, 16, 64, 64, 1.0, rs.TAYLOR_BF16)
+    assert rs.taylor_prefill_varlen_workspace_bytes(cfg, 8, 16, 4096, 0) == 0
+    assert rs.taylor_prefill_varlen_workspace_bytes(cfg, 0, 16, 4096, 0) == 0
+    assert rs.taylor_prefill_varlen_workspace_bytes(cfg, 8, 16, 4096, 10000) > 0
+    for n, dt in ((1, rs.TAYLOR_F32), (3, rs.TAYLOR_F32), (4, rs.TAYLOR_BF16), (5, rs.TAYLOR_F32)):
+        assert rs.taylor_prefill_varlen_workspace_bytes(rs.config(n, 16, 64, 0, 1.0, dt), 8, 16, 4096, 10000) > 0
+    L = rs.lib()
+
+    def q(c, *a):
+        return L.taylor_prefill_varlen_workspace_bytes(ctypes.byref(c) if c else None, *a)
+
+    E = rs.TAYLOR_ERR_INVALID_ARG
+    assert q(None, 8, 16, 4096, 100) == E
+    assert q(cfg, -1, 16, 4096, 100) == E
+    assert q(cfg, 8, -1, 4096, 100) == E
+    assert q(cfg, 8, 16, -1, 100) == E
+    assert q(cfg, 8, 16, 4096, -1) == E
+    assert q(cfg, 8, 16, 100, 801) == E  # more tokens than n_seqs * max_seqlen
+    assert q(cfg, 300, 300, 64, 100) == rs.TAYLOR_ERR_UNSUPPORTED  # too many (sequence, head) pairs
+    # ragged batches run on the d_k = 16, d_v = 64 kernels only
+    assert q(rs.config(3, 8, 32, 64), 8, 16, 4096, 100) == rs.TAYLOR_ERR_UNSUPPORTED
+    assert q(rs.config(3, 4, 4, 64), 8, 16, 4096, 100) == rs.TAYLOR_ERR_UNSUPPORTED
+
+
+def _varlen(q, k, v, o, st, ws, cu, n_seqs, H, N, T, cfg):
+    return rs.lib().taylor_attn_prefill_varlen(q, k, v, o, st, ws, cu, n_seqs, H, N, T,
+                                               ctypes.byref(cfg) if cfg else None, None)
+
+
+def test_varlen_validation():
+    cfg = rs.config(3, 16, 64, 64, 1.0, rs.TAYLOR_BF16)
+    E = rs.TAYLOR_ERR_INVALID_ARG
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 100, 300)
+    assert _varlen(*ok, None) == E
+    assert _varlen(FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 4, 2, 100, 300, cfg) == E  # nothing to produce
+    for i in range(7):
+        args = list(ok)
+        args[i] = MIS if i < 6 else FAKE + 2  # cu_seqlens needs 4-byte alignment only
+        if i == 4 or i == 3:
+            continue  # misaligned o / state checked below with the other argument present
+        assert _varlen(*args, cfg) == E, i
+    for i in (0, 1, 2, 6):  # q (outputs wanted), k, v, cu_seqlens
+        args = list(ok)
+        args[i] = None
+        assert _varlen(*args, cfg) == E, i
+    assert _varlen(FAKE, FAKE, FAKE, MIS, FAKE, FAKE, FAKE, 4, 2, 100, 300, cfg) == E
+    assert _varlen(FAKE, FAKE, FAKE, FAKE, MIS, FAKE, FAKE, 4, 2, 100, 300, cfg) == E
+    assert _varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 2, 100, 300, cfg) == E  # workspace required
+    assert _varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 100, 401, cfg) == E  # T > n_seqs * max
+    assert _varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -4, 2, 100, 300, cfg) == E
+    assert _varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 100, -3, cfg) == E
+    assert _varlen(*ok, rs.config(3, 8, 32, 64)) == rs.TAYLOR_ERR_UNSUPPORTED
+    assert _varlen(*ok, rs.config(7, 16, 64)) == rs.TAYLOR_ERR_UNSUPPORTED
+    # documented no-ops (no launch): no tokens, no pairs
+    assert _varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 4, 2, 100, 0, cfg) == rs.TAYLOR_OK
+    assert _varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, 2, 100, 0, cfg) == rs.TAYLOR_OK
+    assert _varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 4, 0, 100, 300, cfg) == rs.TAYLOR_OK
 
 
 def test_decode_validation():
