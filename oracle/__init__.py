@@ -19,7 +19,10 @@ no code):
   formula) and the "AI Radio" episode page on it (transcript: unit-ratio
   normalisation of q and k, truncation at an even highest order).
 * Su Jianlin, kexue.fm translation 11814, section "Linear Attention" -- a
-  second-order expansion of exp is non-negative (the "Based" remark).
+  second-order expansion of exp is non-negative (the "Based" remark); sections
+  "Basic Expansion", "Calculating the Gradient" and "Linear Attention" -- the
+  softmax expanded about the mean score, a second linear-attention readout of
+  the same moment states.
 
 Modules:
 
@@ -28,6 +31,8 @@ Modules:
 * ``attention`` -- direct O(N^2) truncated-kernel attention (the definition),
   causal softmax attention, and the separate state / recurrence / chunk routines
   used only to pin the pages' claims.
+* ``centered`` -- direct O(N^2) causal attention with the softmax expanded about
+  the mean score (orders 1, 2), and the logsumexp series it is the gradient of.
 
 Every function that has no independent pin says "parity unpinned" in its
 docstring; at present every function is pinned (see tests/test_oracle_*.py).
@@ -35,6 +40,8 @@ docstring; at present every function is pinned (see tests/test_oracle_*.py).
 
 from .tables import monomials, exponents, coefficient, feature_table, index_table, coef_table, feature_width
 from .features import features, features_by_order
+from . import centered
+from .centered import centered_weights, centered_attention, centered_attention_rows, lse_series
 from .attention import (
     truncated_kernel,
     truncated_attention,
@@ -52,4 +59,5 @@ __all__ = [
     "features", "features_by_order",
     "truncated_kernel", "truncated_attention", "truncated_attention_rows", "softmax_attention",
     "state", "recurrent", "chunked_state", "decode_reference", "batched",
+    "centered", "centered_weights", "centered_attention", "centered_attention_rows", "lse_series",
 ]
