@@ -17,8 +17,9 @@ events on the stream it runs on.
 
 Secondary timings after the timed steps (each can be skipped by a flag): decode over
 512 sequences whose states exceed the last-level cache, the float32 prefill at
-n = 1..5 (B=1, H=16, N=16,384), and a ragged-batch prefill (32 prompts of seeded
-lengths 1..2,047, 16 heads, bfloat16, n = 3).
+n = 1..5 (B=1, H=16, N=16,384), the expanded-softmax readout (orders 1, 2) on the
+main prefill inputs, and a ragged-batch prefill (32 prompts of seeded lengths
+1..2,047, 16 heads, bfloat16, n = 3).
 """
 
 import argparse
@@ -227,6 +228,35 @@ def varlen_prefill(rs, synth, torch, dev, reps=5):
     return {"sequences": len(lens), "heads": H, "tokens": T, "max_len": N, "us": us, "tok_s": T / us * 1e6}
 
 
+def centered_prefill(rs, torch, dev, q, k, v, reps=5):
+    """The expanded-softmax readout (orders 1, 2) on the main step's prefill inputs (B4 x H16 x N8192,
+    bfloat16): state init + prefill, HIP events; the states are the truncated kernel's of n = order+1."""
+    B, H, N = k.shape[:3]
+    o = torch.empty((B, H, N, DV), dtype=torch.float32, device=dev)
+    res = {}
+    for order in (1, 2):
+        cfg = rs.config(order + 1, DK, DV, 0, 1.0, rs.TAYLOR_BF16, rs.TAYLOR_READOUT_CENTERED)
+        st = torch.empty((B, H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
+        ws = rs.new_workspace(cfg, B, H, N, dev)
+
+        def step():
+            rs.taylor_state_init(st, cfg)
+            rs.taylor_attn_prefill(q, k, v, o, st, ws, cfg)
+
+        step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res[f"order{order}"] = {"us": us, "tok_s": B * N / us * 1e6}
+        del ws, st
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +270,7 @@ def main():
     ap.add_argument("--big-decode-steps", type=int, default=100)
     ap.add_argument("--no-order-sweep", action="store_true", help="skip the n = 1..5 float32 prefill timings")
     ap.add_argument("--no-varlen", action="store_true", help="skip the ragged-batch prefill timing")
+    ap.add_argument("--no-centered", action="store_true", help="skip the expanded-softmax readout timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (scale reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -410,6 +441,9 @@ def main():
     if not args.no_order_sweep:
         log("order sweep n = 1..5 (float32 prefill, B1 H16 N16384)")
         out["order_sweep_prefill_f32_B1xH16xN16384"] = order_sweep(rs, synth, torch, dev)
+    if not args.no_centered:
+        log("expanded-softmax readout (orders 1, 2) on the prefill inputs")
+        out["prefill_centered_bf16_B4xH16xN8192"] = centered_prefill(rs, torch, dev, pq, pk, pv)
     if not args.no_varlen:
         log("ragged-batch prefill (32 prompts, 16 heads, bf16)")
         out["prefill_varlen_bf16_32seqs_H16"] = varlen_prefill(rs, synth, torch, dev)

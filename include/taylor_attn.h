@@ -68,6 +68,22 @@ typedef enum {
 
 typedef enum { TAYLOR_F32 = 0, TAYLOR_BF16 = 1 } taylor_dtype;
 
+/* How the states are read out.
+ *   TAYLOR_READOUT_KERNEL   (0): the truncated exp kernel, normalised -- the
+ *       method above (Abstract of "Expanding Attention").
+ *   TAYLOR_READOUT_CENTERED (1): softmax expanded about the mean score (Su
+ *       Jianlin, kexue.fm translation 11814, "Calculating the Gradient" and
+ *       "Linear Attention"), truncated at order n_terms - 1 (1 or 2).  Token i
+ *       weights key j <= i by, with x_j = scale * q_i.k_j, y_j = x_j - mean(x)
+ *       over the i+1 keys, p_j = (1 + y_j)/(i+1) at order 1 and
+ *       (1 + y_j + (y_j^2 - mean(y^2))/2)/(i+1) at order 2, and outputs
+ *       o_i = sum_j p_j v_j (the weights sum to one and may be negative).  It
+ *       reads the same states (S, z of n_terms terms: counts, sums of k, of
+ *       phi_2(k) and their products with v), so a state written under one
+ *       readout continues under the other.  Compiled for n_terms = 2, 3 at
+ *       d_k = 16, d_v = 64. */
+typedef enum { TAYLOR_READOUT_KERNEL = 0, TAYLOR_READOUT_CENTERED = 1 } taylor_readout;
+
 typedef struct {
   int n_terms;  /* n: Taylor terms, orders 0..n-1 (1..5 compiled)                         */
   int d_k;      /* q/k head dimension (4, 8 or 16 compiled)                                */
@@ -75,6 +91,7 @@ typedef struct {
   int chunk;    /* prefill chunk length C: 64 or 128; 0 selects the default for the shape */
   float scale;  /* score scale sigma: s = scale * q.k                                      */
   int in_dtype; /* taylor_dtype of q, k, v                                                 */
+  int readout;  /* taylor_readout (0 = the truncated kernel)                               */
 } taylor_config;
 
 /* Human-readable name of a taylor_status; never NULL. */
@@ -105,7 +122,7 @@ int64_t taylor_state_stride(const taylor_config* cfg);
 int taylor_monomial_table(int n_terms, int d_k, int32_t* idx_out, double* coef_out, size_t cap_rows);
 
 /* TAYLOR_OK if kernels are compiled for this config (n_terms, d_k, d_v, chunk,
- * in_dtype); TAYLOR_ERR_UNSUPPORTED if valid but not compiled;
+ * in_dtype, readout); TAYLOR_ERR_UNSUPPORTED if valid but not compiled;
  * TAYLOR_ERR_INVALID_ARG if invalid.  Host only. */
 int taylor_supported(const taylor_config* cfg);
 
@@ -173,7 +190,8 @@ int taylor_attn_prefill_varlen(const void* q, const void* k, const void* v, floa
 
 /* One decode step per (b, h): S += phi(k_t) [v_t | 1]^T (one rank-one update),
  * then o_t = (phi(scale*q_t)^T S)[:d_v] / (phi(scale*q_t)^T z) -- the update comes
- * first, so the current token attends to itself.
+ * first, so the current token attends to itself.  (TAYLOR_READOUT_CENTERED: the
+ * same update, then the expanded-softmax output of the token over its history.)
  *   q, k, v : [B,H,d_k], [B,H,d_k], [B,H,d_v] in cfg->in_dtype;
  *   o       : [B,H,d_v] float32;
  *   state   : [B,H,stride] float32, updated in place.

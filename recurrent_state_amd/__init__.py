@@ -24,6 +24,8 @@ TAYLOR_ERR_UNSUPPORTED = -2
 TAYLOR_ERR_HIP = -3
 TAYLOR_F32 = 0
 TAYLOR_BF16 = 1
+TAYLOR_READOUT_KERNEL = 0
+TAYLOR_READOUT_CENTERED = 1
 
 # Every symbol the header declares.
 EXPORTS = (
@@ -58,17 +60,18 @@ class taylor_config(ctypes.Structure):
         ("chunk", ctypes.c_int),
         ("scale", ctypes.c_float),
         ("in_dtype", ctypes.c_int),
+        ("readout", ctypes.c_int),
     ]
 
     def __repr__(self):
         return (f"taylor_config(n_terms={self.n_terms}, d_k={self.d_k}, d_v={self.d_v}, chunk={self.chunk}, "
-                f"scale={self.scale}, in_dtype={self.in_dtype})")
+                f"scale={self.scale}, in_dtype={self.in_dtype}, readout={self.readout})")
 
 
-def config(n_terms, d_k, d_v, chunk=0, scale=1.0, in_dtype=TAYLOR_F32):
+def config(n_terms, d_k, d_v, chunk=0, scale=1.0, in_dtype=TAYLOR_F32, readout=TAYLOR_READOUT_KERNEL):
     if not isinstance(in_dtype, int):
         in_dtype = dtype_code(in_dtype)
-    return taylor_config(n_terms, d_k, d_v, chunk, scale, in_dtype)
+    return taylor_config(n_terms, d_k, d_v, chunk, scale, in_dtype, readout)
 
 
 _lib = None

@@ -28,6 +28,7 @@ int check_config(const taylor_config* cfg, Shape* s) {
   if (!cfg) return TAYLOR_ERR_INVALID_ARG;
   if (cfg->n_terms < 1 || cfg->d_k < 1 || cfg->d_v < 1) return TAYLOR_ERR_INVALID_ARG;
   if (cfg->in_dtype != TAYLOR_F32 && cfg->in_dtype != TAYLOR_BF16) return TAYLOR_ERR_INVALID_ARG;
+  if (cfg->readout != TAYLOR_READOUT_KERNEL && cfg->readout != TAYLOR_READOUT_CENTERED) return TAYLOR_ERR_INVALID_ARG;
   if (cfg->chunk < 0) return TAYLOR_ERR_INVALID_ARG;
   if (!std::isfinite(cfg->scale)) return TAYLOR_ERR_INVALID_ARG;
   if (cfg->n_terms > taylor::kMaxTerms) return TAYLOR_ERR_UNSUPPORTED;
@@ -40,6 +41,7 @@ int check_config(const taylor_config* cfg, Shape* s) {
     s->dk = cfg->d_k;
     s->dv = cfg->d_v;
     s->dtype = cfg->in_dtype;
+    s->readout = cfg->readout;
     s->scale = cfg->scale;
     s->W = W;
     s->stride = (W * (cfg->d_v + 1) + 3) / 4 * 4;
@@ -58,9 +60,15 @@ Path prefill_path(const Shape& s, int C) {
   return Path::None;
 }
 
+// The expanded-softmax readout is compiled for orders 1 and 2 on the matrix-core shapes.
+bool centered_ok(const Shape& s) {
+  return s.readout != TAYLOR_READOUT_CENTERED || ((s.nt == 2 || s.nt == 3) && s.dk == 16 && s.dv == 64);
+}
+
 int supported(const taylor_config* cfg, const Shape& s) {
   const int C = chunk_of(cfg);
   if (C != 64 && C != 128) return TAYLOR_ERR_UNSUPPORTED;
+  if (!centered_ok(s)) return TAYLOR_ERR_UNSUPPORTED;
   if (!taylor::decode_has(s.nt, s.dk, s.dv)) return TAYLOR_ERR_UNSUPPORTED;
   if (prefill_path(s, C) == Path::None) return TAYLOR_ERR_UNSUPPORTED;
   return TAYLOR_OK;
@@ -252,6 +260,7 @@ int taylor_attn_decode_step(const void* q, const void* k, const void* v, float* 
   int rc = check_config(cfg, &s);
   if (rc != TAYLOR_OK) return rc;
   if (!taylor::decode_has(s.nt, s.dk, s.dv)) return TAYLOR_ERR_UNSUPPORTED;
+  if (!centered_ok(s)) return TAYLOR_ERR_UNSUPPORTED;
   if ((rc = check_sizes(B, H, 1)) != TAYLOR_OK) return rc;
   const int BH = B * H;
   if (BH == 0) return TAYLOR_OK;

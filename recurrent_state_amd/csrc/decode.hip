@@ -26,7 +26,21 @@ namespace {
 
 constexpr int kDecodeThreads = 256;
 
-template <int NT, int DK, int DV, typename T>
+// Order of feature a in the table (orders ascend: 1 feature of order 0, then d_k of order 1, ...);
+// used at n <= 3 only.
+template <int DK>
+__device__ __forceinline__ int order_of(int a) {
+  return a == 0 ? 0 : a <= DK ? 1 : 2;
+}
+
+// CENT: the softmax expanded about the mean score (Su Jianlin, kexue.fm translation 11814, "Linear
+// Attention"), order n - 1: with d_m = phi_m(a) . z_m over the inclusive history (a = sigma q),
+// c = d_0 and u = d_1 / c, the output is sum_m gamma_m phi_m(a)^T S_m with
+//     order 1: gamma = ((1 - u) / c, 1 / c)
+//     order 2: gamma = ((1 - u + u^2 - d_2 / c) / c, (1 - u) / c, 1 / c)
+// and no normaliser (the weights sum to one).  The d_m are reduced first, phi(a) is scaled by the
+// gammas, and the state pass below runs unchanged.
+template <int NT, int DK, int DV, typename T, bool CENT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                                 const T* __restrict__ v, float* __restrict__ o,
                                                                 float* __restrict__ state, long long stride,
@@ -44,6 +58,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
   __shared__ float s_phik[W], s_phiq[W];
   __shared__ float4 s_red[NWAVE][CG];
   __shared__ float s_redz[NWAVE];
+  __shared__ float s_redm[NWAVE][3];
 
   const int tid = threadIdx.x;
   const long long h = blockIdx.x;
@@ -73,6 +88,30 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
     s_phik[a] = feature_at<NT, DK>(s_k, a);
   }
   __syncthreads();
+  if constexpr (CENT) {
+    static_assert(NT == 2 || NT == 3, "orders 1 and 2");
+    static_assert(W <= kDecodeThreads, "one feature per thread");
+    float dm[3] = {0.f, 0.f, 0.f};
+    const int m = order_of<DK>(tid);
+    if (tid < W) dm[m] = s_phiq[tid] * (z0 + s_phik[tid]);
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      for (int off = 1; off < 64; off <<= 1) dm[j] += __shfl_xor(dm[j], off);
+    if ((tid & 63) == 0)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) s_redm[tid >> 6][j] = dm[j];
+    __syncthreads();
+    float d[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) d[j] += s_redm[w][j];
+    const float ic = 1.0f / d[0], u = d[1] * ic;
+    const float g[3] = {NT == 2 ? (1.0f - u) * ic : (1.0f - u + u * u - d[2] * ic) * ic,
+                        NT == 2 ? ic : (1.0f - u) * ic, ic};
+    if (tid < W) s_phiq[tid] *= g[m];
+    __syncthreads();
+  }
 
   const float4 vv = *reinterpret_cast<const float4*>(s_v + cg * 4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -125,7 +164,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
       t = add4(t, s_red[w][tid]);
       den += s_redz[w];
     }
-    *reinterpret_cast<float4*>(o + h * DV + tid * 4) = make_float4(t.x / den, t.y / den, t.z / den, t.w / den);
+    if constexpr (CENT)
+      *reinterpret_cast<float4*>(o + h * DV + tid * 4) = t;
+    else
+      *reinterpret_cast<float4*>(o + h * DV + tid * 4) = make_float4(t.x / den, t.y / den, t.z / den, t.w / den);
   }
 }
 
@@ -134,16 +176,33 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, long 
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-template <int NT, int DK, int DV>
-int decode_run(const DecodeArgs& a) {
+template <int NT, int DK, int DV, bool CENT>
+int decode_go(const DecodeArgs& a) {
   const dim3 grid(a.BH), block(kDecodeThreads);
   if (a.s.dtype == 0)
-    decode_kernel<NT, DK, DV, float><<<grid, block, 0, a.stream>>>(
+    decode_kernel<NT, DK, DV, float, CENT><<<grid, block, 0, a.stream>>>(
         (const float*)a.q, (const float*)a.k, (const float*)a.v, a.o, a.state, a.s.stride, a.s.scale);
   else
-    decode_kernel<NT, DK, DV, uint16_t><<<grid, block, 0, a.stream>>>(
+    decode_kernel<NT, DK, DV, uint16_t, CENT><<<grid, block, 0, a.stream>>>(
         (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.state, a.s.stride, a.s.scale);
   return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// The expanded-softmax readout is compiled for n = 2, 3 at d_k = 16, d_v = 64.
+template <int NT, int DK, int DV>
+constexpr bool has_centered() {
+  return (NT == 2 || NT == 3) && DK == 16 && DV == 64;
+}
+
+template <int NT, int DK, int DV>
+int decode_run(const DecodeArgs& a) {
+  if (a.s.readout == 1) {
+    if constexpr (has_centered<NT, DK, DV>())
+      return decode_go<NT, DK, DV, true>(a);
+    else
+      return -2;
+  }
+  return decode_go<NT, DK, DV, false>(a);
 }
 
 using DecodeFn = int (*)(const DecodeArgs&);

@@ -10,6 +10,7 @@ struct Shape {
   int nt;       // Taylor terms
   int dk, dv;   // head dims
   int dtype;    // 0 = float32, 1 = bfloat16 inputs
+  int readout;  // 0 = truncated kernel, normalised; 1 = softmax expanded about the mean score
   float scale;  // score scale
   long long W;       // feature width
   long long stride;  // floats per head block in the state
@@ -120,6 +121,22 @@ struct SeqMap {
     const long long c0 = off(b), c1 = off(b + 1);
     first = h * nslot + c0 / L + b;
     count = c1 > c0 ? (int)((c1 - 1) / L - c0 / L + 1) : 0;
+  }
+
+  // Index of chunk c (chunks of CH tokens, CH dividing L) of piece p in a per-chunk array: equal
+  // lengths, pair * ceil(N / CH) + (the chunk's position in the pair) / CH; ragged, per head
+  // floor(position / CH) + b, which keeps consecutive sequences apart as the slots do, with
+  // floor(T / CH) + B + 1 entries per head.
+  __device__ __forceinline__ long long chunk_index(const SeqPiece& p, int c, int CH) const {
+    if (!packed) {
+      const long long per = (N + (long long)CH - 1) / CH;
+      return p.pair * per + (p.tok - p.pair * (long long)N) / CH + c;
+    }
+    const long long b = p.pair / H, h = p.pair - b * H;
+    return h * (T / CH + B + 1) + (p.tok - h * T) / CH + c + b;
+  }
+  long long chunk_count(int BH, int CH) const {
+    return packed ? (long long)H * (T / CH + B + 1) : (long long)BH * ((N + (long long)CH - 1) / CH);
   }
 
   // Token-heads covered: the extent of an output or per-token workspace array.

@@ -20,6 +20,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "centered.hpp"
 #include "features.hpp"
 #include "prefill_mfma.hpp"
 
@@ -169,10 +170,35 @@ __device__ __forceinline__ void pipe_phik_rows(PipeSmem<NT, READOUT>& sm, int b,
   }(std::make_integer_sequence<int, SP::RK / 2>{});
 }
 
-// Writes this wave's phi(sQ) groups of token j and returns their part of phi(sq_j) . z.
-template <int NT, bool READOUT, int G>
+// Order of feature A (0 for the padding slots past the table, whose features are zero).
+template <int NT, int A>
+constexpr int feature_order() {
+  if constexpr (A < Geo<NT>::W)
+    return FeatureTable<NT, kDK>::T.order[A];
+  else
+    return 0;
+}
+
+// Feature A of x, scaled by its order's coefficient in CENT mode (expanded-softmax readout).  There
+// the constant feature is left out (zero): its term gamma_0 S_{<c} row 0 is added by the consumers
+// in float32, since a bfloat16 gamma_0 would carry a 2^-9 relative error into the largest term of the
+// output (the truncated-kernel readout shares its feature roundings with its normaliser; this one
+// has none).
+template <int NT, bool CENT, int A>
+__device__ __forceinline__ float qfeat(const float (&x)[kDK], const f32x4& cq) {
+  if constexpr (CENT && A == 0)
+    return 0.f;
+  else if constexpr (CENT)
+    return feat<NT, A>(x) * cq[feature_order<NT, A>()];
+  else
+    return feat<NT, A>(x);
+}
+
+// Writes this wave's phi(sQ) groups of token j and returns their part of phi(sq_j) . z (CENT: the
+// features scaled by the token's coefficients gamma_m, and no denominator part).
+template <int NT, bool READOUT, bool CENT, int G>
 __device__ __forceinline__ float pipe_phiq_groups(PipeSmem<NT, READOUT>& sm, int b, int zb, int j,
-                                                  const float (&x)[kDK]) {
+                                                  const float (&x)[kDK], const f32x4& cq) {
   using SP = PipeSplit<NT>;
   float acc = 0.f;
   [&]<int... P>(std::integer_sequence<int, P...>) {
@@ -182,11 +208,15 @@ __device__ __forceinline__ float pipe_phiq_groups(PipeSmem<NT, READOUT>& sm, int
          constexpr int s0 = grp * 8;
          uint32_t v[4];
          [&]<int... R>(std::integer_sequence<int, R...>) {
-           ((v[R] = __builtin_bit_cast(uint32_t, to_bf16x2(feat<NT, slot_feature_bf16(s0 + 2 * R)>(x),
-                                                            feat<NT, slot_feature_bf16(s0 + 2 * R + 1)>(x)))),
+           ((v[R] = __builtin_bit_cast(uint32_t,
+                                       to_bf16x2(qfeat<NT, CENT, slot_feature_bf16(s0 + 2 * R)>(x, cq),
+                                                 qfeat<NT, CENT, slot_feature_bf16(s0 + 2 * R + 1)>(x, cq)))),
             ...);
-           ((acc = fmaf(__uint_as_float(v[R] << 16), sm.z[zb][slot_feature_bf16(s0 + 2 * R)], acc)), ...);
-           ((acc = fmaf(__uint_as_float(v[R] & 0xffff0000u), sm.z[zb][slot_feature_bf16(s0 + 2 * R + 1)], acc)), ...);
+           if constexpr (!CENT) {
+             ((acc = fmaf(__uint_as_float(v[R] << 16), sm.z[zb][slot_feature_bf16(s0 + 2 * R)], acc)), ...);
+             ((acc = fmaf(__uint_as_float(v[R] & 0xffff0000u), sm.z[zb][slot_feature_bf16(s0 + 2 * R + 1)], acc)),
+              ...);
+           }
          }(std::make_integer_sequence<int, 4>{});
          *reinterpret_cast<uint4*>(&sm.phiq[b][j][s0]) = make_uint4(v[0], v[1], v[2], v[3]);
        }
@@ -210,22 +240,26 @@ constexpr int producer_pairs() {
   return G < kPipePairs ? (kPipePairs - G + kPipeProducers - 1) / kPipeProducers : 0;
 }
 
-// Producer G's inputs for one chunk, loaded a chunk ahead of use (lane = token j of the chunk).
-template <bool READOUT, int G>
+// Producer G's inputs for one chunk, loaded a chunk ahead of use (lane = token j of the chunk).  CENT
+// (expanded-softmax readout) adds the coefficients of the lane's token and of each score tile's
+// query column.
+template <bool READOUT, bool CENT, int G>
 struct PipeIn {
   static constexpr int NS = READOUT ? producer_pairs<G>() : 0;
   static constexpr int NVP = kDV / kPipeProducers / 8;  // 16-byte pieces of v per producer lane
   static_assert(NVP * 8 * kPipeProducers == kDV, "value columns split evenly over producers");
   uint4 k[2], q[READOUT ? 2 : 1], v[NVP];
   uint2 sk[NS > 0 ? NS : 1], sq[NS > 0 ? NS : 1];  // score MFMA operands of this producer's tiles
+  f32x4 cq, csq[CENT && NS > 0 ? NS : 1];
 
   // Tokens past the end read the chunk's first row (always valid), so every load is an
   // unconditional global load whose result is not touched until it is used a chunk later.  Only
   // k needs masking (its features enter S and z) and that happens at unpack time; q, v and the
   // score operands of such tokens never reach a stored output (causal mask, output guard).
-  __device__ __forceinline__ void load(const __bf16* qg, const __bf16* kg, const __bf16* vg, long long tok0, int nv,
-                                       int l) {
+  __device__ __forceinline__ void load(const __bf16* qg, const __bf16* kg, const __bf16* vg, const float* cf,
+                                       long long tok0, int nv, int l) {
     const long long row = tok0 + (l < nv ? l : 0);
+    if constexpr (CENT) cq = *reinterpret_cast<const f32x4*>(cf + 4 * row);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       k[u] = *reinterpret_cast<const uint4*>(kg + row * kDK + 8 * u);
@@ -240,6 +274,7 @@ struct PipeIn {
          const int rk = 16 * pair_jt(p) + l16, rq = 16 * pair_it(p) + l16;
          sk[S] = *reinterpret_cast<const uint2*>(kg + (tok0 + (rk < nv ? rk : 0)) * kDK + 4 * lg);
          sq[S] = *reinterpret_cast<const uint2*>(qg + (tok0 + (rq < nv ? rq : 0)) * kDK + 4 * lg);
+         if constexpr (CENT) csq[S] = *reinterpret_cast<const f32x4*>(cf + 4 * (tok0 + (rq < nv ? rq : 0)));
        }()),
        ...);
     }(std::make_integer_sequence<int, NS>{});
@@ -259,12 +294,18 @@ __device__ __forceinline__ void unpack_row16(const uint4 (&r)[2], float (&x)[kDK
 }
 
 // Producer wave G prepares chunk data in buffer b (chunk parity), with z_{<chunk} in z[b].
-template <int NT, bool READOUT, int G>
-__device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const PipeIn<READOUT, G>& in, int b, int l,
-                                             int nv, float scale) {
+template <int NT, bool READOUT, bool CENT, int G>
+__device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const PipeIn<READOUT, CENT, G>& in, int b,
+                                             int l, int nv, float scale, float* zrow) {
   using SP = PipeSplit<NT>;
   constexpr int WP = Geo<NT>::WP;
   const int l16 = l & 15, lg = l >> 4;
+  if constexpr (!READOUT && CENT) {
+    // state pass before an expanded-softmax readout: z of the piece's tokens before this chunk, into
+    // this chunk's row of the per-chunk array (the coefficient kernel adds the piece's prefix)
+    const int row = G * SP::RK + l;
+    if (l < SP::RK && row < Geo<NT>::W) zrow[row] = sm.z[b][row];
+  }
   {
     float x[kDK];
     const bool valid = l < nv;  // a token past the end has a zero k row
@@ -275,12 +316,16 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
   if constexpr (READOUT) {
     float x[kDK];
     unpack_row16(in.q, x, scale);
-    sm.den_part[b][G][l] = pipe_phiq_groups<NT, READOUT, G>(sm, b, b, l, x);
+    const float dp = pipe_phiq_groups<NT, READOUT, CENT, G>(sm, b, b, l, x, in.cq);
+    if constexpr (!CENT)
+      sm.den_part[b][G][l] = dp;
+    else if constexpr (G == 0)
+      sm.den_part[b][0][l] = in.cq[0];  // gamma_0 of token l, for the consumers' constant-feature term
   }
   // V^T: this producer's value columns of token l (16-bit stores: the dword pairing measured no
   // faster here)
 #pragma unroll
-  for (int u = 0; u < PipeIn<READOUT, G>::NVP; ++u) {
+  for (int u = 0; u < PipeIn<READOUT, CENT, G>::NVP; ++u) {
     const uint32_t w[4] = {in.v[u].x, in.v[u].y, in.v[u].z, in.v[u].w};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -300,7 +345,14 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
 #pragma unroll
          for (int r = 0; r < 4; ++r) {
            const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
-           wgt[r] = (jt < it || j <= i) ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
+           const float s = scale * sc[r];
+           // CENT: gamma_0 + gamma_1 s + gamma_2 s^2 / 2 of query i (gamma_2 = 0 at order 1)
+           float poly;
+           if constexpr (CENT)
+             poly = fmaf(s, fmaf(0.5f * s, in.csq[S][2], in.csq[S][1]), in.csq[S][0]);
+           else
+             poly = taylor_kernel<NT>(s);
+           wgt[r] = (jt < it || j <= i) ? poly : 0.f;
          }
          bf16x2 h0, l0, h1, l1;
          split_bf16x2(wgt[0], wgt[1], h0, l0);
@@ -308,15 +360,17 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
          const bf16x4 hi = {h0[0], h0[1], h1[0], h1[1]}, lo = {l0[0], l0[1], l1[0], l1[1]};
          sm.a[b][p][l] = hi;
          sm.alo[b][p][l] = lo;
-         // column sums over the 16 key rows, as ones^T (hi + lo): every row of the product holds them
-         const i16x4 ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
-         f32x4 cs = {0.f, 0.f, 0.f, 0.f};
-         cs = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_bit_cast(i16x4, hi), cs, 0, 0, 0);
-         cs = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_bit_cast(i16x4, lo), cs, 0, 0, 0);
-         if (lg == 0) sm.den_intra[b][p][l16] = cs[0];
+         if constexpr (!CENT) {
+           // column sums over the 16 key rows, as ones^T (hi + lo): every row of the product holds them
+           const i16x4 ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
+           f32x4 cs = {0.f, 0.f, 0.f, 0.f};
+           cs = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_bit_cast(i16x4, hi), cs, 0, 0, 0);
+           cs = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_bit_cast(i16x4, lo), cs, 0, 0, 0);
+           if (lg == 0) sm.den_intra[b][p][l16] = cs[0];
+         }
        }()),
        ...);
-    }(std::make_integer_sequence<int, PipeIn<READOUT, G>::NS>{});
+    }(std::make_integer_sequence<int, PipeIn<READOUT, CENT, G>::NS>{});
   }
   // z_{<next} = z_{<this} + column sums of this wave's phi(K)^T rows (read back from LDS: the
   // rows were written by this same wave above, and a wave's LDS accesses complete in order)
@@ -341,38 +395,39 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
 // so no loaded value is copied.  The steady-state loop has no conditional load or produce (every
 // load issued in it is consumed in it), so the compiler's memory-counter waits stay exact; the
 // last one to three phases are peeled.  Executes exactly 2 + nch barriers.
-template <int NT, bool READOUT, int G>
+template <int NT, bool READOUT, bool CENT, int G>
 __device__ __forceinline__ void pipe_producer(PipeSmem<NT, READOUT>& sm, const __bf16* q, const __bf16* k,
-                                              const __bf16* v, float* slot, long long tok_base, int n_tok, int nch,
-                                              int l, float scale) {
+                                              const __bf16* v, const float* cf, float* slot, float* zc0,
+                                              long long tok_base, int n_tok, int nch, int l, float scale) {
   using SP = PipeSplit<NT>;
   constexpr int W = Geo<NT>::W, WP = Geo<NT>::WP, CS = kPipeChunk;
   auto nv_of = [&](int c) { return min(CS, n_tok - c * CS); };
   auto tok_of = [&](int c) { return tok_base + (long long)c * CS; };
+  auto zrow = [&](int c) { return CENT && !READOUT ? zc0 + (long long)c * W : nullptr; };
   // z prefix of this producer's rows
   const int row = G * SP::RK + l;
   if (l < SP::RK && row < WP) sm.z[0][row] = (READOUT && row < W) ? slot[(long long)W * kDV + row] : 0.f;
-  PipeIn<READOUT, G> pa, pb;
-  pa.load(q, k, v, tok_of(0), nv_of(0), l);
+  PipeIn<READOUT, CENT, G> pa, pb;
+  pa.load(q, k, v, cf, tok_of(0), nv_of(0), l);
   __syncthreads();  // z prefix visible to every producer
-  if (nch > 1) pb.load(q, k, v, tok_of(1), nv_of(1), l);
-  pipe_produce<NT, READOUT, G>(sm, pa, 0, l, nv_of(0), scale);
+  if (nch > 1) pb.load(q, k, v, cf, tok_of(1), nv_of(1), l);
+  pipe_produce<NT, READOUT, CENT, G>(sm, pa, 0, l, nv_of(0), scale, zrow(0));
   __syncthreads();  // chunk 0 ready
   int c = 0;
   for (; c + 3 < nch; c += 2) {
-    pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l);
-    pipe_produce<NT, READOUT, G>(sm, pb, (c + 1) & 1, l, nv_of(c + 1), scale);
+    pa.load(q, k, v, cf, tok_of(c + 2), nv_of(c + 2), l);
+    pipe_produce<NT, READOUT, CENT, G>(sm, pb, (c + 1) & 1, l, nv_of(c + 1), scale, zrow(c + 1));
     __syncthreads();
-    pb.load(q, k, v, tok_of(c + 3), nv_of(c + 3), l);
-    pipe_produce<NT, READOUT, G>(sm, pa, c & 1, l, nv_of(c + 2), scale);
+    pb.load(q, k, v, cf, tok_of(c + 3), nv_of(c + 3), l);
+    pipe_produce<NT, READOUT, CENT, G>(sm, pa, c & 1, l, nv_of(c + 2), scale, zrow(c + 2));
     __syncthreads();
   }
   // nch - c phases remain (1 to 3); chunks c+1 and c+2 may still need preparing
-  if (c + 2 < nch) pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l);
-  if (c + 1 < nch) pipe_produce<NT, READOUT, G>(sm, pb, (c + 1) & 1, l, nv_of(c + 1), scale);
+  if (c + 2 < nch) pa.load(q, k, v, cf, tok_of(c + 2), nv_of(c + 2), l);
+  if (c + 1 < nch) pipe_produce<NT, READOUT, CENT, G>(sm, pb, (c + 1) & 1, l, nv_of(c + 1), scale, zrow(c + 1));
   __syncthreads();
   if (c + 1 < nch) {
-    if (c + 2 < nch) pipe_produce<NT, READOUT, G>(sm, pa, c & 1, l, nv_of(c + 2), scale);
+    if (c + 2 < nch) pipe_produce<NT, READOUT, CENT, G>(sm, pa, c & 1, l, nv_of(c + 2), scale, zrow(c + 2));
     __syncthreads();
     if (c + 2 < nch) __syncthreads();
   }
@@ -381,13 +436,14 @@ __device__ __forceinline__ void pipe_producer(PipeSmem<NT, READOUT>& sm, const _
   }
 }
 
-template <int NT, bool READOUT, bool PACKED>
+template <int NT, bool READOUT, bool PACKED, bool CENT>
 __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16* __restrict__ q,
                                                                     const __bf16* __restrict__ k,
                                                                     const __bf16* __restrict__ v,
+                                                                    const float* __restrict__ cf,
                                                                     float* __restrict__ o, float* __restrict__ ws,
-                                                                    SeqMap seq, int L, long long nslot,
-                                                                    long long stride, float scale) {
+                                                                    float* __restrict__ zc, SeqMap seq, int L,
+                                                                    long long nslot, long long stride, float scale) {
   using G = Geo<NT>;
   using SM = PipeSmem<NT, READOUT>;
   constexpr int W = G::W, NAT = G::NAT, NKB = G::NKB;
@@ -408,7 +464,9 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
   case G_:                                                                                          \
     if constexpr (G_ < kPipeProducers)                                                              \
       for_each_piece<PACKED>(seq, bx, by, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {                       \
-        pipe_producer<NT, READOUT, G_>(sm, q, k, v, ws + pc.slot * stride, pc.tok, pc.n,            \
+        pipe_producer<NT, READOUT, CENT, G_>(sm, q, k, v, cf, ws + pc.slot * stride,                \
+                                             zc ? zc + seq.chunk_index(pc, 0, CS) * W : nullptr,    \
+                                             pc.tok, pc.n,                                          \
                                        (pc.n + CS - 1) / CS, l, scale);                             \
       });                                                                                           \
     break;
@@ -446,6 +504,7 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
       const int b = c & 1;
       const int nv = min(CS, pc.n - c * CS);
       const long long tok0 = pc.tok + (long long)c * CS;
+      const float srow0 = Srun[0][0];  // S_{<c}[0][16w + l16] on lanes 0..15 (CENT)
       f32x4 O[READOUT ? NIT : 1];
       if constexpr (READOUT) {
 #pragma unroll
@@ -498,13 +557,21 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           const int i = 16 * it + l16;
-          float d = 0.f;
+          float d = 1.f;  // the expanded-softmax readout has no normaliser
+          if constexpr (!CENT) {
+            d = 0.f;
 #pragma unroll
-          for (int pp = 0; pp < kPipeProducers; ++pp) d += sm.den_part[b][pp][i];
+            for (int pp = 0; pp < kPipeProducers; ++pp) d += sm.den_part[b][pp][i];
 #pragma unroll
-          for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][pair_index(jt, it)][l16];
+            for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][pair_index(jt, it)][l16];
+          } else {
+            // + gamma_0(i) S_{<c}[0][16w + 4lg + r]: row 0 of columns 16w + 4lg .. lives on lanes 4lg ..
+            const float g0 = sm.den_part[b][0][i];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[it][r] = fmaf(g0, __shfl(srow0, 4 * lg + r), O[it][r]);
+          }
           if (i < nv) {
-            const float inv = __builtin_amdgcn_rcpf(d);
+            const float inv = CENT ? 1.0f : __builtin_amdgcn_rcpf(d);
             const f32x4 r = O[it];
             *reinterpret_cast<f32x4*>(o + (tok0 + i) * kDV + 16 * w + 4 * lg) =
                 f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
@@ -527,6 +594,7 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
 }
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
 
 // Segments per head: about `target` workgroups in total, never more than the chunks.
 int n_segments(int BH, int nchunk, int target) {
@@ -560,23 +628,42 @@ PipePlan pipe_plan(int BH, const SeqMap& seq) {
   return p;
 }
 
+// The kernel for a call (the expanded-softmax readout exists for n = 2, 3; its state pass also writes
+// the per-chunk z rows).
+template <int NT, bool READOUT>
+auto pipe_kernel_for(bool packed, bool cent) {
+  if constexpr (NT == 2 || NT == 3) {
+    if (cent) return packed ? prefill_pipe_kernel<NT, READOUT, true, true> : prefill_pipe_kernel<NT, READOUT, false, true>;
+  }
+  return packed ? prefill_pipe_kernel<NT, READOUT, true, false> : prefill_pipe_kernel<NT, READOUT, false, false>;
+}
+
 template <int NT>
 int run_pipe(const PrefillArgs& a) {
   const PipePlan p = pipe_plan(a.BH, a.seq);
+  const bool cent = a.s.readout == 1 && a.o;
   float* ws = (float*)a.ws;
+  // workspace: slots | coefficients (4 per token-head) | z before each chunk (W per chunk)
+  float* coef = ws + round_up(a.seq.rows(a.BH) * p.nslot * a.s.stride, 64);
+  float* zc = coef + round_up(4 * a.seq.tokens(a.BH), 64);
   const long long elems = Geo<NT>::W * (long long)(kDV + 1);
   const dim3 grid((unsigned)a.seq.grid_x(p.L), (unsigned)a.seq.grid_y(a.BH)), block(kPipeThreads);
   const __bf16* q = (const __bf16*)a.q;
   const __bf16* k = (const __bf16*)a.k;
   const __bf16* v = (const __bf16*)a.v;
-  auto state_pass = a.seq.packed ? prefill_pipe_kernel<NT, false, true> : prefill_pipe_kernel<NT, false, false>;
-  auto readout = a.seq.packed ? prefill_pipe_kernel<NT, true, true> : prefill_pipe_kernel<NT, true, false>;
-  state_pass<<<grid, block, 0, a.stream>>>(q, k, v, nullptr, ws, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
+  pipe_kernel_for<NT, false>(a.seq.packed, cent)<<<grid, block, 0, a.stream>>>(
+      q, k, v, nullptr, nullptr, ws, cent ? zc : nullptr, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
   if (hipGetLastError() != hipSuccess) return -3;
   if (seg_scan_launch(ws, a.state, a.BH, p.nslot, a.s.stride, elems, a.o != nullptr, a.seq, p.L, a.stream))
     return -3;
   if (a.o) {
-    readout<<<grid, block, 0, a.stream>>>(q, k, v, a.o, ws, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
+    if (cent) {
+      // per-token coefficients from the prefixes the readout starts from
+      const CenteredPlan cp{p.L, p.nslot, ws, 1, zc, kPipeChunk, reinterpret_cast<float4*>(coef)};
+      if (const int rc = centered_coef_launch(a, cp)) return rc;
+    }
+    pipe_kernel_for<NT, true>(a.seq.packed, cent)<<<grid, block, 0, a.stream>>>(
+        q, k, v, cent ? coef : nullptr, a.o, ws, nullptr, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
     if (hipGetLastError() != hipSuccess) return -3;
   }
   return 0;
@@ -590,7 +677,9 @@ bool prefill_mfma_has(int nt, int dk, int dv, int dtype) { return dk == kDK && d
 
 long long prefill_mfma_ws_bytes(const Shape& s, int BH, const SeqMap& seq) {
   const PipePlan p = pipe_plan(BH, seq);
-  return seq.rows(BH) * p.nslot * s.stride * 4;
+  const long long slots = round_up(seq.rows(BH) * p.nslot * s.stride, 64);
+  if (s.readout != 1) return slots * 4;
+  return (slots + round_up(4 * seq.tokens(BH), 64) + seq.chunk_count(BH, kPipeChunk) * s.W) * 4;
 }
 
 int prefill_mfma_launch(const PrefillArgs& a) {

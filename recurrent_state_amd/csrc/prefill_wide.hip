@@ -30,6 +30,7 @@
 #include <type_traits>
 #include <utility>
 
+#include "centered.hpp"
 #include "features.hpp"
 #include "prefill_wide.hpp"
 
@@ -94,6 +95,8 @@ struct WideIO {
   long long nslot;     // slots per workspace row
   long long tokens;    // token-heads of the call
   int multi;           // several segments per pair (grid x > 1)
+  const float* coef;   // expanded-softmax readout: [token-heads] (gamma_0, gamma_1, gamma_2, 0), else null
+  float* zc;           // its state pass: z of the piece before each 64 tokens (SeqMap::chunk_index)
 };
 
 // n consecutive elements (n a multiple of 4) of one token row, widened to float32 on unpack.
@@ -133,14 +136,17 @@ struct Piece<__bf16, NE> {
 };
 
 // One producer lane's inputs for one chunk: a k row (lanes 0..31) or a q row (lanes 32..63) of token
-// l % 32, the lane's 8 values of that token, and its score-tile operands (used by block 0 only).
-template <typename E>
+// l % 32, the lane's 8 values of that token, and its score-tile operands (used by block 0 only).  For
+// the expanded-softmax readout (CENT) also the coefficients of the lane's token and of its score
+// column's query token.
+template <typename E, bool CENT>
 struct WideIn {
   Piece<E, kDK> row;
   Piece<E, 8> v;
   Piece<E, 4> sk, sq;
-  __device__ __forceinline__ void load(const E* qg, const E* kg, const E* vg, long long tok0, int nv, int l, int g,
-                                       bool readout) {
+  f32x4 cq, csq;
+  __device__ __forceinline__ void load(const E* qg, const E* kg, const E* vg, const float* cf, long long tok0, int nv,
+                                       int l, int g, bool readout) {
     const int tk = l & 31, h = l >> 5;
     const long long r = tok0 + (tk < nv ? tk : 0);  // tokens past the end read a valid row, masked later
     row.load((readout && h ? qg : kg) + r * kDK);
@@ -151,16 +157,29 @@ struct WideIn {
       const int rk = 16 * pair_jt(p) + l16, rq = 16 * pair_it(p) + l16;
       sk.load(kg + (tok0 + (rk < nv ? rk : 0)) * kDK + 4 * lg);
       sq.load(qg + (tok0 + (rq < nv ? rq : 0)) * kDK + 4 * lg);
+      if constexpr (CENT) {
+        cq = *reinterpret_cast<const f32x4*>(cf + 4 * r);
+        csq = *reinterpret_cast<const f32x4*>(cf + 4 * (tok0 + (rq < nv ? rq : 0)));
+      }
     }
   }
 };
 
+// Order of feature A (0 for the padding rows past the table, whose features are zero).
+template <int NT, int A>
+constexpr int feature_order() {
+  if constexpr (A < FeatureTable<NT, kDK>::W)
+    return FeatureTable<NT, kDK>::T.order[A];
+  else
+    return 0;
+}
+
 // Producer g's features of its FP = FB / 4 block rows for one token: lanes 0..31 from k into
-// phi(K)^T, lanes 32..63 from sq into phi(sQ) (plus their part of the denominators).  F0 = first
-// global feature.
-template <int NT, bool READOUT, int FB, int F0>
+// phi(K)^T, lanes 32..63 from sq into phi(sQ) (plus their part of the denominators; CENT: each scaled
+// by its order's coefficient gamma_m of the token, and no denominator).  F0 = first global feature.
+template <int NT, bool READOUT, bool CENT, int FB, int F0>
 __device__ __forceinline__ void expand_rows(WideSmem<READOUT, FB>& sm, int b, int g, int l, const float (&x)[kDK],
-                                            bool valid) {
+                                            bool valid, const f32x4& cq) {
   constexpr int FP = FB / kProd;
   constexpr int L0 = F0 % FB;  // first block row of this producer
   const int tk = l & 31;
@@ -172,6 +191,13 @@ __device__ __forceinline__ void expand_rows(WideSmem<READOUT, FB>& sm, int b, in
     if constexpr (F0 == 0) f[0] = valid ? 1.f : 0.f;  // the constant feature of a token past the end
 #pragma unroll
     for (int i = 0; i < FP; ++i) sm.phikt[b][L0 + i][tk] = f[i];
+  } else if constexpr (READOUT && CENT) {
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((f[I] *= cq[feature_order<NT, F0 + I>()]), ...);
+    }(std::make_integer_sequence<int, FP>{});
+#pragma unroll
+    for (int u = 0; u < FP / 4; ++u)
+      *reinterpret_cast<f32x4*>(&sm.phiq[b][tk][L0 + 4 * u]) = f32x4{f[4 * u], f[4 * u + 1], f[4 * u + 2], f[4 * u + 3]};
   } else if constexpr (READOUT) {
     float den = 0.f;
 #pragma unroll
@@ -188,12 +214,18 @@ __device__ __forceinline__ void expand_rows(WideSmem<READOUT, FB>& sm, int b, in
 }
 
 // Producer g prepares the chunk in buffer b from its inputs.
-template <int NT, typename E, bool READOUT>
-__device__ __forceinline__ void wide_produce(WideSmem<READOUT, block_features<NT>()>& sm, const WideIn<E>& in, int b,
-                                             int fb, int g, int l, int nv, float scale) {
+template <int NT, typename E, bool READOUT, bool CENT>
+__device__ __forceinline__ void wide_produce(WideSmem<READOUT, block_features<NT>()>& sm, const WideIn<E, CENT>& in,
+                                             int b, int fb, int g, int l, int nv, float scale, float* zrow) {
   constexpr int NB = n_blocks<NT>(), FB = block_features<NT>(), FP = FB / kProd;
   const int tk = l & 31, h = l >> 5, l16 = l & 15, lg = l >> 4;
   const bool valid = tk < nv;
+  if constexpr (!READOUT && CENT) {
+    // state pass before an expanded-softmax readout (one block): z of the piece before this chunk,
+    // at every other chunk (the coefficient kernel works on 64 tokens)
+    const int row = FP * g + l;
+    if (zrow && l < FP && row < FeatureTable<NT, kDK>::W) zrow[row] = sm.z[row];
+  }
   {
     float x[kDK];
     // k rows of tokens past the end are zero (their features vanish except the constant one)
@@ -201,7 +233,7 @@ __device__ __forceinline__ void wide_produce(WideSmem<READOUT, block_features<NT
 #pragma unroll
     for (int d = 0; d < kDK; ++d) x[d] = sx * in.row.get(d);
     dispatch_index<0, NB * kProd>(fb * kProd + g, [&](auto I) {
-      expand_rows<NT, READOUT, FB, decltype(I)::value * FP>(sm, b, g, l, x, valid);
+      expand_rows<NT, READOUT, CENT, FB, decltype(I)::value * FP>(sm, b, g, l, x, valid, in.cq);
     });
   }
   // V^T: columns 16g + 8h .. + 7 of token tk
@@ -219,13 +251,18 @@ __device__ __forceinline__ void wide_produce(WideSmem<READOUT, block_features<NT
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = 16 * jt + 4 * lg + r, i = 16 * it + l16;
-        wt[r] = (jt < it || j <= i) ? taylor_kernel<NT>(scale * sc[r]) : 0.f;
+        const float s = scale * sc[r];
+        // CENT: gamma_0 + gamma_1 s + gamma_2 s^2 / 2 of query i (gamma_2 = 0 at order 1)
+        const float poly = CENT ? fmaf(s, fmaf(0.5f * s, in.csq[2], in.csq[1]), in.csq[0]) : taylor_kernel<NT>(s);
+        wt[r] = (jt < it || j <= i) ? poly : 0.f;
       }
       sm.a[b][g][l] = wt;
-      f32x4 cs = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!CENT) {
+        f32x4 cs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) cs = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, wt[r], cs, 0, 0, 0);
-      if (lg == 0) sm.den_intra[b][g][l16] = cs[0];
+        for (int r = 0; r < 4; ++r) cs = __builtin_amdgcn_mfma_f32_16x16x4f32(1.0f, wt[r], cs, 0, 0, 0);
+        if (lg == 0) sm.den_intra[b][g][l16] = cs[0];
+      }
     }
   }
   // z_{<next} = z + row sums of this producer's phi(K)^T rows (written by this wave above; a wave's
@@ -264,7 +301,7 @@ __device__ __forceinline__ void piece_state(const WideIO& io, const SeqPiece& pc
 
 // The pieces of one workgroup (see SeqMap: a segment of one pair, or the pieces of one token
 // range of one head), one feature block; grid = (segments or ranges, pairs or heads, blocks).
-template <int NT, typename E, bool READOUT, bool PACKED>
+template <int NT, typename E, bool READOUT, bool PACKED, bool CENT>
 __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                                 const E* __restrict__ v, WideIO io, SeqMap seq,
                                                                 int L, float scale) {
@@ -287,6 +324,11 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(const E* __restr
       const int nch = (pc.n + kCS - 1) / kCS;
       auto nv_of = [&](int c) { return min(kCS, pc.n - c * kCS); };
       auto tok_of = [&](int c) { return pc.tok + (long long)c * kCS; };
+      auto zrow = [&](int c) {
+        return CENT && !READOUT && c % 2 == 0
+                   ? io.zc + (seq.chunk_index(pc, 0, 2 * kCS) + c / 2) * FeatureTable<NT, kDK>::W
+                   : nullptr;
+      };
       const float* init;
       float* dst;
       piece_state<READOUT>(io, pc, init, dst);
@@ -295,27 +337,27 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(const E* __restr
         const int a = f0 + FP * g + l;
         sm.z[FP * g + l] = (init && a < W) ? init[(long long)W * kDV + a] : 0.f;
       }
-      WideIn<E> pa, pb;
-      pa.load(q, k, v, tok_of(0), nv_of(0), l, g, READOUT);
+      WideIn<E, CENT> pa, pb;
+      pa.load(q, k, v, io.coef, tok_of(0), nv_of(0), l, g, READOUT);
       __syncthreads();
-      if (nch > 1) pb.load(q, k, v, tok_of(1), nv_of(1), l, g, READOUT);
-      wide_produce<NT, E, READOUT>(sm, pa, 0, fb, g, l, nv_of(0), scale);
+      if (nch > 1) pb.load(q, k, v, io.coef, tok_of(1), nv_of(1), l, g, READOUT);
+      wide_produce<NT, E, READOUT, CENT>(sm, pa, 0, fb, g, l, nv_of(0), scale, zrow(0));
       __syncthreads();  // chunk 0 ready
       int c = 0;
       for (; c + 3 < nch; c += 2) {
-        pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
-        wide_produce<NT, E, READOUT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale);
+        pa.load(q, k, v, io.coef, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
+        wide_produce<NT, E, READOUT, CENT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale, zrow(c + 1));
         __syncthreads();
-        pb.load(q, k, v, tok_of(c + 3), nv_of(c + 3), l, g, READOUT);
-        wide_produce<NT, E, READOUT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale);
+        pb.load(q, k, v, io.coef, tok_of(c + 3), nv_of(c + 3), l, g, READOUT);
+        wide_produce<NT, E, READOUT, CENT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale, zrow(c + 2));
         __syncthreads();
       }
       // nch - c phases remain (1 to 3); chunks c+1 and c+2 may still need preparing
-      if (c + 2 < nch) pa.load(q, k, v, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
-      if (c + 1 < nch) wide_produce<NT, E, READOUT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale);
+      if (c + 2 < nch) pa.load(q, k, v, io.coef, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
+      if (c + 1 < nch) wide_produce<NT, E, READOUT, CENT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale, zrow(c + 1));
       __syncthreads();
       if (c + 1 < nch) {
-        if (c + 2 < nch) wide_produce<NT, E, READOUT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale);
+        if (c + 2 < nch) wide_produce<NT, E, READOUT, CENT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale, zrow(c + 2));
         __syncthreads();
         if (c + 2 < nch) __syncthreads();
       }
@@ -389,16 +431,20 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(const E* __restr
         }
       }
       if constexpr (READOUT && n_blocks<NT>() == 1) {
-        // a single block: the outputs are final (columns 16w + 4lg .. + 3 of token 16it + l16)
+        // a single block: the outputs are final (columns 16w + 4lg .. + 3 of token 16it + l16); the
+        // expanded-softmax readout has no normaliser (its weights already sum to one)
 #pragma unroll
         for (int it = 0; it < kNIT; ++it) {
           const int i = 16 * it + l16;
-          float d = 0.f;
+          float d = 1.f;
+          if constexpr (!CENT) {
+            d = 0.f;
 #pragma unroll
-          for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
-          for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][it * (it + 1) / 2 + jt][l16];
+            for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
+            for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][it * (it + 1) / 2 + jt][l16];
+          }
           if (i < nv) {
-            const float inv = 1.0f / d;
+            const float inv = CENT ? 1.0f : 1.0f / d;
             const f32x4 r = O[it];
             *reinterpret_cast<f32x4*>(io.out + (tok0 + i) * kDV + 16 * w + 4 * lg) =
                 f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
@@ -473,28 +519,45 @@ int wide_segments(int BH, int nb, int nchunk, bool outputs) {
 
 struct WideLayout {
   int L;  // piece (segment or range) length
-  long long gx, nslot, slot_floats, part_floats;
+  long long gx, nslot, slot_floats, part_floats, coef_floats, zc_floats;
+  bool multi;  // state pass + scan before the readout (several pieces per pair, or the expanded-softmax
+               // readout, whose coefficient kernel reads the per-chunk z the state pass writes)
 };
 
 template <int NT>
 WideLayout wide_layout(const Shape& s, int BH, const SeqMap& seq, bool outputs) {
   constexpr int NB = n_blocks<NT>();
   WideLayout lay;
+  const bool cent = outputs && s.readout == 1;
+  const int unit = cent ? 2 * kCS : kCS;  // the coefficient kernel takes 64-token chunks
   if (seq.packed) {
     // ragged: ranges of the packed token axis, about target workgroups over heads and blocks
     const long long target = wide_target(outputs);
     const long long per = std::max<long long>(1, (seq.tokens(BH) * NB + target - 1) / target);
-    lay.L = (int)std::min<long long>((per + kCS - 1) / kCS * kCS, 1 << 30);
+    lay.L = (int)std::min<long long>((per + unit - 1) / unit * unit, 1 << 30);
   } else {
-    const int nchunk = cdiv(seq.N, kCS);
-    lay.L = cdiv(nchunk, wide_segments(BH, NB, nchunk, outputs)) * kCS;
+    const int nchunk = cdiv(seq.N, unit);
+    lay.L = cdiv(nchunk, wide_segments(BH, NB, nchunk, outputs)) * unit;
   }
   lay.gx = seq.grid_x(lay.L);
   lay.nslot = seq.row_slots(lay.L);
-  // slots are needed for several pieces per pair, and always for a state-only call (the scan sums them)
-  lay.slot_floats = (lay.gx > 1 || !outputs) ? seq.rows(BH) * lay.nslot * s.stride : 0;
+  lay.multi = lay.gx > 1 || cent;
+  // slots are needed for a state pass, and always for a state-only call (the scan sums them)
+  lay.slot_floats = (lay.multi || !outputs) ? seq.rows(BH) * lay.nslot * s.stride : 0;
   lay.part_floats = (outputs && NB > 1) ? (long long)NB * seq.tokens(BH) * (kDV + 1) : 0;
+  lay.coef_floats = cent ? 4 * seq.tokens(BH) : 0;
+  lay.zc_floats = cent ? seq.chunk_count(BH, 2 * kCS) * FeatureTable<NT, kDK>::W : 0;
   return lay;
+}
+
+// The readout or state-pass kernel for a call (the expanded-softmax readout exists for n = 2, 3 with
+// float32 inputs).
+template <int NT, typename E, bool READOUT>
+auto wide_kernel_for(bool packed, bool cent) {
+  if constexpr ((NT == 2 || NT == 3) && std::is_same_v<E, float>) {
+    if (cent) return packed ? prefill_wide_kernel<NT, E, READOUT, true, true> : prefill_wide_kernel<NT, E, READOUT, false, true>;
+  }
+  return packed ? prefill_wide_kernel<NT, E, READOUT, true, false> : prefill_wide_kernel<NT, E, READOUT, false, false>;
 }
 
 long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
@@ -502,31 +565,41 @@ long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
 template <int NT, typename E>
 int wide_run(const PrefillArgs& a) {
   constexpr int NB = n_blocks<NT>();
-  const bool outputs = a.o != nullptr;
+  const bool outputs = a.o != nullptr, cent = a.s.readout == 1;
   const WideLayout lay = wide_layout<NT>(a.s, a.BH, a.seq, outputs);
   const long long tokens = a.seq.tokens(a.BH);
   float* ws = (float*)a.ws;
   float* slots = ws;
   float* part_num = ws + round_up(lay.slot_floats, 64);
   float* part_den = part_num + (long long)NB * tokens * kDV;
+  float* coef = part_num + round_up(lay.part_floats, 64);
+  float* zc = coef + round_up(lay.coef_floats, 64);
   const E* q = (const E*)a.q;
   const E* k = (const E*)a.k;
   const E* v = (const E*)a.v;
   const long long elems = FeatureTable<NT, kDK>::W * (long long)(kDV + 1);
-  const int multi = lay.gx > 1;
+  const int multi = lay.multi;
   const dim3 grid((unsigned)lay.gx, (unsigned)a.seq.grid_y(a.BH), NB), block(kThreads);
   if (!outputs || multi) {
-    const WideIO io{slots, nullptr, nullptr, nullptr, nullptr, a.s.stride, lay.nslot, tokens, multi};
-    auto state_pass = a.seq.packed ? prefill_wide_kernel<NT, E, false, true> : prefill_wide_kernel<NT, E, false, false>;
-    state_pass<<<grid, block, 0, a.stream>>>(q, k, v, io, a.seq, lay.L, a.s.scale);
+    const bool zpass = cent && outputs;
+    const WideIO io{slots, nullptr, nullptr, nullptr, nullptr, a.s.stride, lay.nslot, tokens, multi, nullptr,
+                    zpass ? zc : nullptr};
+    wide_kernel_for<NT, E, false>(a.seq.packed, zpass)<<<grid, block, 0, a.stream>>>(q, k, v, io, a.seq, lay.L,
+                                                                                    a.s.scale);
     if (hipGetLastError() != hipSuccess) return -3;
     if (seg_scan_launch(slots, a.state, a.BH, lay.nslot, a.s.stride, elems, outputs, a.seq, lay.L, a.stream))
       return -3;
     if (!outputs) return 0;
   }
-  const WideIO io{slots, multi ? nullptr : a.state, part_num, part_den, a.o, a.s.stride, lay.nslot, tokens, multi};
-  auto readout = a.seq.packed ? prefill_wide_kernel<NT, E, true, true> : prefill_wide_kernel<NT, E, true, false>;
-  readout<<<grid, block, 0, a.stream>>>(q, k, v, io, a.seq, lay.L, a.s.scale);
+  if (cent) {
+    // per-token coefficients from the prefixes the readout starts from
+    const CenteredPlan cp{lay.L, lay.nslot, slots, multi, zc, 2 * kCS, reinterpret_cast<float4*>(coef)};
+    if (const int rc = centered_coef_launch(a, cp)) return rc;
+  }
+  const WideIO io{slots,  multi ? nullptr : a.state, part_num, part_den, a.o, a.s.stride, lay.nslot, tokens, multi,
+                  cent ? coef : nullptr, nullptr};
+  wide_kernel_for<NT, E, true>(a.seq.packed, cent)<<<grid, block, 0, a.stream>>>(q, k, v, io, a.seq, lay.L,
+                                                                                a.s.scale);
   if (hipGetLastError() != hipSuccess) return -3;
   if (NB == 1) return 0;  // the outputs are final
   wide_reduce_kernel<<<dim3((unsigned)cdiv(tokens * 16, 256)), dim3(256), 0, a.stream>>>(part_num, part_den, a.o,
@@ -543,7 +616,10 @@ bool prefill_wide_has(int nt, int dk, int dv, int dtype) {
 
 // An upper bound over both uses (with and without outputs): the query does not know which follows.
 long long prefill_wide_ws_bytes(const Shape& s, int BH, const SeqMap& seq) {
-  auto bytes = [](const WideLayout& lay) { return (round_up(lay.slot_floats, 64) + lay.part_floats) * 4; };
+  auto bytes = [](const WideLayout& lay) {
+    return (round_up(lay.slot_floats, 64) + round_up(lay.part_floats, 64) + round_up(lay.coef_floats, 64) +
+            lay.zc_floats) * 4;
+  };
   auto both = [&](auto layout) { return std::max(bytes(layout(true)), bytes(layout(false))); };
   switch (s.nt) {
     case 1: return both([&](bool o) { return wide_layout<1>(s, BH, seq, o); });

@@ -146,6 +146,29 @@ def test_prefill_validation():
     assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, cfg) == rs.TAYLOR_OK
 
 
+def test_readout_field():
+    # TAYLOR_READOUT_CENTERED: orders 1, 2 (n_terms 2, 3) at d_k = 16, d_v = 64, either input type
+    C = rs.TAYLOR_READOUT_CENTERED
+    for n in (2, 3):
+        for dt in (rs.TAYLOR_F32, rs.TAYLOR_BF16):
+            cfg = rs.config(n, 16, 64, 0, 1.0, dt, C)
+            assert rs.taylor_supported(cfg) == rs.TAYLOR_OK
+            assert rs.taylor_prefill_workspace_bytes(cfg, 4, 16, 8192) > 0
+            assert rs.taylor_prefill_varlen_workspace_bytes(cfg, 8, 16, 4096, 10000) > 0
+    for n in (1, 4, 5):
+        assert rs.taylor_supported(rs.config(n, 16, 64, 0, 1.0, 0, C)) == rs.TAYLOR_ERR_UNSUPPORTED
+    assert rs.taylor_supported(rs.config(3, 8, 32, 0, 1.0, 0, C)) == rs.TAYLOR_ERR_UNSUPPORTED
+    assert rs.taylor_supported(rs.config(3, 16, 64, 0, 1.0, 0, 2)) == rs.TAYLOR_ERR_INVALID_ARG
+    assert rs.taylor_supported(rs.config(3, 16, 64, 0, 1.0, 0, -1)) == rs.TAYLOR_ERR_INVALID_ARG
+    # the state layout does not depend on the readout
+    assert rs.taylor_state_stride(rs.config(3, 16, 64, 0, 1.0, 0, C)) == rs.taylor_state_stride(rs.config(3, 16, 64))
+    L = rs.lib()
+    bad = rs.config(3, 8, 32, 0, 1.0, 0, C)
+    assert L.taylor_attn_decode_step(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, ctypes.byref(bad), None) == \
+        rs.TAYLOR_ERR_UNSUPPORTED
+    assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, bad) == rs.TAYLOR_ERR_UNSUPPORTED
+
+
 def test_varlen_workspace_bytes():
     cfg = rs.config(3, 16, 64, 64, 1.0, rs.TAYLOR_BF16)
     assert rs.taylor_prefill_varlen_workspace_bytes(cfg, 8, 16, 4096, 0) == 0
