@@ -33,6 +33,8 @@ Modules:
   used only to pin the pages' claims.
 * ``centered`` -- direct O(N^2) causal attention with the softmax expanded about
   the mean score (orders 1, 2), and the logsumexp series it is the gradient of.
+* ``backward`` -- gradients of the truncated-kernel attention (dq, dk, dv, and the
+  incoming state's), differentiated by hand from the definition.
 
 Every function that has no independent pin says "parity unpinned" in its
 docstring; at present every function is pinned (see tests/test_oracle_*.py).
@@ -41,6 +43,7 @@ docstring; at present every function is pinned (see tests/test_oracle_*.py).
 from .tables import monomials, exponents, coefficient, feature_table, index_table, coef_table, feature_width
 from .features import features, features_by_order
 from . import centered
+from .backward import attention_backward, attention_backward_from_state
 from .centered import centered_weights, centered_attention, centered_attention_rows, lse_series
 from .attention import (
     truncated_kernel,
@@ -60,4 +63,5 @@ __all__ = [
     "truncated_kernel", "truncated_attention", "truncated_attention_rows", "softmax_attention",
     "state", "recurrent", "chunked_state", "decode_reference", "batched",
     "centered", "centered_weights", "centered_attention", "centered_attention_rows", "lse_series",
+    "attention_backward", "attention_backward_from_state",
 ]

@@ -1,0 +1,92 @@
+"""Gradients of truncated-kernel causal attention (oracle; test infrastructure only).
+
+Source: "Expanding Attention" (Huang, arXiv:2610.20637), Abstract, for the forward
+definition (see ``oracle.attention``); the pages are silent on gradients, so this
+module differentiates that definition by hand, and the tests pin it against
+central finite differences of the forward oracle.
+
+For one head, with w_ij = K_n(s_ij), s_ij = sigma q_i . k_j (j <= i),
+den_i = sum_j w_ij, o_i = sum_j w_ij v_j / den_i and an upstream gradient g_i:
+
+    dw_ij = g_i . (v_j - o_i) / den_i          (j <= i)
+    dv_j  = sum_{i>=j} w_ij g_i / den_i
+    ds_ij = dw_ij K_{n-1}(s_ij)                  (K_n' = K_{n-1}; K_0 = 0)
+    dq_i  = sigma sum_{j<=i} ds_ij k_j
+    dk_j  = sigma sum_{i>=j} ds_ij q_i
+
+``attention_backward`` writes these out directly in O(N^2).  With a state S0, z0
+carried in from earlier tokens (the forward's ``recurrent`` with ``state0``), the
+extra history adds phi(sigma q_i) . [S0 | z0] to the numerator and denominator of
+every row; ``attention_backward_from_state`` covers that case and also returns the
+gradient with respect to [S0 | z0]:
+
+    dS0 = sum_i phi(sigma q_i) g_i^T / den_i,   dz0 = - sum_i phi(sigma q_i) (g_i . o_i) / den_i
+"""
+
+import numpy as np
+
+from .attention import truncated_kernel
+from .features import features
+from .tables import feature_table
+
+
+def _kernel_derivative(s, n):
+    """K_n'(s) = K_{n-1}(s) (zero for n = 1)."""
+    if n == 1:
+        return np.zeros_like(np.asarray(s, dtype=np.float64))
+    return truncated_kernel(s, n - 1)
+
+
+def attention_backward(q, k, v, g, n, scale=1.0):
+    """(dq, dk, dv) of L = sum_i g_i . o_i for one head, from an empty history; float64."""
+    return attention_backward_from_state(q, k, v, g, n, scale)[:3]
+
+
+def attention_backward_from_state(q, k, v, g, n, scale=1.0, state0=None):
+    """(dq, dk, dv, dstate0) with an incoming state [W, d_v + 1] (zero if None); float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    N, dv_ = v.shape
+    s = scale * (q @ k.T)
+    mask = np.tril(np.ones((N, N), dtype=bool))
+    w = np.where(mask, truncated_kernel(s, n), 0.0)
+    num = w @ v
+    den = w.sum(axis=1)
+    fq = features(scale * q, n)
+    if state0 is not None:
+        st = np.asarray(state0, dtype=np.float64)
+        num = num + fq @ st[:, :dv_]
+        den = den + fq @ st[:, dv_]
+    o = num / den[:, None]
+    gh = g / den[:, None]                      # dL/dnum_i
+    delta = np.sum(g * o, axis=1) / den        # -dL/dden_i
+    dw = np.where(mask, gh @ v.T - delta[:, None], 0.0)
+    dv = w.T @ gh
+    ds = dw * _kernel_derivative(s, n)
+    dq = scale * (ds @ k)
+    dk = scale * (ds.T @ q)
+    if state0 is not None:
+        # the state enters through phi(sigma q_i): d/dq_i of phi(a_i) . (S0 gh_i - z0 delta_i), a = sigma q
+        y = st[:, :dv_] @ gh.T - np.outer(st[:, dv_], delta)  # [W, N]
+        dq = dq + scale * _feature_vjp(scale * q, y.T, n)
+    dstate = np.concatenate([fq.T @ gh, -(fq.T @ delta)[:, None]], axis=1)
+    return dq, dk, dv, dstate
+
+
+def _feature_vjp(x, y, n):
+    """sum_f y_f d phi_f(x) / dx, row by row: d/dx_d of c prod_{t in tup} x_t is c times the number of
+    times d occurs in tup times the product over tup with one occurrence of d removed."""
+    x = np.asarray(x, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    out = np.zeros_like(x)
+    for f, (m, tup, c) in enumerate(feature_table(n, x.shape[1])):
+        for d in set(tup):
+            rest = list(tup)
+            rest.remove(d)
+            term = np.full(x.shape[0], c * tup.count(d))
+            for t in rest:
+                term = term * x[:, t]
+            out[:, d] += y[:, f] * term
+    return out
