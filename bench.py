@@ -18,8 +18,8 @@ events on the stream it runs on.
 Secondary timings after the timed steps (each can be skipped by a flag): decode over
 512 sequences whose states exceed the last-level cache, the float32 prefill at
 n = 1..5 (B=1, H=16, N=16,384), the expanded-softmax readout (orders 1, 2) on the
-main prefill inputs, and a ragged-batch prefill (32 prompts of seeded lengths
-1..2,047, 16 heads, bfloat16, n = 3).
+main prefill inputs, the backward (gradients of that prefill), and a ragged-batch
+prefill (32 prompts of seeded lengths 1..2,047, 16 heads, bfloat16, n = 3).
 """
 
 import argparse
@@ -257,6 +257,38 @@ def centered_prefill(rs, torch, dev, q, k, v, reps=5):
     return res
 
 
+def backward_prefill(rs, torch, dev, q, k, v, reps=3):
+    """taylor_attn_prefill_backward on the main step's prefill inputs (B4 x H16 x N8192, bfloat16, n = 3),
+    with outputs from the float32 forward and a seeded upstream gradient; HIP events.  Algorithmic
+    flops per token-head (float32 matrix work, unpadded W = 153): state pass 2*W*65, pass A
+    (S^T gh, S update, G update) 6*W*64 + 2*W, pass B (G^T phi(k), G v, G update) 6*W*64, plus the
+    intra-chunk products 4*(C+1)/2*(16 + 64) at C = 16."""
+    B, H, N = k.shape[:3]
+    cfg = rs.config(NT, DK, DV, 0, 1.0, rs.TAYLOR_BF16)
+    f32 = rs.config(NT, DK, DV, 0, 1.0, rs.TAYLOR_F32)
+    o = torch.empty((B, H, N, DV), dtype=torch.float32, device=dev)
+    rs.taylor_attn_prefill(q.float(), k.float(), v.float(), o, None, rs.new_workspace(f32, B, H, N, dev), f32)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    g = torch.randn((B, H, N, DV), generator=gen, device=dev)
+    dq = torch.empty((B, H, N, DK), device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(o)
+    ws = rs.new_backward_workspace(cfg, B, H, N, dev)
+    rs.taylor_attn_prefill_backward(q, k, v, o, g, None, None, dq, dk, dv, ws, cfg)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        rs.taylor_attn_prefill_backward(q, k, v, o, g, None, None, dq, dk, dv, ws, cfg)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    flops = B * H * N * (2 * W * (DV + 1) + 12 * W * DV + 2 * W + 4 * 17 / 2 * (DK + DV))
+    return {"us": us, "tok_s": B * N / us * 1e6, "TFLOPs": flops / us / 1e6,
+            "frac_fp32_mfma": flops / us / 1e6 / FP32_PEAK_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +303,7 @@ def main():
     ap.add_argument("--no-order-sweep", action="store_true", help="skip the n = 1..5 float32 prefill timings")
     ap.add_argument("--no-varlen", action="store_true", help="skip the ragged-batch prefill timing")
     ap.add_argument("--no-centered", action="store_true", help="skip the expanded-softmax readout timing")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (scale reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -444,6 +477,9 @@ def main():
     if not args.no_centered:
         log("expanded-softmax readout (orders 1, 2) on the prefill inputs")
         out["prefill_centered_bf16_B4xH16xN8192"] = centered_prefill(rs, torch, dev, pq, pk, pv)
+    if not args.no_backward:
+        log("backward (gradients of the prefill)")
+        out["backward_bf16_B4xH16xN8192"] = backward_prefill(rs, torch, dev, pq, pk, pv)
     if not args.no_varlen:
         log("ragged-batch prefill (32 prompts, 16 heads, bf16)")
         out["prefill_varlen_bf16_32seqs_H16"] = varlen_prefill(rs, synth, torch, dev)

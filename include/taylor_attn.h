@@ -188,6 +188,34 @@ int taylor_attn_prefill_varlen(const void* q, const void* k, const void* v, floa
                                const int32_t* cu_seqlens, int n_seqs, int H, int max_seqlen, int64_t total_tokens,
                                const taylor_config* cfg, hipStream_t stream);
 
+/* Bytes of device workspace taylor_attn_prefill_backward needs (may be 0).  Host
+ * only.  Negative taylor_status if cfg or sizes are invalid, or
+ * TAYLOR_ERR_UNSUPPORTED where no backward kernel is compiled (below). */
+int64_t taylor_prefill_backward_workspace_bytes(const taylor_config* cfg, int B, int H, int N);
+
+/* Gradients of one taylor_attn_prefill call (truncated-kernel readout; the pages
+ * give no gradients -- they are the derivatives of the Abstract's definition).
+ * With L a loss of the outputs o = taylor_attn_prefill(q, k, v | state):
+ *   q, k, v : the forward's inputs, [B,H,N,d_k], [B,H,N,d_k], [B,H,N,d_v] in cfg->in_dtype;
+ *   o       : the forward's outputs [B,H,N,d_v] float32;
+ *   g       : dL/do, [B,H,N,d_v] float32;
+ *   state   : the forward's incoming state [B,H,stride] (NULL: empty history);
+ *             read only;
+ *   dstate  : [B,H,stride] float32 in/out, or NULL.  On entry dL/d(the final
+ *             state the forward returned) (NULL: zero); on return dL/d(the
+ *             incoming state), in the state layout (S rows then z);
+ *   dq, dk, dv : [B,H,N,d_k], [B,H,N,d_k], [B,H,N,d_v] float32 outputs (dq, dk
+ *             include the score scale);
+ *   workspace : taylor_prefill_backward_workspace_bytes(cfg, B, H, N) bytes.
+ * So a sequence prefilled in pieces is differentiated piece by piece in reverse,
+ * passing dstate along.  Compiled for cfg->readout = TAYLOR_READOUT_KERNEL,
+ * n_terms = 1..3, d_k = 16, d_v = 64, either input type (float32 arithmetic);
+ * otherwise TAYLOR_ERR_UNSUPPORTED.  B*H == 0 or N == 0 is a no-op (dstate
+ * unchanged).  Calls sharing a workspace must not overlap. */
+int taylor_attn_prefill_backward(const void* q, const void* k, const void* v, const float* o, const float* g,
+                                 const float* state, float* dstate, float* dq, float* dk, float* dv, void* workspace,
+                                 int B, int H, int N, const taylor_config* cfg, hipStream_t stream);
+
 /* One decode step per (b, h): S += phi(k_t) [v_t | 1]^T (one rank-one update),
  * then o_t = (phi(scale*q_t)^T S)[:d_v] / (phi(scale*q_t)^T z) -- the update comes
  * first, so the current token attends to itself.  (TAYLOR_READOUT_CENTERED: the

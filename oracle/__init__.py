@@ -43,7 +43,7 @@ docstring; at present every function is pinned (see tests/test_oracle_*.py).
 from .tables import monomials, exponents, coefficient, feature_table, index_table, coef_table, feature_width
 from .features import features, features_by_order
 from . import centered
-from .backward import attention_backward, attention_backward_from_state
+from .backward import attention_backward, attention_backward_from_state, attention_backward_dq_rows
 from .centered import centered_weights, centered_attention, centered_attention_rows, lse_series
 from .attention import (
     truncated_kernel,
@@ -63,5 +63,5 @@ __all__ = [
     "truncated_kernel", "truncated_attention", "truncated_attention_rows", "softmax_attention",
     "state", "recurrent", "chunked_state", "decode_reference", "batched",
     "centered", "centered_weights", "centered_attention", "centered_attention_rows", "lse_series",
-    "attention_backward", "attention_backward_from_state",
+    "attention_backward", "attention_backward_from_state", "attention_backward_dq_rows",
 ]

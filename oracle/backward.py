@@ -75,6 +75,24 @@ def attention_backward_from_state(q, k, v, g, n, scale=1.0, state0=None):
     return dq, dk, dv, dstate
 
 
+def attention_backward_dq_rows(q, k, v, g, n, rows, scale=1.0):
+    """dq at the query rows ``rows`` only (empty history): O(N) per row, for sampled checks at sizes
+    where the full O(N^2) pass is too large.  g is [N, d_v]; only its rows in ``rows`` matter."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    out = np.empty((len(rows), q.shape[1]))
+    for r, i in enumerate(np.asarray(rows, dtype=np.int64)):
+        s = scale * (k[: i + 1] @ q[i])
+        w = truncated_kernel(s, n)
+        den = w.sum()
+        o = (w @ v[: i + 1]) / den
+        dw = (v[: i + 1] @ g[i] - g[i] @ o) / den
+        out[r] = scale * ((dw * _kernel_derivative(s, n)) @ k[: i + 1])
+    return out
+
+
 def _feature_vjp(x, y, n):
     """sum_f y_f d phi_f(x) / dx, row by row: d/dx_d of c prod_{t in tup} x_t is c times the number of
     times d occurs in tup times the product over tup with one occurrence of d removed."""

@@ -40,6 +40,8 @@ EXPORTS = (
     "taylor_attn_prefill",
     "taylor_prefill_varlen_workspace_bytes",
     "taylor_attn_prefill_varlen",
+    "taylor_prefill_backward_workspace_bytes",
+    "taylor_attn_prefill_backward",
     "taylor_attn_decode_step",
 )
 
@@ -101,6 +103,8 @@ def lib():
         "taylor_attn_prefill": (i, [p, p, p, p, p, p, i, i, i, cfgp, p]),
         "taylor_prefill_varlen_workspace_bytes": (i64, [cfgp, i, i, i, i64]),
         "taylor_attn_prefill_varlen": (i, [p, p, p, p, p, p, p, i, i, i, i64, cfgp, p]),
+        "taylor_prefill_backward_workspace_bytes": (i64, [cfgp, i, i, i]),
+        "taylor_attn_prefill_backward": (i, [p, p, p, p, p, p, p, p, p, p, p, i, i, i, cfgp, p]),
         "taylor_attn_decode_step": (i, [p, p, p, p, p, i, i, cfgp, p]),
     }
     for name, (res, args) in sig.items():
@@ -194,6 +198,11 @@ def taylor_prefill_varlen_workspace_bytes(cfg, n_seqs, H, max_seqlen, total_toke
         "taylor_prefill_varlen_workspace_bytes")
 
 
+def taylor_prefill_backward_workspace_bytes(cfg, B, H, N):
+    return _check_nonneg(lib().taylor_prefill_backward_workspace_bytes(ctypes.byref(cfg), B, H, N),
+                         "taylor_prefill_backward_workspace_bytes")
+
+
 # ---- device entry points ------------------------------------------------------------------------
 
 
@@ -221,6 +230,27 @@ def taylor_attn_prefill_varlen(q, k, v, o, state, workspace, cu_seqlens, max_seq
                                           _ptr(cu_seqlens), n_seqs, H, int(max_seqlen), T, ctypes.byref(cfg),
                                           _stream(stream, k.device))
     _check(rc, "taylor_attn_prefill_varlen")
+
+
+def taylor_attn_prefill_backward(q, k, v, o, g, state, dstate, dq, dk, dv, workspace, cfg, stream=None):
+    """Gradients of a prefill over [B, H, N, d] inputs: dq, dk, dv (float32, written); dstate in/out
+    (gradient of the final state in, of the incoming state out) or None; state: the forward's
+    incoming state or None."""
+    B, H, N = k.shape[:3]
+    rc = lib().taylor_attn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(g), _ptr(state), _ptr(dstate),
+                                            _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), B, H, N,
+                                            ctypes.byref(cfg), _stream(stream, k.device))
+    _check(rc, "taylor_attn_prefill_backward")
+
+
+def new_backward_workspace(cfg, B, H, N, device):
+    """A workspace tensor of taylor_prefill_backward_workspace_bytes() bytes (None when none is needed)."""
+    import torch
+
+    n = taylor_prefill_backward_workspace_bytes(cfg, B, H, N)
+    if n == 0:
+        return None
+    return torch.empty(((n + 15) // 16 * 16,), dtype=torch.uint8, device=device)
 
 
 def taylor_attn_decode_step(q, k, v, o, state, cfg, stream=None):

@@ -10,6 +10,7 @@
 
 #include "../../include/taylor_attn.h"
 #include "common.hpp"
+#include "backward.hpp"
 #include "launch.hpp"
 #include "prefill_mfma.hpp"
 #include "prefill_wide.hpp"
@@ -252,6 +253,55 @@ int taylor_attn_prefill_varlen(const void* q, const void* k, const void* v, floa
   if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return TAYLOR_ERR_INVALID_ARG;
   return prefill_common(s, chunk_of(cfg), q, k, v, o, state, workspace, BH,
                         packed_map(cu_seqlens, n_seqs, H, max_seqlen, total_tokens), stream);
+}
+
+int64_t taylor_prefill_backward_workspace_bytes(const taylor_config* cfg, int B, int H, int N) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if (s.readout != TAYLOR_READOUT_KERNEL || !taylor::backward_has(s.nt, s.dk, s.dv)) return TAYLOR_ERR_UNSUPPORTED;
+  if ((rc = check_sizes(B, H, N)) != TAYLOR_OK) return rc;
+  return taylor::backward_ws_bytes(s, B * H, N);
+}
+
+int taylor_attn_prefill_backward(const void* q, const void* k, const void* v, const float* o, const float* g,
+                                 const float* state, float* dstate, float* dq, float* dk, float* dv, void* workspace,
+                                 int B, int H, int N, const taylor_config* cfg, hipStream_t stream) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if (s.readout != TAYLOR_READOUT_KERNEL || !taylor::backward_has(s.nt, s.dk, s.dv)) return TAYLOR_ERR_UNSUPPORTED;
+  if ((rc = check_sizes(B, H, N)) != TAYLOR_OK) return rc;
+  const int BH = B * H;
+  if (BH == 0) return TAYLOR_OK;
+  if (N == 0) {
+    // no tokens: the incoming state's gradient is the final state's; dstate is left as it is
+    return TAYLOR_OK;
+  }
+  const void* need16[] = {q, k, v, o, g, dq, dk, dv};
+  for (const void* p : need16)
+    if (!p || !aligned16(p)) return TAYLOR_ERR_INVALID_ARG;
+  if ((state && !aligned16(state)) || (dstate && !aligned16(dstate))) return TAYLOR_ERR_INVALID_ARG;
+  if ((long long)(N + 15) / 16 > 0x7fffffffLL / 256) return TAYLOR_ERR_UNSUPPORTED;
+  const long long need = taylor::backward_ws_bytes(s, BH, N);
+  if (need > 0 && (!workspace || !aligned16(workspace))) return TAYLOR_ERR_INVALID_ARG;
+  taylor::BwdArgs a{};
+  a.s = s;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.g = g;
+  a.state = state;
+  a.dstate = dstate;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.ws = workspace;
+  a.BH = BH;
+  a.N = N;
+  a.stream = stream;
+  return map_launch(taylor::backward_launch(a));
 }
 
 int taylor_attn_decode_step(const void* q, const void* k, const void* v, float* o, float* state, int B, int H,

@@ -30,7 +30,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     declared = _header_functions()
-    assert len(declared) == 12
+    assert len(declared) == 14
     assert sorted(rs.EXPORTS) == declared
     out = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(taylor_[a-z_0-9]+)$", out, re.M))
@@ -227,6 +227,50 @@ def test_varlen_validation():
     assert _varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 4, 2, 100, 0, cfg) == rs.TAYLOR_OK
     assert _varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, 2, 100, 0, cfg) == rs.TAYLOR_OK
     assert _varlen(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 4, 0, 100, 300, cfg) == rs.TAYLOR_OK
+
+
+def test_backward_queries_and_validation():
+    L = rs.lib()
+    for n in (1, 2, 3):
+        for dt in (rs.TAYLOR_F32, rs.TAYLOR_BF16):
+            assert rs.taylor_prefill_backward_workspace_bytes(rs.config(n, 16, 64, 0, 1.0, dt), 4, 16, 8192) > 0
+    cfg = rs.config(3, 16, 64)
+    assert rs.taylor_prefill_backward_workspace_bytes(cfg, 0, 16, 8192) == 0
+    assert rs.taylor_prefill_backward_workspace_bytes(cfg, 4, 16, 0) == 0
+    U = rs.TAYLOR_ERR_UNSUPPORTED
+    E = rs.TAYLOR_ERR_INVALID_ARG
+
+    def wsb(c, B=1, H=1, N=64):
+        return L.taylor_prefill_backward_workspace_bytes(ctypes.byref(c) if c else None, B, H, N)
+
+    assert wsb(rs.config(4, 16, 64)) == U
+    assert wsb(rs.config(3, 8, 32)) == U
+    assert wsb(rs.config(3, 16, 64, 0, 1.0, 0, rs.TAYLOR_READOUT_CENTERED)) == U
+    assert wsb(None) == E
+    assert wsb(cfg, -1) == E
+
+    def bwd(args, B=1, H=1, N=64, c=cfg):
+        return L.taylor_attn_prefill_backward(*args, B, H, N, ctypes.byref(c) if c else None, None)
+
+    ok = [FAKE] * 11  # q k v o g state dstate dq dk dv ws
+    for i in (0, 1, 2, 3, 4, 7, 8, 9):  # required pointers
+        a = list(ok)
+        a[i] = None
+        assert bwd(a) == E, i
+        a[i] = MIS
+        assert bwd(a) == E, i
+    for i in (5, 6, 10):  # optional, but aligned when given
+        a = list(ok)
+        a[i] = MIS
+        assert bwd(a) == E, i
+    a = list(ok)
+    a[10] = None
+    assert bwd(a) == E  # workspace required
+    assert bwd(ok, c=None) == E
+    assert bwd(ok, c=rs.config(4, 16, 64)) == U
+    # documented no-ops: no pairs, no tokens
+    assert bwd([None] * 11, B=0) == rs.TAYLOR_OK
+    assert bwd([None] * 11, N=0) == rs.TAYLOR_OK
 
 
 def test_decode_validation():

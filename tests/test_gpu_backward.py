@@ -1,0 +1,222 @@
+"""GPU parity of taylor_attn_prefill_backward against the float64 oracle's gradients.
+
+The oracle's gradients are pinned by finite differences of the forward definition
+(tests/test_oracle_backward.py).  The kernels compute in float32 from the same
+(rounded) inputs, so both input types share the bar: relative Frobenius error per
+tensor at most 1e-5 (2e-5 for dk, whose terms cancel more).  The forward outputs o
+given to the backward are the oracle's, rounded to float32, so that the check
+isolates the backward; one case feeds the library's own forward outputs.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import recurrent_state_amd as rs
+import synth
+from gpu_util import announce
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+DK, DV = 16, 64
+
+
+def _rel(got, ref, floor=0.0):
+    # relative Frobenius error; `floor` bounds the denominator from below where the reference itself
+    # vanishes (a single token has dq = dk = 0: its output is v_0 whatever q_0 and k_0 are)
+    return float(np.linalg.norm(np.asarray(got, dtype=np.float64) - ref) / max(np.linalg.norm(ref), floor))
+
+
+def _cfg(n, dtype, scale=1.0):
+    return rs.config(n, DK, DV, 64, scale, rs.TAYLOR_BF16 if dtype == "bf16" else rs.TAYLOR_F32)
+
+
+def _grad_inputs(x, seed):
+    B, H, N = x.k64.shape[:3]
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((B, H, N, DV)).astype(np.float32)
+
+
+def _run(x, g, o, cfg, state=None, dstate=None):
+    import torch
+
+    q, k, v = x.torch(DEV)
+    B, H, N = k.shape[:3]
+    dq = torch.empty((B, H, N, DK), device=DEV)
+    dk = torch.empty((B, H, N, DK), device=DEV)
+    dv = torch.empty((B, H, N, DV), device=DEV)
+    ws = rs.new_backward_workspace(cfg, B, H, N, DEV)
+    rs.taylor_attn_prefill_backward(q, k, v, torch.from_numpy(o).to(DEV), torch.from_numpy(g).to(DEV), state, dstate,
+                                    dq, dk, dv, ws, cfg)
+    return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+def _oracle_fwd(x, n, scale):
+    o, _ = oracle.batched(oracle.truncated_attention, x.q64, x.k64, x.v64, n, scale)
+    return o
+
+
+def _check(got, x, g, n, scale, tol=1e-5, label=""):
+    B, H = x.k64.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            ref = oracle.attention_backward(x.q64[b, h], x.k64[b, h], x.v64[b, h], g[b, h].astype(np.float64), n, scale)
+            # a tenth of the dv norm (the scale of the gradients): where dq, dk vanish exactly (one
+            # token), float32 cancellation in g . (v - o) leaves about 1e-6 of it
+            floor = 0.1 * np.linalg.norm(ref[2])
+            for name, gt, rf, t in zip(("dq", "dk", "dv"), got, ref, (tol, 2 * tol, tol)):
+                if n == 1 and name != "dv":
+                    assert np.all(gt[b, h] == 0), f"{label} {name} ({b}, {h}) nonzero at n = 1"
+                    continue
+                err = _rel(gt[b, h], rf, floor)
+                assert err <= t, f"{label} {name} ({b}, {h}): rel err {err:.3e}"
+
+
+@pytest.mark.parametrize("n", [1, 2, 3])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_matches_oracle(n, dtype):
+    x = synth.make_qkv(110 + n, 2, 2, 333, DK, DV, dtype)
+    g = _grad_inputs(x, 1100 + n)
+    cfg = _cfg(n, dtype)
+    announce("backward", n, dtype, 333)
+    o = _oracle_fwd(x, n, 1.0).astype(np.float32)
+    _check(_run(x, g, o, cfg), x, g, n, 1.0, label="backward")
+
+
+@pytest.mark.parametrize("N", [1, 15, 16, 17, 100])
+def test_backward_short_lengths(N):
+    x = synth.make_qkv(115, 1, 3, N, DK, DV)
+    g = _grad_inputs(x, 1150 + N)
+    cfg = _cfg(3, "f32")
+    announce("backward-lengths", N)
+    o = _oracle_fwd(x, 3, 1.0).astype(np.float32)
+    _check(_run(x, g, o, cfg), x, g, 3, 1.0, label=f"N={N}")
+
+
+def test_backward_raw_scores():
+    x = synth.make_qkv(116, 1, 2, 300, DK, DV, unit_norm=False)
+    g = _grad_inputs(x, 1160)
+    cfg = _cfg(3, "f32", 0.25)
+    announce("backward-raw")
+    o = _oracle_fwd(x, 3, 0.25).astype(np.float32)
+    _check(_run(x, g, o, cfg), x, g, 3, 0.25, tol=1e-4, label="raw")
+
+
+def test_backward_with_the_library_forward():
+    # end to end: the library's own float32 forward outputs feed the backward
+    import torch
+
+    n, B, H, N = 3, 1, 4, 2048
+    x = synth.make_qkv(117, B, H, N, DK, DV)
+    g = _grad_inputs(x, 1170)
+    cfg = _cfg(n, "f32")
+    announce("backward-e2e", N)
+    q, k, v = x.torch(DEV)
+    o = torch.empty((B, H, N, DV), device=DEV)
+    rs.taylor_attn_prefill(q, k, v, o, None, rs.new_workspace(cfg, B, H, N, DEV), cfg)
+    _check(_run(x, g, o.cpu().numpy(), cfg), x, g, n, 1.0, label="e2e")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_from_a_state_and_its_gradient(dtype):
+    # the forward continued from an incoming state: gradients of q, k, v and of that state
+    import torch
+
+    n, H, N0, N = 3, 2, 200, 300
+    x0 = synth.make_qkv(118, 1, H, N0, DK, DV, dtype)
+    x = synth.make_qkv(119, 1, H, N, DK, DV, dtype)
+    g = _grad_inputs(x, 1190)
+    cfg = _cfg(n, dtype)
+    announce("backward-state", dtype)
+    st0 = np.stack([oracle.state(x0.k64[0, h], x0.v64[0, h], n) for h in range(H)])  # [H, W, 65]
+    stride = rs.taylor_state_stride(cfg)
+    W = st0.shape[1]
+    flat = np.zeros((1, H, stride), dtype=np.float32)
+    flat[0, :, : W * DV] = st0[:, :, :DV].reshape(H, -1)
+    flat[0, :, W * DV : W * (DV + 1)] = st0[:, :, DV]
+    o = np.empty((1, H, N, DV), dtype=np.float32)
+    refs = []
+    for h in range(H):
+        oh, _ = oracle.recurrent(x.q64[0, h], x.k64[0, h], x.v64[0, h], n, 1.0, st0[h])
+        o[0, h] = oh
+        refs.append(oracle.attention_backward_from_state(x.q64[0, h], x.k64[0, h], x.v64[0, h], g[0, h], n, 1.0, st0[h]))
+    state = torch.from_numpy(flat).to(DEV)
+    dstate = torch.zeros_like(state)
+    got = _run(x, g, o, cfg, state, dstate)
+    ds = dstate.cpu().numpy()
+    for h in range(H):
+        for name, gt, rf, t in zip(("dq", "dk", "dv"), (a[0, h] for a in got), refs[h][:3], (1e-5, 2e-5, 1e-5)):
+            err = _rel(gt, rf)
+            assert err <= t, f"{name} head {h}: {err:.3e}"
+        want = refs[h][3]
+        gs = np.concatenate([ds[0, h, : W * DV].reshape(W, DV), ds[0, h, W * DV : W * (DV + 1)][:, None]], axis=1)
+        assert _rel(gs, want) <= 1e-5, f"dstate head {h}: {_rel(gs, want):.3e}"
+
+
+def test_backward_in_pieces_passes_the_state_gradient():
+    # A sequence prefilled in two calls is differentiated in reverse: the second call's backward
+    # returns dL/d(state between the calls), which seeds the first call's backward.
+    import torch
+
+    n, H, N1, N2 = 3, 2, 400, 250
+    x = synth.make_qkv(120, 1, H, N1 + N2, DK, DV)
+    g = _grad_inputs(x, 1200)
+    cfg = _cfg(n, "f32")
+    announce("backward-pieces")
+    o = _oracle_fwd(x, n, 1.0).astype(np.float32)
+    q, k, v = x.torch(DEV)
+    st = rs.new_state(1, H, cfg, DEV)
+    parts1 = [t[:, :, :N1].contiguous() for t in (q, k, v)]
+    o1 = torch.empty((1, H, N1, DV), device=DEV)
+    rs.taylor_attn_prefill(*parts1, o1, st, rs.new_workspace(cfg, 1, H, N1, DEV), cfg)  # st = state after piece 1
+    outs = []
+    dstate = torch.zeros_like(st)
+    for lo, hi, state in ((N1, N1 + N2, st), (0, N1, None)):
+        parts = [t[:, :, lo:hi].contiguous() for t in (q, k, v)]
+        dq = torch.empty((1, H, hi - lo, DK), device=DEV)
+        dk = torch.empty((1, H, hi - lo, DK), device=DEV)
+        dv = torch.empty((1, H, hi - lo, DV), device=DEV)
+        rs.taylor_attn_prefill_backward(*parts, torch.from_numpy(o[:, :, lo:hi].copy()).to(DEV),
+                                        torch.from_numpy(g[:, :, lo:hi].copy()).to(DEV), state, dstate, dq, dk, dv,
+                                        rs.new_backward_workspace(cfg, 1, H, hi - lo, DEV), cfg)
+        outs.append((dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()))
+    got = [np.concatenate([outs[1][i], outs[0][i]], axis=2) for i in range(3)]
+    _check(got, x, g, n, 1.0, label="pieces")
+
+
+def test_backward_full_size_properties():
+    # the bfloat16 prefill shape B4 x H16 x N8192: finite gradients, the sum rule of dv (each output is
+    # an average: sum_j dv_j = sum_i g_i) and sampled rows of dq against the oracle
+    import torch
+
+    n, B, H, N = 3, 4, 16, 8192
+    x = synth.make_qkv(3, B, H, N, DK, DV, "bf16")
+    cfg = _cfg(n, "bf16")
+    announce("backward-full", B, H, N)
+    q, k, v = x.torch(DEV)
+    # forward outputs from the float32 kernels on the same (exactly widened) inputs, so that the
+    # sampled rows below see float32-accurate o
+    f32 = _cfg(n, "f32")
+    o = torch.empty((B, H, N, DV), device=DEV)
+    rs.taylor_attn_prefill(q.float(), k.float(), v.float(), o, None, rs.new_workspace(f32, B, H, N, DEV), f32)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1210)
+    g = torch.randn((B, H, N, DV), generator=gen, device=DEV)
+    dq = torch.empty((B, H, N, DK), device=DEV)
+    dk = torch.empty((B, H, N, DK), device=DEV)
+    dv = torch.empty((B, H, N, DV), device=DEV)
+    rs.taylor_attn_prefill_backward(q, k, v, o, g, None, None, dq, dk, dv, rs.new_backward_workspace(cfg, B, H, N, DEV),
+                                    cfg)
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    sdv = dv.double().sum(dim=2)
+    sg = g.double().sum(dim=2)
+    assert float((sdv - sg).abs().max()) <= 1e-3 * float(sg.abs().max())
+    gn = g.cpu().numpy()
+    dqn = dq.cpu().numpy()
+    rng = np.random.default_rng(1211)
+    for b, h in ((0, 0), (3, 15), (1, 7)):
+        rows = np.unique(np.concatenate([[1, N - 1], rng.integers(1, N, 4)]))  # row 0 has dq = 0
+        ref = oracle.attention_backward_dq_rows(x.q64[b, h], x.k64[b, h], x.v64[b, h], gn[b, h], n, rows)
+        err = float(np.max(np.linalg.norm(dqn[b, h, rows] - ref, axis=1) / np.linalg.norm(ref, axis=1)))
+        assert err <= 1e-4, f"dq rows ({b}, {h}): {err:.3e}"

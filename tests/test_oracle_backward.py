@@ -99,3 +99,11 @@ def test_planted_mistakes_are_caught():
     delta = np.sum(g * o, 1) / den
     wrong_deriv = np.where(mask, gh @ v.T - delta[:, None], 0.0) * oracle.truncated_kernel(s, n)
     assert np.max(np.abs(scale * (wrong_deriv @ k) - fd)) > 1e-3
+
+
+def test_dq_rows_form_matches_full():
+    q, k, v, g = _inputs(70, N=20, d=4, dv=3)
+    dq = oracle.attention_backward(q, k, v, g, 3, 0.6)[0]
+    rows = [0, 5, 19, 11]
+    np.testing.assert_allclose(oracle.attention_backward_dq_rows(q, k, v, g, 3, rows, 0.6), dq[rows], rtol=1e-12,
+                               atol=1e-14)
