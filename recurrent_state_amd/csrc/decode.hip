@@ -26,6 +26,17 @@ namespace {
 
 constexpr int kDecodeThreads = 256;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// A state row piece, read with the nontemporal hint: each element is read once per step, and the
+// hint measured 2% faster with the state in the last-level cache (64 x 16 heads, 41 MB) and 9%
+// faster above it (512 x 16 heads, 326 MB) than plain loads.  (Nontemporal stores as well, or
+// instead, were slower at one size or the other.)
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(x[0], x[1], x[2], x[3]);
+}
+
 // Order of feature a in the table (orders ascend: 1 feature of order 0, then d_k of order 1, ...);
 // used at n <= 3 only.
 template <int DK>
@@ -73,7 +84,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
 #pragma unroll
   for (int u = 0; u < RB; ++u) {
     const int r = r0 + u * RSTEP;
-    if (r < W) buf[u] = *reinterpret_cast<const float4*>(S + (long long)r * DV + cg * 4);
+    if (r < W) buf[u] = load_stream(S + (long long)r * DV + cg * 4);
   }
   const float z0 = tid < W ? z[tid] : 0.f;
 
@@ -120,7 +131,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(const T* __restr
 #pragma unroll
       for (int u = 0; u < RB; ++u) {
         const int r = base + u * RSTEP;
-        if (r < W) buf[u] = *reinterpret_cast<const float4*>(S + (long long)r * DV + cg * 4);
+        if (r < W) buf[u] = load_stream(S + (long long)r * DV + cg * 4);
       }
     }
 #pragma unroll
