@@ -16,14 +16,27 @@
 // G at the start of the call is the incoming state's gradient; a gradient for the final state seeds
 // G at the end.  J_phi is the Jacobian of the monomial features (orders <= 2 here: n <= 3).
 //
-// Passes over segments of L tokens (one workgroup of 8 wavefronts per segment, 16-token chunks,
-// the running state in LDS, float32 16x16x4 MFMAs with operands read from LDS):
+// Passes over segments of L tokens (one workgroup of 8 wavefronts per segment, 64-token chunks):
 //   1. state pass: the S, z increments of each segment;
 //   2. forward scan: exclusive prefixes, seeded with the incoming state;
 //   3. pass A (chunks in order): den, gh, delta (kept for pass B), dq, the segment's G increments;
 //   4. reverse scan of the G increments, seeded with the final state's gradient (its total is the
 //      incoming state's gradient);
 //   5. pass B (chunks in reverse): dv, dk.
+//
+// Layout.  Features are split into 16-row tiles; wavefront w owns tiles w and w + 8 and keeps their
+// rows of S and G in float32 MFMA accumulators for the whole segment, transposed (the lane holding
+// feature f = 16 ft + l16 and value columns d = 16 dt + 4 lg + r), which is exactly the A operand of a
+// product that contracts over d (S gh in pass A, G v in pass B).  The feature operands of the state
+// updates are formed as the products are issued: each lane's feature is fixed, so phi_f(x_t) is a
+// coefficient times two entries of the row of x_t, whose columns 16 and 17 hold ones (orders 0 and 1)
+// and 18 a zero (padding features); nothing of phi is stored.  Intra-chunk score tiles stay in
+// registers from the scores to the products that consume them: in pass A a tile [key j][query i] is
+// the A operand of ds k over j; in pass B a tile [query i][key j] is the A operand of w^T gh and
+// ds^T a over i.  dv in pass B contracts G over the features, so the owners copy G into LDS once per
+// chunk and every wavefront reads it for two 16x16 tiles of dv.  The feature Jacobians run with one
+// lane per token over the wavefront's own (compile-time) features; each wavefront leaves its partial
+// dq (dk) rows in its own LDS rows, summed after the chunk.
 #include <type_traits>
 #include <utility>
 
@@ -34,495 +47,832 @@ namespace taylor {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kDK = 16, kDV = 64;
-constexpr int kC = 16;  // tokens per chunk
+constexpr int kC = 64;  // tokens per chunk
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLR = kDK + 4;  // LDS row strides (floats): 16-wide rows,
-constexpr int kLV = kDV + 4;  // 64-wide rows,
-constexpr int kLC = kC + 4;   // [query][key] tiles
+constexpr int kLR = 20;  // a, k rows: 16 coordinates, two ones, two zeros
+constexpr int kLV = 68;  // 64-wide rows and feature-major rows
+constexpr int kOne0 = 16, kOne1 = 17, kZero = 18;
+constexpr int kLP = 17;  // row stride of a wavefront's partial dq (dk) rows: 64 x 17 floats = its 16 rows
 
 template <int NT>
 struct BG {
   static constexpr int W = FeatureTable<NT, kDK>::W;
-  static constexpr int WP = (W + 15) / 16 * 16;  // features padded to 16-row tiles
-  static constexpr int FPW = WP / kWaves;         // features per wavefront (expansion, Jacobian)
-  static constexpr int LF = WP + 4;
-  static constexpr int NFT = WP / 16;             // feature tiles
-  static constexpr int NTILE = NFT * (kDV / 16);  // 16x16 tiles of a state
-  static constexpr int TPW = (NTILE + kWaves - 1) / kWaves;
+  static constexpr int NFT = (W + 15) / 16;                       // feature tiles
+  static constexpr int WP = 16 * NFT;                             // padded features
+  static constexpr int NU = (NFT + kWaves - 1) / kWaves;          // tiles per wavefront, at most
+  static constexpr int NWF = NFT < kWaves ? NFT : kWaves;         // wavefronts owning tiles
+  static constexpr int YR = WP > 16 * kWaves ? WP : 16 * kWaves;  // rows of a feature-major buffer
 };
 
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void wave_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Feature f as (row offset c0) | (row offset c1) << 8: phi_f(x) = cf x[c0] x[c1] on an extended row.
 template <int NT>
-struct BSmem {
-  using G = BG<NT>;
-  alignas(16) float st[G::WP][kLV];  // S (pass A) or G_S (pass B); rows past W stay zero
-  float zt[G::WP];                   // z or G_z
-  alignas(16) float phia[kC][G::LF];
-  alignas(16) float phik[kC][G::LF];
-  alignas(16) float ar[kC][kLR];  // a = sigma q
-  alignas(16) float kr[kC][kLR];
-  alignas(16) float vr[kC][kLV];
-  alignas(16) float gr[kC][kLV];  // g, then gh
-  float wt[kC][kLC], kp[kC][kLC], ds[kC][kLC];  // [query i][key j]
-  alignas(16) float y[kC][G::LF];
-  float dpart[kWaves][kC][kDK + 1];
-  float den[kC], delta[kC], go[kC];  // go: g . o
+__device__ __forceinline__ int feature_code(int f) {
+  if (f >= BG<NT>::W) return kZero | (kZero << 8);
+  const Monomials<NT, kDK>& T = kMono<NT, kDK>;
+  const int m = T.order[f];
+  const int c0 = m == 0 ? kOne0 : T.coord[f][0];
+  const int c1 = m == 0 ? kOne1 : (m == 1 ? kOne0 : T.coord[f][1]);
+  return c0 | (c1 << 8);
+}
+struct LaneF {
+  int o0, o1;
+  float cf;  // 1/sqrt(2) for x_c^2 (and the zero padding), else 1
+};
+__device__ __forceinline__ LaneF unpack(int code) {
+  LaneF r;
+  r.o0 = code & 255;
+  r.o1 = code >> 8;
+  r.cf = r.o0 == r.o1 ? 0.70710678118654752f : 1.f;
+  return r;
+}
+__device__ __forceinline__ float phi(const float* row, const LaneF& f) { return f.cf * row[f.o0] * row[f.o1]; }
+
+// Element loads: pairs of q, k coordinates, eight-column slices of v (and of g, o, gh: float32).
+__device__ __forceinline__ void ld2(const float* p, float (&x)[2]) {
+  const f32x2 t = *reinterpret_cast<const f32x2*>(p);
+  x[0] = t[0];
+  x[1] = t[1];
+}
+__device__ __forceinline__ void ld2(const uint16_t* p, float (&x)[2]) {
+  const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+  x[0] = __uint_as_float(u << 16);
+  x[1] = __uint_as_float(u & 0xffff0000u);
+}
+__device__ __forceinline__ void ld8(const float* p, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = a[e];
+    x[4 + e] = b[e];
+  }
+}
+__device__ __forceinline__ void ld8(const uint16_t* p, float (&x)[8]) {
+  const uint4 t = *reinterpret_cast<const uint4*>(p);
+  const uint32_t wd[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    x[2 * h] = __uint_as_float(wd[h] << 16);
+    x[2 * h + 1] = __uint_as_float(wd[h] & 0xffff0000u);
+  }
+}
+
+// LDS rows of one chunk.
+struct Rows {
+  float (*ax)[kLR];  // a = sigma q, extended (null in the state pass)
+  float (*kx)[kLR];  // k, extended
+  float (*v)[kLV];
+  float (*g)[kLV];  // g (pass A) or gh (pass B)
+  float* go;        // g . o per token (pass A)
+  float* delta;     // delta per token (pass B)
 };
 
-__device__ __forceinline__ float ld(const float* p) { return *p; }
-__device__ __forceinline__ float ld(const uint16_t* p) { return __uint_as_float(((uint32_t)*p) << 16); }
-
-// acc += A B over K (a multiple of 4), one 16x16 output tile: a(m, k) and b(k, n) read LDS (m, n in
-// 0..15).  Lane (l16, lg) holds D[4lg + r][l16] in element r.
-template <int K, class FA, class FB>
-__device__ __forceinline__ f32x4 mm(f32x4 acc, int l16, int lg, FA a, FB b) {
+// One thread's share of a chunk's inputs, loaded a chunk ahead and stored to LDS when the chunk starts,
+// so that the global loads of the next chunk are in flight while one is computed.  Thread tid takes
+// token tid / 8: coordinates 2 (tid % 8) and + 1 of q and k, columns 8 (tid % 8) .. + 7 of v, g, o,
+// gh.  Tokens past the end read the chunk's first row (no conditional load) and store zeros.
+// MODE 0: k, v (state pass); 1: q, k, v, g, o (pass A); 2: q, k, v, gh, delta (pass B).
+template <typename E, int MODE>
+struct Pre {
+  float qa[2], kk[2], vv[8], gg[8], oo[8], dl;
+  __device__ __forceinline__ void load(const E* q, const E* k, const E* v, const float* g, const float* o,
+                                       const float* dlt, long long tok0, int nv, int tid) {
+    const int t = tid >> 3, c = tid & 7;
+    const long long row = tok0 + (t < nv ? t : 0);
+    ld2(k + row * kDK + 2 * c, kk);
+    if constexpr (MODE != 0) ld2(q + row * kDK + 2 * c, qa);
+    ld8(v + row * kDV + 8 * c, vv);
+    if constexpr (MODE != 0) ld8(g + row * kDV + 8 * c, gg);
+    if constexpr (MODE == 1) ld8(o + row * kDV + 8 * c, oo);
+    if constexpr (MODE == 2) dl = dlt[tok0 + (tid < nv ? tid : 0)];
+  }
+  __device__ __forceinline__ void store(const Rows& R, int nv, float scale, int tid) const {
+    const int t = tid >> 3, c = tid & 7;
+    const bool ok = t < nv;
+    const float one = ok ? 1.f : 0.f;
+    *reinterpret_cast<f32x2*>(&R.kx[t][2 * c]) = f32x2{ok ? kk[0] : 0.f, ok ? kk[1] : 0.f};
+    if (c == 0) *reinterpret_cast<f32x4*>(&R.kx[t][kDK]) = f32x4{one, one, 0.f, 0.f};
+    if constexpr (MODE != 0) {
+      *reinterpret_cast<f32x2*>(&R.ax[t][2 * c]) = f32x2{ok ? scale * qa[0] : 0.f, ok ? scale * qa[1] : 0.f};
+      if (c == 0) *reinterpret_cast<f32x4*>(&R.ax[t][kDK]) = f32x4{one, one, 0.f, 0.f};
+    }
 #pragma unroll
-  for (int k = 0; k < K; k += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a(l16, k + lg), b(k + lg, l16), acc, 0, 0, 0);
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<f32x4*>(&R.v[t][8 * c + 4 * h]) =
+          ok ? f32x4{vv[4 * h], vv[4 * h + 1], vv[4 * h + 2], vv[4 * h + 3]} : zero4();
+      if constexpr (MODE != 0)
+        *reinterpret_cast<f32x4*>(&R.g[t][8 * c + 4 * h]) =
+            ok ? f32x4{gg[4 * h], gg[4 * h + 1], gg[4 * h + 2], gg[4 * h + 3]} : zero4();
+    }
+    if constexpr (MODE == 1) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf(gg[e], oo[e], s);
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      if (c == 0) R.go[t] = ok ? s : 0.f;
+    }
+    if constexpr (MODE == 2)
+      if (tid < kC) R.delta[tid] = tid < nv ? dl : 0.f;
+  }
+};
+
+// Feature of wavefront WW's share at position I (slot I / 16 is tile WW + 8 (I / 16)), or -1.
+template <int NT, int WW, int I>
+constexpr int own_feature() {
+  constexpr int ft = WW + kWaves * (I / 16);
+  constexpr int F = 16 * ft + I % 16;
+  return (ft < BG<NT>::NFT && F < BG<NT>::W) ? F : -1;
+}
+
+// out += J_phi(x)^T y over wavefront WW's features, y_F = ycol[F * kLV] (orders <= 2): order 1 feature
+// e_c adds y to out[c]; order 2 feature cf x_c0 x_c1 adds cf y x_c1 to out[c0] and cf y x_c0 to out[c1].
+template <int NT, int WW>
+__device__ __forceinline__ void own_vjp(const float (&x)[kDK], const float* ycol, float (&out)[kDK]) {
+  using FT = FeatureTable<NT, kDK>;
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (([&] {
+       constexpr int F = own_feature<NT, WW, I>();
+       if constexpr (F >= 0) {
+         constexpr int m = FT::T.order[F];
+         if constexpr (m == 1) {
+           out[FT::T.coord[F][0]] += ycol[F * kLV];
+         } else if constexpr (m == 2) {
+           constexpr int c0 = FT::T.coord[F][0], c1 = FT::T.coord[F][1];
+           constexpr float cf = coef_of_afact(FT::T.afact[F]);
+           const float t = cf * ycol[F * kLV];
+           out[c0] = fmaf(t, x[c1], out[c0]);
+           out[c1] = fmaf(t, x[c0], out[c1]);
+         }
+       }
+     }()),
+     ...);
+  }(std::make_integer_sequence<int, 16 * BG<NT>::NU>{});
+}
+
+// Sum over wavefront WW's features of phi_F(x) z_F.
+template <int NT, int WW>
+__device__ __forceinline__ float own_dot(const float (&x)[kDK], const float* z) {
+  float acc = 0.f;
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (([&] {
+       constexpr int F = own_feature<NT, WW, I>();
+       if constexpr (F >= 0) acc = fmaf(feature_ct<NT, kDK, F>(x), z[F], acc);
+     }()),
+     ...);
+  }(std::make_integer_sequence<int, 16 * BG<NT>::NU>{});
   return acc;
 }
 
-// Features of wavefront w's share [w FPW, (w+1) FPW) for the chunk's tokens: lanes 0..15 phi(k) of
-// token l, lanes 16..31 phi(a) of token l - 16 (WITH_A).  Tokens past the end have zero rows; their
-// constant feature is zeroed too.
-template <int NT, bool WITH_A>
-__device__ __forceinline__ void expand(BSmem<NT>& sm, int w, int l, int nv) {
-  using G = BG<NT>;
-  if (l >= (WITH_A ? 2 * kC : kC)) return;
-  const int t = l & (kC - 1);
-  const bool is_a = l >= kC;
-  float x[kDK];
+__device__ __forceinline__ void load_coords(const float* row, float (&x)[kDK]) {
 #pragma unroll
-  for (int d = 0; d < kDK; ++d) x[d] = is_a ? sm.ar[t][d] : sm.kr[t][d];
-  float* dst = is_a ? &sm.phia[t][0] : &sm.phik[t][0];
-  const bool valid = t < nv;
-  dispatch_index<0, kWaves>(w, [&](auto WI) {
-    constexpr int F0 = decltype(WI)::value * G::FPW;
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      (([&] {
-         constexpr int F = F0 + I;
-         float f = feature_ct<NT, kDK, F>(x);
-         if constexpr (F == 0) f = valid ? 1.f : 0.f;
-         dst[F] = f;
-       }()),
-       ...);
-    }(std::make_integer_sequence<int, G::FPW>{});
-  });
+  for (int u = 0; u < 4; ++u) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(row + 4 * u);
+    x[4 * u] = t[0];
+    x[4 * u + 1] = t[1];
+    x[4 * u + 2] = t[2];
+    x[4 * u + 3] = t[3];
+  }
 }
 
-// out += J_phi(x)^T y over wavefront w's share of the features (orders <= 2): order 1 feature e_c
-// adds y to out[c]; order 2 feature c * x_c0 x_c1 adds c y x_c1 to out[c0] and c y x_c0 to out[c1].
-template <int NT>
-__device__ __forceinline__ void feature_vjp(int w, const float (&x)[kDK], const float* y, float (&out)[kDK]) {
-  using G = BG<NT>;
-  using FT = FeatureTable<NT, kDK>;
-  dispatch_index<0, kWaves>(w, [&](auto WI) {
-    constexpr int F0 = decltype(WI)::value * G::FPW;
-    [&]<int... I>(std::integer_sequence<int, I...>) {
-      (([&] {
-         constexpr int F = F0 + I;
-         if constexpr (F < G::W) {
-           constexpr int m = FT::T.order[F];
-           if constexpr (m == 1) {
-             out[FT::T.coord[F][0]] += y[F];
-           } else if constexpr (m == 2) {
-             constexpr int c0 = FT::T.coord[F][0], c1 = FT::T.coord[F][1];
-             constexpr float cf = coef_of_afact(FT::T.afact[F]);
-             const float t = cf * y[F];
-             out[c0] = fmaf(t, x[c1], out[c0]);
-             out[c1] = fmaf(t, x[c0], out[c1]);
-           }
-         }
-       }()),
-       ...);
-    }(std::make_integer_sequence<int, G::FPW>{});
-  });
+// Sum of the eight wavefronts' partial rows (dq or dk) of a finished chunk, times `mul`.
+__device__ __forceinline__ void reduce_rows(const float (*buf)[kLV], float* out, long long tok0, int nv, float mul,
+                                            int tid) {
+  for (int e = tid; e < kC * kDK; e += kThreads) {
+    const int i = e >> 4, d = e & 15;
+    float s = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) s += (&buf[16 * ww][0])[i * kLP + d];
+    if (i < nv) out[(tok0 + i) * kDK + d] = mul * s;
+  }
 }
 
-// One thread's share of a chunk's input rows, loaded a chunk ahead (registers) and stored to LDS when
-// the chunk starts, so the global loads of chunk c+1 are in flight while chunk c is computed.
-// Element tid of k (tid < 256) or of a = sigma q (tid >= 256); elements tid and tid + 512 of v and of
-// g (pass A) or gh (pass B), and of o (pass A: g . o is reduced per token at the store); delta
-// (pass B, tid < 16).  Rows past the end are zero.  MODE 0: k, v; 1: pass A; 2: pass B.
-template <typename E, int MODE>
-struct Pre {
-  float kq, v[2], g[2], o[2], dl;
-  __device__ __forceinline__ void load(const E* q, const E* k, const E* vg, const float* gg, const float* og,
-                                       const float* dlt, long long tok0, int nv, float scale, int tid) {
-    // every load reads a valid row (tokens past the end read the chunk's first) and is masked after,
-    // so no load is conditional
-    const int e = tid & 255, i = e / kDK, d = e % kDK;
-    const bool ok = i < nv;
-    const long long rk = (tok0 + (ok ? i : 0)) * kDK + d;
-    float x = 0.f;
-    if (tid < 256)
-      x = ld(k + rk);
-    else if (MODE != 0)
-      x = scale * ld(q + rk);
-    kq = ok ? x : 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = (tid >> 6) + 8 * u, c = tid & 63;
-      const bool okt = t < nv;
-      const long long r = (tok0 + (okt ? t : 0)) * kDV + c;
-      const float xv = ld(vg + r);
-      v[u] = okt ? xv : 0.f;
-      if constexpr (MODE != 0) {
-        const float xg = gg[r];
-        g[u] = okt ? xg : 0.f;
-      } else {
-        g[u] = 0.f;
-      }
-      if constexpr (MODE == 1) {
-        const float xo = og[r];
-        o[u] = okt ? xo : 0.f;
-      } else {
-        o[u] = 0.f;
-      }
-    }
-    dl = 0.f;
-    if constexpr (MODE == 2) {
-      const float xd = dlt[tok0 + (tid < kC && tid < nv ? tid : 0)];
-      dl = (tid < kC && tid < nv) ? xd : 0.f;
-    }
-  }
-  template <int NT>
-  __device__ __forceinline__ void store(BSmem<NT>& sm, int tid) const {
-    const int e = tid & 255, i = e / kDK, d = e % kDK;
-    if (tid < 256)
-      sm.kr[i][d] = kq;
-    else if (MODE != 0)
-      sm.ar[i][d] = kq;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = (tid >> 6) + 8 * u, c = tid & 63;
-      sm.vr[t][c] = v[u];
-      if constexpr (MODE != 0) sm.gr[t][c] = g[u];
-      if constexpr (MODE == 1) {
-        float go = g[u] * o[u];
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) go += __shfl_xor(go, off);
-        if (c == 0) sm.go[t] = go;
-      }
-    }
-    if (MODE == 2 && tid < kC) sm.delta[tid] = dl;
-  }
+// ---------------------------------------------------------------------------------------------------
+// 1. State pass: S, z increments of each segment.
+
+struct SmemS {
+  alignas(16) float kx[kC][kLR];
+  alignas(16) float v[kC][kLV];
 };
 
-// Wavefront 0: the chunk's weights w_ij = K_n(s_ij) and K_{n-1}(s_ij) for keys j <= i (zero else),
-// then ds_ij = (gh_i . v_j - delta_i) K_{n-1}(s_ij).  Needs gh, delta.
-template <int NT>
-__device__ __forceinline__ void weights(BSmem<NT>& sm, int l16, int lg, int nv) {
-  const f32x4 sc = mm<kDK>(f32x4{0.f, 0.f, 0.f, 0.f}, l16, lg, [&](int m, int kk) { return sm.kr[m][kk]; },
-                           [&](int kk, int n) { return sm.ar[n][kk]; });
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int j = 4 * lg + r, i = l16;  // D[key j][query i]
-    const bool ok = j <= i && j < nv;
-    const float s = sc[r];
-    sm.wt[i][j] = ok ? taylor_kernel<NT>(s) : 0.f;
-    float d = 0.f;
-    if constexpr (NT > 1) d = taylor_kernel<NT - 1>(s);
-    sm.kp[i][j] = ok ? d : 0.f;
-  }
-}
-
-template <int NT>
-__device__ __forceinline__ void dscores(BSmem<NT>& sm, int l16, int lg) {
-  const f32x4 dw = mm<kDV>(f32x4{0.f, 0.f, 0.f, 0.f}, l16, lg, [&](int m, int kk) { return sm.gr[m][kk]; },
-                           [&](int kk, int n) { return sm.vr[n][kk]; });
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 4 * lg + r, j = l16;  // D[query i][key j]
-    sm.ds[i][j] = (dw[r] - sm.delta[i]) * sm.kp[i][j];
-  }
-}
-
-// Pass 1 (MODE 0: S, z increments of each segment) and pass A (MODE 1).  grid = (segments, pairs).
-template <int NT, typename E, int MODE>
-__global__ __launch_bounds__(kThreads) void bwd_forward_kernel(const E* __restrict__ q, const E* __restrict__ k,
-                                                               const E* __restrict__ v, const float* __restrict__ g,
-                                                               const float* __restrict__ o,
-                                                               float* __restrict__ sslots,
-                                                               float* __restrict__ gslots,
-                                                               float* __restrict__ ghat, float* __restrict__ dlt,
-                                                               float* __restrict__ dq, SeqMap seq, int L,
-                                                               long long nslot, long long stride, float scale) {
+template <int NT, typename E>
+__global__ __launch_bounds__(kThreads) void bwd_state_kernel(const E* __restrict__ k, const E* __restrict__ v,
+                                                             float* __restrict__ sslots, SeqMap seq, int L,
+                                                             long long nslot, long long stride) {
   using G = BG<NT>;
-  constexpr int W = G::W, WP = G::WP;
-  __shared__ BSmem<NT> sm;
+  constexpr int W = G::W, NU = G::NU;
+  __shared__ SmemS sm;
   const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const Rows R{nullptr, sm.kx, sm.v, nullptr, nullptr, nullptr};
+  LaneF lf[NU];
+  bool has[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    lf[u] = unpack(feature_code<NT>(16 * (w + kWaves * u) + l16));
+    has[u] = w + kWaves * u < G::NFT;
+  }
 
   for_each_piece<false>(seq, blockIdx.x, blockIdx.y, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
-    float* sslot = sslots + pc.slot * stride;
-    float* gslot = gslots + pc.slot * stride;
-    // the running S, z: zero (increments) or the segment's prefix
-    for (int e = tid; e < WP * kDV; e += kThreads) {
-      const int f = e / kDV, d = e % kDV;
-      sm.st[f][d] = (MODE == 1 && f < W) ? sslot[(long long)f * kDV + d] : 0.f;
-    }
-    for (int f = tid; f < WP; f += kThreads) sm.zt[f] = (MODE == 1 && f < W) ? sslot[(long long)W * kDV + f] : 0.f;
-    f32x4 gacc[G::TPW];  // G_S increments, tiles w, w + 8, ...
+    f32x4 st[NU][4];
+    float zs[NU];
 #pragma unroll
-    for (int u = 0; u < G::TPW; ++u) gacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float gz = 0.f;  // G_z increment of feature tid
+    for (int u = 0; u < NU; ++u) {
+      zs[u] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) st[u][dt] = zero4();
+    }
     const int nch = (pc.n + kC - 1) / kC;
     auto nv_of = [&](int c) { return min(kC, pc.n - c * kC); };
     auto tok_of = [&](int c) { return pc.tok + (long long)c * kC; };
-    Pre<E, MODE> pre;
-    pre.load(q, k, v, g, o, nullptr, tok_of(0), nv_of(0), scale, tid);
-    __syncthreads();
+    Pre<E, 0> pre;
+    pre.load(nullptr, k, v, nullptr, nullptr, nullptr, tok_of(0), nv_of(0), tid);
     for (int c = 0; c < nch; ++c) {
-      const int nv = nv_of(c);
-      const long long tok0 = tok_of(c);
-      pre.store(sm, tid);
+      pre.store(R, nv_of(c), 1.f, tid);
       const int cn = c + 1 < nch ? c + 1 : c;  // the last chunk reloads itself (no conditional load)
-      pre.load(q, k, v, g, o, nullptr, tok_of(cn), nv_of(cn), scale, tid);
+      pre.load(nullptr, k, v, nullptr, nullptr, nullptr, tok_of(cn), nv_of(cn), tid);
       __syncthreads();
-      expand<NT, MODE == 1>(sm, w, l, nv);
-      __syncthreads();
-      if constexpr (MODE == 1) {
-        if (w == 0) {
-          weights<NT>(sm, l16, lg, nv);
-        } else if (w == 1) {
-          // phi(a_i) . z over the tokens before the chunk: 4 lanes per token
-          float acc = 0.f;
-          for (int f = lg; f < WP; f += 4) acc = fmaf(sm.phia[l16][f], sm.zt[f], acc);
-          acc += __shfl_xor(acc, 16);
-          acc += __shfl_xor(acc, 32);
-          if (lg == 0) sm.den[l16] = acc;
-        }
-        __syncthreads();
-        // gh, delta: wavefront w takes tokens 2w, 2w + 1, lane = value column
+      if (has[0]) {
+        // S^T += V^T phi(K), z += sum phi(k): tokens t = 16 qq + 4 lg + r of the contraction
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int t = 2 * w + u;
-          float dn = sm.den[t];
-#pragma unroll
-          for (int j = 0; j < kC; ++j) dn += sm.wt[t][j];
-          const float gv = sm.gr[t][l];
-          const bool ok = t < nv;
-          const float inv = ok ? 1.0f / dn : 0.f;
-          const float gh = gv * inv, dl = sm.go[t] * inv;
-          sm.gr[t][l] = gh;
-          if (l == 0) sm.delta[t] = dl;
-          if (ok) {
-            ghat[(tok0 + t) * kDV + l] = gh;
-            if (l == 0) dlt[tok0 + t] = dl;
-          }
-        }
-        __syncthreads();
-        if (w == 0) dscores<NT>(sm, l16, lg);
-        // Y = gh S^T - delta z^T, feature tiles w, w + 8, ...
-        for (int t = w; t < G::NFT; t += kWaves) {
-          const f32x4 yv = mm<kDV>(f32x4{0.f, 0.f, 0.f, 0.f}, l16, lg, [&](int m, int kk) { return sm.gr[m][kk]; },
-                                   [&](int kk, int n) { return sm.st[16 * t + n][kk]; });
+        for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int i = 4 * lg + r, f = 16 * t + l16;
-            sm.y[i][f] = yv[r] - sm.delta[i] * sm.zt[f];
+            const int t = 16 * qq + 4 * lg + r;
+            float b[NU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+              b[u] = phi(&sm.kx[t][0], lf[u]);
+              zs[u] += b[u];
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              const float a = sm.v[t][16 * dt + l16];
+#pragma unroll
+              for (int u = 0; u < NU; ++u)
+                if (has[u]) st[u][dt] = mfma(a, b[u], st[u][dt]);
+            }
           }
-        }
-        __syncthreads();
-        // dq: the Jacobian over this wavefront's features (lanes 0..15 = tokens), and (wavefront 0)
-        // the intra-chunk sum_j ds_ij k_j into wt
-        if (l < kC) {
-          float x[kDK], out[kDK];
-#pragma unroll
-          for (int d = 0; d < kDK; ++d) {
-            x[d] = sm.ar[l][d];
-            out[d] = 0.f;
-          }
-          feature_vjp<NT>(w, x, &sm.y[l][0], out);
-#pragma unroll
-          for (int d = 0; d < kDK; ++d) sm.dpart[w][l][d] = out[d];
-        }
-        if (w == 0) {
-          const f32x4 di = mm<kC>(f32x4{0.f, 0.f, 0.f, 0.f}, l16, lg, [&](int m, int kk) { return sm.ds[m][kk]; },
-                                  [&](int kk, int n) { return sm.kr[kk][n]; });
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sm.wt[4 * lg + r][l16] = di[r];
-        }
-        __syncthreads();
-        if (tid < kC * kDK) {
-          const int i = tid / kDK, d = tid % kDK;
-          float s = sm.wt[i][d];
-#pragma unroll
-          for (int ww = 0; ww < kWaves; ++ww) s += sm.dpart[ww][i][d];
-          if (i < nv) dq[(tok0 + i) * kDK + d] = scale * s;
-        }
-      }
-      // S += phi(K)^T V, z += sum phi(k); pass A also G_S += phi(A)^T gh, G_z -= phi(A)^T delta
-#pragma unroll
-      for (int u = 0; u < G::TPW; ++u) {
-        const int t = w + u * kWaves;
-        if (t < G::NTILE) {
-          const int ft = t / (kDV / 16), dt = t % (kDV / 16);
-          f32x4 acc;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] = sm.st[16 * ft + 4 * lg + r][16 * dt + l16];
-          acc = mm<kC>(acc, l16, lg, [&](int m, int kk) { return sm.phik[kk][16 * ft + m]; },
-                       [&](int kk, int n) { return sm.vr[kk][16 * dt + n]; });
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sm.st[16 * ft + 4 * lg + r][16 * dt + l16] = acc[r];
-          if constexpr (MODE == 1)
-            gacc[u] = mm<kC>(gacc[u], l16, lg, [&](int m, int kk) { return sm.phia[kk][16 * ft + m]; },
-                             [&](int kk, int n) { return sm.gr[kk][16 * dt + n]; });
-        }
-      }
-      if (tid < WP) {
-        float sz = 0.f, sg = 0.f;
-#pragma unroll
-        for (int j = 0; j < kC; ++j) {
-          sz += sm.phik[j][tid];
-          if constexpr (MODE == 1) sg = fmaf(sm.phia[j][tid], sm.delta[j], sg);
-        }
-        sm.zt[tid] += sz;
-        gz -= sg;
       }
       __syncthreads();
     }
-    if constexpr (MODE == 0) {
-      for (int e = tid; e < W * kDV; e += kThreads) sslot[e] = sm.st[e / kDV][e % kDV];
-      for (int f = tid; f < W; f += kThreads) sslot[(long long)W * kDV + f] = sm.zt[f];
-    } else {
+    float* slot = sslots + pc.slot * stride;
 #pragma unroll
-      for (int u = 0; u < G::TPW; ++u) {
-        const int t = w + u * kWaves;
-        if (t < G::NTILE) {
-          const int ft = t / (kDV / 16), dt = t % (kDV / 16);
+    for (int u = 0; u < NU; ++u) {
+      const int f = 16 * (w + kWaves * u) + l16;
+      float z = zs[u];
+      z += __shfl_xor(z, 16);
+      z += __shfl_xor(z, 32);
+      if (has[u] && f < W) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int f = 16 * ft + 4 * lg + r;
-            if (f < W) gslot[(long long)f * kDV + 16 * dt + l16] = gacc[u][r];
-          }
-        }
+        for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(slot + (long long)f * kDV + 16 * dt + 4 * lg) = st[u][dt];
+        if (lg == 0) slot[(long long)W * kDV + f] = z;
       }
-      if (tid < W) gslot[(long long)W * kDV + tid] = gz;
     }
-    __syncthreads();
   });
 }
 
-// Pass B: chunks in reverse, the running G (the gradient of the state after the chunk) in LDS,
-// seeded with the segment's suffix from the reverse scan.  grid = (segments, pairs).
-template <int NT, typename E>
-__global__ __launch_bounds__(kThreads) void bwd_reverse_kernel(const E* __restrict__ q, const E* __restrict__ k,
-                                                               const E* __restrict__ v,
-                                                               const float* __restrict__ gslots,
-                                                               const float* __restrict__ ghat,
-                                                               const float* __restrict__ dlt, float* __restrict__ dk,
-                                                               float* __restrict__ dv, SeqMap seq, int L,
-                                                               long long nslot, long long stride, float scale) {
+// ---------------------------------------------------------------------------------------------------
+// 3. Pass A: den, gh, delta, dq and the segment's G increments.
+
+template <int NT>
+struct SmemA {
   using G = BG<NT>;
-  constexpr int W = G::W, WP = G::WP;
-  __shared__ BSmem<NT> sm;
+  alignas(16) float y[G::YR][kLV];  // Y^T rows of each owner, then each wavefront's partial dq rows
+  alignas(16) float ax[kC][kLR];
+  alignas(16) float kx[kC][kLR];
+  alignas(16) float v[kC][kLV];
+  alignas(16) float g[kC][kLV];
+  float denp[kWaves][kC];  // phi(a_i) . z over each owner's features
+  float inv[kC], delta[kC], go[kC];
+  float zt[G::WP];  // z before the chunk
+};
+
+// Query-row tile of the intra-chunk work in pass A, by wavefront: waves 2, 3, 6, 7 own one feature
+// tile each (0 and 1 own two), and the heavier rows go where the SIMD's other wavefront carries less.
+__device__ __forceinline__ int row_of_wave(int w) {
+  switch (w) {
+    case 2: return 3;
+    case 3: return 2;
+    case 6: return 0;
+    case 7: return 1;
+    default: return -1;
+  }
+}
+
+template <int NT, typename E>
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const E* __restrict__ q, const E* __restrict__ k,
+                                                          const E* __restrict__ v, const float* __restrict__ g,
+                                                          const float* __restrict__ o,
+                                                          const float* __restrict__ sslots,
+                                                          float* __restrict__ gslots, float* __restrict__ ghat,
+                                                          float* __restrict__ dlt, float* __restrict__ dq,
+                                                          SeqMap seq, int L, long long nslot, long long stride,
+                                                          float scale) {
+  using G = BG<NT>;
+  constexpr int W = G::W, NU = G::NU;
+  __shared__ SmemA<NT> sm;
   const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row = row_of_wave(w);
+  const Rows R{sm.ax, sm.kx, sm.v, sm.g, sm.go, nullptr};
+  LaneF lf[NU];
+  bool has[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    lf[u] = unpack(feature_code<NT>(16 * (w + kWaves * u) + l16));
+    has[u] = w + kWaves * u < G::NFT;
+  }
+  float* part = &sm.y[16 * w][0];  // this wavefront's partial dq rows [token][coordinate]
+
+  for_each_piece<false>(seq, blockIdx.x, blockIdx.y, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
+    const float* sslot = sslots + pc.slot * stride;
+    float* gslot = gslots + pc.slot * stride;
+    f32x4 st[NU][4], gt[NU][4];
+    float zf[NU], gzs[NU];  // z (one feature per lane) and this lane's share of sum phi(a) delta
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int f = 16 * (w + kWaves * u) + l16;
+      const bool fv = has[u] && f < W;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        st[u][dt] = fv ? *reinterpret_cast<const f32x4*>(sslot + (long long)f * kDV + 16 * dt + 4 * lg) : zero4();
+        gt[u][dt] = zero4();
+      }
+      zf[u] = fv ? sslot[(long long)W * kDV + f] : 0.f;
+      gzs[u] = 0.f;
+    }
+    for (int f = tid; f < G::WP; f += kThreads) sm.zt[f] = f < W ? sslot[(long long)W * kDV + f] : 0.f;
+    const int nch = (pc.n + kC - 1) / kC;
+    auto nv_of = [&](int c) { return min(kC, pc.n - c * kC); };
+    auto tok_of = [&](int c) { return pc.tok + (long long)c * kC; };
+    Pre<E, 1> pre;
+    pre.load(q, k, v, g, o, nullptr, tok_of(0), nv_of(0), tid);
+    for (int c = 0; c < nch; ++c) {
+      const int nv = nv_of(c);
+      const long long tok0 = tok_of(c);
+      pre.store(R, nv, scale, tid);
+      if (c > 0) reduce_rows(sm.y, dq, tok_of(c - 1), nv_of(c - 1), scale, tid);
+      const int cn = c + 1 < nch ? c + 1 : c;
+      pre.load(q, k, v, g, o, nullptr, tok_of(cn), nv_of(cn), tid);
+      __syncthreads();
+
+      // Owners: phi(a_i) . z over their features, the part of den from before the chunk.
+      if (has[0]) {
+        dispatch_index<0, kWaves>(w, [&](auto WI) {
+          constexpr int WW = decltype(WI)::value;
+          if constexpr (WW < G::NWF) {
+            float x[kDK];
+            load_coords(&sm.ax[l][0], x);
+            sm.denp[WW][l] = own_dot<NT, WW>(x, sm.zt);
+          }
+        });
+      }
+      // Row owners: scores [key j][query i] for key tiles jt <= row, weights, K_{n-1}, row sums.
+      f32x4 kp[4];
+      float dsum = 0.f;
+      if (row >= 0) {
+        const f32x4 aa = *reinterpret_cast<const f32x4*>(&sm.ax[16 * row + l16][4 * lg]);
+        const int i = 16 * row + l16;
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          kp[jt] = zero4();
+          if (jt <= row) {
+            const f32x4 ka = *reinterpret_cast<const f32x4*>(&sm.kx[16 * jt + l16][4 * lg]);
+            f32x4 sc = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) sc = mfma(ka[s], aa[s], sc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = 16 * jt + 4 * lg + r;
+              const bool ok = j <= i && i < nv;
+              dsum += ok ? taylor_kernel<NT>(sc[r]) : 0.f;
+              float d = 0.f;
+              if constexpr (NT > 1) d = taylor_kernel<NT - 1>(sc[r]);
+              kp[jt][r] = ok ? d : 0.f;
+            }
+          }
+        }
+        dsum += __shfl_xor(dsum, 16);
+        dsum += __shfl_xor(dsum, 32);
+      }
+      __syncthreads();
+
+      // Row owners: den, 1/den and delta of their 16 queries.
+      float iv = 0.f, dl = 0.f;
+      if (row >= 0) {
+        const int i = 16 * row + l16;
+        float den = dsum;
+#pragma unroll
+        for (int ww = 0; ww < G::NWF; ++ww) den += sm.denp[ww][i];
+        iv = i < nv ? 1.0f / den : 0.f;
+        dl = sm.go[i] * iv;
+        if (lg == 0) {
+          sm.inv[i] = iv;
+          sm.delta[i] = dl;
+        }
+      }
+      __syncthreads();
+
+      if (has[0]) {
+        // Y^T = S^T-tiles x g / den_i - z delta_i (S, z before the chunk) into the owner's rows
+        float zp[NU][4];  // z[16 ft + 4 lg + r]
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) zp[u][r] = __shfl(zf[u], 4 * lg + r);
+#pragma unroll 1
+        for (int it = 0; it < 4; ++it) {
+          f32x4 yr[NU];
+#pragma unroll
+          for (int u = 0; u < NU; ++u) yr[u] = zero4();
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const f32x4 gv = *reinterpret_cast<const f32x4*>(&sm.g[16 * it + l16][16 * dt + 4 * lg]);
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+              if (has[u])
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yr[u] = mfma(st[u][dt][r], gv[r], yr[u]);
+          }
+          const int i = 16 * it + l16;
+          const float ivi = sm.inv[i], dli = sm.delta[i];
+#pragma unroll
+          for (int u = 0; u < NU; ++u)
+            if (has[u])
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                sm.y[16 * (w + kWaves * u) + 4 * lg + r][i] = yr[u][r] * ivi - zp[u][r] * dli;
+        }
+        // S^T += V^T phi(K), z += sum phi(k)
+        float zs[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) zs[u] = 0.f;
+#pragma unroll 2
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * qq + 4 * lg + r;
+            float b[NU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+              b[u] = phi(&sm.kx[t][0], lf[u]);
+              zs[u] += b[u];
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              const float a = sm.v[t][16 * dt + l16];
+#pragma unroll
+              for (int u = 0; u < NU; ++u)
+                if (has[u]) st[u][dt] = mfma(a, b[u], st[u][dt]);
+            }
+          }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          float z = zs[u];
+          z += __shfl_xor(z, 16);
+          z += __shfl_xor(z, 32);
+          zf[u] += z;
+          if (has[u] && lg == 0) sm.zt[16 * (w + kWaves * u) + l16] = zf[u];
+        }
+        // G^T += g^T (phi(a) / den), and this lane's share of sum phi(a) delta
+        float gs[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) gs[u] = 0.f;
+#pragma unroll 2
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * qq + 4 * lg + r;
+            const float ivi = sm.inv[i], dli = sm.delta[i];
+            float b[NU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+              const float p = phi(&sm.ax[i][0], lf[u]);
+              b[u] = p * ivi;
+              gs[u] = fmaf(p, dli, gs[u]);
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              const float a = sm.g[i][16 * dt + l16];
+#pragma unroll
+              for (int u = 0; u < NU; ++u)
+                if (has[u]) gt[u][dt] = mfma(a, b[u], gt[u][dt]);
+            }
+          }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) gzs[u] += gs[u];
+        wave_fence();
+        // J_phi(a_i)^T Y_i over the owner's features, one lane per query
+        dispatch_index<0, kWaves>(w, [&](auto WI) {
+          constexpr int WW = decltype(WI)::value;
+          if constexpr (WW < G::NWF) {
+            float x[kDK], out[kDK];
+            load_coords(&sm.ax[l][0], x);
+#pragma unroll
+            for (int d = 0; d < kDK; ++d) out[d] = 0.f;
+            own_vjp<NT, WW>(x, &sm.y[0][l], out);
+            wave_fence();
+#pragma unroll
+            for (int d = 0; d < kDK; ++d) part[l * kLP + d] = out[d];
+          }
+        });
+      } else {
+#pragma unroll
+        for (int d = 0; d < kDK; ++d) part[l * kLP + d] = 0.f;
+      }
+      if (row >= 0) {
+        const int i = 16 * row + l16;
+        // gh and delta for pass B
+        if (i < nv) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x4 gv = *reinterpret_cast<const f32x4*>(&sm.g[i][16 * lg + 4 * e]);
+            *reinterpret_cast<f32x4*>(ghat + (tok0 + i) * kDV + 16 * lg + 4 * e) = gv * iv;
+          }
+          if (lg == 0) dlt[tok0 + i] = dl;
+        }
+        // dw^T = v gh^T - delta, ds^T = dw^T K_{n-1}, dq += ds k over the key tiles jt <= row
+        f32x4 gq[4];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) gq[qq] = *reinterpret_cast<const f32x4*>(&sm.g[i][16 * qq + 4 * lg]);
+        f32x4 dqi = zero4();
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+          if (jt <= row) {
+            f32x4 dw = zero4();
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.v[16 * jt + l16][16 * qq + 4 * lg]);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) dw = mfma(av[r], gq[qq][r], dw);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float ds = (dw[r] * iv - dl) * kp[jt][r];
+              dqi = mfma(ds, sm.kx[16 * jt + 4 * lg + r][l16], dqi);
+            }
+          }
+        }
+        wave_fence();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[(16 * row + 4 * lg + r) * kLP + l16] += dqi[r];
+      }
+      __syncthreads();
+    }
+    reduce_rows(sm.y, dq, tok_of(nch - 1), nv_of(nch - 1), scale, tid);
+    // the segment's G increments
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int f = 16 * (w + kWaves * u) + l16;
+      float z = gzs[u];
+      z += __shfl_xor(z, 16);
+      z += __shfl_xor(z, 32);
+      if (has[u] && f < W) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(gslot + (long long)f * kDV + 16 * dt + 4 * lg) = gt[u][dt];
+        if (lg == 0) gslot[(long long)W * kDV + f] = -z;
+      }
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------------------------------
+// 5. Pass B: dv, dk, chunks in reverse, G (the gradient of the state after the chunk) in the owners'
+// accumulators, seeded with the segment's suffix from the reverse scan.
+
+template <int NT>
+struct SmemB {
+  using G = BG<NT>;
+  alignas(16) float z[G::YR][kLV];   // Z^T rows of each owner, then each wavefront's partial dk rows
+  alignas(16) float gm[G::WP][kLV];  // G [f][d], copied by the owners at the chunk start
+  alignas(16) float ax[kC][kLR];
+  alignas(16) float kx[kC][kLR];
+  alignas(16) float v[kC][kLV];
+  alignas(16) float gh[kC][kLV];
+  float delta[kC];
+  int code[G::WP];
+};
+
+template <int NT, typename E>
+__global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(const E* __restrict__ q, const E* __restrict__ k,
+                                                           const E* __restrict__ v,
+                                                           const float* __restrict__ gslots,
+                                                           const float* __restrict__ ghat,
+                                                           const float* __restrict__ dlt, float* __restrict__ dk,
+                                                           float* __restrict__ dv, SeqMap seq, int L,
+                                                           long long nslot, long long stride, float scale) {
+  using G = BG<NT>;
+  constexpr int W = G::W, NU = G::NU, NFT = G::NFT;
+  __shared__ SmemB<NT> sm;
+  const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // dv tiles (key tile jw, value tiles 2 hw and 2 hw + 1) with the intra-chunk part of key tile jw;
+  // the wavefronts with hw = 1 also take dw, ds and ds^T a of that key tile.  The pairing puts the
+  // heavy key tiles on the SIMDs whose other wavefront owns fewer feature tiles.
+  const int jw = (0x23231010 >> (4 * w)) & 15, hw = (w >> 1) & 1;
+  const Rows R{sm.ax, sm.kx, sm.v, sm.gh, nullptr, sm.delta};
+  LaneF lf[NU];
+  bool has[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    lf[u] = unpack(feature_code<NT>(16 * (w + kWaves * u) + l16));
+    has[u] = w + kWaves * u < NFT;
+  }
+  for (int f = tid; f < G::WP; f += kThreads) sm.code[f] = feature_code<NT>(f);
+  float* part = &sm.z[16 * w][0];  // this wavefront's partial dk rows [token][coordinate]
 
   for_each_piece<false>(seq, blockIdx.x, blockIdx.y, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
     const float* gslot = gslots + pc.slot * stride;
-    for (int e = tid; e < WP * kDV; e += kThreads) {
-      const int f = e / kDV, d = e % kDV;
-      sm.st[f][d] = f < W ? gslot[(long long)f * kDV + d] : 0.f;
+    f32x4 gt[NU][4];
+    float gzf[NU];  // G_z, one feature per lane
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int f = 16 * (w + kWaves * u) + l16;
+      const bool fv = has[u] && f < W;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        gt[u][dt] = fv ? *reinterpret_cast<const f32x4*>(gslot + (long long)f * kDV + 16 * dt + 4 * lg) : zero4();
+      gzf[u] = fv ? gslot[(long long)W * kDV + f] : 0.f;
     }
-    for (int f = tid; f < WP; f += kThreads) sm.zt[f] = f < W ? gslot[(long long)W * kDV + f] : 0.f;
     const int nch = (pc.n + kC - 1) / kC;
     auto nv_of = [&](int c) { return min(kC, pc.n - c * kC); };
     auto tok_of = [&](int c) { return pc.tok + (long long)c * kC; };
     Pre<E, 2> pre;
-    pre.load(q, k, v, ghat, nullptr, dlt, tok_of(nch - 1), nv_of(nch - 1), scale, tid);
-    __syncthreads();
+    pre.load(q, k, v, ghat, nullptr, dlt, tok_of(nch - 1), nv_of(nch - 1), tid);
     for (int c = nch - 1; c >= 0; --c) {
       const int nv = nv_of(c);
       const long long tok0 = tok_of(c);
-      pre.store(sm, tid);
-      const int cn = c > 0 ? c - 1 : c;  // the first chunk reloads itself (no conditional load)
-      pre.load(q, k, v, ghat, nullptr, dlt, tok_of(cn), nv_of(cn), scale, tid);
-      __syncthreads();
-      expand<NT, true>(sm, w, l, nv);
-      __syncthreads();
-      if (w == 0) {
-        weights<NT>(sm, l16, lg, nv);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        dscores<NT>(sm, l16, lg);
+      pre.store(R, nv, scale, tid);
+      if (c < nch - 1) reduce_rows(sm.z, dk, tok_of(c + 1), nv_of(c + 1), 1.f, tid);
+      if (has[0]) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+          if (has[u])
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+              *reinterpret_cast<f32x4*>(&sm.gm[16 * (w + kWaves * u) + l16][16 * dt + 4 * lg]) = gt[u][dt];
       }
+      const int cn = c > 0 ? c - 1 : c;  // the first chunk reloads itself (no conditional load)
+      pre.load(q, k, v, ghat, nullptr, dlt, tok_of(cn), nv_of(cn), tid);
       __syncthreads();
-      if (w < kDV / 16) {
-        // dv, value tile dt = w: sum_{i>=j} w_ij gh_i (intra) + phi(k_j)^T G_S
-        const int dt = w;
-        f32x4 acc = mm<kC>(f32x4{0.f, 0.f, 0.f, 0.f}, l16, lg, [&](int m, int kk) { return sm.wt[kk][m]; },
-                           [&](int kk, int n) { return sm.gr[kk][16 * dt + n]; });
-        acc = mm<WP>(acc, l16, lg, [&](int m, int kk) { return sm.phik[m][kk]; },
-                     [&](int kk, int n) { return sm.st[kk][16 * dt + n]; });
+
+      if (has[0]) {
+        // Z^T = G^T-tiles x v + G_z into the owner's rows
+#pragma unroll 1
+        for (int jt = 0; jt < 4; ++jt) {
+          f32x4 zt[NU];
+#pragma unroll
+          for (int u = 0; u < NU; ++u) zt[u] = zero4();
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const f32x4 vv = *reinterpret_cast<const f32x4*>(&sm.v[16 * jt + l16][16 * dt + 4 * lg]);
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+              if (has[u])
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zt[u] = mfma(gt[u][dt][r], vv[r], zt[u]);
+          }
+#pragma unroll
+          for (int u = 0; u < NU; ++u)
+            if (has[u])
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                sm.z[16 * (w + kWaves * u) + 4 * lg + r][16 * jt + l16] = zt[u][r] + __shfl(gzf[u], 4 * lg + r);
+        }
+        // G^T += gh^T phi(a), G_z -= phi(a)^T delta
+        float gs[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) gs[u] = 0.f;
+#pragma unroll 2
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * qq + 4 * lg + r;
+            const float dli = sm.delta[i];
+            float b[NU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+              b[u] = phi(&sm.ax[i][0], lf[u]);
+              gs[u] = fmaf(b[u], dli, gs[u]);
+            }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              const float a = sm.gh[i][16 * dt + l16];
+#pragma unroll
+              for (int u = 0; u < NU; ++u)
+                if (has[u]) gt[u][dt] = mfma(a, b[u], gt[u][dt]);
+            }
+          }
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+          float z = gs[u];
+          z += __shfl_xor(z, 16);
+          z += __shfl_xor(z, 32);
+          gzf[u] -= z;
+        }
+        wave_fence();
+        // J_phi(k_j)^T Z_j over the owner's features, one lane per key
+        dispatch_index<0, kWaves>(w, [&](auto WI) {
+          constexpr int WW = decltype(WI)::value;
+          if constexpr (WW < G::NWF) {
+            float x[kDK], out[kDK];
+            load_coords(&sm.kx[l][0], x);
+#pragma unroll
+            for (int d = 0; d < kDK; ++d) out[d] = 0.f;
+            own_vjp<NT, WW>(x, &sm.z[0][l], out);
+            wave_fence();
+#pragma unroll
+            for (int d = 0; d < kDK; ++d) part[l * kLP + d] = out[d];
+          }
+        });
+      } else {
+#pragma unroll
+        for (int d = 0; d < kDK; ++d) part[l * kLP + d] = 0.f;
+      }
+
+      // dv tiles (jw, 2 hw + e): phi(K) G over all features (the copy in LDS), plus w^T gh in the chunk
+      f32x4 acc[2] = {zero4(), zero4()};
+#pragma unroll 1
+      for (int qq = 0; qq < NFT; ++qq)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int j = 4 * lg + r;
-          if (j < nv) dv[(tok0 + j) * kDV + 16 * dt + l16] = acc[r];
+          const int f = 16 * qq + 4 * lg + r;
+          const float a = phi(&sm.kx[16 * jw + l16][0], unpack(sm.code[f]));
+#pragma unroll
+          for (int e = 0; e < 2; ++e) acc[e] = mfma(a, sm.gm[f][16 * (2 * hw + e) + l16], acc[e]);
         }
-      } else {
-        // Z = V G_S^T + G_z, feature tiles w - 4, w, w + 4, ...
-        for (int t = w - kDV / 16; t < G::NFT; t += kWaves - kDV / 16) {
-          const f32x4 zv = mm<kDV>(f32x4{0.f, 0.f, 0.f, 0.f}, l16, lg, [&](int m, int kk) { return sm.vr[m][kk]; },
-                                   [&](int kk, int n) { return sm.st[16 * t + n][kk]; });
+      const f32x4 kb = *reinterpret_cast<const f32x4*>(&sm.kx[16 * jw + l16][4 * lg]);
+      const int j = 16 * jw + l16;
+      f32x4 dki = zero4();
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sm.y[4 * lg + r][16 * t + l16] = zv[r] + sm.zt[16 * t + l16];
-        }
-      }
-      __syncthreads();
-      // dk: the Jacobian over this wavefront's features (lanes 0..15 = tokens), and (wavefront 0) the
-      // intra-chunk sum_{i>=j} ds_ij a_i into wt
-      if (l < kC) {
-        float x[kDK], out[kDK];
+      for (int it = 0; it < 4; ++it) {
+        if (it >= jw) {
+          const f32x4 aa = *reinterpret_cast<const f32x4*>(&sm.ax[16 * it + l16][4 * lg]);
+          f32x4 sc = zero4();
 #pragma unroll
-        for (int d = 0; d < kDK; ++d) {
-          x[d] = sm.kr[l][d];
-          out[d] = 0.f;
-        }
-        feature_vjp<NT>(w, x, &sm.y[l][0], out);
+          for (int s = 0; s < 4; ++s) sc = mfma(aa[s], kb[s], sc);  // [query i][key j]
+          f32x4 wt, kp;
 #pragma unroll
-        for (int d = 0; d < kDK; ++d) sm.dpart[w][l][d] = out[d];
-      }
-      if (w == 0) {
-        const f32x4 di = mm<kC>(f32x4{0.f, 0.f, 0.f, 0.f}, l16, lg, [&](int m, int kk) { return sm.ds[kk][m]; },
-                                [&](int kk, int n) { return sm.ar[kk][n]; });
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * it + 4 * lg + r;
+            const bool ok = j <= i && i < nv;
+            wt[r] = ok ? taylor_kernel<NT>(sc[r]) : 0.f;
+            float d = 0.f;
+            if constexpr (NT > 1) d = taylor_kernel<NT - 1>(sc[r]);
+            kp[r] = ok ? d : 0.f;
+          }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sm.wt[4 * lg + r][l16] = di[r];
-      }
-      __syncthreads();
-      if (tid < kC * kDK) {
-        const int j = tid / kDK, d = tid % kDK;
-        float s = sm.wt[j][d];
+          for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) s += sm.dpart[ww][j][d];
-        if (j < nv) dk[(tok0 + j) * kDK + d] = s;
-      }
-      // G_S += phi(A)^T gh, G_z -= phi(A)^T delta
+            for (int r = 0; r < 4; ++r)
+              acc[e] = mfma(wt[r], sm.gh[16 * it + 4 * lg + r][16 * (2 * hw + e) + l16], acc[e]);
+          if (hw) {
+            f32x4 dw = zero4();
 #pragma unroll
-      for (int u = 0; u < G::TPW; ++u) {
-        const int t = w + u * kWaves;
-        if (t < G::NTILE) {
-          const int ft = t / (kDV / 16), dt = t % (kDV / 16);
-          f32x4 acc;
+            for (int qq = 0; qq < 4; ++qq) {
+              const f32x4 ga = *reinterpret_cast<const f32x4*>(&sm.gh[16 * it + l16][16 * qq + 4 * lg]);
+              const f32x4 vb = *reinterpret_cast<const f32x4*>(&sm.v[j][16 * qq + 4 * lg]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[r] = sm.st[16 * ft + 4 * lg + r][16 * dt + l16];
-          acc = mm<kC>(acc, l16, lg, [&](int m, int kk) { return sm.phia[kk][16 * ft + m]; },
-                       [&](int kk, int n) { return sm.gr[kk][16 * dt + n]; });
+              for (int r = 0; r < 4; ++r) dw = mfma(ga[r], vb[r], dw);
+            }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sm.st[16 * ft + 4 * lg + r][16 * dt + l16] = acc[r];
+            for (int r = 0; r < 4; ++r) {
+              const int i = 16 * it + 4 * lg + r;
+              const float ds = (dw[r] - sm.delta[i]) * kp[r];
+              dki = mfma(ds, sm.ax[i][l16], dki);
+            }
+          }
         }
       }
-      if (tid < WP) {
-        float sg = 0.f;
 #pragma unroll
-        for (int i = 0; i < kC; ++i) sg = fmaf(sm.phia[i][tid], sm.delta[i], sg);
-        sm.zt[tid] -= sg;
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jj = 16 * jw + 4 * lg + r;
+          if (jj < nv) dv[(tok0 + jj) * kDV + 16 * (2 * hw + e) + l16] = acc[e][r];
+        }
+      if (hw) {
+        wave_fence();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[(16 * jw + 4 * lg + r) * kLP + l16] += dki[r];
       }
       __syncthreads();
     }
+    reduce_rows(sm.z, dk, tok_of(0), nv_of(0), 1.f, tid);
   });
 }
 
@@ -569,8 +919,8 @@ __global__ __launch_bounds__(256) void bwd_rscan_kernel(float* __restrict__ ws, 
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Segments: about 256 workgroups (one per CU: the LDS holds the running state), never more than the
-// chunks.
+// Segments: about 256 workgroups (one per CU: the LDS holds a chunk's rows and the feature-major
+// buffers), never more than the chunks.
 BwdPlan plan_for(int BH, int N) {
   const int nchunk = cdiv(N, kC);
   long long want = (256 + BH - 1) / BH;
@@ -598,15 +948,13 @@ int bwd_run(const BwdArgs& a) {
   const dim3 grid(p.nseg, a.BH), block(kThreads);
   const long long elems = BG<NT>::W * (long long)(kDV + 1);
   const dim3 sgrid(cdiv(elems, 256), a.BH), sblock(256);
-  bwd_forward_kernel<NT, E, 0><<<grid, block, 0, a.stream>>>(q, k, v, nullptr, nullptr, sslots, nullptr, nullptr,
-                                                              nullptr, nullptr, seq, p.L, p.nseg, a.s.stride,
-                                                              a.s.scale);
+  bwd_state_kernel<NT, E><<<grid, block, 0, a.stream>>>(k, v, sslots, seq, p.L, p.nseg, a.s.stride);
   bwd_scan_kernel<<<sgrid, sblock, 0, a.stream>>>(sslots, a.state, p.nseg, a.s.stride, elems, seq, p.L);
-  bwd_forward_kernel<NT, E, 1><<<grid, block, 0, a.stream>>>(q, k, v, a.g, a.o, sslots, gslots, ghat, dlt, a.dq, seq,
-                                                              p.L, p.nseg, a.s.stride, a.s.scale);
+  bwd_dq_kernel<NT, E><<<grid, block, 0, a.stream>>>(q, k, v, a.g, a.o, sslots, gslots, ghat, dlt, a.dq, seq, p.L,
+                                                     p.nseg, a.s.stride, a.s.scale);
   bwd_rscan_kernel<<<sgrid, sblock, 0, a.stream>>>(gslots, a.dstate, p.nseg, a.s.stride, elems, seq, p.L);
-  bwd_reverse_kernel<NT, E><<<grid, block, 0, a.stream>>>(q, k, v, gslots, ghat, dlt, a.dk, a.dv, seq, p.L, p.nseg,
-                                                          a.s.stride, a.s.scale);
+  bwd_dkv_kernel<NT, E><<<grid, block, 0, a.stream>>>(q, k, v, gslots, ghat, dlt, a.dk, a.dv, seq, p.L, p.nseg,
+                                                      a.s.stride, a.s.scale);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
