@@ -248,6 +248,49 @@ __device__ __forceinline__ void load_coords(const float* row, float (&x)[kDK]) {
   }
 }
 
+// Runs f with the number of feature-tile slots this wavefront owns as a compile-time constant, so
+// that the per-slot work of a phase has no branches inside its unrolled loops.
+template <int NU, class F>
+__device__ __forceinline__ void with_slots(bool two, F&& f) {
+  if constexpr (NU > 1) {
+    if (two)
+      f(std::integral_constant<int, 2>{});
+    else
+      f(std::integral_constant<int, 1>{});
+  } else {
+    f(std::integral_constant<int, 1>{});
+  }
+}
+
+// acc[u][dt] += sum over the chunk's tokens t of A[t][16 dt + l16] sw(t) phi_f(x_t), f the lane's feature
+// of slot u (the transposed state tiles), and zs[u] += sum_t phi_f(x_t) zw(t) over this lane's tokens,
+// for the first NA slots.  Tokens of the contraction: t = 16 qq + 4 lg + r at step (qq, r).
+template <int NA, int NU, class SW, class ZW>
+__device__ __forceinline__ void state_update(f32x4 (&acc)[NU][4], float (&zs)[NU], const float (*A)[kLV],
+                                             const float (*X)[kLR], const LaneF (&lf)[NU], int l16, int lg, SW sw,
+                                             ZW zw) {
+#pragma unroll 2
+  for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 16 * qq + 4 * lg + r;
+      const float s = sw(t), z = zw(t);
+      float b[NA];
+#pragma unroll
+      for (int u = 0; u < NA; ++u) {
+        const float p = phi(&X[t][0], lf[u]);
+        b[u] = p * s;
+        zs[u] = fmaf(p, z, zs[u]);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const float a = A[t][16 * dt + l16];
+#pragma unroll
+        for (int u = 0; u < NA; ++u) acc[u][dt] = mfma(a, b[u], acc[u][dt]);
+      }
+    }
+}
+
 // Sum of the eight wavefronts' partial rows (dq or dk) of a finished chunk, times `mul`.
 __device__ __forceinline__ void reduce_rows(const float (*buf)[kLV], float* out, long long tok0, int nv, float mul,
                                             int tid) {
@@ -258,6 +301,18 @@ __device__ __forceinline__ void reduce_rows(const float (*buf)[kLV], float* out,
     for (int ww = 0; ww < kWaves; ++ww) s += (&buf[16 * ww][0])[i * kLP + d];
     if (i < nv) out[(tok0 + i) * kDK + d] = mul * s;
   }
+}
+
+// dv tiles (jw, 2 hw + e) of a chunk: lane element r is dv[16 jw + 4 lg + r][16 (2 hw + e) + l16].
+__device__ __forceinline__ void store_dv(const f32x4 (&t)[2], float* dv, long long tok0, int nv, int jw, int hw, int l16,
+                                         int lg) {
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = 16 * jw + 4 * lg + r;
+      if (j < nv) dv[(tok0 + j) * kDV + 16 * (2 * hw + e) + l16] = t[e][r];
+    }
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -285,6 +340,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(const E* __restrict
     lf[u] = unpack(feature_code<NT>(16 * (w + kWaves * u) + l16));
     has[u] = w + kWaves * u < G::NFT;
   }
+  const bool two = NU > 1 && has[NU - 1];  // a second feature tile
 
   for_each_piece<false>(seq, blockIdx.x, blockIdx.y, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
     f32x4 st[NU][4];
@@ -306,26 +362,11 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(const E* __restrict
       pre.load(nullptr, k, v, nullptr, nullptr, nullptr, tok_of(cn), nv_of(cn), tid);
       __syncthreads();
       if (has[0]) {
-        // S^T += V^T phi(K), z += sum phi(k): tokens t = 16 qq + 4 lg + r of the contraction
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * qq + 4 * lg + r;
-            float b[NU];
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-              b[u] = phi(&sm.kx[t][0], lf[u]);
-              zs[u] += b[u];
-            }
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-              const float a = sm.v[t][16 * dt + l16];
-#pragma unroll
-              for (int u = 0; u < NU; ++u)
-                if (has[u]) st[u][dt] = mfma(a, b[u], st[u][dt]);
-            }
-          }
+        // S^T += V^T phi(K), z += sum phi(k)
+        with_slots<NU>(two, [&](auto NAc) __attribute__((always_inline)) {
+          state_update<decltype(NAc)::value>(st, zs, sm.v, sm.kx, lf, l16, lg, [](int) { return 1.f; },
+                                             [](int) { return 1.f; });
+        });
       }
       __syncthreads();
     }
@@ -396,6 +437,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const E* __restrict__ 
     lf[u] = unpack(feature_code<NT>(16 * (w + kWaves * u) + l16));
     has[u] = w + kWaves * u < G::NFT;
   }
+  const bool two = NU > 1 && has[NU - 1];  // a second feature tile
   float* part = &sm.y[16 * w][0];  // this wavefront's partial dq rows [token][coordinate]
 
   for_each_piece<false>(seq, blockIdx.x, blockIdx.y, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
@@ -488,93 +530,52 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const E* __restrict__ 
       __syncthreads();
 
       if (has[0]) {
-        // Y^T = S^T-tiles x g / den_i - z delta_i (S, z before the chunk) into the owner's rows
-        float zp[NU][4];  // z[16 ft + 4 lg + r]
+        with_slots<NU>(two, [&](auto NAc) __attribute__((always_inline)) {
+          constexpr int NA = decltype(NAc)::value;
+          // Y^T = S^T-tiles x g / den_i - z delta_i (S, z before the chunk) into the owner's rows
+          float zp[NA][4];  // z[16 ft + 4 lg + r]
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
+          for (int u = 0; u < NA; ++u)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) zp[u][r] = __shfl(zf[u], 4 * lg + r);
+            for (int r = 0; r < 4; ++r) zp[u][r] = __shfl(zf[u], 4 * lg + r);
 #pragma unroll 1
-        for (int it = 0; it < 4; ++it) {
-          f32x4 yr[NU];
+          for (int it = 0; it < 4; ++it) {
+            f32x4 yr[NA];
 #pragma unroll
-          for (int u = 0; u < NU; ++u) yr[u] = zero4();
+            for (int u = 0; u < NA; ++u) yr[u] = zero4();
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const f32x4 gv = *reinterpret_cast<const f32x4*>(&sm.g[16 * it + l16][16 * dt + 4 * lg]);
+            for (int dt = 0; dt < 4; ++dt) {
+              const f32x4 gv = *reinterpret_cast<const f32x4*>(&sm.g[16 * it + l16][16 * dt + 4 * lg]);
 #pragma unroll
-            for (int u = 0; u < NU; ++u)
-              if (has[u])
+              for (int u = 0; u < NA; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) yr[u] = mfma(st[u][dt][r], gv[r], yr[u]);
-          }
-          const int i = 16 * it + l16;
-          const float ivi = sm.inv[i], dli = sm.delta[i];
+            }
+            const int i = 16 * it + l16;
+            const float ivi = sm.inv[i], dli = sm.delta[i];
 #pragma unroll
-          for (int u = 0; u < NU; ++u)
-            if (has[u])
+            for (int u = 0; u < NA; ++u)
 #pragma unroll
               for (int r = 0; r < 4; ++r)
                 sm.y[16 * (w + kWaves * u) + 4 * lg + r][i] = yr[u][r] * ivi - zp[u][r] * dli;
-        }
-        // S^T += V^T phi(K), z += sum phi(k)
-        float zs[NU];
-#pragma unroll
-        for (int u = 0; u < NU; ++u) zs[u] = 0.f;
-#pragma unroll 2
-        for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * qq + 4 * lg + r;
-            float b[NU];
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-              b[u] = phi(&sm.kx[t][0], lf[u]);
-              zs[u] += b[u];
-            }
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-              const float a = sm.v[t][16 * dt + l16];
-#pragma unroll
-              for (int u = 0; u < NU; ++u)
-                if (has[u]) st[u][dt] = mfma(a, b[u], st[u][dt]);
-            }
           }
+          // S^T += V^T phi(K), z += sum phi(k)
+          float zs[NU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          float z = zs[u];
-          z += __shfl_xor(z, 16);
-          z += __shfl_xor(z, 32);
-          zf[u] += z;
-          if (has[u] && lg == 0) sm.zt[16 * (w + kWaves * u) + l16] = zf[u];
-        }
-        // G^T += g^T (phi(a) / den), and this lane's share of sum phi(a) delta
-        float gs[NU];
+          for (int u = 0; u < NU; ++u) zs[u] = 0.f;
+          state_update<NA>(st, zs, sm.v, sm.kx, lf, l16, lg, [](int) { return 1.f; }, [](int) { return 1.f; });
 #pragma unroll
-        for (int u = 0; u < NU; ++u) gs[u] = 0.f;
-#pragma unroll 2
-        for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 16 * qq + 4 * lg + r;
-            const float ivi = sm.inv[i], dli = sm.delta[i];
-            float b[NU];
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-              const float p = phi(&sm.ax[i][0], lf[u]);
-              b[u] = p * ivi;
-              gs[u] = fmaf(p, dli, gs[u]);
-            }
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-              const float a = sm.g[i][16 * dt + l16];
-#pragma unroll
-              for (int u = 0; u < NU; ++u)
-                if (has[u]) gt[u][dt] = mfma(a, b[u], gt[u][dt]);
-            }
+          for (int u = 0; u < NA; ++u) {
+            float z = zs[u];
+            z += __shfl_xor(z, 16);
+            z += __shfl_xor(z, 32);
+            zf[u] += z;
+            if (lg == 0) sm.zt[16 * (w + kWaves * u) + l16] = zf[u];
           }
-#pragma unroll
-        for (int u = 0; u < NU; ++u) gzs[u] += gs[u];
+          // G^T += g^T (phi(a) / den), and this lane's share of sum phi(a) delta
+          state_update<NA>(gt, gzs, sm.g, sm.ax, lf, l16, lg, [&](int i) { return sm.inv[i]; },
+                           [&](int i) { return sm.delta[i]; });
+        });
         wave_fence();
         // J_phi(a_i)^T Y_i over the owner's features, one lane per query
         dispatch_index<0, kWaves>(w, [&](auto WI) {
@@ -692,6 +693,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(const E* __restrict__
     lf[u] = unpack(feature_code<NT>(16 * (w + kWaves * u) + l16));
     has[u] = w + kWaves * u < NFT;
   }
+  const bool two = NU > 1 && has[NU - 1];  // a second feature tile
   for (int f = tid; f < G::WP; f += kThreads) sm.code[f] = feature_code<NT>(f);
   float* part = &sm.z[16 * w][0];  // this wavefront's partial dk rows [token][coordinate]
 
@@ -719,71 +721,55 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(const E* __restrict__
       pre.store(R, nv, scale, tid);
       if (c < nch - 1) reduce_rows(sm.z, dk, tok_of(c + 1), nv_of(c + 1), 1.f, tid);
       if (has[0]) {
+        with_slots<NU>(two, [&](auto NAc) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
-          if (has[u])
+          for (int u = 0; u < decltype(NAc)::value; ++u)
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
               *reinterpret_cast<f32x4*>(&sm.gm[16 * (w + kWaves * u) + l16][16 * dt + 4 * lg]) = gt[u][dt];
+        });
       }
       const int cn = c > 0 ? c - 1 : c;  // the first chunk reloads itself (no conditional load)
       pre.load(q, k, v, ghat, nullptr, dlt, tok_of(cn), nv_of(cn), tid);
       __syncthreads();
 
       if (has[0]) {
-        // Z^T = G^T-tiles x v + G_z into the owner's rows
+        with_slots<NU>(two, [&](auto NAc) __attribute__((always_inline)) {
+          constexpr int NA = decltype(NAc)::value;
+          // Z^T = G^T-tiles x v + G_z into the owner's rows
 #pragma unroll 1
-        for (int jt = 0; jt < 4; ++jt) {
-          f32x4 zt[NU];
+          for (int jt = 0; jt < 4; ++jt) {
+            f32x4 zt[NA];
 #pragma unroll
-          for (int u = 0; u < NU; ++u) zt[u] = zero4();
+            for (int u = 0; u < NA; ++u) zt[u] = zero4();
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const f32x4 vv = *reinterpret_cast<const f32x4*>(&sm.v[16 * jt + l16][16 * dt + 4 * lg]);
+            for (int dt = 0; dt < 4; ++dt) {
+              const f32x4 vv = *reinterpret_cast<const f32x4*>(&sm.v[16 * jt + l16][16 * dt + 4 * lg]);
 #pragma unroll
-            for (int u = 0; u < NU; ++u)
-              if (has[u])
+              for (int u = 0; u < NA; ++u)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) zt[u] = mfma(gt[u][dt][r], vv[r], zt[u]);
-          }
+            }
 #pragma unroll
-          for (int u = 0; u < NU; ++u)
-            if (has[u])
+            for (int u = 0; u < NA; ++u)
 #pragma unroll
               for (int r = 0; r < 4; ++r)
                 sm.z[16 * (w + kWaves * u) + 4 * lg + r][16 * jt + l16] = zt[u][r] + __shfl(gzf[u], 4 * lg + r);
-        }
-        // G^T += gh^T phi(a), G_z -= phi(a)^T delta
-        float gs[NU];
-#pragma unroll
-        for (int u = 0; u < NU; ++u) gs[u] = 0.f;
-#pragma unroll 2
-        for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 16 * qq + 4 * lg + r;
-            const float dli = sm.delta[i];
-            float b[NU];
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-              b[u] = phi(&sm.ax[i][0], lf[u]);
-              gs[u] = fmaf(b[u], dli, gs[u]);
-            }
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-              const float a = sm.gh[i][16 * dt + l16];
-#pragma unroll
-              for (int u = 0; u < NU; ++u)
-                if (has[u]) gt[u][dt] = mfma(a, b[u], gt[u][dt]);
-            }
           }
+          // G^T += gh^T phi(a), G_z -= phi(a)^T delta
+          float gs[NU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          float z = gs[u];
-          z += __shfl_xor(z, 16);
-          z += __shfl_xor(z, 32);
-          gzf[u] -= z;
-        }
+          for (int u = 0; u < NU; ++u) gs[u] = 0.f;
+          state_update<NA>(gt, gs, sm.gh, sm.ax, lf, l16, lg, [](int) { return 1.f; },
+                           [&](int i) { return sm.delta[i]; });
+#pragma unroll
+          for (int u = 0; u < NA; ++u) {
+            float z = gs[u];
+            z += __shfl_xor(z, 16);
+            z += __shfl_xor(z, 32);
+            gzf[u] -= z;
+          }
+        });
         wave_fence();
         // J_phi(k_j)^T Z_j over the owner's features, one lane per key
         dispatch_index<0, kWaves>(w, [&](auto WI) {
@@ -858,13 +844,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(const E* __restrict__
           }
         }
       }
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int jj = 16 * jw + 4 * lg + r;
-          if (jj < nv) dv[(tok0 + jj) * kDV + 16 * (2 * hw + e) + l16] = acc[e][r];
-        }
+      store_dv(acc, dv, tok0, nv, jw, hw, l16, lg);
       if (hw) {
         wave_fence();
 #pragma unroll
