@@ -265,11 +265,11 @@ __device__ __forceinline__ void with_slots(bool two, F&& f) {
 // acc[u][dt] += sum over the chunk's tokens t of A[t][16 dt + l16] sw(t) phi_f(x_t), f the lane's feature
 // of slot u (the transposed state tiles), and zs[u] += sum_t phi_f(x_t) zw(t) over this lane's tokens,
 // for the first NA slots.  Tokens of the contraction: t = 16 qq + 4 lg + r at step (qq, r).
-template <int NA, int NU, class SW, class ZW>
+template <int NA, int UNR = 2, int NU, class SW, class ZW>
 __device__ __forceinline__ void state_update(f32x4 (&acc)[NU][4], float (&zs)[NU], const float (*A)[kLV],
                                              const float (*X)[kLR], const LaneF (&lf)[NU], int l16, int lg, SW sw,
                                              ZW zw) {
-#pragma unroll 2
+#pragma unroll UNR
   for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(const E* __restrict
       if (has[0]) {
         // S^T += V^T phi(K), z += sum phi(k)
         with_slots<NU>(two, [&](auto NAc) __attribute__((always_inline)) {
-          state_update<decltype(NAc)::value>(st, zs, sm.v, sm.kx, lf, l16, lg, [](int) { return 1.f; },
+          state_update<decltype(NAc)::value, 4>(st, zs, sm.v, sm.kx, lf, l16, lg, [](int) { return 1.f; },
                                              [](int) { return 1.f; });
         });
       }
@@ -760,7 +760,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(const E* __restrict__
           float gs[NU];
 #pragma unroll
           for (int u = 0; u < NU; ++u) gs[u] = 0.f;
-          state_update<NA>(gt, gs, sm.gh, sm.ax, lf, l16, lg, [](int) { return 1.f; },
+          state_update<NA, 4>(gt, gs, sm.gh, sm.ax, lf, l16, lg, [](int) { return 1.f; },
                            [&](int i) { return sm.delta[i]; });
 #pragma unroll
           for (int u = 0; u < NA; ++u) {
@@ -792,7 +792,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(const E* __restrict__
 
       // dv tiles (jw, 2 hw + e): phi(K) G over all features (the copy in LDS), plus w^T gh in the chunk
       f32x4 acc[2] = {zero4(), zero4()};
-#pragma unroll 1
+#pragma unroll 2
       for (int qq = 0; qq < NFT; ++qq)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
