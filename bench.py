@@ -262,7 +262,7 @@ def backward_prefill(rs, torch, dev, q, k, v, reps=3):
     with outputs from the float32 forward and a seeded upstream gradient; HIP events.  Algorithmic
     flops per token-head (float32 matrix work, unpadded W = 153): state pass 2*W*65, pass A
     (S^T gh, S update, G update) 6*W*64 + 2*W, pass B (G^T phi(k), G v, G update) 6*W*64, plus the
-    intra-chunk products 4*(C+1)/2*(16 + 64) at C = 16."""
+    intra-chunk products 4*(C+1)/2*(16 + 64) at C = 64."""
     B, H, N = k.shape[:3]
     cfg = rs.config(NT, DK, DV, 0, 1.0, rs.TAYLOR_BF16)
     f32 = rs.config(NT, DK, DV, 0, 1.0, rs.TAYLOR_F32)
@@ -284,7 +284,7 @@ def backward_prefill(rs, torch, dev, q, k, v, reps=3):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
-    flops = B * H * N * (2 * W * (DV + 1) + 12 * W * DV + 2 * W + 4 * 17 / 2 * (DK + DV))
+    flops = B * H * N * (2 * W * (DV + 1) + 12 * W * DV + 2 * W + 4 * 65 / 2 * (DK + DV))
     return {"us": us, "tok_s": B * N / us * 1e6, "TFLOPs": flops / us / 1e6,
             "frac_fp32_mfma": flops / us / 1e6 / FP32_PEAK_TFLOPS}
 
