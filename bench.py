@@ -1,8 +1,9 @@
 """Benchmark of the Taylor-attention hot path on one MI355X.
 
 One step = one pass of the whole path:
-  * taylor_state_init + taylor_attn_prefill over one batch of B=4 x H=16 x N=8192
-    bfloat16 tokens (d_k=16, d_v=64, n=3, chunk 128), float32 outputs and final state;
+  * taylor_attn_prefill_into from an empty history (no incoming state array) over one
+    batch of B=4 x H=16 x N=8192 bfloat16 tokens (d_k=16, d_v=64, n=3, chunk 128),
+    float32 outputs and final state;
   * 1,000 taylor_attn_decode_step calls on 64 sequences x 16 heads whose float32
     states (153 x 65 per head) were built by a state-only prefill of a seeded
     65,536-token prefix (setup, untimed).  The 1,000 decode launches are replayed
@@ -168,7 +169,7 @@ def big_decode(rs, synth, torch, dev, seqs=512, steps=100, reps=3, eager=False):
 
 def order_sweep(rs, synth, torch, dev, reps=3):
     """Prefill at the order-sweep shape (B=1, H=16, N=16,384, float32, chunk 64) for n = 1..5, timed with
-    HIP events (state init + prefill, as in the main step).  Algorithmic flops per token-head:
+    HIP events (a prefill from an empty history writing the final state, as in the main step).  Algorithmic flops per token-head:
     2*W*65 (state update) + 2*W*65 (readout) + intra-chunk scores 2*d_k*(C+1)/2 + PV 2*65*(C+1)/2."""
     B, H, N, C = 1, 16, 16384, 64
     x = synth.make_qkv(5, B, H, N, DK, DV, synth.F32)
@@ -179,14 +180,12 @@ def order_sweep(rs, synth, torch, dev, reps=3):
         cfg = rs.config(n, DK, DV, C, 1.0, rs.TAYLOR_F32)
         st = torch.empty((B, H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
         ws = rs.new_workspace(cfg, B, H, N, dev)
-        rs.taylor_state_init(st, cfg)
-        rs.taylor_attn_prefill(q, k, v, o, st, ws, cfg)
+        rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            rs.taylor_state_init(st, cfg)
-            rs.taylor_attn_prefill(q, k, v, o, st, ws, cfg)
+            rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg)
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
@@ -230,7 +229,8 @@ def varlen_prefill(rs, synth, torch, dev, reps=5):
 
 def centered_prefill(rs, torch, dev, q, k, v, reps=5):
     """The expanded-softmax readout (orders 1, 2) on the main step's prefill inputs (B4 x H16 x N8192,
-    bfloat16): state init + prefill, HIP events; the states are the truncated kernel's of n = order+1."""
+    bfloat16): a prefill from an empty history writing the final state, HIP events; the states are the
+    truncated kernel's of n = order+1."""
     B, H, N = k.shape[:3]
     o = torch.empty((B, H, N, DV), dtype=torch.float32, device=dev)
     res = {}
@@ -240,8 +240,7 @@ def centered_prefill(rs, torch, dev, q, k, v, reps=5):
         ws = rs.new_workspace(cfg, B, H, N, dev)
 
         def step():
-            rs.taylor_state_init(st, cfg)
-            rs.taylor_attn_prefill(q, k, v, o, st, ws, cfg)
+            rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg)
 
         step()
         torch.cuda.synchronize()
@@ -387,8 +386,7 @@ def main():
     def step(evs):
         cur = torch.cuda.current_stream()
         evs[0].record(cur)
-        rs.taylor_state_init(pstate, pcfg)
-        rs.taylor_attn_prefill(pq, pk, pv, po, pstate, pws, pcfg)
+        rs.taylor_attn_prefill_into(pq, pk, pv, po, None, pstate, pws, pcfg)
         evs[1].record(cur)
         if graph is not None:
             graph.replay()

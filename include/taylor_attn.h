@@ -152,6 +152,25 @@ int taylor_state_init(float* state, int B, int H, const taylor_config* cfg, hipS
 int taylor_attn_prefill(const void* q, const void* k, const void* v, float* o, float* state, void* workspace, int B,
                         int H, int N, const taylor_config* cfg, hipStream_t stream);
 
+/* taylor_attn_prefill with the incoming and the final state in separate arrays
+ * (Abstract: the state after the call is the state before it plus the sum over
+ * the call's tokens, so where each lives is free).
+ *   state_in  : [B,H,stride] float32, read only: the state of the tokens before
+ *               this call; NULL = an empty history (no zeroed array needed);
+ *   state_out : [B,H,stride] float32, written: the state including these N
+ *               tokens; NULL = discarded.  At least one of o and state_out must
+ *               be non-NULL.  state_out may be state_in (in place, as
+ *               taylor_attn_prefill) or an array that does not overlap it
+ *               (TAYLOR_ERR_INVALID_ARG otherwise); out of place it serves
+ *               e.g. continuing a cached prefix state without overwriting it;
+ *   q, k, v, o, workspace, B, H, N, cfg: as taylor_attn_prefill (the same
+ *               workspace size).
+ * N == 0 copies state_in to state_out (zero when state_in is NULL).  B*H == 0
+ * is a no-op. */
+int taylor_attn_prefill_into(const void* q, const void* k, const void* v, float* o, const float* state_in,
+                             float* state_out, void* workspace, int B, int H, int N, const taylor_config* cfg,
+                             hipStream_t stream);
+
 /* Bytes of device workspace taylor_attn_prefill_varlen needs for these sizes
  * (may be 0); it depends on the sizes only, not on the individual lengths.
  * Host only.  Negative taylor_status if cfg or sizes are invalid;

@@ -38,6 +38,7 @@ EXPORTS = (
     "taylor_prefill_workspace_bytes",
     "taylor_state_init",
     "taylor_attn_prefill",
+    "taylor_attn_prefill_into",
     "taylor_prefill_varlen_workspace_bytes",
     "taylor_attn_prefill_varlen",
     "taylor_prefill_backward_workspace_bytes",
@@ -101,6 +102,7 @@ def lib():
         "taylor_prefill_workspace_bytes": (i64, [cfgp, i, i, i]),
         "taylor_state_init": (i, [p, i, i, cfgp, p]),
         "taylor_attn_prefill": (i, [p, p, p, p, p, p, i, i, i, cfgp, p]),
+        "taylor_attn_prefill_into": (i, [p, p, p, p, p, p, p, i, i, i, cfgp, p]),
         "taylor_prefill_varlen_workspace_bytes": (i64, [cfgp, i, i, i, i64]),
         "taylor_attn_prefill_varlen": (i, [p, p, p, p, p, p, p, i, i, i, i64, cfgp, p]),
         "taylor_prefill_backward_workspace_bytes": (i64, [cfgp, i, i, i]),
@@ -219,6 +221,15 @@ def taylor_attn_prefill(q, k, v, o, state, workspace, cfg, stream=None):
     rc = lib().taylor_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), _ptr(workspace), B, H, N,
                                    ctypes.byref(cfg), _stream(stream, k.device))
     _check(rc, "taylor_attn_prefill")
+
+
+def taylor_attn_prefill_into(q, k, v, o, state_in, state_out, workspace, cfg, stream=None):
+    """Causal prefill over [B, H, N, d] inputs from state_in (or None: empty history) into state_out
+    (or None: discarded; the same tensor as state_in, or one that does not overlap it)."""
+    B, H, N = k.shape[:3]
+    rc = lib().taylor_attn_prefill_into(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state_in), _ptr(state_out),
+                                        _ptr(workspace), B, H, N, ctypes.byref(cfg), _stream(stream, k.device))
+    _check(rc, "taylor_attn_prefill_into")
 
 
 def taylor_attn_prefill_varlen(q, k, v, o, state, workspace, cu_seqlens, max_seqlen, cfg, stream=None):

@@ -111,11 +111,12 @@ taylor::SeqMap packed_map(const int32_t* cu, int n_seqs, int H, int max_seqlen, 
 int map_launch(int rc) { return rc == 0 ? TAYLOR_OK : rc == -2 ? TAYLOR_ERR_UNSUPPORTED : TAYLOR_ERR_HIP; }
 
 // Shared by the equal-length and ragged prefills once sizes are checked: pointers, workspace and launch.
-int prefill_common(const Shape& s, int C, const void* q, const void* k, const void* v, float* o, float* state,
-                   void* workspace, int BH, const taylor::SeqMap& seq, hipStream_t stream) {
+int prefill_common(const Shape& s, int C, const void* q, const void* k, const void* v, float* o,
+                   const float* state_in, float* state, void* workspace, int BH, const taylor::SeqMap& seq,
+                   hipStream_t stream) {
   if (!k || !v || !aligned16(k) || !aligned16(v)) return TAYLOR_ERR_INVALID_ARG;
   if (o && (!q || !aligned16(q) || !aligned16(o))) return TAYLOR_ERR_INVALID_ARG;
-  if (state && !aligned16(state)) return TAYLOR_ERR_INVALID_ARG;
+  if ((state && !aligned16(state)) || (state_in && !aligned16(state_in))) return TAYLOR_ERR_INVALID_ARG;
   const int64_t need = ws_bytes(s, C, BH, seq);
   if (need < 0) return (int)need;
   if (need > 0 && (!workspace || !aligned16(workspace))) return TAYLOR_ERR_INVALID_ARG;
@@ -127,6 +128,7 @@ int prefill_common(const Shape& s, int C, const void* q, const void* k, const vo
   a.k = k;
   a.v = v;
   a.o = o;
+  a.state_in = state_in;
   a.state = state;
   a.ws = workspace;
   a.BH = BH;
@@ -236,7 +238,35 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, float* o, f
   if (!o && !state) return TAYLOR_ERR_INVALID_ARG;
   const int BH = B * H;
   if (BH == 0 || N == 0) return TAYLOR_OK;
-  return prefill_common(s, chunk_of(cfg), q, k, v, o, state, workspace, BH, equal_lengths(B, H, N), stream);
+  return prefill_common(s, chunk_of(cfg), q, k, v, o, state, state, workspace, BH, equal_lengths(B, H, N), stream);
+}
+
+int taylor_attn_prefill_into(const void* q, const void* k, const void* v, float* o, const float* state_in,
+                             float* state_out, void* workspace, int B, int H, int N, const taylor_config* cfg,
+                             hipStream_t stream) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if ((rc = supported(cfg, s)) != TAYLOR_OK) return rc;
+  if ((rc = check_sizes(B, H, N)) != TAYLOR_OK) return rc;
+  if (!o && !state_out) return TAYLOR_ERR_INVALID_ARG;
+  const long long BH = (long long)B * H;
+  if (BH == 0) return TAYLOR_OK;
+  if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out))) return TAYLOR_ERR_INVALID_ARG;
+  if (state_in && state_out && state_in != state_out) {
+    // the two state arrays are the same array or disjoint
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(state_in), b0 = reinterpret_cast<uintptr_t>(state_out);
+    const uintptr_t bytes = (uintptr_t)(BH * s.stride) * sizeof(float);
+    if (a0 < b0 + bytes && b0 < a0 + bytes) return TAYLOR_ERR_INVALID_ARG;
+  }
+  if (N == 0) {
+    // no tokens: the final state is the incoming one
+    if (!state_out || state_out == state_in) return TAYLOR_OK;
+    return map_launch(state_in ? taylor::state_copy_launch(state_out, state_in, BH * s.stride, stream)
+                               : taylor::state_zero_launch(state_out, BH * s.stride, stream));
+  }
+  return prefill_common(s, chunk_of(cfg), q, k, v, o, state_in, state_out, workspace, (int)BH, equal_lengths(B, H, N),
+                        stream);
 }
 
 int taylor_attn_prefill_varlen(const void* q, const void* k, const void* v, float* o, float* state, void* workspace,
@@ -251,7 +281,7 @@ int taylor_attn_prefill_varlen(const void* q, const void* k, const void* v, floa
   const int BH = n_seqs * H;
   if (BH == 0 || total_tokens == 0) return TAYLOR_OK;  // every sequence is empty: states unchanged
   if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return TAYLOR_ERR_INVALID_ARG;
-  return prefill_common(s, chunk_of(cfg), q, k, v, o, state, workspace, BH,
+  return prefill_common(s, chunk_of(cfg), q, k, v, o, state, state, workspace, BH,
                         packed_map(cu_seqlens, n_seqs, H, max_seqlen, total_tokens), stream);
 }
 

@@ -162,7 +162,7 @@ template <int NT, typename E>
 int coef_run(const PrefillArgs& a, const CenteredPlan& p) {
   const dim3 grid((unsigned)a.seq.grid_x(p.L), (unsigned)a.seq.grid_y(a.BH)), block(kThreads);
   auto kern = a.seq.packed ? centered_coef_kernel<NT, E, true> : centered_coef_kernel<NT, E, false>;
-  kern<<<grid, block, 0, a.stream>>>((const E*)a.q, (const E*)a.k, p.slots, a.state, p.multi ? 1 : 0, p.zc, a.seq,
+  kern<<<grid, block, 0, a.stream>>>((const E*)a.q, (const E*)a.k, p.slots, a.state_in, p.multi ? 1 : 0, p.zc, a.seq,
                                      p.L, p.nslot, a.s.stride, a.s.scale, p.coef);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }

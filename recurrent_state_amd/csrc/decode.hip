@@ -187,6 +187,10 @@ __global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ p, long 
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+__global__ __launch_bounds__(256) void copy_kernel(float4* __restrict__ d, const float4* __restrict__ s, long long n4) {
+  for (long long i = blockIdx.x * 256ll + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) d[i] = s[i];
+}
+
 template <int NT, int DK, int DV, bool CENT>
 int decode_go(const DecodeArgs& a) {
   const dim3 grid(a.BH), block(kDecodeThreads);
@@ -245,6 +249,16 @@ bool decode_has(int nt, int dk, int dv) { return decode_find(nt, dk, dv) != null
 int decode_launch(const DecodeArgs& a) {
   DecodeFn f = decode_find(a.s.nt, a.s.dk, a.s.dv);
   return f ? f(a) : -2;
+}
+
+int state_copy_launch(float* dst, const float* src, long long count, hipStream_t stream) {
+  const long long n4 = count / 4;
+  long long blocks = (n4 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  copy_kernel<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(reinterpret_cast<float4*>(dst),
+                                                                 reinterpret_cast<const float4*>(src), n4);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 int state_zero_launch(float* state, long long count, hipStream_t stream) {

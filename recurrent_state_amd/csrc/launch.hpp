@@ -164,8 +164,9 @@ __device__ __forceinline__ void for_each_piece(const SeqMap& seq, long long x, l
 struct PrefillArgs {
   Shape s;
   const void *q, *k, *v;
-  float* o;        // may be null (state-only)
-  float* state;    // may be null (start from zero, discard)
+  float* o;               // may be null (state-only)
+  const float* state_in;  // the history before the call; null: empty
+  float* state;           // where the final state goes; null: discarded.  Equal to state_in or disjoint
   void* ws;        // workspace
   int BH, N, C;    // (sequence, head) pairs, tokens per sequence (the longest when ragged), chunk
   SeqMap seq;      // token placement
@@ -179,11 +180,13 @@ bool decode_has(int nt, int dk, int dv);
 int state_zero_launch(float* state, long long count, hipStream_t stream);
 
 // Exclusive prefix over the pieces of each (sequence, head) pair in `ws` (slots of `stride` floats
-// placed as SeqMap describes for pieces of L tokens, `nslot` per row), seeded with `state` when
-// non-null, else zero; the total is written to `state` when non-null.  Only the first `elems`
-// floats of each slot are touched.
-int seg_scan_launch(float* ws, float* state, int BH, long long nslot, long long stride, long long elems,
-                    bool write_prefix, const SeqMap& seq, int L, hipStream_t stream);
+// placed as SeqMap describes for pieces of L tokens, `nslot` per row), seeded with `seed` when
+// non-null, else zero; the total is written to `total` when non-null (it may be `seed`).  Only the
+// first `elems` floats of each slot are touched.
+int seg_scan_launch(float* ws, const float* seed, float* total, int BH, long long nslot, long long stride,
+                    long long elems, bool write_prefix, const SeqMap& seq, int L, hipStream_t stream);
+// dst = src over `count` floats (a multiple of 4; 16-byte aligned).
+int state_copy_launch(float* dst, const float* src, long long count, hipStream_t stream);
 
 // Portable prefill path (any compiled (n, d_k, d_v), chunk 64 or 128), VALU float32.
 bool prefill_generic_has(int nt, int dk, int dv, int C);

@@ -100,25 +100,30 @@ __global__ __launch_bounds__(kThreads) void seg_state_kernel(const T* __restrict
   if (tid < kFB && fb0 + tid < W) out[(long long)W * DV + fb0 + tid] = accz;
 }
 
-// Exclusive prefix over the segments of each (sequence, head) pair, seeded with the incoming state;
-// the total goes back to the state.  grid = (ceil(elems/256), pairs).
-__global__ __launch_bounds__(kThreads) void seg_scan_kernel(float* __restrict__ ws, float* __restrict__ state,
+// Exclusive prefix over the segments of each (sequence, head) pair, seeded with the incoming state
+// (`seed`, null: zero); the total goes to `total` (null: discarded; may be `seed`).
+// grid = (ceil(elems/256), pairs).
+__global__ __launch_bounds__(kThreads) void seg_scan_kernel(float* __restrict__ ws, const float* seed, float* total,
                                                             long long nslot, long long stride, long long elems,
                                                             int write_prefix, SeqMap seq, int L) {
   const long long e = blockIdx.x * (long long)kThreads + threadIdx.x;
-  if (e >= elems) return;
   const long long bh = blockIdx.y;
+  if (e >= elems) {
+    // the padding after S and z of the final state: zero, whatever the array held before
+    if (total && e < stride) total[bh * stride + e] = 0.f;
+    return;
+  }
   long long first;
   int n;
   seq.pair_slots(bh, nslot, L, first, n);
-  float run = state ? state[bh * stride + e] : 0.f;
+  float run = seed ? seed[bh * stride + e] : 0.f;
   float* w = ws + first * stride + e;
   for (int s = 0; s < n; ++s) {
     const float t = w[s * stride];
     if (write_prefix) w[s * stride] = run;
     run += t;
   }
-  if (state) state[bh * stride + e] = run;
+  if (total) total[bh * stride + e] = run;
 }
 
 // Outputs of one chunk.  grid = (chunks, heads).  The chunk's exclusive prefix
@@ -243,10 +248,10 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
 
-int seg_scan_launch(float* ws, float* state, int BH, long long nslot, long long stride, long long elems,
-                    bool write_prefix, const SeqMap& seq, int L, hipStream_t stream) {
-  seg_scan_kernel<<<dim3(cdiv(elems, kThreads), BH), dim3(kThreads), 0, stream>>>(ws, state, nslot, stride, elems,
-                                                                                  write_prefix ? 1 : 0, seq, L);
+int seg_scan_launch(float* ws, const float* seed, float* total, int BH, long long nslot, long long stride,
+                    long long elems, bool write_prefix, const SeqMap& seq, int L, hipStream_t stream) {
+  seg_scan_kernel<<<dim3(cdiv(total ? stride : elems, kThreads), BH), dim3(kThreads), 0, stream>>>(
+      ws, seed, total, nslot, stride, elems, write_prefix ? 1 : 0, seq, L);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
@@ -274,7 +279,9 @@ int generic_run(const PrefillArgs& a) {
   seg_state_kernel<NT, DK, DV, T><<<dim3(nseg_used, a.BH, nfb), dim3(kThreads), 0, a.stream>>>(
       (const T*)a.k, (const T*)a.v, ws, a.N, L, nseg_used, a.s.stride);
   if (hipGetLastError() != hipSuccess) return -3;
-  if (seg_scan_launch(ws, a.state, a.BH, nseg_used, a.s.stride, elems, a.o != nullptr, a.seq, L, a.stream)) return -3;
+  if (seg_scan_launch(ws, a.state_in, a.state, a.BH, nseg_used, a.s.stride, elems, a.o != nullptr, a.seq, L,
+                      a.stream))
+    return -3;
   if (a.o) {
     if (a.C == 64)
       readout_kernel<NT, DK, DV, 64, T><<<dim3(nchunk, a.BH), dim3(kThreads), 0, a.stream>>>(

@@ -654,7 +654,8 @@ int run_pipe(const PrefillArgs& a) {
   pipe_kernel_for<NT, false>(a.seq.packed, cent)<<<grid, block, 0, a.stream>>>(
       q, k, v, nullptr, nullptr, ws, cent ? zc : nullptr, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
   if (hipGetLastError() != hipSuccess) return -3;
-  if (seg_scan_launch(ws, a.state, a.BH, p.nslot, a.s.stride, elems, a.o != nullptr, a.seq, p.L, a.stream))
+  if (seg_scan_launch(ws, a.state_in, a.state, a.BH, p.nslot, a.s.stride, elems, a.o != nullptr, a.seq, p.L,
+                      a.stream))
     return -3;
   if (a.o) {
     if (cent) {

@@ -87,7 +87,8 @@ struct WideSmem {
 struct WideIO {
   float* slots;        // several segments per pair: workspace slots (placed as SeqMap describes) of
                        // prefixes (readout) or increments (state pass)
-  float* state;        // one segment per pair: incoming / final state [pairs][stride], or null
+  float* state;        // one segment per pair: the final state [pairs][stride], or null
+  const float* state_in;  // one segment per pair: the incoming state, or null (may equal state)
   float* part_num;     // [blocks][token-heads][d_v] partial numerators
   float* part_den;     // [blocks][token-heads] partial denominators
   float* out;          // a single block: the outputs [token-heads][d_v]
@@ -290,8 +291,8 @@ __device__ __forceinline__ void piece_state(const WideIO& io, const SeqPiece& pc
   dst = nullptr;
   if (io.multi) {
     if (READOUT) init = io.slots + pc.slot * io.stride;
-  } else if (READOUT && io.state) {
-    init = io.state + pc.pair * io.stride;
+  } else if (READOUT && io.state_in) {
+    init = io.state_in + pc.pair * io.stride;
   }
   if (!READOUT)
     dst = io.slots + pc.slot * io.stride;
@@ -365,6 +366,8 @@ __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(const E* __restr
         const int a = f0 + FP * g + l;
         if (a < W) dst[(long long)W * kDV + a] = sm.z[FP * g + l];
       }
+      // the padding after S and z: zero, whatever the array held before
+      if (dst && fb == 0 && g == 0 && l < io.stride - (long long)W * (kDV + 1)) dst[(long long)W * (kDV + 1) + l] = 0.f;
     });
     return;
   }
@@ -582,12 +585,13 @@ int wide_run(const PrefillArgs& a) {
   const dim3 grid((unsigned)lay.gx, (unsigned)a.seq.grid_y(a.BH), NB), block(kThreads);
   if (!outputs || multi) {
     const bool zpass = cent && outputs;
-    const WideIO io{slots, nullptr, nullptr, nullptr, nullptr, a.s.stride, lay.nslot, tokens, multi, nullptr,
+    const WideIO io{slots, nullptr, nullptr, nullptr, nullptr, nullptr, a.s.stride, lay.nslot, tokens, multi, nullptr,
                     zpass ? zc : nullptr};
     wide_kernel_for<NT, E, false>(a.seq.packed, zpass)<<<grid, block, 0, a.stream>>>(q, k, v, io, a.seq, lay.L,
                                                                                     a.s.scale);
     if (hipGetLastError() != hipSuccess) return -3;
-    if (seg_scan_launch(slots, a.state, a.BH, lay.nslot, a.s.stride, elems, outputs, a.seq, lay.L, a.stream))
+    if (seg_scan_launch(slots, a.state_in, a.state, a.BH, lay.nslot, a.s.stride, elems, outputs, a.seq, lay.L,
+                        a.stream))
       return -3;
     if (!outputs) return 0;
   }
@@ -596,7 +600,8 @@ int wide_run(const PrefillArgs& a) {
     const CenteredPlan cp{lay.L, lay.nslot, slots, multi, zc, 2 * kCS, reinterpret_cast<float4*>(coef)};
     if (const int rc = centered_coef_launch(a, cp)) return rc;
   }
-  const WideIO io{slots,  multi ? nullptr : a.state, part_num, part_den, a.o, a.s.stride, lay.nslot, tokens, multi,
+  const WideIO io{slots,  multi ? nullptr : a.state, multi ? nullptr : a.state_in, part_num, part_den, a.o, a.s.stride,
+                  lay.nslot, tokens, multi,
                   cent ? coef : nullptr, nullptr};
   wide_kernel_for<NT, E, true>(a.seq.packed, cent)<<<grid, block, 0, a.stream>>>(q, k, v, io, a.seq, lay.L,
                                                                                 a.s.scale);

@@ -30,7 +30,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     declared = _header_functions()
-    assert len(declared) == 14
+    assert len(declared) == 15
     assert sorted(rs.EXPORTS) == declared
     out = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(taylor_[a-z_0-9]+)$", out, re.M))
@@ -144,6 +144,31 @@ def test_prefill_validation():
     # documented no-ops (no launch): N == 0, B*H == 0
     assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 0, cfg) == rs.TAYLOR_OK
     assert _prefill(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, cfg) == rs.TAYLOR_OK
+
+
+def _into(q, k, v, o, sin, sout, ws, B, H, N, cfg):
+    return rs.lib().taylor_attn_prefill_into(q, k, v, o, sin, sout, ws, B, H, N, ctypes.byref(cfg) if cfg else None,
+                                             None)
+
+
+def test_prefill_into_validation():
+    cfg = rs.config(3, 16, 64, 64)
+    E = rs.TAYLOR_ERR_INVALID_ARG
+    stride_bytes = 4 * rs.taylor_state_stride(cfg)
+    assert _into(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, None) == E
+    assert _into(FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1, 1, 64, cfg) == E  # nothing to produce
+    assert _into(FAKE, FAKE, FAKE, FAKE, MIS, FAKE, FAKE, 1, 1, 64, cfg) == E
+    assert _into(FAKE, FAKE, FAKE, FAKE, FAKE, MIS, FAKE, 1, 1, 64, cfg) == E
+    # the two state arrays must be the same array or disjoint (2 x 2 heads here)
+    assert _into(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, FAKE, 2, 2, 64, cfg) == E
+    assert _into(FAKE, FAKE, FAKE, FAKE, FAKE + 4 * stride_bytes - 16, FAKE, FAKE, 2, 2, 64, cfg) == E
+    assert _into(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 1, 64, cfg) == E
+    assert _into(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, cfg) == E  # workspace required
+    assert _into(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, rs.config(7, 16, 64)) == rs.TAYLOR_ERR_UNSUPPORTED
+    # no launch: B*H == 0; N == 0 in place or with the final state discarded
+    assert _into(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 64, cfg) == rs.TAYLOR_OK
+    assert _into(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 4, 0, cfg) == rs.TAYLOR_OK
+    assert _into(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 1, 4, 0, cfg) == rs.TAYLOR_OK
 
 
 def test_readout_field():

@@ -1,0 +1,108 @@
+"""GPU tests of taylor_attn_prefill_into: the incoming and the final state in separate arrays.
+
+"Expanding Attention" (Huang, arXiv:2610.20637), Abstract: the state after a call is the state
+before it plus the call's own sum, so where the two live is free.  A fresh call (no incoming array)
+must give exactly what zeroing a state and prefilling in place gives, and a continuation from one
+array into another exactly what the in-place continuation gives, leaving the incoming array as it
+was.  The arithmetic is the same in both forms, so the comparisons are bit for bit; every prefill
+path is exercised (bf16 matrix-core kernel, float32 feature-block kernel with one and with several
+segments per head, n = 4, the portable kernel, the expanded-softmax readout).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import recurrent_state_amd as rs
+import synth
+from gpu_util import announce
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+CASES = [  # (label, n, d_k, d_v, chunk, dtype, readout, B, H, N)
+    ("bf16-n3", 3, 16, 64, 64, "bf16", 0, 2, 3, 700),
+    ("f32-n3-segments", 3, 16, 64, 64, "f32", 0, 1, 2, 900),
+    ("f32-n3-one-segment", 3, 16, 64, 64, "f32", 0, 4, 64, 128),
+    ("f32-n4", 4, 16, 64, 64, "f32", 0, 1, 16, 200),
+    ("portable-d8", 3, 8, 32, 64, "f32", 0, 2, 2, 300),
+    ("centered-bf16", 3, 16, 64, 64, "bf16", 1, 1, 2, 500),
+    ("centered-f32", 3, 16, 64, 64, "f32", 1, 1, 2, 500),
+]
+
+
+def _cfg(n, dk, dv, C, dtype, readout):
+    return rs.config(n, dk, dv, C, 1.0, rs.TAYLOR_BF16 if dtype == "bf16" else rs.TAYLOR_F32, readout)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fresh_equals_init_then_prefill(case):
+    import torch
+
+    label, n, dk, dv, C, dtype, readout, B, H, N = case
+    cfg = _cfg(n, dk, dv, C, dtype, readout)
+    x = synth.make_qkv(500 + n, B, H, N, dk, dv, dtype)
+    announce("prefill-into fresh", label)
+    q, k, v = x.torch(DEV)
+    ws = rs.new_workspace(cfg, B, H, N, DEV)
+    o1 = torch.empty((B, H, N, dv), device=DEV)
+    st1 = rs.new_state(B, H, cfg, DEV)
+    rs.taylor_state_init(st1, cfg)
+    rs.taylor_attn_prefill(q, k, v, o1, st1, ws, cfg)
+    o2 = torch.empty_like(o1)
+    st2 = torch.full_like(st1, float("nan"))  # never read
+    rs.taylor_attn_prefill_into(q, k, v, o2, None, st2, ws, cfg)
+    assert torch.equal(o1, o2)
+    assert torch.equal(st1, st2)
+    # state only
+    st3 = torch.full_like(st1, float("nan"))
+    rs.taylor_attn_prefill_into(q, k, v, None, None, st3, ws, cfg)
+    S, z = rs.state_views(st3, cfg)
+    ref = oracle.state(x.k64[0, 0], x.v64[0, 0], n)
+    got = np.concatenate([S[0, 0].cpu().numpy(), z[0, 0].cpu().numpy()[:, None]], axis=1)
+    tol = 2.0**-7 if dtype == "bf16" else 1e-5
+    assert np.max(np.abs(got - ref)) <= tol * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_out_of_place_continuation(case):
+    import torch
+
+    label, n, dk, dv, C, dtype, readout, B, H, N = case
+    cfg = _cfg(n, dk, dv, C, dtype, readout)
+    N1 = N // 3
+    x = synth.make_qkv(600 + n, B, H, N, dk, dv, dtype)
+    announce("prefill-into continuation", label)
+    q, k, v = x.torch(DEV)
+    part = lambda t, a, b: t[:, :, a:b].contiguous()
+    ws = rs.new_workspace(cfg, B, H, N, DEV)
+    prefix = torch.empty(rs.new_state(B, H, cfg, DEV).shape, device=DEV)
+    rs.taylor_attn_prefill_into(part(q, 0, N1), part(k, 0, N1), part(v, 0, N1), None, None, prefix, ws, cfg)
+    keep = prefix.clone()
+    # in place on a copy, and out of place from the cached prefix
+    inplace = prefix.clone()
+    o1 = torch.empty((B, H, N - N1, dv), device=DEV)
+    rs.taylor_attn_prefill(part(q, N1, N), part(k, N1, N), part(v, N1, N), o1, inplace, ws, cfg)
+    out = torch.full_like(prefix, float("nan"))
+    o2 = torch.empty_like(o1)
+    rs.taylor_attn_prefill_into(part(q, N1, N), part(k, N1, N), part(v, N1, N), o2, prefix, out, ws, cfg)
+    assert torch.equal(prefix, keep), "the incoming state changed"
+    assert torch.equal(o1, o2)
+    assert torch.equal(inplace, out)
+
+
+def test_no_tokens_copies_or_zeroes():
+    import torch
+
+    cfg = _cfg(3, 16, 64, 64, "bf16", 0)
+    announce("prefill-into N=0")
+    x = synth.make_qkv(700, 2, 3, 100, 16, 64, "bf16")
+    q, k, v = x.torch(DEV)
+    src = torch.empty(rs.new_state(2, 3, cfg, DEV).shape, device=DEV)
+    rs.taylor_attn_prefill_into(q, k, v, None, None, src, rs.new_workspace(cfg, 2, 3, 100, DEV), cfg)
+    empty = [t[:, :, :0].contiguous() for t in (q, k, v)]
+    dst = torch.full_like(src, float("nan"))
+    rs.taylor_attn_prefill_into(*empty, None, src, dst, None, cfg)
+    assert torch.equal(dst, src)
+    rs.taylor_attn_prefill_into(*empty, None, None, dst, None, cfg)
+    assert bool((dst == 0).all())
