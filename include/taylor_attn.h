@@ -207,6 +207,18 @@ int taylor_attn_prefill_varlen(const void* q, const void* k, const void* v, floa
                                const int32_t* cu_seqlens, int n_seqs, int H, int max_seqlen, int64_t total_tokens,
                                const taylor_config* cfg, hipStream_t stream);
 
+/* taylor_attn_prefill_varlen with the incoming and the final states in separate
+ * arrays, as taylor_attn_prefill_into: state_in [n_seqs][H][stride] read only
+ * (NULL = empty histories), state_out written (NULL = discarded; the same array
+ * as state_in or one that does not overlap it, else TAYLOR_ERR_INVALID_ARG).
+ * Every row of state_out is written, an empty sequence's with its incoming
+ * state (zero when state_in is NULL).  Other arguments, sizes and errors as
+ * taylor_attn_prefill_varlen. */
+int taylor_attn_prefill_varlen_into(const void* q, const void* k, const void* v, float* o, const float* state_in,
+                                    float* state_out, void* workspace, const int32_t* cu_seqlens, int n_seqs, int H,
+                                    int max_seqlen, int64_t total_tokens, const taylor_config* cfg,
+                                    hipStream_t stream);
+
 /* Bytes of device workspace taylor_attn_prefill_backward needs (may be 0).  Host
  * only.  Negative taylor_status if cfg or sizes are invalid, or
  * TAYLOR_ERR_UNSUPPORTED where no backward kernel is compiled (below). */

@@ -41,6 +41,7 @@ EXPORTS = (
     "taylor_attn_prefill_into",
     "taylor_prefill_varlen_workspace_bytes",
     "taylor_attn_prefill_varlen",
+    "taylor_attn_prefill_varlen_into",
     "taylor_prefill_backward_workspace_bytes",
     "taylor_attn_prefill_backward",
     "taylor_attn_decode_step",
@@ -105,6 +106,7 @@ def lib():
         "taylor_attn_prefill_into": (i, [p, p, p, p, p, p, p, i, i, i, cfgp, p]),
         "taylor_prefill_varlen_workspace_bytes": (i64, [cfgp, i, i, i, i64]),
         "taylor_attn_prefill_varlen": (i, [p, p, p, p, p, p, p, i, i, i, i64, cfgp, p]),
+        "taylor_attn_prefill_varlen_into": (i, [p, p, p, p, p, p, p, p, i, i, i, i64, cfgp, p]),
         "taylor_prefill_backward_workspace_bytes": (i64, [cfgp, i, i, i]),
         "taylor_attn_prefill_backward": (i, [p, p, p, p, p, p, p, p, p, p, p, i, i, i, cfgp, p]),
         "taylor_attn_decode_step": (i, [p, p, p, p, p, i, i, cfgp, p]),
@@ -241,6 +243,18 @@ def taylor_attn_prefill_varlen(q, k, v, o, state, workspace, cu_seqlens, max_seq
                                           _ptr(cu_seqlens), n_seqs, H, int(max_seqlen), T, ctypes.byref(cfg),
                                           _stream(stream, k.device))
     _check(rc, "taylor_attn_prefill_varlen")
+
+
+def taylor_attn_prefill_varlen_into(q, k, v, o, state_in, state_out, workspace, cu_seqlens, max_seqlen, cfg,
+                                    stream=None):
+    """Ragged-batch prefill (as taylor_attn_prefill_varlen) from state_in (or None: empty histories) into
+    state_out (or None: discarded; the same tensor as state_in, or one that does not overlap it)."""
+    H, T = k.shape[:2]
+    n_seqs = cu_seqlens.shape[0] - 1
+    rc = lib().taylor_attn_prefill_varlen_into(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state_in), _ptr(state_out),
+                                               _ptr(workspace), _ptr(cu_seqlens), n_seqs, H, int(max_seqlen), T,
+                                               ctypes.byref(cfg), _stream(stream, k.device))
+    _check(rc, "taylor_attn_prefill_varlen_into")
 
 
 def taylor_attn_prefill_backward(q, k, v, o, g, state, dstate, dq, dk, dv, workspace, cfg, stream=None):

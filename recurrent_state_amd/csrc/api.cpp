@@ -285,6 +285,36 @@ int taylor_attn_prefill_varlen(const void* q, const void* k, const void* v, floa
                         packed_map(cu_seqlens, n_seqs, H, max_seqlen, total_tokens), stream);
 }
 
+int taylor_attn_prefill_varlen_into(const void* q, const void* k, const void* v, float* o, const float* state_in,
+                                    float* state_out, void* workspace, const int32_t* cu_seqlens, int n_seqs, int H,
+                                    int max_seqlen, int64_t total_tokens, const taylor_config* cfg,
+                                    hipStream_t stream) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if ((rc = supported(cfg, s)) != TAYLOR_OK) return rc;
+  if ((rc = check_varlen(n_seqs, H, max_seqlen, total_tokens)) != TAYLOR_OK) return rc;
+  if (!o && !state_out) return TAYLOR_ERR_INVALID_ARG;
+  const long long BH = (long long)n_seqs * H;
+  if (BH == 0) return TAYLOR_OK;
+  if ((state_in && !aligned16(state_in)) || (state_out && !aligned16(state_out))) return TAYLOR_ERR_INVALID_ARG;
+  if (state_in && state_out && state_in != state_out) {
+    // the two state arrays are the same array or disjoint
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(state_in), b0 = reinterpret_cast<uintptr_t>(state_out);
+    const uintptr_t bytes = (uintptr_t)(BH * s.stride) * sizeof(float);
+    if (a0 < b0 + bytes && b0 < a0 + bytes) return TAYLOR_ERR_INVALID_ARG;
+  }
+  if (total_tokens == 0) {
+    // every sequence is empty: each final state is its incoming one
+    if (!state_out || state_out == state_in) return TAYLOR_OK;
+    return map_launch(state_in ? taylor::state_copy_launch(state_out, state_in, BH * s.stride, stream)
+                               : taylor::state_zero_launch(state_out, BH * s.stride, stream));
+  }
+  if (!cu_seqlens || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) return TAYLOR_ERR_INVALID_ARG;
+  return prefill_common(s, chunk_of(cfg), q, k, v, o, state_in, state_out, workspace, (int)BH,
+                        packed_map(cu_seqlens, n_seqs, H, max_seqlen, total_tokens), stream);
+}
+
 int64_t taylor_prefill_backward_workspace_bytes(const taylor_config* cfg, int B, int H, int N) {
   Shape s;
   int rc = check_config(cfg, &s);

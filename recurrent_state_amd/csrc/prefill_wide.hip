@@ -544,7 +544,9 @@ WideLayout wide_layout(const Shape& s, int BH, const SeqMap& seq, bool outputs) 
   }
   lay.gx = seq.grid_x(lay.L);
   lay.nslot = seq.row_slots(lay.L);
-  lay.multi = lay.gx > 1 || cent;
+  // ragged batches always take the state pass and the scan, which writes the final state of every
+  // (sequence, head) row, empty sequences included (a single range writes only the rows it walks)
+  lay.multi = seq.packed || lay.gx > 1 || cent;
   // slots are needed for a state pass, and always for a state-only call (the scan sums them)
   lay.slot_floats = (lay.multi || !outputs) ? seq.rows(BH) * lay.nslot * s.stride : 0;
   lay.part_floats = (outputs && NB > 1) ? (long long)NB * seq.tokens(BH) * (kDV + 1) : 0;

@@ -30,7 +30,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     declared = _header_functions()
-    assert len(declared) == 15
+    assert len(declared) == 16
     assert sorted(rs.EXPORTS) == declared
     out = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(taylor_[a-z_0-9]+)$", out, re.M))
@@ -222,6 +222,25 @@ def test_varlen_workspace_bytes():
 def _varlen(q, k, v, o, st, ws, cu, n_seqs, H, N, T, cfg):
     return rs.lib().taylor_attn_prefill_varlen(q, k, v, o, st, ws, cu, n_seqs, H, N, T,
                                                ctypes.byref(cfg) if cfg else None, None)
+
+
+def test_varlen_into_validation():
+    cfg = rs.config(3, 16, 64, 64, 1.0, rs.TAYLOR_BF16)
+    E = rs.TAYLOR_ERR_INVALID_ARG
+    L = rs.lib()
+
+    def call(o, sin, sout, ws, cu, n_seqs, H, N, T):
+        return L.taylor_attn_prefill_varlen_into(FAKE, FAKE, FAKE, o, sin, sout, ws, cu, n_seqs, H, N, T,
+                                                 ctypes.byref(cfg), None)
+
+    assert call(None, FAKE, None, FAKE, FAKE, 4, 2, 100, 300) == E  # nothing to produce
+    assert call(FAKE, MIS, FAKE, FAKE, FAKE, 4, 2, 100, 300) == E
+    assert call(FAKE, FAKE, FAKE + 16, FAKE, FAKE, 4, 2, 100, 300) == E  # overlapping state arrays
+    assert call(FAKE, FAKE, FAKE, FAKE, None, 4, 2, 100, 300) == E  # offsets required
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 4, 2, 100, 300) == E
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 100, 401) == E  # more tokens than n_seqs * max_seqlen
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2, 100, 0) == rs.TAYLOR_OK  # no rows
+    assert call(FAKE, FAKE, FAKE, None, None, 4, 2, 100, 0) == rs.TAYLOR_OK  # in place, no tokens
 
 
 def test_varlen_validation():

@@ -106,3 +106,46 @@ def test_no_tokens_copies_or_zeroes():
     assert torch.equal(dst, src)
     rs.taylor_attn_prefill_into(*empty, None, None, dst, None, cfg)
     assert bool((dst == 0).all())
+
+
+RAGGED = [  # (label, n, dtype, lengths)
+    ("bf16-n3", 3, "bf16", [1, 63, 0, 700, 65, 5]),
+    ("f32-n3", 3, "f32", [200, 0, 31, 333]),
+    ("f32-n5", 5, "f32", [70, 0, 130]),
+    ("tiny", 3, "f32", [5, 0, 9]),  # a batch shorter than one chunk
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=[c[0] for c in RAGGED])
+def test_varlen_into(case):
+    # fresh = init + prefill, and out of place = in place, bit for bit, empty sequences included
+    import torch
+
+    label, n, dtype, lens = case
+    H = 2
+    cfg = _cfg(n, 16, 64, 64, dtype, 0)
+    x = synth.make_ragged(800 + n, lens, H, 16, 64, dtype)
+    announce("varlen-into", label, lens)
+    q, k, v = x.torch(DEV)
+    cu = x.torch_cu(DEV)
+    T, N = sum(lens), max(lens)
+    ws = rs.new_varlen_workspace(cfg, len(lens), H, N, T, DEV)
+    shape = (len(lens), H, rs.taylor_state_stride(cfg))
+    o1 = torch.empty((H, T, 64), device=DEV)
+    st1 = torch.empty(shape, device=DEV)
+    rs.taylor_state_init(st1, cfg)
+    rs.taylor_attn_prefill_varlen(q, k, v, o1, st1, ws, cu, N, cfg)
+    o2 = torch.empty_like(o1)
+    st2 = torch.full(shape, float("nan"), device=DEV)
+    rs.taylor_attn_prefill_varlen_into(q, k, v, o2, None, st2, ws, cu, N, cfg)
+    assert torch.equal(o1, o2)
+    assert torch.equal(st1, st2)
+    # continue the same batch from those states: in place on a copy, and out of place
+    inplace = st1.clone()
+    rs.taylor_attn_prefill_varlen(q, k, v, o1, inplace, ws, cu, N, cfg)
+    keep = st1.clone()
+    out = torch.full(shape, float("nan"), device=DEV)
+    rs.taylor_attn_prefill_varlen_into(q, k, v, o2, st1, out, ws, cu, N, cfg)
+    assert torch.equal(st1, keep), "the incoming states changed"
+    assert torch.equal(o1, o2)
+    assert torch.equal(inplace, out)
