@@ -48,6 +48,9 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDK = 16, kDV = 64;
 constexpr int kC = 64;  // tokens per chunk
@@ -71,6 +74,16 @@ struct BG {
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ f32x4 mfma(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// Two floats split into bfloat16 pairs hi = bf16(x), lo = bf16(x - hi) (nearest even).  For a product
+// of two bfloat16 values (at most 16 significant bits) hi + lo is exact.
+__device__ __forceinline__ void split_bf16x2(float a, float b, bf16x2& hi, bf16x2& lo) {
+  hi = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  const uint32_t u = __builtin_bit_cast(uint32_t, hi);
+  lo = __builtin_convertvector(f32x2{a - __uint_as_float(u << 16), b - __uint_as_float(u & 0xffff0000u)}, bf16x2);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(i16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ void wave_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -137,6 +150,7 @@ struct Rows {
   float (*g)[kLV];  // g (pass A) or gh (pass B)
   float* go;        // g . o per token (pass A)
   float* delta;     // delta per token (pass B)
+  uint16_t (*vt)[kC + 8] = nullptr;  // bfloat16 inputs: V^T as raw bfloat16 (the exact products' operand)
 };
 
 // One thread's share of a chunk's inputs, loaded a chunk ahead and stored to LDS when the chunk starts,
@@ -167,6 +181,10 @@ struct Pre {
     if constexpr (MODE != 0) {
       *reinterpret_cast<f32x2*>(&R.ax[t][2 * c]) = f32x2{ok ? scale * qa[0] : 0.f, ok ? scale * qa[1] : 0.f};
       if (c == 0) *reinterpret_cast<f32x4*>(&R.ax[t][kDK]) = f32x4{one, one, 0.f, 0.f};
+    }
+    if (R.vt) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) R.vt[8 * c + e][t] = ok ? (uint16_t)(__float_as_uint(vv[e]) >> 16) : (uint16_t)0;
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -291,6 +309,44 @@ __device__ __forceinline__ void state_update(f32x4 (&acc)[NU][4], float (&zs)[NU
     }
 }
 
+// bfloat16 inputs: acc[u][dt] += sum_t v[t][16 dt + l16] p_f(k_t) over the chunk's tokens, where
+// p_f = x[c0] x[c1] is the feature without its coefficient (applied by the caller), a product of two
+// bfloat16 values and so exactly hi + lo in bfloat16: two 16x16x16 bfloat16 MFMAs per 16 tokens give
+// the float32 products exactly.  zs[u] += sum_t p_f(k_t) over this lane's tokens.  Tokens of the
+// contraction at step qq: k = 4 lg + j <-> t = 16 qq + 4 lg + j.
+template <int NA, int NU>
+__device__ __forceinline__ void state_update_bf16(f32x4 (&acc)[NU][4], float (&zs)[NU], const uint16_t (*VT)[kC + 8],
+                                                  const float (*X)[kLR], const LaneF (&lf)[NU], int l16, int lg) {
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) {
+    const int t0 = 16 * qq + 4 * lg;
+    bf16x4 bh[NA], bl[NA];
+#pragma unroll
+    for (int u = 0; u < NA; ++u) {
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        p[j] = X[t0 + j][lf[u].o0] * X[t0 + j][lf[u].o1];
+        zs[u] += p[j];
+      }
+      bf16x2 h0, l0, h1, l1;
+      split_bf16x2(p[0], p[1], h0, l0);
+      split_bf16x2(p[2], p[3], h1, l1);
+      bh[u] = bf16x4{h0[0], h0[1], h1[0], h1[1]};
+      bl[u] = bf16x4{l0[0], l0[1], l1[0], l1[1]};
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const i16x4 a = *reinterpret_cast<const i16x4*>(&VT[16 * dt + l16][t0]);
+#pragma unroll
+      for (int u = 0; u < NA; ++u) {
+        acc[u][dt] = mfma_bf16(a, bh[u], acc[u][dt]);
+        acc[u][dt] = mfma_bf16(a, bl[u], acc[u][dt]);
+      }
+    }
+  }
+}
+
 // Sum of the eight wavefronts' partial rows (dq or dk) of a finished chunk, times `mul`.
 __device__ __forceinline__ void reduce_rows(const float (*buf)[kLV], float* out, long long tok0, int nv, float mul,
                                             int tid) {
@@ -321,6 +377,7 @@ __device__ __forceinline__ void store_dv(const f32x4 (&t)[2], float* dv, long lo
 struct SmemS {
   alignas(16) float kx[kC][kLR];
   alignas(16) float v[kC][kLV];
+  alignas(16) uint16_t vt[kDV][kC + 8];  // bfloat16 inputs
 };
 
 template <int NT, typename E>
@@ -332,7 +389,8 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(const E* __restrict
   __shared__ SmemS sm;
   const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const Rows R{nullptr, sm.kx, sm.v, nullptr, nullptr, nullptr};
+  constexpr bool BF = std::is_same_v<E, uint16_t>;
+  const Rows R{nullptr, sm.kx, sm.v, nullptr, nullptr, nullptr, BF ? sm.vt : nullptr};
   LaneF lf[NU];
   bool has[NU];
 #pragma unroll
@@ -364,8 +422,11 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(const E* __restrict
       if (has[0]) {
         // S^T += V^T phi(K), z += sum phi(k)
         with_slots<NU>(two, [&](auto NAc) __attribute__((always_inline)) {
-          state_update<decltype(NAc)::value, 4>(st, zs, sm.v, sm.kx, lf, l16, lg, [](int) { return 1.f; },
-                                             [](int) { return 1.f; });
+          if constexpr (BF)
+            state_update_bf16<decltype(NAc)::value>(st, zs, sm.vt, sm.kx, lf, l16, lg);
+          else
+            state_update<decltype(NAc)::value, 4>(st, zs, sm.v, sm.kx, lf, l16, lg, [](int) { return 1.f; },
+                                                  [](int) { return 1.f; });
         });
       }
       __syncthreads();
@@ -377,6 +438,12 @@ __global__ __launch_bounds__(kThreads) void bwd_state_kernel(const E* __restrict
       float z = zs[u];
       z += __shfl_xor(z, 16);
       z += __shfl_xor(z, 32);
+      if constexpr (BF) {
+        // the feature coefficient, left out of the products
+        z *= lf[u].cf;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) st[u][dt] *= lf[u].cf;
+      }
       if (has[u] && f < W) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(slot + (long long)f * kDV + 16 * dt + 4 * lg) = st[u][dt];
@@ -400,6 +467,7 @@ struct SmemA {
   float denp[kWaves][kC];  // phi(a_i) . z over each owner's features
   float inv[kC], delta[kC], go[kC];
   float zt[G::WP];  // z before the chunk
+  alignas(16) uint16_t vt[kDV][kC + 8];  // bfloat16 inputs
 };
 
 // Query-row tile of the intra-chunk work in pass A, by wavefront: waves 2, 3, 6, 7 own one feature
@@ -429,7 +497,10 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const E* __restrict__ 
   const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int row = row_of_wave(w);
-  const Rows R{sm.ax, sm.kx, sm.v, sm.g, sm.go, nullptr};
+  // bfloat16 inputs: S += phi(K)^T V on exact bfloat16 products; the registers then hold S_f / cf_f
+  // (cf_f the feature's coefficient), which the S gh product multiplies back
+  constexpr bool BF = std::is_same_v<E, uint16_t>;
+  const Rows R{sm.ax, sm.kx, sm.v, sm.g, sm.go, nullptr, BF ? sm.vt : nullptr};
   LaneF lf[NU];
   bool has[NU];
 #pragma unroll
@@ -452,6 +523,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const E* __restrict__ 
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         st[u][dt] = fv ? *reinterpret_cast<const f32x4*>(sslot + (long long)f * kDV + 16 * dt + 4 * lg) : zero4();
+        if constexpr (BF) st[u][dt] *= 1.0f / lf[u].cf;
         gt[u][dt] = zero4();
       }
       zf[u] = fv ? sslot[(long long)W * kDV + f] : 0.f;
@@ -549,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const E* __restrict__ 
 #pragma unroll
               for (int u = 0; u < NA; ++u)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) yr[u] = mfma(st[u][dt][r], gv[r], yr[u]);
+                for (int r = 0; r < 4; ++r) yr[u] = mfma(BF ? st[u][dt][r] * lf[u].cf : st[u][dt][r], gv[r], yr[u]);
             }
             const int i = 16 * it + l16;
             const float ivi = sm.inv[i], dli = sm.delta[i];
@@ -563,13 +635,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const E* __restrict__ 
           float zs[NU];
 #pragma unroll
           for (int u = 0; u < NU; ++u) zs[u] = 0.f;
-          state_update<NA>(st, zs, sm.v, sm.kx, lf, l16, lg, [](int) { return 1.f; }, [](int) { return 1.f; });
+          if constexpr (BF)
+            state_update_bf16<NA>(st, zs, sm.vt, sm.kx, lf, l16, lg);
+          else
+            state_update<NA>(st, zs, sm.v, sm.kx, lf, l16, lg, [](int) { return 1.f; }, [](int) { return 1.f; });
 #pragma unroll
           for (int u = 0; u < NA; ++u) {
             float z = zs[u];
             z += __shfl_xor(z, 16);
             z += __shfl_xor(z, 32);
-            zf[u] += z;
+            zf[u] += BF ? lf[u].cf * z : z;
             if (lg == 0) sm.zt[16 * (w + kWaves * u) + l16] = zf[u];
           }
           // G^T += g^T (phi(a) / den), and this lane's share of sum phi(a) delta
