@@ -82,6 +82,25 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, bf16x2& hi, bf16x
   const uint32_t u = __builtin_bit_cast(uint32_t, hi);
   lo = __builtin_convertvector(f32x2{a - __uint_as_float(u << 16), b - __uint_as_float(u & 0xffff0000u)}, bf16x2);
 }
+// Four floats as three bfloat16 terms hi + mid + lo (each the nearest bfloat16 of what the previous
+// terms leave): 24 significant bits, a float32 value to within a unit of its last place.
+__device__ __forceinline__ void split3(const f32x4& x, bf16x4& h, bf16x4& m, bf16x4& l) {
+  bf16x2 hh[2], mm[2], ll[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const float a = x[2 * p], b = x[2 * p + 1];
+    hh[p] = __builtin_convertvector(f32x2{a, b}, bf16x2);
+    const uint32_t uh = __builtin_bit_cast(uint32_t, hh[p]);
+    const float ra = a - __uint_as_float(uh << 16), rb = b - __uint_as_float(uh & 0xffff0000u);
+    mm[p] = __builtin_convertvector(f32x2{ra, rb}, bf16x2);
+    const uint32_t um = __builtin_bit_cast(uint32_t, mm[p]);
+    ll[p] = __builtin_convertvector(f32x2{ra - __uint_as_float(um << 16), rb - __uint_as_float(um & 0xffff0000u)},
+                                    bf16x2);
+  }
+  h = bf16x4{hh[0][0], hh[0][1], hh[1][0], hh[1][1]};
+  m = bf16x4{mm[0][0], mm[0][1], mm[1][0], mm[1][1]};
+  l = bf16x4{ll[0][0], ll[0][1], ll[1][0], ll[1][1]};
+}
 __device__ __forceinline__ f32x4 mfma_bf16(i16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
@@ -151,6 +170,7 @@ struct Rows {
   float* go;        // g . o per token (pass A)
   float* delta;     // delta per token (pass B)
   uint16_t (*vt)[kC + 8] = nullptr;  // bfloat16 inputs: V^T as raw bfloat16 (the exact products' operand)
+  uint16_t (*vb)[kDV + 8] = nullptr;  // bfloat16 inputs: V rows as raw bfloat16
 };
 
 // One thread's share of a chunk's inputs, loaded a chunk ahead and stored to LDS when the chunk starts,
@@ -185,6 +205,13 @@ struct Pre {
     if (R.vt) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) R.vt[8 * c + e][t] = ok ? (uint16_t)(__float_as_uint(vv[e]) >> 16) : (uint16_t)0;
+    }
+    if (R.vb) {
+      uint32_t wd[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        wd[h] = ok ? (__float_as_uint(vv[2 * h]) >> 16) | (__float_as_uint(vv[2 * h + 1]) & 0xffff0000u) : 0u;
+      *reinterpret_cast<uint4*>(&R.vb[t][8 * c]) = uint4{wd[0], wd[1], wd[2], wd[3]};
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -741,6 +768,7 @@ struct SmemB {
   alignas(16) float gh[kC][kLV];
   float delta[kC];
   int code[G::WP];
+  alignas(16) uint16_t vb[kC][kDV + 8];  // bfloat16 inputs
 };
 
 template <int NT, typename E>
@@ -760,7 +788,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(const E* __restrict__
   // the wavefronts with hw = 1 also take dw, ds and ds^T a of that key tile.  The pairing puts the
   // heavy key tiles on the SIMDs whose other wavefront owns fewer feature tiles.
   const int jw = (0x23231010 >> (4 * w)) & 15, hw = (w >> 1) & 1;
-  const Rows R{sm.ax, sm.kx, sm.v, sm.gh, nullptr, sm.delta};
+  constexpr bool BF = std::is_same_v<E, uint16_t>;
+  const Rows R{sm.ax, sm.kx, sm.v, sm.gh, nullptr, sm.delta, nullptr, BF ? sm.vb : nullptr};
   LaneF lf[NU];
   bool has[NU];
 #pragma unroll
@@ -812,30 +841,64 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(const E* __restrict__
         with_slots<NU>(two, [&](auto NAc) __attribute__((always_inline)) {
           constexpr int NA = decltype(NAc)::value;
           // Z^T = G^T-tiles x v + G_z into the owner's rows
-#pragma unroll 1
-          for (int jt = 0; jt < 4; ++jt) {
-            f32x4 zt[NA];
-#pragma unroll
-            for (int u = 0; u < NA; ++u) zt[u] = zero4();
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-              const f32x4 vv = *reinterpret_cast<const f32x4*>(&sm.v[16 * jt + l16][16 * dt + 4 * lg]);
-#pragma unroll
-              for (int u = 0; u < NA; ++u)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) zt[u] = mfma(gt[u][dt][r], vv[r], zt[u]);
-            }
+          if constexpr (BF) {
+            // v is exact in bfloat16 and G enters as three bfloat16 terms: the lane's four accumulator
+            // elements of value tile dt are its A operand of a 16-deep product over the value index
+            f32x4 zt[NA][4];
 #pragma unroll
             for (int u = 0; u < NA; ++u)
 #pragma unroll
-              for (int r = 0; r < 4; ++r)
-                sm.z[16 * (w + kWaves * u) + 4 * lg + r][16 * jt + l16] = zt[u][r] + __shfl(gzf[u], 4 * lg + r);
+              for (int jt = 0; jt < 4; ++jt) zt[u][jt] = zero4();
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              bf16x4 gs3[NA][3];
+#pragma unroll
+              for (int u = 0; u < NA; ++u) split3(gt[u][dt], gs3[u][0], gs3[u][1], gs3[u][2]);
+#pragma unroll
+              for (int jt = 0; jt < 4; ++jt) {
+                const bf16x4 vv = *reinterpret_cast<const bf16x4*>(&sm.vb[16 * jt + l16][16 * dt + 4 * lg]);
+#pragma unroll
+                for (int u = 0; u < NA; ++u)
+#pragma unroll
+                  for (int e = 0; e < 3; ++e)
+                    zt[u][jt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, gs3[u][e]),
+                                                                          __builtin_bit_cast(i16x4, vv), zt[u][jt], 0,
+                                                                          0, 0);
+              }
+            }
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+              for (int u = 0; u < NA; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  sm.z[16 * (w + kWaves * u) + 4 * lg + r][16 * jt + l16] = zt[u][jt][r] + __shfl(gzf[u], 4 * lg + r);
+          } else {
+#pragma unroll 1
+            for (int jt = 0; jt < 4; ++jt) {
+              f32x4 zt[NA];
+#pragma unroll
+              for (int u = 0; u < NA; ++u) zt[u] = zero4();
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt) {
+                const f32x4 vv = *reinterpret_cast<const f32x4*>(&sm.v[16 * jt + l16][16 * dt + 4 * lg]);
+#pragma unroll
+                for (int u = 0; u < NA; ++u)
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) zt[u] = mfma(gt[u][dt][r], vv[r], zt[u]);
+              }
+#pragma unroll
+              for (int u = 0; u < NA; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  sm.z[16 * (w + kWaves * u) + 4 * lg + r][16 * jt + l16] = zt[u][r] + __shfl(gzf[u], 4 * lg + r);
+            }
           }
           // G^T += gh^T phi(a), G_z -= phi(a)^T delta
           float gs[NU];
 #pragma unroll
           for (int u = 0; u < NU; ++u) gs[u] = 0.f;
-          state_update<NA, 4>(gt, gs, sm.gh, sm.ax, lf, l16, lg, [](int) { return 1.f; },
+          state_update<NA, BF ? 2 : 4>(gt, gs, sm.gh, sm.ax, lf, l16, lg, [](int) { return 1.f; },
                            [&](int i) { return sm.delta[i]; });
 #pragma unroll
           for (int u = 0; u < NA; ++u) {
