@@ -102,6 +102,17 @@ def test_backward_raw_scores():
     _check(_run(x, g, o, cfg), x, g, 3, 0.25, tol=1e-4, label="raw")
 
 
+def test_backward_bf16_scale_not_a_power_of_two():
+    # bfloat16 inputs take exact bfloat16 products for the state (k, v are exact) while a = sigma q is
+    # not exact at sigma = 0.3: the float32 paths for everything a enters
+    x = synth.make_qkv(121, 1, 2, 300, DK, DV, "bf16", unit_norm=False)
+    g = _grad_inputs(x, 1210)
+    cfg = _cfg(3, "bf16", 0.3)
+    announce("backward-bf16-scale")
+    o = _oracle_fwd(x, 3, 0.3).astype(np.float32)
+    _check(_run(x, g, o, cfg), x, g, 3, 0.3, tol=1e-4, label="bf16 sigma 0.3")
+
+
 def test_backward_with_the_library_forward():
     # end to end: the library's own float32 forward outputs feed the backward
     import torch
