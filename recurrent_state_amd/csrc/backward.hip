@@ -1,5 +1,5 @@
 // Backward of truncated-kernel causal attention (gfx950): dq, dk, dv and the gradient of the incoming
-// state, float32 matrix cores.
+// state; float32 matrix cores, and for bfloat16 inputs bfloat16 matrix cores on exact products.
 //
 // The forward is the method of "Expanding Attention" (Huang, arXiv:2610.20637), Abstract; the pages
 // give no gradients, so they are derived here.  With w_ij = K_n(s_ij), s_ij = a_i . k_j, a = sigma q,
@@ -37,6 +37,12 @@
 // chunk and every wavefront reads it for two 16x16 tiles of dv.  The feature Jacobians run with one
 // lane per token over the wavefront's own (compile-time) features; each wavefront leaves its partial
 // dq (dk) rows in its own LDS rows, summed after the chunk.
+//
+// bfloat16 inputs.  v is exact in bfloat16, and so is the hi + lo pair of a feature without its
+// coefficient (x_c0 x_c1 has at most 16 significant bits).  S += phi(K)^T V (state pass, pass A) then runs
+// as two 16x16x16 bfloat16 MFMAs per 16 tokens with the same float32 products, the coefficient applied
+// once (pass A keeps S_f / cf_f in its accumulators); G v (pass B) takes G as three bfloat16 terms
+// (24 significant bits) against exact v.
 #include <type_traits>
 #include <utility>
 
