@@ -19,8 +19,10 @@ events on the stream it runs on.
 Secondary timings after the timed steps (each can be skipped by a flag): decode over
 512 sequences whose states exceed the last-level cache, the float32 prefill at
 n = 1..5 (B=1, H=16, N=16,384), the expanded-softmax readout (orders 1, 2) on the
-main prefill inputs, the backward (gradients of that prefill), and a ragged-batch
-prefill (32 prompts of seeded lengths 1..2,047, 16 heads, bfloat16, n = 3).
+main prefill inputs, the backward (gradients of that prefill), a ragged-batch
+prefill (32 prompts of seeded lengths 1..2,047, 16 heads, bfloat16, n = 3), and, as
+context, exact causal softmax attention (torch's flash kernel) next to the bf16 prefill
+at B=4, H=16, N=128..8,192.
 """
 
 import argparse
@@ -288,6 +290,61 @@ def backward_prefill(rs, torch, dev, q, k, v, reps=3):
             "frac_fp32_mfma": flops / us / 1e6 / FP32_PEAK_TFLOPS}
 
 
+def softmax_crossover(rs, synth, torch, dev, reps=5):
+    """Context: exact causal softmax attention (torch's fused flash kernel, bfloat16, scale 1) against the
+    bfloat16 prefill (n = 3, from an empty history, final state written) at B = 4, H = 16 for N = 128 ..
+    8192, both timed with HIP events.  The flash kernel takes equal head widths, so q and k are padded
+    with zero columns to d_v = 64 (the scores are unchanged).  Only the flash and memory-efficient
+    backends are allowed; if neither runs, the error is reported instead of a time."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import torch.nn.functional as F
+    B, H = 4, 16
+    cfg = rs.config(NT, DK, DV, 0, 1.0, rs.TAYLOR_BF16)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    res, backend, crossover = {}, None, None
+    for N in (128, 256, 512, 1024, 2048, 4096, 8192):
+        x = synth.make_qkv(3, B, H, N, DK, DV, synth.BF16)
+        q, k, v = x.torch(dev)
+        o = torch.empty((B, H, N, DV), dtype=torch.float32, device=dev)
+        st = torch.empty((B, H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
+        ws = rs.new_workspace(cfg, B, H, N, dev)
+        t_us = timed(lambda: rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg))
+        qp = torch.nn.functional.pad(q, (0, DV - DK)).contiguous()
+        kp = torch.nn.functional.pad(k, (0, DV - DK)).contiguous()
+        s_us, err = None, None
+        for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+            try:
+                with sdpa_kernel([be]):
+                    s_us = timed(lambda: F.scaled_dot_product_attention(qp, kp, v, is_causal=True, scale=1.0))
+                backend = str(be).split(".")[-1]
+                break
+            except RuntimeError as e:
+                err = str(e).splitlines()[0][:200]
+        row = {"taylor_us": t_us, "softmax_us": s_us}
+        if s_us is None:
+            row["softmax_error"] = err
+        else:
+            row["softmax_over_taylor"] = s_us / t_us
+            if crossover is None and s_us > t_us:
+                crossover = N
+        res[f"N{N}"] = row
+        del x, q, k, v, o, st, ws, qp, kp
+    res["softmax_backend"] = backend
+    res["first_N_taylor_faster"] = crossover
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +359,7 @@ def main():
     ap.add_argument("--no-order-sweep", action="store_true", help="skip the n = 1..5 float32 prefill timings")
     ap.add_argument("--no-varlen", action="store_true", help="skip the ragged-batch prefill timing")
     ap.add_argument("--no-centered", action="store_true", help="skip the expanded-softmax readout timing")
+    ap.add_argument("--no-softmax", action="store_true", help="skip the exact softmax attention comparison")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (scale reference for "
@@ -481,6 +539,9 @@ def main():
     if not args.no_varlen:
         log("ragged-batch prefill (32 prompts, 16 heads, bf16)")
         out["prefill_varlen_bf16_32seqs_H16"] = varlen_prefill(rs, synth, torch, dev)
+    if not args.no_softmax:
+        log("exact softmax attention (flash kernel) against the prefill, N = 128 .. 8192")
+        out["softmax_vs_prefill_bf16_B4xH16"] = softmax_crossover(rs, synth, torch, dev)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline(x)
