@@ -336,12 +336,15 @@ def softmax_crossover(rs, synth, torch, dev, reps=5):
             row["softmax_error"] = err
         else:
             row["softmax_over_taylor"] = s_us / t_us
-            if crossover is None and s_us > t_us:
-                crossover = N
         res[f"N{N}"] = row
         del x, q, k, v, o, st, ws, qp, kp
+    # the smallest N from which the prefill is faster at every larger N of the sweep
+    for key in sorted((kk for kk in res if kk.startswith("N")), key=lambda kk: -int(kk[1:])):
+        if res[key].get("softmax_over_taylor", 0.0) <= 1.0:
+            break
+        crossover = int(key[1:])
     res["softmax_backend"] = backend
-    res["first_N_taylor_faster"] = crossover
+    res["prefill_faster_from_N"] = crossover
     return res
 
 
