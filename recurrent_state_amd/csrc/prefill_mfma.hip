@@ -394,11 +394,13 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
 // in buffer (c+1) & 1 and issues the loads of chunk c+2; the two register sets a and b alternate
 // so no loaded value is copied.  The steady-state loop has no conditional load or produce (every
 // load issued in it is consumed in it), so the compiler's memory-counter waits stay exact; the
-// last one to three phases are peeled.  Executes exactly 2 + nch barriers.
+// last one to three phases are peeled.  z starts from src (null: zero) and ends in dst (null: not
+// written).  Executes exactly 2 + nch barriers.
 template <int NT, bool READOUT, bool CENT, int G>
 __device__ __forceinline__ void pipe_producer(PipeSmem<NT, READOUT>& sm, const __bf16* q, const __bf16* k,
-                                              const __bf16* v, const float* cf, float* slot, float* zc0,
-                                              long long tok_base, int n_tok, int nch, int l, float scale) {
+                                              const __bf16* v, const float* cf, const float* src, float* dst,
+                                              float* zc0, long long tok_base, int n_tok, int nch, int l,
+                                              float scale) {
   using SP = PipeSplit<NT>;
   constexpr int W = Geo<NT>::W, WP = Geo<NT>::WP, CS = kPipeChunk;
   auto nv_of = [&](int c) { return min(CS, n_tok - c * CS); };
@@ -406,7 +408,7 @@ __device__ __forceinline__ void pipe_producer(PipeSmem<NT, READOUT>& sm, const _
   auto zrow = [&](int c) { return CENT && !READOUT ? zc0 + (long long)c * W : nullptr; };
   // z prefix of this producer's rows
   const int row = G * SP::RK + l;
-  if (l < SP::RK && row < WP) sm.z[0][row] = (READOUT && row < W) ? slot[(long long)W * kDV + row] : 0.f;
+  if (l < SP::RK && row < WP) sm.z[0][row] = (src && row < W) ? src[(long long)W * kDV + row] : 0.f;
   PipeIn<READOUT, CENT, G> pa, pb;
   pa.load(q, k, v, cf, tok_of(0), nv_of(0), l);
   __syncthreads();  // z prefix visible to every producer
@@ -431,9 +433,7 @@ __device__ __forceinline__ void pipe_producer(PipeSmem<NT, READOUT>& sm, const _
     __syncthreads();
     if (c + 2 < nch) __syncthreads();
   }
-  if constexpr (!READOUT) {
-    if (l < SP::RK && row < W) slot[(long long)W * kDV + row] = sm.z[nch & 1][row];
-  }
+  if (dst && l < SP::RK && row < W) dst[(long long)W * kDV + row] = sm.z[nch & 1][row];
 }
 
 template <int NT, bool READOUT, bool PACKED, bool CENT>
@@ -442,7 +442,8 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
                                                                     const __bf16* __restrict__ v,
                                                                     const float* __restrict__ cf,
                                                                     float* __restrict__ o, float* __restrict__ ws,
-                                                                    float* __restrict__ zc, SeqMap seq, int L,
+                                                                    float* __restrict__ zc, const float* sin,
+                                                                    float* sout, int direct, SeqMap seq, int L,
                                                                     long long nslot, long long stride, float scale) {
   using G = Geo<NT>;
   using SM = PipeSmem<NT, READOUT>;
@@ -458,13 +459,25 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
   const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long bx = blockIdx.x, by = blockIdx.y;
+  // Where a piece's state starts and ends.  Segments: the readout pass starts from its prefix slot and
+  // the state pass writes its increment to the slot.  Direct (one segment per pair): the piece starts
+  // from the incoming state (null: empty history) and writes the final state (null: discarded), with
+  // no state pass and no scan; in place is safe, each value being read and written by one lane.
+  auto state_src = [&](const SeqPiece& pc) -> const float* {
+    if (direct) return sin ? sin + pc.pair * stride : nullptr;
+    return READOUT ? ws + pc.slot * stride : nullptr;
+  };
+  auto state_dst = [&](const SeqPiece& pc) -> float* {
+    if (direct) return sout ? sout + pc.pair * stride : nullptr;
+    return READOUT ? nullptr : ws + pc.slot * stride;
+  };
   if (w >= kPipeConsumers) {
     static_assert(kPipeProducers <= 8, "dispatch below lists up to 8 producers");
 #define TAYLOR_PRODUCER(G_)                                                                           \
   case G_:                                                                                          \
     if constexpr (G_ < kPipeProducers)                                                              \
       for_each_piece<PACKED>(seq, bx, by, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {                       \
-        pipe_producer<NT, READOUT, CENT, G_>(sm, q, k, v, cf, ws + pc.slot * stride,                \
+        pipe_producer<NT, READOUT, CENT, G_>(sm, q, k, v, cf, state_src(pc), state_dst(pc),         \
                                              zc ? zc + seq.chunk_index(pc, 0, CS) * W : nullptr,    \
                                              pc.tok, pc.n,                                          \
                                        (pc.n + CS - 1) / CS, l, scale);                             \
@@ -487,7 +500,8 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
 
   for_each_piece<PACKED>(seq, bx, by, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
     const int nch = (pc.n + CS - 1) / CS;
-    float* slot = ws + pc.slot * stride;
+    const float* src = state_src(pc);
+    float* dst = state_dst(pc);
 
     // ---- consumers: wave w owns value columns 16w..16w+15 ----
     f32x4 Srun[NAT];
@@ -496,7 +510,7 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int a = 16 * t + 4 * lg + r;
-        Srun[t][r] = (READOUT && a < W) ? slot[(long long)a * kDV + 16 * w + l16] : 0.f;
+        Srun[t][r] = (src && a < W) ? src[(long long)a * kDV + 16 * w + l16] : 0.f;
       }
     __syncthreads();
     __syncthreads();
@@ -581,14 +595,16 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
       __syncthreads();
     }
 
-    if constexpr (!READOUT) {
+    if (dst) {
 #pragma unroll
       for (int t = 0; t < NAT; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int a = 16 * t + 4 * lg + r;
-          if (a < W) slot[(long long)a * kDV + 16 * w + l16] = Srun[t][r];
+          if (a < W) dst[(long long)a * kDV + 16 * w + l16] = Srun[t][r];
         }
+      if (direct && w == 0)  // the padding after z
+        for (long long e = (long long)W * (kDV + 1) + l; e < stride; e += 64) dst[e] = 0.f;
     }
   });
 }
@@ -613,16 +629,30 @@ constexpr int kSegTargetPipe = 256;
 struct PipePlan {
   int L;            // piece (segment or range) length
   long long nslot;  // workspace slots per row
+  bool direct;      // one segment per pair, read and written in one pass (no state pass, no scan)
 };
 
-PipePlan pipe_plan(int BH, const SeqMap& seq) {
+// Equal lengths run in one pass (one segment per pair) when that is estimated faster than S segments:
+// a chunk costs about kReadoutChunk in the readout pass and kStateChunk in the state pass (tenths of a
+// microsecond), and the split form's state pass, scan and two more launches add about kSplitFixed.
+// One pass: nchunk * kReadoutChunk; segments: nchunk / S * (kStateChunk + kReadoutChunk) + kSplitFixed.
+// The figures are fits to both forms timed at n = 3, bfloat16, 64 to 256 pairs, N = 128 to 4096.
+constexpr int kReadoutChunk = 23, kStateChunk = 11, kSplitFixed = 150;
+bool one_pass_faster(int nchunk, int segs) {
+  return (long long)nchunk * (kReadoutChunk * segs - kReadoutChunk - kStateChunk) < (long long)kSplitFixed * segs;
+}
+
+PipePlan pipe_plan(int BH, const SeqMap& seq, bool direct_ok) {
   PipePlan p;
+  p.direct = false;
   if (seq.packed) {
     const long long per = std::max<long long>(1, (seq.tokens(BH) + kSegTargetPipe - 1) / kSegTargetPipe);
     p.L = (int)std::min<long long>((per + kPipeChunk - 1) / kPipeChunk * kPipeChunk, 1 << 30);
   } else {
     const int nchunk = cdiv(seq.N, kPipeChunk);
-    p.L = cdiv(nchunk, n_segments(BH, nchunk, kSegTargetPipe)) * kPipeChunk;
+    const int segs = n_segments(BH, nchunk, kSegTargetPipe);
+    p.direct = direct_ok && one_pass_faster(nchunk, segs);
+    p.L = (p.direct ? nchunk : cdiv(nchunk, segs)) * kPipeChunk;
   }
   p.nslot = seq.row_slots(p.L);
   return p;
@@ -640,7 +670,7 @@ auto pipe_kernel_for(bool packed, bool cent) {
 
 template <int NT>
 int run_pipe(const PrefillArgs& a) {
-  const PipePlan p = pipe_plan(a.BH, a.seq);
+  const PipePlan p = pipe_plan(a.BH, a.seq, a.s.readout != 1);
   const bool cent = a.s.readout == 1 && a.o;
   float* ws = (float*)a.ws;
   // workspace: slots | coefficients (4 per token-head) | z before each chunk (W per chunk)
@@ -651,8 +681,22 @@ int run_pipe(const PrefillArgs& a) {
   const __bf16* q = (const __bf16*)a.q;
   const __bf16* k = (const __bf16*)a.k;
   const __bf16* v = (const __bf16*)a.v;
+  if (p.direct) {
+    // one pass: the readout (or, for a state-only call, the state walk) from the incoming state to the
+    // final one; a state-only call that discards the state has nothing to do
+    if (!a.o && !a.state) return 0;
+    if (a.o)
+      pipe_kernel_for<NT, true>(false, false)<<<grid, block, 0, a.stream>>>(
+          q, k, v, nullptr, a.o, ws, nullptr, a.state_in, a.state, 1, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
+    else
+      pipe_kernel_for<NT, false>(false, false)<<<grid, block, 0, a.stream>>>(
+          q, k, v, nullptr, nullptr, ws, nullptr, a.state_in, a.state, 1, a.seq, p.L, p.nslot, a.s.stride,
+          a.s.scale);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+  }
   pipe_kernel_for<NT, false>(a.seq.packed, cent)<<<grid, block, 0, a.stream>>>(
-      q, k, v, nullptr, nullptr, ws, cent ? zc : nullptr, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
+      q, k, v, nullptr, nullptr, ws, cent ? zc : nullptr, nullptr, nullptr, 0, a.seq, p.L, p.nslot, a.s.stride,
+      a.s.scale);
   if (hipGetLastError() != hipSuccess) return -3;
   if (seg_scan_launch(ws, a.state_in, a.state, a.BH, p.nslot, a.s.stride, elems, a.o != nullptr, a.seq, p.L,
                       a.stream))
@@ -664,7 +708,8 @@ int run_pipe(const PrefillArgs& a) {
       if (const int rc = centered_coef_launch(a, cp)) return rc;
     }
     pipe_kernel_for<NT, true>(a.seq.packed, cent)<<<grid, block, 0, a.stream>>>(
-        q, k, v, cent ? coef : nullptr, a.o, ws, nullptr, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
+        q, k, v, cent ? coef : nullptr, a.o, ws, nullptr, nullptr, nullptr, 0, a.seq, p.L, p.nslot, a.s.stride,
+        a.s.scale);
     if (hipGetLastError() != hipSuccess) return -3;
   }
   return 0;
@@ -677,7 +722,7 @@ int run_pipe(const PrefillArgs& a) {
 bool prefill_mfma_has(int nt, int dk, int dv, int dtype) { return dk == kDK && dv == kDV && nt >= 1 && nt <= 3 && dtype == 1; }
 
 long long prefill_mfma_ws_bytes(const Shape& s, int BH, const SeqMap& seq) {
-  const PipePlan p = pipe_plan(BH, seq);
+  const PipePlan p = pipe_plan(BH, seq, s.readout != 1);
   const long long slots = round_up(seq.rows(BH) * p.nslot * s.stride, 64);
   if (s.readout != 1) return slots * 4;
   return (slots + round_up(4 * seq.tokens(BH), 64) + seq.chunk_count(BH, kPipeChunk) * s.W) * 4;
