@@ -108,6 +108,12 @@ struct SeqMap {
     return false;
   }
 
+  // Ragged, one pass: the whole of sequence b in head h as one piece (n may be 0).
+  __device__ __forceinline__ SeqPiece whole_piece(long long b, long long h) const {
+    const long long c0 = off((int)b), c1n = off((int)b + 1), c1 = c1n > c0 ? c1n : c0;
+    return SeqPiece{h * T + c0, (int)(c1 - c0), 0, b * H + h};
+  }
+
   // Slots of pair bh's pieces, in token order: first, first + 1, ..., first + count - 1.
   __device__ __forceinline__ void pair_slots(long long bh, long long nslot, int L, long long& first,
                                              int& count) const {

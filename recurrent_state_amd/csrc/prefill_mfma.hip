@@ -471,12 +471,31 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
     if (direct) return sout ? sout + pc.pair * stride : nullptr;
     return READOUT ? nullptr : ws + pc.slot * stride;
   };
+  // The pieces of this workgroup.  Ragged batches in one pass: grid (sequence, head), the whole
+  // sequence as one piece; an empty one only has its state carried over (by the consumer waves, with
+  // no barrier, every value by one thread).
+  auto walk = [&](bool consumer, auto&& f) __attribute__((always_inline)) {
+    if (PACKED && direct) {
+      const SeqPiece pc = seq.whole_piece(bx, by);
+      if (pc.n > 0) {
+        f(pc);
+      } else if (consumer) {
+        const float* src = state_src(pc);
+        float* dst = state_dst(pc);
+        if (dst)
+          for (long long e = tid; e < stride; e += 64 * kPipeConsumers)
+            dst[e] = (src && e < (long long)W * (kDV + 1)) ? src[e] : 0.f;
+      }
+    } else {
+      for_each_piece<PACKED>(seq, bx, by, L, nslot, f);
+    }
+  };
   if (w >= kPipeConsumers) {
     static_assert(kPipeProducers <= 8, "dispatch below lists up to 8 producers");
 #define TAYLOR_PRODUCER(G_)                                                                           \
   case G_:                                                                                          \
     if constexpr (G_ < kPipeProducers)                                                              \
-      for_each_piece<PACKED>(seq, bx, by, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {                       \
+      walk(false, [&](const SeqPiece& pc) __attribute__((always_inline)) {                          \
         pipe_producer<NT, READOUT, CENT, G_>(sm, q, k, v, cf, state_src(pc), state_dst(pc),         \
                                              zc ? zc + seq.chunk_index(pc, 0, CS) * W : nullptr,    \
                                              pc.tok, pc.n,                                          \
@@ -498,7 +517,7 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
     return;
   }
 
-  for_each_piece<PACKED>(seq, bx, by, L, nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
+  walk(true, [&](const SeqPiece& pc) __attribute__((always_inline)) {
     const int nch = (pc.n + CS - 1) / CS;
     const float* src = state_src(pc);
     float* dst = state_dst(pc);
@@ -625,7 +644,7 @@ constexpr int kSegTargetPipe = 256;
 
 // Piece length and slots.  Equal lengths: about kSegTargetPipe workgroups, each pair cut into
 // equal segments.  Ragged: ranges of the packed token axis of about total / kSegTargetPipe
-// token-heads each (a multiple of the chunk).
+// token-heads each (a multiple of the chunk).  Either may instead run in one pass per pair.
 struct PipePlan {
   int L;            // piece (segment or range) length
   long long nslot;  // workspace slots per row
@@ -648,6 +667,13 @@ PipePlan pipe_plan(int BH, const SeqMap& seq, bool direct_ok) {
   if (seq.packed) {
     const long long per = std::max<long long>(1, (seq.tokens(BH) + kSegTargetPipe - 1) / kSegTargetPipe);
     p.L = (int)std::min<long long>((per + kPipeChunk - 1) / kPipeChunk * kPipeChunk, 1 << 30);
+    // One pass per (sequence, head) pair against the balanced ranges: chunks per CU (half a chunk of
+    // ragged tail per sequence) for both, plus, for pairs dealt to CUs in launch order, about half the
+    // longest pair's walk as the tail of the last CU to finish.
+    const long long nch_max = cdiv(seq.N, kPipeChunk);
+    const long long per_cu = cdiv((seq.T + 32LL * seq.B) / kPipeChunk * seq.H, kSegTargetPipe);
+    p.direct = direct_ok && kReadoutChunk * std::max(nch_max, per_cu + nch_max / 2) <
+                                (kStateChunk + kReadoutChunk) * per_cu + kSplitFixed;
   } else {
     const int nchunk = cdiv(seq.N, kPipeChunk);
     const int segs = n_segments(BH, nchunk, kSegTargetPipe);
@@ -677,7 +703,8 @@ int run_pipe(const PrefillArgs& a) {
   float* coef = ws + round_up(a.seq.rows(a.BH) * p.nslot * a.s.stride, 64);
   float* zc = coef + round_up(4 * a.seq.tokens(a.BH), 64);
   const long long elems = Geo<NT>::W * (long long)(kDV + 1);
-  const dim3 grid((unsigned)a.seq.grid_x(p.L), (unsigned)a.seq.grid_y(a.BH)), block(kPipeThreads);
+  const dim3 grid((unsigned)(p.direct && a.seq.packed ? a.seq.B : a.seq.grid_x(p.L)), (unsigned)a.seq.grid_y(a.BH)),
+      block(kPipeThreads);
   const __bf16* q = (const __bf16*)a.q;
   const __bf16* k = (const __bf16*)a.k;
   const __bf16* v = (const __bf16*)a.v;
@@ -686,10 +713,10 @@ int run_pipe(const PrefillArgs& a) {
     // final one; a state-only call that discards the state has nothing to do
     if (!a.o && !a.state) return 0;
     if (a.o)
-      pipe_kernel_for<NT, true>(false, false)<<<grid, block, 0, a.stream>>>(
+      pipe_kernel_for<NT, true>(a.seq.packed, false)<<<grid, block, 0, a.stream>>>(
           q, k, v, nullptr, a.o, ws, nullptr, a.state_in, a.state, 1, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
     else
-      pipe_kernel_for<NT, false>(false, false)<<<grid, block, 0, a.stream>>>(
+      pipe_kernel_for<NT, false>(a.seq.packed, false)<<<grid, block, 0, a.stream>>>(
           q, k, v, nullptr, nullptr, ws, nullptr, a.state_in, a.state, 1, a.seq, p.L, p.nslot, a.s.stride,
           a.s.scale);
     return hipGetLastError() == hipSuccess ? 0 : -3;

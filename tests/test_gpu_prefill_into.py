@@ -199,3 +199,57 @@ def test_one_pass_bf16(B, H, N):
     ref, _ = oracle.truncated_attention(x.q64[b, h], x.k64[b, h], x.v64[b, h], 3)
     err = np.max(np.abs(o2[b, h].cpu().numpy() - ref[N1:]) / np.max(np.abs(ref[N1:]), axis=1, keepdims=True))
     assert err <= 3e-3, f"continuation: rel err {err:.3e}"
+
+
+def test_one_pass_ragged_bf16():
+    # A ragged batch the bfloat16 kernel runs in one pass per (sequence, head) pair (40 short
+    # sequences, some empty, 8 heads): outputs and final states against the oracle on sampled pairs;
+    # fresh = init + prefill and out of place = in place, bit for bit; an empty sequence's final state
+    # is its incoming one (zero when fresh), padding zeroed.
+    import torch
+
+    H = 8
+    lens = synth.ragged_lengths(921, 40, 1, 300)
+    lens[3] = lens[17] = 0
+    lens[-1] = 0
+    cfg = _cfg(3, 16, 64, 64, "bf16", 0)
+    x = synth.make_ragged(921, lens, H, 16, 64, "bf16")
+    announce("varlen one pass", len(lens), H, max(lens))
+    q, k, v = x.torch(DEV)
+    cu = x.torch_cu(DEV)
+    T, N = sum(lens), max(lens)
+    ws = rs.new_varlen_workspace(cfg, len(lens), H, N, T, DEV)
+    shape = (len(lens), H, rs.taylor_state_stride(cfg))
+    o = torch.empty((H, T, 64), device=DEV)
+    st = torch.full(shape, float("nan"), device=DEV)
+    rs.taylor_attn_prefill_varlen_into(q, k, v, o, None, st, ws, cu, N, cfg)
+    W = rs.taylor_feature_width(3, 16)
+    assert bool((st[:, :, W * 65:] == 0).all())
+    assert bool((st[3] == 0).all()) and bool((st[-1] == 0).all())
+    S, z = rs.state_views(st, cfg)
+    cuh = np.concatenate([[0], np.cumsum(lens)])
+    b_long = int(np.argmax(lens))
+    for b, h in [(0, 0), (b_long, H - 1), (len(lens) - 2, 3)]:
+        a, e = cuh[b], cuh[b + 1]
+        ref, _ = oracle.truncated_attention(x.q64[h, a:e], x.k64[h, a:e], x.v64[h, a:e], 3)
+        err = np.max(np.abs(o[h, a:e].cpu().numpy() - ref) / np.max(np.abs(ref), axis=1, keepdims=True))
+        assert err <= 3e-3, f"pair ({b}, {h}): rel err {err:.3e}"
+        sref = oracle.state(x.k64[h, a:e], x.v64[h, a:e], 3)
+        got = np.concatenate([S[b, h].cpu().numpy(), z[b, h].cpu().numpy()[:, None]], axis=1)
+        assert np.max(np.abs(got - sref)) <= 2.0**-7 * np.max(np.abs(sref))
+    st1 = torch.empty(shape, device=DEV)
+    rs.taylor_state_init(st1, cfg)
+    o1 = torch.empty_like(o)
+    rs.taylor_attn_prefill_varlen(q, k, v, o1, st1, ws, cu, N, cfg)
+    assert torch.equal(o1, o)
+    assert torch.equal(st1, st)
+    inplace = st1.clone()
+    rs.taylor_attn_prefill_varlen(q, k, v, o1, inplace, ws, cu, N, cfg)
+    keep = st1.clone()
+    out = torch.full(shape, float("nan"), device=DEV)
+    o2 = torch.empty_like(o)
+    rs.taylor_attn_prefill_varlen_into(q, k, v, o2, st1, out, ws, cu, N, cfg)
+    assert torch.equal(st1, keep), "the incoming states changed"
+    assert torch.equal(o1, o2)
+    assert torch.equal(inplace, out)
+    assert torch.equal(out[3], st1[3]) and torch.equal(out[17], st1[17])
