@@ -151,30 +151,30 @@ def test_varlen_into(case):
     assert torch.equal(inplace, out)
 
 
-@pytest.mark.parametrize("B,H,N", [(2, 128, 1000), (4, 16, 300)])
-def test_one_pass_bf16(B, H, N):
+@pytest.mark.parametrize("n,B,H,N", [(3, 2, 128, 1000), (3, 4, 16, 300), (2, 4, 16, 300), (1, 4, 16, 300)])
+def test_one_pass_bf16(n, B, H, N):
     # Shapes the bfloat16 kernel runs in one pass per (sequence, head) pair (no state pass, no scan):
-    # 256 pairs at 16 chunks, and 64 short pairs.  Outputs and final states against the oracle on
+    # 256 pairs at 16 chunks, and 64 short pairs at n = 1, 2, 3.  Outputs and final states against the oracle on
     # sampled heads; state-only = the full call's state, in place = out of place, bit for bit; the
     # padding after z is written as zeros.
     import torch
 
-    cfg = _cfg(3, 16, 64, 128, "bf16", 0)
-    x = synth.make_qkv(910, B, H, N, 16, 64, "bf16")
-    announce("prefill one pass", B, H, N)
+    cfg = _cfg(n, 16, 64, 128, "bf16", 0)
+    x = synth.make_qkv(910 + n, B, H, N, 16, 64, "bf16")
+    announce("prefill one pass", n, B, H, N)
     q, k, v = x.torch(DEV)
     ws = rs.new_workspace(cfg, B, H, N, DEV)
     o = torch.empty((B, H, N, 64), device=DEV)
     st = torch.full(rs.new_state(B, H, cfg, DEV).shape, float("nan"), device=DEV)
     rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg)
-    W = rs.taylor_feature_width(3, 16)
+    W = rs.taylor_feature_width(n, 16)
     assert bool((st[:, :, W * 65:] == 0).all())
     S, z = rs.state_views(st, cfg)
     for b, h in [(0, 0), (B - 1, H // 2 + 1), (B - 1, H - 1)]:
-        ref, den = oracle.truncated_attention(x.q64[b, h], x.k64[b, h], x.v64[b, h], 3)
+        ref, den = oracle.truncated_attention(x.q64[b, h], x.k64[b, h], x.v64[b, h], n)
         err = np.max(np.abs(o[b, h].cpu().numpy() - ref) / np.max(np.abs(ref), axis=1, keepdims=True))
         assert err <= 3e-3, f"head ({b}, {h}): rel err {err:.3e}"
-        sref = oracle.state(x.k64[b, h], x.v64[b, h], 3)
+        sref = oracle.state(x.k64[b, h], x.v64[b, h], n)
         got = np.concatenate([S[b, h].cpu().numpy(), z[b, h].cpu().numpy()[:, None]], axis=1)
         assert np.max(np.abs(got - sref)) <= 2.0**-7 * np.max(np.abs(sref))
     st_only = torch.full_like(st, float("nan"))
@@ -196,7 +196,7 @@ def test_one_pass_bf16(B, H, N):
     assert torch.equal(o1, o2)
     assert torch.equal(inplace, out)
     b, h = B - 1, H - 1
-    ref, _ = oracle.truncated_attention(x.q64[b, h], x.k64[b, h], x.v64[b, h], 3)
+    ref, _ = oracle.truncated_attention(x.q64[b, h], x.k64[b, h], x.v64[b, h], n)
     err = np.max(np.abs(o2[b, h].cpu().numpy() - ref[N1:]) / np.max(np.abs(ref[N1:]), axis=1, keepdims=True))
     assert err <= 3e-3, f"continuation: rel err {err:.3e}"
 
