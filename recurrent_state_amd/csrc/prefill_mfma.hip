@@ -12,7 +12,9 @@
 // One workgroup walks a segment of consecutive 64-token chunks with the running state S_{<c} of the
 // segment in MFMA accumulator registers; two launches bracket the scan: a state-only pass writes
 // each segment's (S, z) increment to the workspace, the scan turns those into exclusive prefixes,
-// and the readout pass starts each segment from its prefix.  q, k, v, phi and the score weights
+// and the readout pass starts each segment from its prefix.  Where one segment per (sequence, head)
+// pair is estimated faster (short prompts, many pairs), the readout pass alone runs, from the
+// incoming state to the final one.  q, k, v, phi and the score weights
 // enter bfloat16 MFMAs; S and the weights are split as bfloat16 hi + lo where they meet the MFMAs
 // (float32 accuracy for the state), and all accumulation and the outputs are float32.  (float32
 // inputs run on the feature-block kernels of prefill_wide.hip.)
