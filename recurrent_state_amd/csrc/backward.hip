@@ -1014,7 +1014,7 @@ __global__ __launch_bounds__(256) void bwd_scan_kernel(float* __restrict__ ws, c
   float run = seed ? seed[bh * stride + e] : 0.f;
   float* p = ws + first * stride + e;
   for (int s = 0; s < n; ++s) {
-    const float t = p[s * stride];
+    const float t = s + 1 < n ? p[s * stride] : 0.f;  // the last increment enters no prefix
     p[s * stride] = run;
     run += t;
   }
@@ -1072,7 +1072,9 @@ int bwd_run(const BwdArgs& a) {
   const dim3 grid(p.nseg, a.BH), block(kThreads);
   const long long elems = BG<NT>::W * (long long)(kDV + 1);
   const dim3 sgrid(cdiv(elems, 256), a.BH), sblock(256);
-  bwd_state_kernel<NT, E><<<grid, block, 0, a.stream>>>(k, v, sslots, seq, p.L, p.nseg, a.s.stride);
+  // the state pass feeds only the prefixes of later segments: with one segment per pair the scan alone
+  // seeds it with the incoming state (its increment is never read)
+  if (p.nseg > 1) bwd_state_kernel<NT, E><<<grid, block, 0, a.stream>>>(k, v, sslots, seq, p.L, p.nseg, a.s.stride);
   bwd_scan_kernel<<<sgrid, sblock, 0, a.stream>>>(sslots, a.state, p.nseg, a.s.stride, elems, seq, p.L);
   bwd_dq_kernel<NT, E><<<grid, block, 0, a.stream>>>(q, k, v, a.g, a.o, sslots, gslots, ghat, dlt, a.dq, seq, p.L,
                                                      p.nseg, a.s.stride, a.s.scale);

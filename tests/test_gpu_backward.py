@@ -128,17 +128,19 @@ def test_backward_with_the_library_forward():
     _check(_run(x, g, o.cpu().numpy(), cfg), x, g, n, 1.0, label="e2e")
 
 
+@pytest.mark.parametrize("N", [300, 50])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_from_a_state_and_its_gradient(dtype):
-    # the forward continued from an incoming state: gradients of q, k, v and of that state
+def test_backward_from_a_state_and_its_gradient(dtype, N):
+    # the forward continued from an incoming state: gradients of q, k, v and of that state (N = 50:
+    # one segment, where no state pass runs)
     import torch
 
-    n, H, N0, N = 3, 2, 200, 300
+    n, H, N0 = 3, 2, 200
     x0 = synth.make_qkv(118, 1, H, N0, DK, DV, dtype)
     x = synth.make_qkv(119, 1, H, N, DK, DV, dtype)
     g = _grad_inputs(x, 1190)
     cfg = _cfg(n, dtype)
-    announce("backward-state", dtype)
+    announce("backward-state", dtype, N)
     st0 = np.stack([oracle.state(x0.k64[0, h], x0.v64[0, h], n) for h in range(H)])  # [H, W, 65]
     stride = rs.taylor_state_stride(cfg)
     W = st0.shape[1]
