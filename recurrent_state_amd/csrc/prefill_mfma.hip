@@ -96,6 +96,7 @@ __device__ __forceinline__ uint4 keep_if(bool ok, uint4 x) {
 // is a fraction of it.
 // ------------------------------------------------------------------------------------------------
 constexpr int kPipeConsumers = 4;  // one per 16 value columns
+constexpr int kRankMax = 512;      // ragged one-pass batches up to this many sequences run longest first
 constexpr int kPipeProducers = 4;
 constexpr int kPipeThreads = 64 * (kPipeConsumers + kPipeProducers);
 constexpr int kPipeChunk = 64;
@@ -476,9 +477,36 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
   // The pieces of this workgroup.  Ragged batches in one pass: grid (sequence, head), the whole
   // sequence as one piece; an empty one only has its state carried over (by the consumer waves, with
   // no barrier, every value by one thread).
+  // direct & 2 (ragged, at most kRankMax sequences): pairs are taken longest first — workgroup i in
+  // launch order walks the (i / H)-th longest sequence (ties: lower index first) of head i % H, so the
+  // last workgroups to start are the shortest and the CUs finish together.  Each workgroup ranks the
+  // lengths itself (B comparisons per thread), so the host asks for it only where the walks are long.
+  long long pb = bx, ph = by;
+  if constexpr (PACKED) {
+    if ((direct & 2) && seq.B <= kRankMax) {
+      __shared__ int lens[kRankMax];
+      __shared__ int pick;
+      const long long lin = bx + by * (long long)gridDim.x;
+      const int r = (int)(lin / seq.H);
+      ph = lin - (long long)r * seq.H;
+      if (tid < seq.B) {
+        const long long c0 = seq.off(tid), c1 = seq.off(tid + 1);
+        lens[tid] = c1 > c0 ? (int)(c1 - c0) : 0;
+      }
+      __syncthreads();
+      if (tid < seq.B) {
+        const int me = lens[tid];
+        int rank = 0;
+        for (int u = 0; u < seq.B; ++u) rank += (lens[u] > me) || (lens[u] == me && u < tid);
+        if (rank == r) pick = tid;
+      }
+      __syncthreads();
+      pb = pick;
+    }
+  }
   auto walk = [&](bool consumer, auto&& f) __attribute__((always_inline)) {
     if (PACKED && direct) {
-      const SeqPiece pc = seq.whole_piece(bx, by);
+      const SeqPiece pc = seq.whole_piece(pb, ph);
       if (pc.n > 0) {
         f(pc);
       } else if (consumer) {
@@ -651,6 +679,7 @@ struct PipePlan {
   int L;            // piece (segment or range) length
   long long nslot;  // workspace slots per row
   bool direct;      // one segment per pair, read and written in one pass (no state pass, no scan)
+  bool longest_first;  // ragged, one pass: the longest sequences first (ranked in the kernel)
 };
 
 // Equal lengths run in one pass (one segment per pair) when that is estimated faster than S segments:
@@ -665,7 +694,7 @@ bool one_pass_faster(int nchunk, int segs) {
 
 PipePlan pipe_plan(int BH, const SeqMap& seq, bool direct_ok) {
   PipePlan p;
-  p.direct = false;
+  p.direct = p.longest_first = false;
   if (seq.packed) {
     const long long per = std::max<long long>(1, (seq.tokens(BH) + kSegTargetPipe - 1) / kSegTargetPipe);
     p.L = (int)std::min<long long>((per + kPipeChunk - 1) / kPipeChunk * kPipeChunk, 1 << 30);
@@ -676,6 +705,7 @@ PipePlan pipe_plan(int BH, const SeqMap& seq, bool direct_ok) {
     const long long per_cu = cdiv((seq.T + 32LL * seq.B) / kPipeChunk * seq.H, kSegTargetPipe);
     p.direct = direct_ok && kReadoutChunk * std::max(nch_max, per_cu + nch_max / 2) <
                                 (kStateChunk + kReadoutChunk) * per_cu + kSplitFixed;
+    p.longest_first = p.direct && seq.B <= kRankMax && seq.B <= 16 * nch_max;
   } else {
     const int nchunk = cdiv(seq.N, kPipeChunk);
     const int segs = n_segments(BH, nchunk, kSegTargetPipe);
@@ -716,11 +746,12 @@ int run_pipe(const PrefillArgs& a) {
     if (!a.o && !a.state) return 0;
     if (a.o)
       pipe_kernel_for<NT, true>(a.seq.packed, false)<<<grid, block, 0, a.stream>>>(
-          q, k, v, nullptr, a.o, ws, nullptr, a.state_in, a.state, 1, a.seq, p.L, p.nslot, a.s.stride, a.s.scale);
+          q, k, v, nullptr, a.o, ws, nullptr, a.state_in, a.state, p.longest_first ? 3 : 1, a.seq, p.L, p.nslot,
+          a.s.stride, a.s.scale);
     else
       pipe_kernel_for<NT, false>(a.seq.packed, false)<<<grid, block, 0, a.stream>>>(
-          q, k, v, nullptr, nullptr, ws, nullptr, a.state_in, a.state, 1, a.seq, p.L, p.nslot, a.s.stride,
-          a.s.scale);
+          q, k, v, nullptr, nullptr, ws, nullptr, a.state_in, a.state, p.longest_first ? 3 : 1, a.seq, p.L,
+          p.nslot, a.s.stride, a.s.scale);
     return hipGetLastError() == hipSuccess ? 0 : -3;
   }
   pipe_kernel_for<NT, false>(a.seq.packed, cent)<<<grid, block, 0, a.stream>>>(

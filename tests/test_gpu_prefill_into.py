@@ -201,19 +201,21 @@ def test_one_pass_bf16(n, B, H, N):
     assert err <= 3e-3, f"continuation: rel err {err:.3e}"
 
 
-def test_one_pass_ragged_bf16():
-    # A ragged batch the bfloat16 kernel runs in one pass per (sequence, head) pair (40 short
-    # sequences, some empty, 8 heads): outputs and final states against the oracle on sampled pairs;
-    # fresh = init + prefill and out of place = in place, bit for bit; an empty sequence's final state
-    # is its incoming one (zero when fresh), padding zeroed.
+@pytest.mark.parametrize("seed,n_seqs,hi", [(921, 40, 300), (922, 100, 120)])
+def test_one_pass_ragged_bf16(seed, n_seqs, hi):
+    # Ragged batches the bfloat16 kernel runs in one pass per (sequence, head) pair (short sequences,
+    # some empty, 8 heads; 40 of up to 300 tokens are taken longest first, 100 of up to 120 in order):
+    # outputs and final states against the oracle on sampled pairs; fresh = init + prefill and out of
+    # place = in place, bit for bit; an empty sequence's final state is its incoming one (zero when
+    # fresh), padding zeroed.
     import torch
 
     H = 8
-    lens = synth.ragged_lengths(921, 40, 1, 300)
+    lens = synth.ragged_lengths(seed, n_seqs, 1, hi)
     lens[3] = lens[17] = 0
     lens[-1] = 0
     cfg = _cfg(3, 16, 64, 64, "bf16", 0)
-    x = synth.make_ragged(921, lens, H, 16, 64, "bf16")
+    x = synth.make_ragged(seed, lens, H, 16, 64, "bf16")
     announce("varlen one pass", len(lens), H, max(lens))
     q, k, v = x.torch(DEV)
     cu = x.torch_cu(DEV)
