@@ -684,12 +684,17 @@ struct PipePlan {
 
 // Equal lengths run in one pass (one segment per pair) when that is estimated faster than S segments:
 // a chunk costs about kReadoutChunk in the readout pass and kStateChunk in the state pass (tenths of a
-// microsecond), and the split form's state pass, scan and two more launches add about kSplitFixed.
-// One pass: nchunk * kReadoutChunk; segments: nchunk / S * (kStateChunk + kReadoutChunk) + kSplitFixed.
-// The figures are fits to both forms timed at n = 3, bfloat16, 64 to 256 pairs, N = 128 to 4096.
+// microsecond), the split form's state pass, scan and two more launches add about kSplitFixed, and a
+// form with more workgroups than CUs runs in rounds of one workgroup per CU.  One pass:
+// rounds(BH) * nchunk * kReadoutChunk; segments: rounds(BH * S) * ceil(nchunk / S) * (kStateChunk +
+// kReadoutChunk) + kSplitFixed.  The figures are fits to both forms timed at n = 3, bfloat16, 64 to
+// 256 pairs, N = 128 to 8192.
 constexpr int kReadoutChunk = 23, kStateChunk = 11, kSplitFixed = 150;
-bool one_pass_faster(int nchunk, int segs) {
-  return (long long)nchunk * (kReadoutChunk * segs - kReadoutChunk - kStateChunk) < (long long)kSplitFixed * segs;
+bool one_pass_faster(int BH, int nchunk, int segs) {
+  const long long one = (long long)cdiv(BH, kSegTargetPipe) * nchunk * kReadoutChunk;
+  const long long split = (long long)cdiv((long long)BH * segs, kSegTargetPipe) * cdiv(nchunk, segs) *
+                              (kStateChunk + kReadoutChunk) + kSplitFixed;
+  return one < split;
 }
 
 PipePlan pipe_plan(int BH, const SeqMap& seq, bool direct_ok) {
@@ -709,7 +714,7 @@ PipePlan pipe_plan(int BH, const SeqMap& seq, bool direct_ok) {
   } else {
     const int nchunk = cdiv(seq.N, kPipeChunk);
     const int segs = n_segments(BH, nchunk, kSegTargetPipe);
-    p.direct = direct_ok && one_pass_faster(nchunk, segs);
+    p.direct = direct_ok && one_pass_faster(BH, nchunk, segs);
     p.L = (p.direct ? nchunk : cdiv(nchunk, segs)) * kPipeChunk;
   }
   p.nslot = seq.row_slots(p.L);
