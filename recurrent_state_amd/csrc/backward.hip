@@ -1044,12 +1044,17 @@ __global__ __launch_bounds__(256) void bwd_rscan_kernel(float* __restrict__ ws, 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 // Segments: about 256 workgroups (one per CU: the LDS holds a chunk's rows and the feature-major
-// buffers), never more than the chunks.
+// buffers), never more than the chunks: the count up to ceil(256 / BH) with the fewest rounds of 256
+// workgroups times chunks per segment (ties: fewer).
 BwdPlan plan_for(int BH, int N) {
   const int nchunk = cdiv(N, kC);
-  long long want = (256 + BH - 1) / BH;
-  if (want < 1) want = 1;
-  if (want > nchunk) want = nchunk;
+  long long hi = (256 + BH - 1) / BH;
+  if (hi > nchunk) hi = nchunk;
+  long long want = 1, cost = -1;
+  for (long long S = 1; S <= hi; ++S) {
+    const long long c = (((long long)BH * S + 255) / 256) * ((nchunk + S - 1) / S);
+    if (cost < 0 || c < cost) cost = c, want = S;
+  }
   BwdPlan p;
   p.L = cdiv(nchunk, want) * kC;
   p.nseg = cdiv(N, p.L);

@@ -661,12 +661,19 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
 
-// Segments per head: about `target` workgroups in total, never more than the chunks.
+// Segments per pair: S <= ceil(target / BH) and <= nchunk, the one with the fewest rounds of `target`
+// workgroups times chunks per segment (ceil(target / BH) itself can spill a second round: 100 pairs
+// take two segments, not three).
 int n_segments(int BH, int nchunk, int target) {
-  long long want = (target + BH - 1) / BH;
-  if (want < 1) want = 1;
-  if (want > nchunk) want = nchunk;
-  return (int)want;
+  long long hi = (target + BH - 1) / BH;
+  if (hi > nchunk) hi = nchunk;
+  int best = 1;
+  long long cost = -1;
+  for (int S = 1; S <= hi; ++S) {  // rounds of `target` workgroups x chunks per segment; ties: fewer
+    const long long c = (((long long)BH * S + target - 1) / target) * ((nchunk + S - 1) / S);
+    if (cost < 0 || c < cost) cost = c, best = S;
+  }
+  return best;
 }
 
 // One workgroup per CU (double-buffered LDS): about 256 workgroups in total.
