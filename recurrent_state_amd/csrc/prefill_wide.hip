@@ -511,13 +511,20 @@ int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 // state-only pass four per CU.
 long long wide_target(bool outputs) { return outputs ? 256 : 1024; }
 
-// Segments per pair (equal lengths): enough (segment, pair, block) workgroups to cover the chip once.
+// Segments per pair (equal lengths): enough (segment, pair, block) workgroups to cover the chip once —
+// the count up to ceil(target / (BH nb)) with the fewest rounds of `target` workgroups times chunks per
+// segment (the ceiling alone can spill a second round; ties: fewer segments).
 int wide_segments(int BH, int nb, int nchunk, bool outputs) {
-  const long long target = wide_target(outputs);
-  long long want = (target + (long long)BH * nb - 1) / ((long long)BH * nb);
-  if (want < 1) want = 1;
-  if (want > nchunk) want = nchunk;
-  return (int)want;
+  const long long target = wide_target(outputs), units = (long long)BH * nb;
+  long long hi = (target + units - 1) / units;
+  if (hi > nchunk) hi = nchunk;
+  int best = 1;
+  long long cost = -1;
+  for (int S = 1; S <= hi; ++S) {
+    const long long c = ((units * S + target - 1) / target) * ((nchunk + S - 1) / S);
+    if (cost < 0 || c < cost) cost = c, best = S;
+  }
+  return best;
 }
 
 struct WideLayout {
