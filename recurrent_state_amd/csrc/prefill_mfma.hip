@@ -708,7 +708,9 @@ PipePlan pipe_plan(int BH, const SeqMap& seq, bool direct_ok) {
   PipePlan p;
   p.direct = p.longest_first = false;
   if (seq.packed) {
-    const long long per = std::max<long long>(1, (seq.tokens(BH) + kSegTargetPipe - 1) / kSegTargetPipe);
+    // floor(target / H) ranges per head at most, so ranges x heads never spill a second round
+    const long long ranges = std::max<long long>(1, kSegTargetPipe / std::max(1, seq.H));
+    const long long per = std::max<long long>(1, (seq.T + ranges - 1) / ranges);
     p.L = (int)std::min<long long>((per + kPipeChunk - 1) / kPipeChunk * kPipeChunk, 1 << 30);
     // One pass per (sequence, head) pair against the balanced ranges: chunks per CU (half a chunk of
     // ragged tail per sequence) for both, plus, for pairs dealt to CUs in launch order, about half the
