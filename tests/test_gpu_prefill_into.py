@@ -255,3 +255,28 @@ def test_one_pass_ragged_bf16(seed, n_seqs, hi):
     assert torch.equal(o1, o2)
     assert torch.equal(inplace, out)
     assert torch.equal(out[3], st1[3]) and torch.equal(out[17], st1[17])
+
+
+def test_split_rounds_bf16():
+    # 96 pairs x 4,096 tokens: split into two segments per pair (192 workgroups, one round; the ceiling
+    # of 256 / 96 = 3 would spill a second round), state pass + scan + readout.  Sampled heads against
+    # the oracle, outputs and final states.
+    import torch
+
+    B, H, N = 6, 16, 4096
+    cfg = _cfg(3, 16, 64, 128, "bf16", 0)
+    x = synth.make_qkv(930, B, H, N, 16, 64, "bf16")
+    announce("prefill split rounds", B, H, N)
+    q, k, v = x.torch(DEV)
+    ws = rs.new_workspace(cfg, B, H, N, DEV)
+    o = torch.empty((B, H, N, 64), device=DEV)
+    st = torch.full(rs.new_state(B, H, cfg, DEV).shape, float("nan"), device=DEV)
+    rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg)
+    S, z = rs.state_views(st, cfg)
+    for b, h in [(0, 1), (B - 1, H - 2)]:
+        ref, _ = oracle.truncated_attention(x.q64[b, h], x.k64[b, h], x.v64[b, h], 3)
+        err = np.max(np.abs(o[b, h].cpu().numpy() - ref) / np.max(np.abs(ref), axis=1, keepdims=True))
+        assert err <= 3e-3, f"head ({b}, {h}): rel err {err:.3e}"
+        sref = oracle.state(x.k64[b, h], x.v64[b, h], 3)
+        got = np.concatenate([S[b, h].cpu().numpy(), z[b, h].cpu().numpy()[:, None]], axis=1)
+        assert np.max(np.abs(got - sref)) <= 2.0**-7 * np.max(np.abs(sref))
