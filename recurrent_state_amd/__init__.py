@@ -324,3 +324,51 @@ def state_views(state, cfg):
     S = state[..., : W * cfg.d_v].unflatten(-1, (W, cfg.d_v))
     z = state[..., W * cfg.d_v : W * (cfg.d_v + 1)]
     return S, z
+
+
+# ---- differentiable op (forward and backward entry points under torch.autograd) ------------------
+
+_AUTOGRAD_FN = None
+
+
+def _autograd_fn():
+    global _AUTOGRAD_FN
+    if _AUTOGRAD_FN is None:
+        import torch
+
+        class _TaylorAttention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, state, cfg):
+                B, H, N = k.shape[:3]
+                o = torch.empty((B, H, N, cfg.d_v), dtype=torch.float32, device=k.device)
+                taylor_attn_prefill_into(q, k, v, o, state, None, new_workspace(cfg, B, H, N, k.device), cfg)
+                ctx.save_for_backward(q, k, v, o, state)
+                ctx.cfg = cfg
+                return o
+
+            @staticmethod
+            def backward(ctx, g):
+                q, k, v, o, state = ctx.saved_tensors
+                cfg = ctx.cfg
+                B, H, N = k.shape[:3]
+                g = g.to(torch.float32).contiguous()
+                dq = torch.empty(q.shape, dtype=torch.float32, device=k.device)
+                dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
+                dv = torch.empty(v.shape, dtype=torch.float32, device=k.device)
+                # the final state is not an output of the op, so its gradient (dstate in) is zero
+                dstate = torch.zeros_like(state) if state is not None and ctx.needs_input_grad[3] else None
+                taylor_attn_prefill_backward(q, k, v, o, g, state, dstate, dq, dk, dv,
+                                             new_backward_workspace(cfg, B, H, N, k.device), cfg)
+                return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dstate, None
+
+        _AUTOGRAD_FN = _TaylorAttention
+    return _AUTOGRAD_FN
+
+
+def taylor_attention(q, k, v, cfg, state=None):
+    """Causal Taylor attention as a differentiable op over contiguous [B, H, N, d] inputs (float32 or
+    bfloat16 as cfg says): the forward is taylor_attn_prefill_into from `state` (a float32 [B, H,
+    stride] incoming state, or None for an empty history), the backward taylor_attn_prefill_backward;
+    returns o [B, H, N, d_v] float32.  q, k, v and `state` receive gradients when they require them
+    (the truncated-kernel readout at n = 1..3, d_k = 16, d_v = 64)."""
+    return _autograd_fn().apply(q, k, v, state, cfg)

@@ -233,3 +233,50 @@ def test_backward_full_size_properties():
         ref = oracle.attention_backward_dq_rows(x.q64[b, h], x.k64[b, h], x.v64[b, h], gn[b, h], n, rows)
         err = float(np.max(np.linalg.norm(dqn[b, h, rows] - ref, axis=1) / np.linalg.norm(ref, axis=1)))
         assert err <= 1e-4, f"dq rows ({b}, {h}): {err:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_autograd_op(dtype, with_state):
+    # rs.taylor_attention under torch.autograd: the gradients equal the explicit entry points' (bit for
+    # bit, cast to the input type), and for float32 inputs the oracle's gradients
+    import torch
+
+    n, B, H, N = 3, 1, 2, 300
+    cfg = _cfg(n, dtype)
+    x = synth.make_qkv(125, B, H, N, DK, DV, dtype)
+    g = _grad_inputs(x, 1250)
+    announce("autograd op", dtype, with_state)
+    q, k, v = (t.clone().requires_grad_(True) for t in x.torch(DEV))
+    state = None
+    if with_state:
+        x0 = synth.make_qkv(126, B, H, 200, DK, DV, dtype)
+        st0 = torch.empty(rs.new_state(B, H, cfg, DEV).shape, device=DEV)
+        rs.taylor_attn_prefill_into(*x0.torch(DEV), None, None, st0, rs.new_workspace(cfg, B, H, 200, DEV), cfg)
+        state = st0.clone().requires_grad_(True)
+    o = rs.taylor_attention(q, k, v, cfg, state)
+    gt = torch.from_numpy(g).to(DEV)
+    (o * gt).sum().backward()
+    # the explicit calls
+    qd, kd, vd = x.torch(DEV)
+    o2 = torch.empty_like(o)
+    rs.taylor_attn_prefill_into(qd, kd, vd, o2, None if state is None else state.detach(), None,
+                                rs.new_workspace(cfg, B, H, N, DEV), cfg)
+    assert torch.equal(o.detach(), o2)
+    dq = torch.empty((B, H, N, DK), device=DEV)
+    dk = torch.empty_like(dq)
+    dv = torch.empty((B, H, N, DV), device=DEV)
+    ds = None if state is None else torch.zeros_like(state)
+    rs.taylor_attn_prefill_backward(qd, kd, vd, o2, gt, None if state is None else state.detach(), ds, dq, dk, dv,
+                                    rs.new_backward_workspace(cfg, B, H, N, DEV), cfg)
+    assert torch.equal(q.grad, dq.to(q.dtype)) and torch.equal(k.grad, dk.to(k.dtype))
+    assert torch.equal(v.grad, dv.to(v.dtype))
+    if state is not None:
+        assert torch.equal(state.grad, ds)
+    if dtype == "f32" and state is None:
+        ref = [oracle.attention_backward(x.q64[0, h], x.k64[0, h], x.v64[0, h], g[0, h].astype(np.float64), n, 1.0)
+               for h in range(H)]
+        for h in range(H):
+            for name, got, rf, t in zip(("dq", "dk", "dv"), (q.grad, k.grad, v.grad), ref[h][:3], (1e-5, 2e-5, 1e-5)):
+                err = _rel(got[0, h].cpu().numpy(), rf)
+                assert err <= t, f"{name} head {h}: {err:.3e}"
