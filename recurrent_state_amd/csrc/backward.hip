@@ -57,6 +57,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kDK = 16, kDV = 64;
 constexpr int kC = 64;  // tokens per chunk
@@ -109,6 +110,13 @@ __device__ __forceinline__ void split3(const f32x4& x, bf16x4& h, bf16x4& m, bf1
 }
 __device__ __forceinline__ f32x4 mfma_bf16(i16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+
+// c + a0 b0 + a1 b1 as one 16x16x32 MFMA: lane group g supplies k = 8g..8g+7 of both operands, so the
+// two 4-element halves pair up as the two products.  On gfx950 it takes the cycles of one 16x16x16.
+__device__ __forceinline__ f32x4 mfma_bf16_pair(bf16x4 a0, bf16x4 a1, bf16x4 b0, bf16x4 b1, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                  __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7), c, 0, 0, 0);
 }
 __device__ __forceinline__ void wave_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -373,8 +381,8 @@ __device__ __forceinline__ void state_update_bf16(f32x4 (&acc)[NU][4], float (&z
       const i16x4 a = *reinterpret_cast<const i16x4*>(&VT[16 * dt + l16][t0]);
 #pragma unroll
       for (int u = 0; u < NA; ++u) {
-        acc[u][dt] = mfma_bf16(a, bh[u], acc[u][dt]);
-        acc[u][dt] = mfma_bf16(a, bl[u], acc[u][dt]);
+        const bf16x4 ab = __builtin_bit_cast(bf16x4, a);
+        acc[u][dt] = mfma_bf16_pair(ab, ab, bh[u], bl[u], acc[u][dt]);
       }
     }
   }
@@ -867,9 +875,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(const E* __restrict__
                 for (int u = 0; u < NA; ++u)
 #pragma unroll
                   for (int e = 0; e < 3; ++e)
-                    zt[u][jt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, gs3[u][e]),
-                                                                          __builtin_bit_cast(i16x4, vv), zt[u][jt], 0,
-                                                                          0, 0);
+                    zt[u][jt] = mfma_bf16(__builtin_bit_cast(i16x4, gs3[u][e]), vv, zt[u][jt]);
               }
             }
 #pragma unroll

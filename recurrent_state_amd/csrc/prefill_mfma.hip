@@ -33,6 +33,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Two floats rounded to bfloat16 (nearest even) by one conversion instruction.
@@ -365,10 +366,12 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
          sm.alo[b][p][l] = lo;
          if constexpr (!CENT) {
            // column sums over the 16 key rows, as ones^T (hi + lo): every row of the product holds them
-           const i16x4 ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
-           f32x4 cs = {0.f, 0.f, 0.f, 0.f};
-           cs = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_bit_cast(i16x4, hi), cs, 0, 0, 0);
-           cs = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, __builtin_bit_cast(i16x4, lo), cs, 0, 0, 0);
+           const bf16x8 ones = __builtin_bit_cast(bf16x8, i16x8{0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80,
+                                                                 0x3f80, 0x3f80});
+           const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+           // hi and lo in the two halves of k: one 16x16x32 MFMA sums both
+           const f32x4 cs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+               ones, __builtin_shufflevector(hi, lo, 0, 1, 2, 3, 4, 5, 6, 7), zero, 0, 0, 0);
            if (lg == 0) sm.den_intra[b][p][l16] = cs[0];
          }
        }()),
@@ -599,10 +602,10 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
             const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.vt[b][16 * w + l16][16 * jt + 4 * lg]);
             const bf16x4 bh = sm.a[b][pair_index(jt, it)][l];
             const bf16x4 bl = sm.alo[b][pair_index(jt, it)][l];
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
-                                                              __builtin_bit_cast(i16x4, bh), O[it], 0, 0, 0);
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, av),
-                                                              __builtin_bit_cast(i16x4, bl), O[it], 0, 0, 0);
+            // V^T (hi + lo) as one 16x16x32 MFMA: the halves of k pair av with bh and av with bl
+            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(av, av, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                           __builtin_shufflevector(bh, bl, 0, 1, 2, 3, 4, 5, 6, 7), O[it],
+                                                           0, 0, 0);
           }
       }
       // state update
