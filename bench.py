@@ -2,8 +2,8 @@
 
 One step = one pass of the whole path:
   * taylor_attn_prefill_into from an empty history (no incoming state array) over one
-    batch of B=4 x H=16 x N=8192 bfloat16 tokens (d_k=16, d_v=64, n=3, chunk 128),
-    float32 outputs and final state;
+    batch of B=4 x H=16 x N=8192 bfloat16 tokens (d_k=16, d_v=64, n=3; the kernels walk
+    64-token chunks), float32 outputs and final state;
   * 1,000 taylor_attn_decode_step calls on 64 sequences x 16 heads whose float32
     states (153 x 65 per head) were built by a state-only prefill of a seeded
     65,536-token prefix (setup, untimed).  The 1,000 decode launches are replayed
@@ -18,11 +18,14 @@ events on the stream it runs on.
 
 Secondary timings after the timed steps (each can be skipped by a flag): decode over
 512 sequences whose states exceed the last-level cache, the float32 prefill at
-n = 1..5 (B=1, H=16, N=16,384), the expanded-softmax readout (orders 1, 2) on the
+B=1, H=8, N=4,096, n = 3 with its error against exact softmax, the float32 prefill at
+n = 1..5 (B=1, H=16, N=16,384) for unit-norm and raw (scale 1/4) inputs with the error of
+each order against exact softmax, the expanded-softmax readout (orders 1, 2) on the
 main prefill inputs, the backward (gradients of that prefill), a ragged-batch
 prefill (32 prompts of seeded lengths 1..2,047, 16 heads, bfloat16, n = 3), and, as
 context, exact causal softmax attention (torch's flash kernel) next to the bf16 prefill
-at B=4, H=16, N=128..8,192.
+at B=4, H=16, N=128..8,192.  Exact softmax for the accuracy figures is evaluated with
+float64 torch operations on the device (a comparator, like the flash kernel for time).
 """
 
 import argparse
@@ -40,8 +43,10 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 matrix
 
-# Prefill workload: B=4, H=16, N=8192, bf16 inputs, fp32 states/outputs, chunk 128.
+# Prefill workload: B=4, H=16, N=8192, bf16 inputs, fp32 states/outputs (the config asks for chunk
+# 128; the matrix-core kernels walk 64-token chunks, which the flop count below uses).
 PB, PH, PN, DK, DV, NT, PC = 4, 16, 8192, 16, 64, 3, 128
+PC_RUN = 64  # chunk the bf16 kernels walk (taylor_prefill_chunk), checked at run time
 # Decode workload: 64 sequences x 16 heads, 65,536-token prefix, 1,000 steps.
 DB, DH, DPREFIX, DSTEPS = 64, 16, 65536, 1000
 
@@ -51,9 +56,17 @@ STATE_BYTES = W * (DV + 1) * 4  # 39,780 B per head
 DECODE_BYTES_PER_HEAD = 2 * STATE_BYTES + 4 * (DK + DK + DV + DV)
 # Algorithmic prefill per token-head: q, k, v (bf16) in, o (fp32) out.
 PREFILL_BYTES_PER_TOKEN_HEAD = 2 * (DK + DK + DV) + 4 * DV
-# Algorithmic prefill flops per token-head at C=128 (unpadded widths, causal half of each chunk):
-# chunk-state GEMM 2*W*(d_v+1) + readout GEMM 2*W*(d_v+1) + intra scores 2*d_k*(C+1)/2 + intra PV 2*(d_v+1)*(C+1)/2.
-PREFILL_FLOPS_PER_TOKEN_HEAD = 2 * W * (DV + 1) * 2 + DK * (PC + 1) + (DV + 1) * (PC + 1)
+
+
+def prefill_flops_per_token_head(w, chunk):
+    """Algorithmic prefill flops per token-head at feature width w and chunk length `chunk` (unpadded
+    widths, causal half of each chunk): chunk-state GEMM 2*W*(d_v+1) + readout GEMM 2*W*(d_v+1) +
+    intra-chunk scores 2*d_k*(C+1)/2 + intra-chunk PV 2*(d_v+1)*(C+1)/2."""
+    return 4 * w * (DV + 1) + DK * (chunk + 1) + (DV + 1) * (chunk + 1)
+
+
+PREFILL_FLOPS_PER_TOKEN_HEAD = prefill_flops_per_token_head(W, PC_RUN)  # 45,045 at n = 3, C = 64
+ABSTRACT_ERROR_N3 = 6.5e-4  # "Expanding Attention", Abstract: error at n = 3 (metric and workload unstated)
 
 DECODE_KERNEL_SOURCE = os.path.join(ROOT, "recurrent_state_amd", "csrc", "decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -169,34 +182,99 @@ def big_decode(rs, synth, torch, dev, seqs=512, steps=100, reps=3, eager=False):
             "us_per_step": us, "achieved_GBs": nbytes / us / 1e3, "frac_hbm": nbytes / us / 1e3 / HBM_PEAK_GBS}
 
 
-def order_sweep(rs, synth, torch, dev, reps=3):
-    """Prefill at the order-sweep shape (B=1, H=16, N=16,384, float32, chunk 64) for n = 1..5, timed with
-    HIP events (a prefill from an empty history writing the final state, as in the main step).  Algorithmic flops per token-head:
-    2*W*65 (state update) + 2*W*65 (readout) + intra-chunk scores 2*d_k*(C+1)/2 + PV 2*65*(C+1)/2."""
-    B, H, N, C = 1, 16, 16384, 64
-    x = synth.make_qkv(5, B, H, N, DK, DV, synth.F32)
-    q, k, v = x.torch(dev)
-    o = torch.empty((B, H, N, DV), dtype=torch.float32, device=dev)
-    res = {}
-    for n in range(1, 6):
-        cfg = rs.config(n, DK, DV, C, 1.0, rs.TAYLOR_F32)
-        st = torch.empty((B, H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
-        ws = rs.new_workspace(cfg, B, H, N, dev)
-        rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg)
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        W = rs.taylor_feature_width(n, DK)
-        flops = B * H * N * (4 * W * (DV + 1) + DK * (C + 1) + (DV + 1) * (C + 1))
-        res[f"n{n}"] = {"W": W, "us": us, "tok_s": B * N / us * 1e6, "TFLOPs": flops / us / 1e6,
-                        "frac_fp32_mfma": flops / us / 1e6 / FP32_PEAK_TFLOPS}
-        del ws, st
+def softmax_rows(torch, q, k, v, rows, scale):
+    """Exact causal softmax attention at the query rows `rows` (a LongTensor) of every (b, h): float64
+    torch operations on the device.  q, k: [B, H, N, d_k]; v: [B, H, N, d_v]; returns [B, H, R, d_v]."""
+    N = k.shape[2]
+    q64 = q[:, :, rows].double()
+    k64t = k.double().transpose(-1, -2).contiguous()
+    s = scale * torch.matmul(q64, k64t)
+    future = torch.arange(N, device=k.device)[None, :] > rows[:, None]
+    s = s.masked_fill(future, float("-inf"))
+    return torch.matmul(torch.softmax(s, dim=-1), v.double())
+
+
+def accuracy(o, ref):
+    """Error of outputs o against a reference (float64 tensors [..., rows, d_v]) under the three
+    metrics reported: max-abs over max |ref|, per-row relative L2 (max and median), relative Frobenius."""
+    diff = o.double() - ref
+    rr = diff.norm(dim=-1) / ref.norm(dim=-1)
+    return {"max_abs_over_max": float(diff.abs().max() / ref.abs().max()), "row_rel_l2_max": float(rr.max()),
+            "row_rel_l2_median": float(rr.median()), "rel_frobenius": float(diff.norm() / ref.norm())}
+
+
+def timed_us(torch, fn, reps):
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def order_sweep(rs, synth, torch, dev, reps=3, rows_per_head=256):
+    """Prefill at the order-sweep shape (B=1, H=16, N=16,384, float32) for n = 1..5, unit-norm inputs
+    (scale 1) and raw ones (q, k ~ N(0, 1) un-normalised, scale 1/sqrt(d_k) = 1/4), timed with HIP
+    events (a prefill from an empty history writing the final state, as in the main step).  Algorithmic
+    flops per token-head at the chunk the kernels walk.  Accuracy: the outputs at `rows_per_head`
+    seeded rows of every head against exact causal softmax on the same inputs (the Abstract: accuracy
+    improves exponentially in n for normalised q, k; without normalisation adding terms stops helping)."""
+    import numpy as np
+
+    B, H, N = 1, 16, 16384
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, N - 1],
+                                     np.random.default_rng(55).integers(0, N, rows_per_head - 5)]))
+    rows_t = torch.from_numpy(rows).to(dev)
+    res = {"rows_per_head": int(len(rows)), "abstract_error_n3": ABSTRACT_ERROR_N3}
+    for variant, unit, scale in (("unit_norm", True, 1.0), ("raw_scale_0.25", False, 0.25)):
+        x = synth.make_qkv(5, B, H, N, DK, DV, synth.F32, unit_norm=unit)
+        q, k, v = x.torch(dev)
+        ref = softmax_rows(torch, q, k, v, rows_t, scale)
+        o = torch.empty((B, H, N, DV), dtype=torch.float32, device=dev)
+        out = {}
+        for n in range(1, 6):
+            cfg = rs.config(n, DK, DV, 0, scale, rs.TAYLOR_F32)
+            chunk = rs.taylor_prefill_chunk(cfg)
+            st = torch.empty((B, H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
+            ws = rs.new_workspace(cfg, B, H, N, dev)
+            us = timed_us(torch, lambda: rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg), reps)
+            w = rs.taylor_feature_width(n, DK)
+            flops = B * H * N * prefill_flops_per_token_head(w, chunk)
+            out[f"n{n}"] = {"W": w, "chunk": chunk, "us": us, "tok_s": B * N / us * 1e6, "TFLOPs": flops / us / 1e6,
+                            "frac_fp32_mfma": flops / us / 1e6 / FP32_PEAK_TFLOPS,
+                            "error_vs_softmax": accuracy(o[:, :, rows_t], ref)}
+            del ws, st
+        res[variant] = out
+        del x, q, k, v, o, ref
     return res
+
+
+def prefill_f32_config(rs, synth, torch, dev, reps=20):
+    """The float32 prefill workload B=1, H=8, N=4,096, n = 3 (unit-norm q, k; scale 1): a prefill from an
+    empty history writing the final state, HIP events; algorithmic flops at the chunk the kernels walk
+    against the float32 matrix peak and bytes (q, k, v in, o out, float32) against HBM; and the error of
+    every output row against exact causal softmax on the same inputs."""
+    B, H, N, n = 1, 8, 4096, 3
+    x = synth.make_qkv(2, B, H, N, DK, DV, synth.F32)
+    q, k, v = x.torch(dev)
+    cfg = rs.config(n, DK, DV, 64, 1.0, rs.TAYLOR_F32)
+    chunk = rs.taylor_prefill_chunk(cfg)
+    o = torch.empty((B, H, N, DV), dtype=torch.float32, device=dev)
+    st = torch.empty((B, H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
+    ws = rs.new_workspace(cfg, B, H, N, dev)
+    us = timed_us(torch, lambda: rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg), reps)
+    w = rs.taylor_feature_width(n, DK)
+    flops = B * H * N * prefill_flops_per_token_head(w, chunk)
+    nbytes = B * H * N * 4 * (DK + DK + DV + DV)
+    ref = softmax_rows(torch, q, k, v, torch.arange(N, device=dev), 1.0)
+    return {"workload": f"prefill B{B}xH{H}xN{N} fp32, n={n}, kernel chunk {chunk}", "us": us,
+            "tok_s": B * N / us * 1e6, "TFLOPs": flops / us / 1e6, "frac_fp32_mfma": flops / us / 1e6 / FP32_PEAK_TFLOPS,
+            "GBs": nbytes / us / 1e3, "frac_hbm": nbytes / us / 1e3 / HBM_PEAK_GBS, "alg_flops": flops,
+            "alg_bytes": nbytes, "error_vs_softmax_all_rows": accuracy(o, ref),
+            "abstract_error_n3": ABSTRACT_ERROR_N3}
 
 
 def varlen_prefill(rs, synth, torch, dev, reps=5):
@@ -261,9 +339,13 @@ def centered_prefill(rs, torch, dev, q, k, v, reps=5):
 def backward_prefill(rs, torch, dev, q, k, v, reps=3):
     """taylor_attn_prefill_backward on the main step's prefill inputs (B4 x H16 x N8192, bfloat16, n = 3),
     with outputs from the float32 forward and a seeded upstream gradient; HIP events.  Algorithmic
-    flops per token-head (float32 matrix work, unpadded W = 153): state pass 2*W*65, pass A
-    (S^T gh, S update, G update) 6*W*64 + 2*W, pass B (G^T phi(k), G v, G update) 6*W*64, plus the
-    intra-chunk products 4*(C+1)/2*(16 + 64) at C = 64."""
+    flops per token-head (unpadded W = 153), split by the matrix cores that run them with bfloat16
+    inputs: on bfloat16 MFMAs (exact products of bfloat16 values) the state updates S += phi(K)^T V of
+    the state pass and pass A and pass B's G v, 3 * 2*W*64; on float32 MFMAs pass A's S^T gh and G
+    update, pass B's G^T phi(k) and G update, 4 * 2*W*64, the normaliser parts 2*W + 2*W, and the
+    intra-chunk products 4*(C+1)/2*(16 + 64) at C = 64.  Each part is reported against its own peak,
+    and `frac_mixed_peak` is the time both parts would take at their peaks, back to back, over the
+    measured time."""
     B, H, N = k.shape[:3]
     cfg = rs.config(NT, DK, DV, 0, 1.0, rs.TAYLOR_BF16)
     f32 = rs.config(NT, DK, DV, 0, 1.0, rs.TAYLOR_F32)
@@ -285,9 +367,13 @@ def backward_prefill(rs, torch, dev, q, k, v, reps=3):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / reps
-    flops = B * H * N * (2 * W * (DV + 1) + 12 * W * DV + 2 * W + 4 * 65 / 2 * (DK + DV))
-    return {"us": us, "tok_s": B * N / us * 1e6, "TFLOPs": flops / us / 1e6,
-            "frac_fp32_mfma": flops / us / 1e6 / FP32_PEAK_TFLOPS}
+    bf16 = B * H * N * 3 * 2 * W * DV
+    fp32 = B * H * N * (4 * 2 * W * DV + 4 * W + 4 * 65 / 2 * (DK + DV))
+    floor_us = bf16 / (BF16_PEAK_TFLOPS * 1e6) + fp32 / (FP32_PEAK_TFLOPS * 1e6)
+    return {"us": us, "tok_s": B * N / us * 1e6,
+            "bf16_mfma": {"alg_flops": bf16, "TFLOPs": bf16 / us / 1e6, "frac_bf16_peak": bf16 / us / 1e6 / BF16_PEAK_TFLOPS},
+            "fp32_mfma": {"alg_flops": fp32, "TFLOPs": fp32 / us / 1e6, "frac_fp32_peak": fp32 / us / 1e6 / FP32_PEAK_TFLOPS},
+            "floor_us_at_peaks": floor_us, "frac_mixed_peak": floor_us / us}
 
 
 def softmax_crossover(rs, synth, torch, dev, reps=5):
@@ -360,6 +446,8 @@ def main():
                     help="skip the secondary decode run whose states exceed the last-level cache")
     ap.add_argument("--big-decode-steps", type=int, default=100)
     ap.add_argument("--no-order-sweep", action="store_true", help="skip the n = 1..5 float32 prefill timings")
+    ap.add_argument("--no-f32-config", action="store_true",
+                    help="skip the float32 B1 x H8 x N4096 prefill and its error against softmax")
     ap.add_argument("--no-varlen", action="store_true", help="skip the ragged-batch prefill timing")
     ap.add_argument("--no-centered", action="store_true", help="skip the expanded-softmax readout timing")
     ap.add_argument("--no-softmax", action="store_true", help="skip the exact softmax attention comparison")
@@ -402,6 +490,8 @@ def main():
     po = torch.empty((PB, PH, PN, DV), dtype=torch.float32, device=dev)
     pstate = torch.empty((PB, PH, rs.taylor_state_stride(pcfg)), dtype=torch.float32, device=dev)
     pws = rs.new_workspace(pcfg, PB, PH, PN, dev)
+    if rs.taylor_prefill_chunk(pcfg) != PC_RUN:
+        raise RuntimeError(f"the bf16 prefill walks {rs.taylor_prefill_chunk(pcfg)}-token chunks, the flop count assumes {PC_RUN}")
     log("prefill inputs ready")
 
     # ---- decode workload: states from a 65,536-token prefix ----
@@ -495,7 +585,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded unit-norm Gaussian q,k; Gaussian v)",
         "config": {
-            "workload": f"prefill B{PB}xH{PH}xN{PN} bf16 in, fp32 state/out, C={PC}; "
+            "workload": f"prefill B{PB}xH{PH}xN{PN} bf16 in, fp32 state/out, kernel chunk {PC_RUN}; "
                         f"decode {DB} seq x {DH} heads, fp32 state, {DPREFIX}-token prefix, {T} steps/step",
             "n_terms": NT, "d_k": DK, "d_v": DV, "global_batch": PB, "seq_len": PN,
             "parallelism": "none (1 GPU)",
@@ -509,7 +599,10 @@ def main():
             "frac_hbm": p_bytes / prefill_s / 1e9 / HBM_PEAK_GBS,
             "achieved_TFLOPs": p_flops / prefill_s / 1e12, "bf16_peak_TFLOPs": BF16_PEAK_TFLOPS,
             "frac_bf16_mfma": p_flops / prefill_s / 1e12 / BF16_PEAK_TFLOPS,
-            "alg_bytes": p_bytes, "alg_flops": p_flops,
+            "alg_bytes": p_bytes, "alg_flops": p_flops, "chunk": PC_RUN,
+            # attainable roofline min(peak_MFMA, AI * BW): the larger of the HBM and matrix-core floors
+            "floor_us": max(p_bytes / (HBM_PEAK_GBS * 1e3), p_flops / (BF16_PEAK_TFLOPS * 1e6)),
+            "frac_attainable": max(p_bytes / (HBM_PEAK_GBS * 1e3), p_flops / (BF16_PEAK_TFLOPS * 1e6)) / (prefill_s * 1e6),
         },
         "roofline": {
             "kernel": "decode_kernel<3,16,64,float>",
@@ -530,8 +623,11 @@ def main():
         torch.cuda.empty_cache()
         out["decode_llc_defeating"] = big_decode(rs, synth, torch, dev, steps=args.big_decode_steps,
                                                  eager=args.eager_decode)
+    if not args.no_f32_config:
+        log("float32 prefill B1 H8 N4096 and its error against exact softmax")
+        out["prefill_f32_B1xH8xN4096"] = prefill_f32_config(rs, synth, torch, dev)
     if not args.no_order_sweep:
-        log("order sweep n = 1..5 (float32 prefill, B1 H16 N16384)")
+        log("order sweep n = 1..5 (float32 prefill, B1 H16 N16384, unit-norm and raw) with errors against softmax")
         out["order_sweep_prefill_f32_B1xH16xN16384"] = order_sweep(rs, synth, torch, dev)
     if not args.no_centered:
         log("expanded-softmax readout (orders 1, 2) on the prefill inputs")

@@ -88,7 +88,13 @@ typedef struct {
   int n_terms;  /* n: Taylor terms, orders 0..n-1 (1..5 compiled)                         */
   int d_k;      /* q/k head dimension (4, 8 or 16 compiled)                                */
   int d_v;      /* v head dimension (multiple of 4; 4, 16, 32, 64, 128 compiled)           */
-  int chunk;    /* prefill chunk length C: 64 or 128; 0 selects the default for the shape */
+  int chunk;    /* requested prefill chunk length C: 0 (default), 64 or 128.  Only the      *
+                 * portable float32 kernels (d_k = 4, 8) walk C-token chunks; the matrix-  *
+                 * core kernels (d_k = 16, d_v = 64) walk a fixed length whatever C is:   *
+                 * 64 tokens (bfloat16 inputs at n <= 3), else 32 (float32 inputs,     *
+                 * and n = 4, 5).                                                      *
+                 * Outputs depend on the chunk length only through float32 rounding     *
+                 * (states add across chunks).  taylor_prefill_chunk() reports it.       */
   float scale;  /* score scale sigma: s = scale * q.k                                      */
   int in_dtype; /* taylor_dtype of q, k, v                                                 */
   int readout;  /* taylor_readout (0 = the truncated kernel)                               */
@@ -110,7 +116,12 @@ int64_t taylor_state_elems(const taylor_config* cfg);
  * up to a multiple of 4.  Host only.  Negative taylor_status if cfg is invalid. */
 int64_t taylor_state_stride(const taylor_config* cfg);
 
-/* Export the monomial table the kernels use (host only, bit-exact):
+/* Export the monomial table the kernels use (host only, bit-exact).  The
+ * Abstract of "Expanding Attention" gives each Taylor term as an inner product
+ * of tensor powers whose m-th state is binom(d+m-1, m) wide: the distinct
+ * monomials of degree m in d coordinates, one per multiset of coordinates.  The
+ * table lists them with the coefficient that splits the term's multiplicity
+ * and 1/m! evenly between query and key:
  *   idx_out  [W][max(n-1,1)] int32: coordinates i_1 <= ... <= i_m of each
  *            feature, -1 padded (row 0, the constant feature, is all -1);
  *   coef_out [W] double: 1/sqrt(alpha!) with alpha the exponent vector, computed
@@ -125,6 +136,14 @@ int taylor_monomial_table(int n_terms, int d_k, int32_t* idx_out, double* coef_o
  * in_dtype, readout); TAYLOR_ERR_UNSUPPORTED if valid but not compiled;
  * TAYLOR_ERR_INVALID_ARG if invalid.  Host only. */
 int taylor_supported(const taylor_config* cfg);
+
+/* The chunk length, in tokens, that the prefill kernels walk for this config
+ * (64 or 32 on the matrix-core kernels whatever cfg->chunk says; cfg->chunk, or
+ * 64 for 0, on the portable ones).  The Abstract of "Expanding Attention" fixes
+ * no chunk length: the states add across chunks, so any length gives the same
+ * result up to rounding.  Host only.  Negative taylor_status if cfg is invalid
+ * or not compiled (taylor_supported). */
+int taylor_prefill_chunk(const taylor_config* cfg);
 
 /* Bytes of device workspace taylor_attn_prefill needs for these sizes (may be 0).
  * Host only.  Negative taylor_status if cfg or sizes are invalid. */
@@ -247,7 +266,10 @@ int taylor_attn_prefill_backward(const void* q, const void* k, const void* v, co
                                  const float* state, float* dstate, float* dq, float* dk, float* dv, void* workspace,
                                  int B, int H, int N, const taylor_config* cfg, hipStream_t stream);
 
-/* One decode step per (b, h): S += phi(k_t) [v_t | 1]^T (one rank-one update),
+/* One decode step per (b, h).  The Abstract of "Expanding Attention": each of
+ * the n states is updated by one rank-one outer product per token, independent
+ * of the context length N, so a step costs the same at any history length:
+ * S += phi(k_t) [v_t | 1]^T (one rank-one update),
  * then o_t = (phi(scale*q_t)^T S)[:d_v] / (phi(scale*q_t)^T z) -- the update comes
  * first, so the current token attends to itself.  (TAYLOR_READOUT_CENTERED: the
  * same update, then the expanded-softmax output of the token over its history.)

@@ -122,6 +122,22 @@ def softmax_attention(q, k, v, scale=1.0, block=512):
     return o
 
 
+def softmax_attention_rows(q, k, v, rows, scale=1.0):
+    """Exact causal softmax attention at the query rows ``rows`` only (row i sees keys 0..i); float64.
+
+    O(len(rows) * N), for accuracy figures at sizes where the full pass is too slow."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    o = np.empty((len(rows), v.shape[1]), dtype=np.float64)
+    for r, i in enumerate(rows):
+        s = scale * (k[: i + 1] @ q[i])
+        e = np.exp(s - s.max())
+        o[r] = (e @ v[: i + 1]) / e.sum()
+    return o
+
+
 def state(k, v, n):
     """Recurrent state sum_j phi(k_j) [v_j, 1]^T: [W, d_v + 1] float64.
 

@@ -75,6 +75,56 @@ def attention_backward_from_state(q, k, v, g, n, scale=1.0, state0=None):
     return dq, dk, dv, dstate
 
 
+def attention_backward_magnitudes(q, k, v, g, n, scale=1.0, state0=None):
+    """Per-element magnitudes (mq, mk, mv, mstate) of the sums behind (dq, dk, dv, dstate0); float64.
+
+    The same sums as ``attention_backward_from_state`` with every factor replaced by its absolute
+    value: scores by s_bar_ij = |sigma| |q_i| . |k_j| (componentwise absolute values), the weights
+    K_n(s) and K_{n-1}(s) by K_n(s_bar) and K_{n-1}(s_bar), and g_i . (v_j - o_i) by
+    |g_i| . |v_j| + |g_i| . o_bar_i with o_bar_i = sum_j K_n(s_bar_ij) |v_j| / den_i (plus the
+    incoming state's part, |phi(sigma q_i)| |S0|).  Since |s^m| <= s_bar^m term by term and
+    phi(|x|) = |phi(x)| (the coefficients are positive), sum_f |phi_f(a)| |phi_f(k)| = K_n(s_bar):
+    each entry is at least the sum of the absolute values of the terms that the direct form, or the
+    factorised state form, adds up to that entry.  A float32 evaluation in any summation order is
+    therefore off by at most a multiple of the float32 unit roundoff times these (the multiple grows
+    with the depth of the summation and the number of roundings per term, not with cancellation).
+    den_i is the true (signed) normaliser.  Not a result to reproduce: the bound parity tests scale
+    their per-row bars by where a row's gradient is a small difference of large terms."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    N, dv_ = v.shape
+    sig = abs(scale)
+    mask = np.tril(np.ones((N, N), dtype=bool))
+    s = scale * (q @ k.T)
+    w = np.where(mask, truncated_kernel(s, n), 0.0)
+    den = w.sum(axis=1)
+    sbar = sig * (np.abs(q) @ np.abs(k).T)
+    wbar = np.where(mask, truncated_kernel(sbar, n), 0.0)
+    dbar = np.where(mask, np.abs(_kernel_derivative(sbar, n)), 0.0)
+    fa = features(sig * np.abs(q), n)  # |phi(sigma q)|
+    onum = wbar @ np.abs(v)
+    if state0 is not None:
+        st = np.abs(np.asarray(state0, dtype=np.float64))
+        den = den + features(scale * q, n) @ np.asarray(state0, dtype=np.float64)[:, dv_]
+        onum = onum + fa @ st[:, :dv_]
+    ad = np.abs(den)
+    obar = onum / ad[:, None]
+    ghbar = np.abs(g) / ad[:, None]
+    dlbar = np.sum(np.abs(g) * obar, axis=1) / ad
+    dwbar = np.where(mask, ghbar @ np.abs(v).T + dlbar[:, None], 0.0)
+    dsbar = dwbar * dbar
+    mq = sig * (dsbar @ np.abs(k))
+    mk = sig * (dsbar.T @ np.abs(q))
+    mv = wbar.T @ ghbar
+    if state0 is not None:
+        y = st[:, :dv_] @ ghbar.T + np.outer(st[:, dv_], dlbar)
+        mq = mq + sig * _feature_vjp(sig * np.abs(q), y.T, n)
+    mstate = np.concatenate([fa.T @ ghbar, (fa.T @ dlbar)[:, None]], axis=1)
+    return mq, mk, mv, mstate
+
+
 def attention_backward_dq_rows(q, k, v, g, n, rows, scale=1.0):
     """dq at the query rows ``rows`` only (empty history): O(N) per row, for sampled checks at sizes
     where the full O(N^2) pass is too large.  g is [N, d_v]; only its rows in ``rows`` matter."""
@@ -90,6 +140,24 @@ def attention_backward_dq_rows(q, k, v, g, n, rows, scale=1.0):
         o = (w @ v[: i + 1]) / den
         dw = (v[: i + 1] @ g[i] - g[i] @ o) / den
         out[r] = scale * ((dw * _kernel_derivative(s, n)) @ k[: i + 1])
+    return out
+
+
+def attention_backward_dq_magnitude_rows(q, k, v, g, n, rows, scale=1.0):
+    """The dq magnitudes of ``attention_backward_magnitudes`` at the query rows ``rows`` only (empty
+    history), O(N) per row, for sampled checks at large N."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    sig = abs(scale)
+    out = np.empty((len(rows), q.shape[1]))
+    for r, i in enumerate(np.asarray(rows, dtype=np.int64)):
+        den = truncated_kernel(scale * (k[: i + 1] @ q[i]), n).sum()
+        sbar = sig * (np.abs(k[: i + 1]) @ np.abs(q[i]))
+        obar = (truncated_kernel(sbar, n) @ np.abs(v[: i + 1])) / abs(den)
+        dwbar = (np.abs(v[: i + 1]) @ np.abs(g[i]) + np.abs(g[i]) @ obar) / abs(den)
+        out[r] = sig * ((dwbar * np.abs(_kernel_derivative(sbar, n))) @ np.abs(k[: i + 1]))
     return out
 
 

@@ -74,6 +74,38 @@ def centered_attention_rows(q, k, v, order, rows, scale=1.0):
     return o
 
 
+def centered_magnitudes(q, k, v, order, scale=1.0):
+    """Per-element magnitudes [N, d_v] of the sums behind ``centered_attention``; float64.
+
+    Expanding the centred powers writes row i's weights as p_ij = g0 + g1 s_ij + g2 s_ij^2 / 2 with
+    coefficients from the prefix sums c = i + 1, d1 = sum_j s_ij, d2 = sum_j s_ij^2 / 2 and u = d1 / c:
+    order 1 g = ((1 - u) / c, 1 / c), order 2 g = ((1 - u + u^2 - d2 / c) / c, (1 - u) / c, 1 / c).
+    The magnitudes replace every factor there by its absolute value (s by s_bar = |sigma| |q_i| . |k_j|,
+    u by sum_j s_bar_ij / c, d2 by sum_j s_bar_ij^2 / 2, the differences in g by sums) and give
+    g0_bar sum_j |v_j| + g1_bar sum_j s_bar_ij |v_j| + g2_bar sum_j s_bar_ij^2 / 2 |v_j|: at least the
+    absolute values of the terms a float32 evaluation of this form adds up, in any order.  Not a
+    result to reproduce: the bound GPU tests scale their per-row bars by."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if order not in (1, 2):
+        raise ValueError("order must be 1 or 2")
+    N = q.shape[0]
+    out = np.empty((N, v.shape[1]), dtype=np.float64)
+    for i in range(N):
+        c = i + 1.0
+        sb = abs(scale) * (np.abs(k[: i + 1]) @ np.abs(q[i]))
+        av = np.abs(v[: i + 1])
+        ub = sb.sum() / c
+        if order == 1:
+            g0, g1, g2 = (1.0 + ub) / c, 1.0 / c, 0.0
+        else:
+            g0 = (1.0 + ub + ub * ub + 0.5 * (sb * sb).sum() / c) / c
+            g1, g2 = (1.0 + ub) / c, 1.0 / c
+        out[i] = g0 * av.sum(axis=0) + g1 * (sb @ av) + g2 * (0.5 * sb * sb) @ av
+    return out
+
+
 def lse_series(x, top):
     """logsumexp of the last axis expanded in y = x - mean(x) ("Basic Expansion"), keeping the terms in
     y^2 (top = 2) or y^2 and y^3 (top = 3): log n + mean(x) + mean(y^2)/2 [+ mean(y^3)/6].

@@ -35,6 +35,7 @@ EXPORTS = (
     "taylor_state_stride",
     "taylor_monomial_table",
     "taylor_supported",
+    "taylor_prefill_chunk",
     "taylor_prefill_workspace_bytes",
     "taylor_state_init",
     "taylor_attn_prefill",
@@ -100,6 +101,7 @@ def lib():
         "taylor_state_stride": (i64, [cfgp]),
         "taylor_monomial_table": (i, [i, i, p, p, ctypes.c_size_t]),
         "taylor_supported": (i, [cfgp]),
+        "taylor_prefill_chunk": (i, [cfgp]),
         "taylor_prefill_workspace_bytes": (i64, [cfgp, i, i, i]),
         "taylor_state_init": (i, [p, i, i, cfgp, p]),
         "taylor_attn_prefill": (i, [p, p, p, p, p, p, i, i, i, cfgp, p]),
@@ -137,6 +139,83 @@ def dtype_code(dtype):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _torch_dtype(code):
+    import torch
+
+    if code == TAYLOR_F32:
+        return torch.float32
+    if code == TAYLOR_BF16:
+        return torch.bfloat16
+    raise ValueError(f"cfg.in_dtype {code} is neither TAYLOR_F32 nor TAYLOR_BF16")
+
+
+class _Args:
+    """Checks the tensors of one call against the layout the C entry point assumes, before any pointer
+    reaches the library: the ABI takes raw pointers and sizes, so it cannot see a wrong dtype, a
+    transposed view or a short buffer itself (a kernel would then read or write past the allocation).
+    Each tensor is checked for type, dtype, shape and contiguity as it comes; `done()` then checks
+    that every tensor of the call sits on one device (a cuda device)."""
+
+    def __init__(self, what):
+        self.what = what
+        self.seen = []
+
+    def tensor(self, t, name, shape, dtype, optional=False):
+        import torch
+
+        if t is None:
+            if optional:
+                return None
+            raise ValueError(f"{self.what}: {name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.what}: {name} must be a torch.Tensor, not {type(t).__name__}")
+        if t.dtype != dtype:
+            raise TypeError(f"{self.what}: {name} has dtype {t.dtype}, expected {dtype}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{self.what}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.what}: {name} must be contiguous (dense row-major)")
+        self.seen.append((name, t))
+        return t
+
+    def rank(self, t, name, dims, last=None):
+        """The leading sizes of a tensor whose shape defines the call's sizes (checked for rank and last dim)."""
+        import torch
+
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.what}: {name} must be a torch.Tensor, not {type(t).__name__}")
+        if t.dim() != dims or (last is not None and t.shape[-1] != last):
+            want = f"{dims}-D" + (f" with last dimension {last}" if last is not None else "")
+            raise ValueError(f"{self.what}: {name} has shape {tuple(t.shape)}, expected {want}")
+        return tuple(t.shape)
+
+    def workspace(self, t, need):
+        import torch
+
+        if need == 0 and t is None:
+            return None
+        if t is None:
+            raise ValueError(f"{self.what}: a workspace of {need} bytes is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.what}: workspace must be a torch.Tensor, not {type(t).__name__}")
+        if not t.is_contiguous():
+            raise ValueError(f"{self.what}: workspace must be contiguous")
+        if t.numel() * t.element_size() < need:
+            raise ValueError(f"{self.what}: workspace holds {t.numel() * t.element_size()} bytes, needs {need}")
+        self.seen.append(("workspace", t))
+        return t
+
+    def done(self):
+        dev = None
+        for name, t in self.seen:
+            if t.device.type != "cuda":
+                raise ValueError(f"{self.what}: {name} is on {t.device}; the library takes device (cuda) tensors")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{self.what}: {name} is on {t.device}, other arguments on {dev}")
 
 
 def _stream(stream, device):
@@ -191,6 +270,11 @@ def taylor_supported(cfg):
     return lib().taylor_supported(ctypes.byref(cfg))
 
 
+def taylor_prefill_chunk(cfg):
+    """Tokens per chunk the prefill kernels walk for this config (the matrix-core kernels ignore cfg.chunk)."""
+    return _check_nonneg(lib().taylor_prefill_chunk(ctypes.byref(cfg)), "taylor_prefill_chunk")
+
+
 def taylor_prefill_workspace_bytes(cfg, B, H, N):
     return _check_nonneg(lib().taylor_prefill_workspace_bytes(ctypes.byref(cfg), B, H, N),
                          "taylor_prefill_workspace_bytes")
@@ -210,16 +294,64 @@ def taylor_prefill_backward_workspace_bytes(cfg, B, H, N):
 # ---- device entry points ------------------------------------------------------------------------
 
 
+def _check_prefill(what, q, k, v, o, states, workspace, cfg):
+    """Checks an equal-length prefill's tensors; returns (B, H, N).  q may be None only for a
+    state-only call (o None)."""
+    import torch
+
+    a = _Args(what)
+    B, H, N = a.rank(k, "k", 4, cfg.d_k)[:3]
+    dt = _torch_dtype(cfg.in_dtype)
+    a.tensor(q, "q", (B, H, N, cfg.d_k), dt, optional=o is None)
+    a.tensor(k, "k", (B, H, N, cfg.d_k), dt)
+    a.tensor(v, "v", (B, H, N, cfg.d_v), dt)
+    a.tensor(o, "o", (B, H, N, cfg.d_v), torch.float32, optional=True)
+    stride = taylor_state_stride(cfg)
+    for name, st in zip(("state_in", "state_out") if len(states) == 2 else ("state",), states):
+        a.tensor(st, name, (B, H, stride), torch.float32, optional=True)
+    a.workspace(workspace, taylor_prefill_workspace_bytes(cfg, B, H, N))
+    a.done()
+    return B, H, N
+
+
+def _check_varlen(what, q, k, v, o, states, workspace, cu_seqlens, max_seqlen, cfg):
+    """Checks a ragged prefill's tensors; returns (H, T, n_seqs)."""
+    import torch
+
+    a = _Args(what)
+    H, T = a.rank(k, "k", 3, cfg.d_k)[:2]
+    n_seqs = a.rank(cu_seqlens, "cu_seqlens", 1)[0] - 1
+    if n_seqs < 0:
+        raise ValueError(f"{what}: cu_seqlens needs n_seqs + 1 >= 1 entries")
+    a.tensor(cu_seqlens, "cu_seqlens", (n_seqs + 1,), torch.int32)
+    dt = _torch_dtype(cfg.in_dtype)
+    a.tensor(q, "q", (H, T, cfg.d_k), dt, optional=o is None)
+    a.tensor(k, "k", (H, T, cfg.d_k), dt)
+    a.tensor(v, "v", (H, T, cfg.d_v), dt)
+    a.tensor(o, "o", (H, T, cfg.d_v), torch.float32, optional=True)
+    stride = taylor_state_stride(cfg)
+    for name, st in zip(("state_in", "state_out") if len(states) == 2 else ("state",), states):
+        a.tensor(st, name, (n_seqs, H, stride), torch.float32, optional=True)
+    a.workspace(workspace, taylor_prefill_varlen_workspace_bytes(cfg, n_seqs, H, int(max_seqlen), T))
+    a.done()
+    return H, T, n_seqs
+
+
 def taylor_state_init(state, cfg, stream=None):
     """Zero a [B, H, stride] float32 state tensor (an empty history)."""
-    B, H = state.shape[:2]
+    import torch
+
+    a = _Args("taylor_state_init")
+    B, H = a.rank(state, "state", 3)[:2]
+    a.tensor(state, "state", (B, H, taylor_state_stride(cfg)), torch.float32)
+    a.done()
     _check(lib().taylor_state_init(_ptr(state), B, H, ctypes.byref(cfg), _stream(stream, state.device)),
            "taylor_state_init")
 
 
 def taylor_attn_prefill(q, k, v, o, state, workspace, cfg, stream=None):
     """Causal prefill over [B, H, N, d] inputs; o [B, H, N, d_v] float32 or None; state in/out or None."""
-    B, H, N = k.shape[:3]
+    B, H, N = _check_prefill("taylor_attn_prefill", q, k, v, o, (state,), workspace, cfg)
     rc = lib().taylor_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), _ptr(workspace), B, H, N,
                                    ctypes.byref(cfg), _stream(stream, k.device))
     _check(rc, "taylor_attn_prefill")
@@ -228,7 +360,7 @@ def taylor_attn_prefill(q, k, v, o, state, workspace, cfg, stream=None):
 def taylor_attn_prefill_into(q, k, v, o, state_in, state_out, workspace, cfg, stream=None):
     """Causal prefill over [B, H, N, d] inputs from state_in (or None: empty history) into state_out
     (or None: discarded; the same tensor as state_in, or one that does not overlap it)."""
-    B, H, N = k.shape[:3]
+    B, H, N = _check_prefill("taylor_attn_prefill_into", q, k, v, o, (state_in, state_out), workspace, cfg)
     rc = lib().taylor_attn_prefill_into(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state_in), _ptr(state_out),
                                         _ptr(workspace), B, H, N, ctypes.byref(cfg), _stream(stream, k.device))
     _check(rc, "taylor_attn_prefill_into")
@@ -237,8 +369,8 @@ def taylor_attn_prefill_into(q, k, v, o, state_in, state_out, workspace, cfg, st
 def taylor_attn_prefill_varlen(q, k, v, o, state, workspace, cu_seqlens, max_seqlen, cfg, stream=None):
     """Causal prefill of a ragged batch packed as [H, T, d]; cu_seqlens is a device int32 tensor of
     n_seqs + 1 offsets; o [H, T, d_v] float32 or None; state [n_seqs, H, stride] in/out or None."""
-    H, T = k.shape[:2]
-    n_seqs = cu_seqlens.shape[0] - 1
+    H, T, n_seqs = _check_varlen("taylor_attn_prefill_varlen", q, k, v, o, (state,), workspace, cu_seqlens,
+                                 max_seqlen, cfg)
     rc = lib().taylor_attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), _ptr(workspace),
                                           _ptr(cu_seqlens), n_seqs, H, int(max_seqlen), T, ctypes.byref(cfg),
                                           _stream(stream, k.device))
@@ -249,8 +381,8 @@ def taylor_attn_prefill_varlen_into(q, k, v, o, state_in, state_out, workspace, 
                                     stream=None):
     """Ragged-batch prefill (as taylor_attn_prefill_varlen) from state_in (or None: empty histories) into
     state_out (or None: discarded; the same tensor as state_in, or one that does not overlap it)."""
-    H, T = k.shape[:2]
-    n_seqs = cu_seqlens.shape[0] - 1
+    H, T, n_seqs = _check_varlen("taylor_attn_prefill_varlen_into", q, k, v, o, (state_in, state_out), workspace,
+                                 cu_seqlens, max_seqlen, cfg)
     rc = lib().taylor_attn_prefill_varlen_into(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state_in), _ptr(state_out),
                                                _ptr(workspace), _ptr(cu_seqlens), n_seqs, H, int(max_seqlen), T,
                                                ctypes.byref(cfg), _stream(stream, k.device))
@@ -261,7 +393,20 @@ def taylor_attn_prefill_backward(q, k, v, o, g, state, dstate, dq, dk, dv, works
     """Gradients of a prefill over [B, H, N, d] inputs: dq, dk, dv (float32, written); dstate in/out
     (gradient of the final state in, of the incoming state out) or None; state: the forward's
     incoming state or None."""
-    B, H, N = k.shape[:3]
+    import torch
+
+    a = _Args("taylor_attn_prefill_backward")
+    B, H, N = a.rank(k, "k", 4, cfg.d_k)[:3]
+    dt, f32 = _torch_dtype(cfg.in_dtype), torch.float32
+    for t, name, d, ty in ((q, "q", cfg.d_k, dt), (k, "k", cfg.d_k, dt), (v, "v", cfg.d_v, dt), (o, "o", cfg.d_v, f32),
+                           (g, "g", cfg.d_v, f32), (dq, "dq", cfg.d_k, f32), (dk, "dk", cfg.d_k, f32),
+                           (dv, "dv", cfg.d_v, f32)):
+        a.tensor(t, name, (B, H, N, d), ty)
+    stride = taylor_state_stride(cfg)
+    a.tensor(state, "state", (B, H, stride), f32, optional=True)
+    a.tensor(dstate, "dstate", (B, H, stride), f32, optional=True)
+    a.workspace(workspace, taylor_prefill_backward_workspace_bytes(cfg, B, H, N))
+    a.done()
     rc = lib().taylor_attn_prefill_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(g), _ptr(state), _ptr(dstate),
                                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), B, H, N,
                                             ctypes.byref(cfg), _stream(stream, k.device))
@@ -280,7 +425,17 @@ def new_backward_workspace(cfg, B, H, N, device):
 
 def taylor_attn_decode_step(q, k, v, o, state, cfg, stream=None):
     """One decode step over [B, H, d] inputs; o [B, H, d_v] float32; state updated in place."""
-    B, H = k.shape[:2]
+    import torch
+
+    a = _Args("taylor_attn_decode_step")
+    B, H = a.rank(k, "k", 3, cfg.d_k)[:2]
+    dt = _torch_dtype(cfg.in_dtype)
+    a.tensor(q, "q", (B, H, cfg.d_k), dt)
+    a.tensor(k, "k", (B, H, cfg.d_k), dt)
+    a.tensor(v, "v", (B, H, cfg.d_v), dt)
+    a.tensor(o, "o", (B, H, cfg.d_v), torch.float32)
+    a.tensor(state, "state", (B, H, taylor_state_stride(cfg)), torch.float32)
+    a.done()
     rc = lib().taylor_attn_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state), B, H,
                                        ctypes.byref(cfg), _stream(stream, k.device))
     _check(rc, "taylor_attn_decode_step")

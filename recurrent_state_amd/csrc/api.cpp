@@ -199,6 +199,18 @@ int taylor_supported(const taylor_config* cfg) {
   return rc != TAYLOR_OK ? rc : supported(cfg, s);
 }
 
+int taylor_prefill_chunk(const taylor_config* cfg) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if ((rc = supported(cfg, s)) != TAYLOR_OK) return rc;
+  switch (prefill_path(s, chunk_of(cfg))) {
+    case Path::Mfma: return taylor::kMfmaChunk;
+    case Path::Wide: return taylor::kWideChunk;
+    default: return chunk_of(cfg);
+  }
+}
+
 int64_t taylor_prefill_workspace_bytes(const taylor_config* cfg, int B, int H, int N) {
   Shape s;
   int rc = check_config(cfg, &s);

@@ -6,6 +6,11 @@
 
 namespace taylor {
 
+// Tokens per chunk walked by the matrix-core prefill kernels (bfloat16 pipeline; float32 feature
+// blocks), whatever the configured chunk length.
+constexpr int kMfmaChunk = 64;
+constexpr int kWideChunk = 32;
+
 struct Shape {
   int nt;       // Taylor terms
   int dk, dv;   // head dims

@@ -100,7 +100,7 @@ constexpr int kPipeConsumers = 4;  // one per 16 value columns
 constexpr int kRankMax = 512;      // ragged one-pass batches up to this many sequences run longest first
 constexpr int kPipeProducers = 4;
 constexpr int kPipeThreads = 64 * (kPipeConsumers + kPipeProducers);
-constexpr int kPipeChunk = 64;
+constexpr int kPipeChunk = kMfmaChunk;
 constexpr int kPipePairs = 10;  // (key tile <= query tile) pairs of 16-token tiles in a chunk
 
 template <int NT, bool READOUT>

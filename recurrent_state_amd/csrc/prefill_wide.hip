@@ -40,7 +40,7 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDK = 16, kDV = 64;
-constexpr int kCS = 32;          // tokens per chunk
+constexpr int kCS = kWideChunk;  // tokens per chunk
 constexpr int kProd = 4;         // producer waves, FB / 4 features each
 constexpr int kCons = 4;         // consumer waves, 16 value columns each
 constexpr int kThreads = 64 * (kProd + kCons);

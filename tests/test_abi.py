@@ -30,7 +30,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     declared = _header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 17
     assert sorted(rs.EXPORTS) == declared
     out = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(taylor_[a-z_0-9]+)$", out, re.M))
@@ -345,3 +345,18 @@ def test_state_init_validation():
     assert L.taylor_state_init(FAKE, 1, 1, None, None) == rs.TAYLOR_ERR_INVALID_ARG
     assert L.taylor_state_init(FAKE, -2, 1, ctypes.byref(cfg), None) == rs.TAYLOR_ERR_INVALID_ARG
     assert L.taylor_state_init(None, 0, 3, ctypes.byref(cfg), None) == rs.TAYLOR_OK
+
+
+def test_prefill_chunk_is_what_the_kernels_walk():
+    # the matrix-core kernels walk a fixed chunk whatever cfg.chunk asks; the portable ones honour it
+    for chunk in (0, 64, 128):
+        for n in (1, 2, 3):
+            assert rs.taylor_prefill_chunk(rs.config(n, 16, 64, chunk, 1.0, rs.TAYLOR_BF16)) == 64
+        for n in (1, 2, 3, 4, 5):
+            assert rs.taylor_prefill_chunk(rs.config(n, 16, 64, chunk, 1.0, rs.TAYLOR_F32)) == 32
+        for n in (4, 5):
+            assert rs.taylor_prefill_chunk(rs.config(n, 16, 64, chunk, 1.0, rs.TAYLOR_BF16)) == 32
+        assert rs.taylor_prefill_chunk(rs.config(3, 4, 4, chunk)) == (chunk or 64)
+    L = rs.lib()
+    assert L.taylor_prefill_chunk(ctypes.byref(rs.config(3, 16, 64, 96))) == rs.TAYLOR_ERR_UNSUPPORTED
+    assert L.taylor_prefill_chunk(ctypes.byref(rs.config(0, 16, 64))) == rs.TAYLOR_ERR_INVALID_ARG

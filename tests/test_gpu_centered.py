@@ -6,16 +6,20 @@ bfloat16 inputs on the pipelined kernel), decode, resume from a state written
 by the truncated-kernel readout (the states are the same sums), ragged batches
 and raw (un-normalised) scores.  Bars: 1e-5 relative per output row for float32
 inputs; bfloat16 inputs 3e-3, as for the truncated kernel (the oracle sees the
-same rounded inputs; the kernel rounds gamma_m * phi_m(sigma q) to bfloat16).
+same rounded inputs; the kernel rounds gamma_m * phi_m(sigma q) to bfloat16).  With raw
+scores a row may be a small difference of larger terms (the weights go negative): there
+the float32 bar is max(1e-5 ||ref_i||, 2^-18 ||M_i||), M_i the sums of absolute values of
+the row's terms (oracle.centered_magnitudes).
 """
 
 import numpy as np
 import pytest
 
 import oracle
+from oracle.centered import centered_magnitudes
 import recurrent_state_amd as rs
 import synth
-from gpu_util import announce, row_rel_err, tol_for
+from gpu_util import TOL_F32, announce, row_rel_err, rows_within, tol_for
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -89,8 +93,13 @@ def test_centered_raw_scores(order):
     o = torch.empty((1, 2, 400, DV), device=DEV)
     rs.taylor_attn_prefill(q, k, v, o, None, rs.new_workspace(cfg, 1, 2, 400, DEV), cfg)
     ref = _ref(x.q64, x.k64, x.v64, order, 0.25)
-    err, _ = row_rel_err(o.cpu().numpy(), ref)
-    assert err <= 1e-4, err  # float32 sums of larger, cancelling terms
+    # per row: 1e-5 relative, or float32 rounding of the row's term magnitudes where its output is a
+    # small difference of larger terms (negative weights)
+    got = o.cpu().numpy()
+    for h in range(2):
+        mag = centered_magnitudes(x.q64[0, h], x.k64[0, h], x.v64[0, h], order, 0.25)
+        r = rows_within(got[0, h], ref[0, h], mag, TOL_F32)
+        assert r <= 1.0, f"head {h}: {r:.2f} x the per-row bar"
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -1,12 +1,13 @@
 """Parity at full workload sizes, in the launch configuration the benchmark times.
 
-* prefill, bfloat16: B=4, H=16, N=8192, n=3, chunk 128 -- every head, sampled rows
-  (chunk and segment edges plus seeded random rows) against the oracle evaluated row by row;
+* prefill, bfloat16: B=4, H=16, N=8192, n=3 -- every row of four heads, and sampled rows
+  (chunk and segment edges plus seeded random rows) of every other head, against the oracle;
+  the final state entry by entry;
 * decode: 64 sequences x 16 heads, states from a seeded 65,536-token prefix, 1,000 steps
   replayed from a HIP graph -- two heads at every step, every head at the first and the last
   step, against the oracle's direct O(N) evaluation over the whole history;
 * order sweep: B=1, H=16, N=16384, float32, n=1..5, unit-norm and raw (scale 1/4) inputs --
-  sampled rows of every head against the oracle.
+  sampled rows of every head (every row of head 0 at n = 3 and 5) against the oracle.
 """
 
 import ctypes
@@ -30,6 +31,9 @@ def _sample_rows(N, seed, extra=8):
     return sorted(rows)
 
 
+FULL_HEADS = ((0, 0), (1, 5), (2, 10), (3, 15))  # (b, h) compared at every row
+
+
 def test_prefill_bf16_full_size():
     B, H, N = 4, 16, 8192
     x = synth.make_qkv(3, B, H, N, 16, 64, synth.BF16)
@@ -41,16 +45,26 @@ def test_prefill_bf16_full_size():
     worst = 0.0
     for b in range(B):
         for h in range(H):
-            rows = _sample_rows(N, 1000 * b + h)
-            ref, den = oracle.truncated_attention_rows(x.q64[b, h], x.k64[b, h], x.v64[b, h], 3, rows)
-            err, _ = row_rel_err(o[b, h, rows], ref, den)
+            if (b, h) in FULL_HEADS:
+                # every row of these heads (the direct O(N^2) oracle, a few seconds per head)
+                ref, den = oracle.truncated_attention(x.q64[b, h], x.k64[b, h], x.v64[b, h], 3)
+                err, _ = row_rel_err(o[b, h], ref, den)
+            else:
+                rows = _sample_rows(N, 1000 * b + h)
+                ref, den = oracle.truncated_attention_rows(x.q64[b, h], x.k64[b, h], x.v64[b, h], 3, rows)
+                err, _ = row_rel_err(o[b, h, rows], ref, den)
             worst = max(worst, err)
     assert worst <= TOL_BF16, worst
+    # Final state, entry by entry: the kernel rounds each feature phi_f(k_j) to bfloat16 (relative
+    # 2^-9) before the float32 sum over tokens, so |S_fc - ref| <= 2^-9 sum_j |phi_f(k_j)| |v_jc| plus the
+    # float32 sum's rounding; the bar is twice the first term (2^-8 sum_j |phi_f(k_j)| |[v_j, 1]_c|,
+    # oracle.state of |k|, |v|), a bound per entry, not a fraction of the largest entry (z_0 = N).
     S, z = rs.state_views(st, cfg)
-    for b, h in ((0, 0), (3, 15)):
+    for b, h in ((0, 0), (3, 15), (2, 9)):
         full = oracle.state(x.k64[b, h], x.v64[b, h], 3)
+        bound = 2.0**-8 * oracle.state(np.abs(x.k64[b, h]), np.abs(x.v64[b, h]), 3)
         got = np.concatenate([S[b, h].cpu().numpy(), z[b, h].cpu().numpy()[:, None]], axis=1)
-        assert np.max(np.abs(got - full)) <= 1e-5 * np.max(np.abs(full))
+        assert np.all(np.abs(got - full) <= bound), float(np.max(np.abs(got - full) / bound))
     print(f"full-size bf16 prefill: worst sampled row error {worst:.2e}")
 
 
@@ -109,9 +123,14 @@ def test_order_sweep_full_size(unit_norm):
         o = o.cpu().numpy()
         worst = 0.0
         for h in range(H):
-            rows = _sample_rows(N, 77 * h + n, extra=4)
-            ref, den = oracle.truncated_attention_rows(x.q64[0, h], x.k64[0, h], x.v64[0, h], n, rows, scale)
-            err, _ = row_rel_err(o[0, h, rows], ref, den)
+            if h == 0 and n in (3, 5):
+                # every row of one head at the orders the bench leads with and the widest one
+                ref, den = oracle.truncated_attention(x.q64[0, h], x.k64[0, h], x.v64[0, h], n, scale)
+                err, _ = row_rel_err(o[0, h], ref, den)
+            else:
+                rows = _sample_rows(N, 77 * h + n, extra=4)
+                ref, den = oracle.truncated_attention_rows(x.q64[0, h], x.k64[0, h], x.v64[0, h], n, rows, scale)
+                err, _ = row_rel_err(o[0, h, rows], ref, den)
             worst = max(worst, err)
         assert worst <= TOL_F32, (n, worst)
         lines.append(f"n={n}: {worst:.1e}")

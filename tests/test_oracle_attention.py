@@ -140,6 +140,14 @@ def test_softmax_against_bruteforce():
     assert _rel(oracle.softmax_attention(q, k, v, 0.5, block=16), ref) < 1e-13
 
 
+def test_softmax_rows_form_matches_full():
+    x = synth.make_qkv(7, 1, 1, 300, 8, 5, unit_norm=False)
+    q, k, v = x.q64[0, 0], x.k64[0, 0], x.v64[0, 0]
+    rows = [0, 1, 150, 299, 64]
+    full = oracle.softmax_attention(q, k, v, 0.6)
+    np.testing.assert_allclose(oracle.softmax_attention_rows(q, k, v, rows, 0.6), full[rows], rtol=1e-13, atol=1e-15)
+
+
 def test_converges_to_softmax_within_lagrange_bound():
     # Abstract: accuracy improves exponentially in n.  For |s| <= smax the relative kernel
     # error is delta_n <= e^{2 smax} smax^n / n! (Lagrange remainder), and the output error
@@ -189,6 +197,33 @@ def test_recursion_equals_truncated_kernel(n):
     o_dir, _ = oracle.truncated_attention(q, k, v, n)
     assert _rel(o_rec, o_dir) < bar
     assert S.shape == (oracle.feature_width(n, 16), 17)
+
+
+def test_state_hand_example():
+    # Two tokens worked by hand: the state is the sum of phi(k_j) [v_j, 1]^T, z in the last column.
+    g = _golden("hand_examples.json")["state_d2_n3_two_tokens"]
+    k, v, want = np.array(g["k"]), np.array(g["v"]), np.array(g["state"])
+    np.testing.assert_allclose(oracle.state(k, v, g["n"]), want, rtol=1e-15, atol=1e-15)
+    # the rank-one recursion reaches the same state token by token
+    _, S = oracle.recurrent(np.zeros_like(k), k, v, g["n"])
+    np.testing.assert_allclose(S, want, rtol=1e-15, atol=1e-15)
+    # planted mistakes the fixture catches: the last token left out; features without 1/sqrt(alpha!)
+    assert not np.allclose(oracle.state(k[:1], v[:1], 3), want)
+    bare = np.array([[1.0, x0, x1, x0 * x0, x0 * x1, x1 * x1] for x0, x1 in k])
+    assert not np.allclose(bare.T @ np.concatenate([v, np.ones((2, 1))], axis=1), want)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+def test_state_equals_the_recursions_final_state(n):
+    # The closed-form sum (one matrix product over all tokens) against the token-by-token rank-one
+    # updates of the recursion: two separate statements of the same state (Abstract: the recurrent
+    # states are sums over the causal history).
+    x = synth.make_qkv(6, 1, 1, 700, 16, 8)
+    k, v = x.k64[0, 0], x.v64[0, 0]
+    _, S = oracle.recurrent(x.q64[0, 0], k, v, n)
+    assert _rel(oracle.state(k, v, n), S) < 1e-14
+    # the normaliser column counts tokens in its constant-feature entry
+    assert S[0, -1] == 700
 
 
 @pytest.mark.parametrize("chunk", [1, 37, 64, 128, 1000])

@@ -107,3 +107,39 @@ def test_dq_rows_form_matches_full():
     rows = [0, 5, 19, 11]
     np.testing.assert_allclose(oracle.attention_backward_dq_rows(q, k, v, g, 3, rows, 0.6), dq[rows], rtol=1e-12,
                                atol=1e-14)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_magnitudes_bound_the_gradients(n, with_state):
+    # the magnitudes are sums of absolute values of the gradients' terms, so they dominate the
+    # gradients entry by entry (raw scores with a negative scale: every sign shows up)
+    q, k, v, g = _inputs(80 + n, N=9, d=3, dv=2)
+    state0 = oracle.state(*_inputs(90 + n, N=4, d=3, dv=2)[1:3], n) if with_state else None
+    scale = -0.9
+    grads = oracle.attention_backward_from_state(q, k, v, g, n, scale, state0)
+    mags = oracle.attention_backward_magnitudes(q, k, v, g, n, scale, state0)
+    for got, m in zip(grads, mags):
+        assert m.shape == got.shape
+        assert np.all(np.abs(got) <= m * (1 + 1e-12) + 1e-15)
+
+
+def test_magnitudes_closed_forms():
+    # n = 1 (weights 1, den_i = i + 1): q and k get no terms at all, and dv_j's terms are g_i / (i + 1)
+    q, k, v, g = _inputs(95, N=8)
+    mq, mk, mv, _ = oracle.attention_backward_magnitudes(q, k, v, g, 1)
+    assert np.all(mq == 0) and np.all(mk == 0)
+    want = np.array([sum(np.abs(g[i]) / (i + 1) for i in range(j, 8)) for j in range(8)])
+    np.testing.assert_allclose(mv, want, rtol=1e-14, atol=0)
+    # all-positive inputs at n = 2 and scale 1: dv's terms have one sign, so its magnitude is |dv|
+    qp, kp, vp, gp = (np.abs(x) for x in _inputs(96, N=8))
+    dv = oracle.attention_backward(qp, kp, vp, gp, 2)[2]
+    np.testing.assert_allclose(oracle.attention_backward_magnitudes(qp, kp, vp, gp, 2)[2], dv, rtol=1e-13)
+
+
+def test_dq_magnitude_rows_form_matches_full():
+    q, k, v, g = _inputs(97, N=20, d=4, dv=3)
+    mq = oracle.attention_backward_magnitudes(q, k, v, g, 3, -0.6)[0]
+    rows = [0, 7, 19]
+    np.testing.assert_allclose(oracle.attention_backward_dq_magnitude_rows(q, k, v, g, 3, rows, -0.6), mq[rows],
+                               rtol=1e-12, atol=1e-14)

@@ -156,3 +156,27 @@ def test_planted_mistakes_are_caught():
     want = np.array([p / q for p, q in g["order2"]])
     uncentred = (1 + x + 0.5 * (x * x - (x * x).mean())) / 3
     assert np.max(np.abs(uncentred - want)) > 1e-3
+
+
+@pytest.mark.parametrize("order", [1, 2])
+@pytest.mark.parametrize("scale", [1.0, -0.7])
+def test_magnitudes_bound_the_output(order, scale):
+    # sums of absolute values of the output's terms dominate the output entry by entry
+    rng = np.random.default_rng(30 + order)
+    q, k, v = rng.standard_normal((40, 5)), rng.standard_normal((40, 5)), rng.standard_normal((40, 3))
+    o = centered.centered_attention(q, k, v, order, scale)
+    m = centered.centered_magnitudes(q, k, v, order, scale)
+    assert m.shape == o.shape
+    assert np.all(np.abs(o) <= m * (1 + 1e-12))
+
+
+def test_magnitudes_single_key_closed_form():
+    # one key: c = 1 and u_bar = s_bar.  Order 1: g0 = 1 + s_bar, g1 = 1.  Order 2: g0 = 1 + s_bar +
+    # s_bar^2 + s_bar^2 / 2, g1 = 1 + s_bar, g2 = 1.  The magnitude is (g0 + g1 s_bar + g2 s_bar^2 / 2) |v_0|.
+    q, k, v = np.array([[0.5, -2.0]]), np.array([[1.0, 1.5]]), np.array([[2.0, -3.0]])
+    sb = 0.5 * 1.0 + 2.0 * 1.5
+    av = np.abs(v[0])
+    np.testing.assert_allclose(centered.centered_magnitudes(q, k, v, 1)[0], (1 + sb) * av + sb * av, rtol=1e-15)
+    g0 = 1 + sb + sb * sb + 0.5 * sb * sb
+    want2 = g0 * av + (1 + sb) * sb * av + 0.5 * sb * sb * av
+    np.testing.assert_allclose(centered.centered_magnitudes(q, k, v, 2)[0], want2, rtol=1e-15)
