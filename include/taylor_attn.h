@@ -35,7 +35,8 @@
  *   Arguments are validated before anything is enqueued; on an error return
  *   nothing has been enqueued (TAYLOR_ERR_HIP: a launch failed; earlier
  *   kernels of the same call may already be queued).  No C++ exception crosses
- *   this boundary.  There is no global mutable state; calls are re-entrant.
+ *   this boundary.  Calls are re-entrant; the only global state is the
+ *   address of taylor_attn_prefill_into_static's workspace on each device.
  *
  * State layout (per head, float32): the "packed" block of
  * W*(d_v+1) values the Abstract counts (9,945 at n=3, d_k=16, d_v=64),
@@ -189,6 +190,27 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, float* o, f
 int taylor_attn_prefill_into(const void* q, const void* k, const void* v, float* o, const float* state_in,
                              float* state_out, void* workspace, int B, int H, int N, const taylor_config* cfg,
                              hipStream_t stream);
+
+/* Size of the static device workspace of taylor_attn_prefill_into_static, per GPU. */
+#define TAYLOR_STATIC_WORKSPACE_BYTES (32u << 20)
+
+/* taylor_attn_prefill_into with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array of
+ * TAYLOR_STATIC_WORKSPACE_BYTES (32 MiB) inside the library, one per GPU, held
+ * from the first call on that GPU until the process ends; the call itself
+ * allocates nothing.  The current device must be the stream's.  Sizes whose
+ * workspace (taylor_prefill_workspace_bytes) exceeds that size return
+ * TAYLOR_ERR_INVALID_ARG before anything is enqueued (at n = 3, d_k = 16,
+ * d_v = 64 up to 843 (sequence, head) pairs of any length fit; float32 inputs at
+ * n = 4, 5 need far more).  Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (other streams, other host threads) race and give undefined
+ * results; calls ordered on one stream are safe.  Nothing in the array needs to
+ * start at zero (every value read is written earlier in the same call).  Other
+ * arguments, results and errors as taylor_attn_prefill_into. */
+int taylor_attn_prefill_into_static(const void* q, const void* k, const void* v, float* o, const float* state_in,
+                                    float* state_out, int B, int H, int N, const taylor_config* cfg,
+                                    hipStream_t stream);
 
 /* Bytes of device workspace taylor_attn_prefill_varlen needs for these sizes
  * (may be 0); it depends on the sizes only, not on the individual lengths.

@@ -40,6 +40,7 @@ EXPORTS = (
     "taylor_state_init",
     "taylor_attn_prefill",
     "taylor_attn_prefill_into",
+    "taylor_attn_prefill_into_static",
     "taylor_prefill_varlen_workspace_bytes",
     "taylor_attn_prefill_varlen",
     "taylor_attn_prefill_varlen_into",
@@ -106,6 +107,7 @@ def lib():
         "taylor_state_init": (i, [p, i, i, cfgp, p]),
         "taylor_attn_prefill": (i, [p, p, p, p, p, p, i, i, i, cfgp, p]),
         "taylor_attn_prefill_into": (i, [p, p, p, p, p, p, p, i, i, i, cfgp, p]),
+        "taylor_attn_prefill_into_static": (i, [p, p, p, p, p, p, i, i, i, cfgp, p]),
         "taylor_prefill_varlen_workspace_bytes": (i64, [cfgp, i, i, i, i64]),
         "taylor_attn_prefill_varlen": (i, [p, p, p, p, p, p, p, i, i, i, i64, cfgp, p]),
         "taylor_attn_prefill_varlen_into": (i, [p, p, p, p, p, p, p, p, i, i, i, i64, cfgp, p]),
@@ -294,7 +296,7 @@ def taylor_prefill_backward_workspace_bytes(cfg, B, H, N):
 # ---- device entry points ------------------------------------------------------------------------
 
 
-def _check_prefill(what, q, k, v, o, states, workspace, cfg):
+def _check_prefill(what, q, k, v, o, states, workspace, cfg, need_ws=True):
     """Checks an equal-length prefill's tensors; returns (B, H, N).  q may be None only for a
     state-only call (o None)."""
     import torch
@@ -309,7 +311,8 @@ def _check_prefill(what, q, k, v, o, states, workspace, cfg):
     stride = taylor_state_stride(cfg)
     for name, st in zip(("state_in", "state_out") if len(states) == 2 else ("state",), states):
         a.tensor(st, name, (B, H, stride), torch.float32, optional=True)
-    a.workspace(workspace, taylor_prefill_workspace_bytes(cfg, B, H, N))
+    if need_ws:
+        a.workspace(workspace, taylor_prefill_workspace_bytes(cfg, B, H, N))
     a.done()
     return B, H, N
 
@@ -364,6 +367,16 @@ def taylor_attn_prefill_into(q, k, v, o, state_in, state_out, workspace, cfg, st
     rc = lib().taylor_attn_prefill_into(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state_in), _ptr(state_out),
                                         _ptr(workspace), B, H, N, ctypes.byref(cfg), _stream(stream, k.device))
     _check(rc, "taylor_attn_prefill_into")
+
+
+def taylor_attn_prefill_into_static(q, k, v, o, state_in, state_out, cfg, stream=None):
+    """taylor_attn_prefill_into with the library's static per-GPU workspace (no workspace argument, no
+    allocation); calls that overlap in time on one GPU race."""
+    B, H, N = _check_prefill("taylor_attn_prefill_into_static", q, k, v, o, (state_in, state_out), None, cfg,
+                             need_ws=False)
+    rc = lib().taylor_attn_prefill_into_static(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(state_in), _ptr(state_out),
+                                               B, H, N, ctypes.byref(cfg), _stream(stream, k.device))
+    _check(rc, "taylor_attn_prefill_into_static")
 
 
 def taylor_attn_prefill_varlen(q, k, v, o, state, workspace, cu_seqlens, max_seqlen, cfg, stream=None):

@@ -2,11 +2,14 @@
 //
 // Everything here is host logic.  Validation happens before any HIP call, so
 // an invalid call returns its status without touching the device (and without
-// needing one).  The library keeps no mutable global state and never
-// allocates, frees or synchronises device memory.
+// needing one).  The library never allocates, frees or synchronises device
+// memory; its one piece of global state is the per-device address of the
+// static workspace array of taylor_attn_prefill_into_static (set once per
+// device under a mutex).
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/taylor_attn.h"
 #include "common.hpp"
@@ -141,6 +144,28 @@ int prefill_common(const Shape& s, int C, const void* q, const void* k, const vo
     case Path::Wide: return map_launch(taylor::prefill_wide_launch(a));
     default: return seq.packed ? TAYLOR_ERR_UNSUPPORTED : map_launch(taylor::prefill_generic_launch(a));
   }
+}
+
+// Workspace of taylor_attn_prefill_into_static: a device array of the library's code object, so each
+// GPU the library runs on holds its own copy (from the first call there until the process ends).  In
+// host code the name `scratch` is a host-side stand-in, never a device address: kernels receive the
+// address hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[TAYLOR_STATIC_WORKSPACE_BYTES];
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TAYLOR_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TAYLOR_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TAYLOR_OK;
 }
 
 }  // namespace
@@ -279,6 +304,23 @@ int taylor_attn_prefill_into(const void* q, const void* k, const void* v, float*
   }
   return prefill_common(s, chunk_of(cfg), q, k, v, o, state_in, state_out, workspace, (int)BH, equal_lengths(B, H, N),
                         stream);
+}
+
+int taylor_attn_prefill_into_static(const void* q, const void* k, const void* v, float* o, const float* state_in,
+                                    float* state_out, int B, int H, int N, const taylor_config* cfg,
+                                    hipStream_t stream) {
+  Shape s;
+  int rc = check_config(cfg, &s);
+  if (rc != TAYLOR_OK) return rc;
+  if ((rc = supported(cfg, s)) != TAYLOR_OK) return rc;
+  if ((rc = check_sizes(B, H, N)) != TAYLOR_OK) return rc;
+  const int BH = B * H;
+  const int64_t need = (BH == 0 || N == 0) ? 0 : ws_bytes(s, chunk_of(cfg), BH, equal_lengths(B, H, N));
+  if (need < 0) return (int)need;
+  if (need > (int64_t)TAYLOR_STATIC_WORKSPACE_BYTES) return TAYLOR_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  if (need > 0 && (rc = scratch_for_current_device(&ws)) != TAYLOR_OK) return rc;
+  return taylor_attn_prefill_into(q, k, v, o, state_in, state_out, ws, B, H, N, cfg, stream);
 }
 
 int taylor_attn_prefill_varlen(const void* q, const void* k, const void* v, float* o, float* state, void* workspace,

@@ -30,7 +30,7 @@ def _header_functions():
 
 def test_every_declared_symbol_is_exported():
     declared = _header_functions()
-    assert len(declared) == 17
+    assert len(declared) == 18
     assert sorted(rs.EXPORTS) == declared
     out = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\sT\s(taylor_[a-z_0-9]+)$", out, re.M))
@@ -360,3 +360,22 @@ def test_prefill_chunk_is_what_the_kernels_walk():
     L = rs.lib()
     assert L.taylor_prefill_chunk(ctypes.byref(rs.config(3, 16, 64, 96))) == rs.TAYLOR_ERR_UNSUPPORTED
     assert L.taylor_prefill_chunk(ctypes.byref(rs.config(0, 16, 64))) == rs.TAYLOR_ERR_INVALID_ARG
+
+
+def test_static_workspace_variant_rejects_sizes_beyond_its_array():
+    # the allocation-free prefill checks the workspace its sizes need against the static array before
+    # any HIP call: float32 n = 5 over 16 heads of 16,384 tokens needs gigabytes
+    L = rs.lib()
+    cfg = rs.config(5, 16, 64, 0, 1.0, rs.TAYLOR_F32)
+    assert rs.taylor_prefill_workspace_bytes(cfg, 1, 16, 16384) > (32 << 20)
+    rc = L.taylor_attn_prefill_into_static(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 16, 16384, ctypes.byref(cfg), None)
+    assert rc == rs.TAYLOR_ERR_INVALID_ARG
+    # the bf16 n = 3 benchmark shape fits, and so do 843 (sequence, head) pairs
+    b3 = rs.config(3, 16, 64, 0, 1.0, rs.TAYLOR_BF16)
+    assert rs.taylor_prefill_workspace_bytes(b3, 4, 16, 8192) <= (32 << 20)
+    assert rs.taylor_prefill_workspace_bytes(b3, 1, 843, 8192) <= (32 << 20)
+    # invalid configurations and sizes fail as in taylor_attn_prefill_into
+    assert L.taylor_attn_prefill_into_static(FAKE, FAKE, FAKE, FAKE, None, FAKE, -1, 16, 64, ctypes.byref(b3),
+                                             None) == rs.TAYLOR_ERR_INVALID_ARG
+    assert L.taylor_attn_prefill_into_static(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 64, None,
+                                             None) == rs.TAYLOR_ERR_INVALID_ARG
