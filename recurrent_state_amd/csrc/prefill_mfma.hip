@@ -19,6 +19,9 @@
 // (float32 accuracy for the state), and all accumulation and the outputs are float32.  (float32
 // inputs run on the feature-block kernels of prefill_wide.hip.)
 #include <algorithm>
+#include <atomic>
+#include <cstddef>
+#include <chrono>
 #include <type_traits>
 #include <utility>
 
@@ -72,6 +75,22 @@ __host__ __device__ constexpr int slot_feature_bf16(int s) {
 }
 
 __device__ __forceinline__ int pair_index(int jt, int it) { return it * (it + 1) / 2 + jt; }
+
+// A state value that other workgroups of the same launch read (the single-pass form's published sums,
+// COH): stored through to the device's point of coherence (an agent-scope store), so that publishing
+// needs no write-back of the XCD's L2, which would also flush every other workgroup's pending outputs.
+template <bool COH>
+__device__ __forceinline__ void put_state(float* p, float v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
+// A value another workgroup of the same launch published (read from the point of coherence).
+__device__ __forceinline__ float get_published(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // x where ok holds, else zero, selected word by word (a select of the whole vector would take the
 // operands' addresses and move them to scratch memory).
@@ -402,11 +421,11 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
 // load issued in it is consumed in it), so the compiler's memory-counter waits stay exact; the
 // last one to three phases are peeled.  z starts from src (null: zero) and ends in dst (null: not
 // written).  Executes exactly 2 + nch barriers.
-template <int NT, bool READOUT, bool CENT, int G>
+template <int NT, bool READOUT, bool CENT, int G, bool COH = false>
 __device__ __forceinline__ void pipe_producer(PipeSmem<NT, READOUT>& sm, const __bf16* q, const __bf16* k,
                                               const __bf16* v, const float* cf, const float* src, float* dst,
                                               float* zc0, long long tok_base, int n_tok, int nch, int l,
-                                              float scale) {
+                                              float scale, float* keep = nullptr) {
   using SP = PipeSplit<NT>;
   constexpr int W = Geo<NT>::W, WP = Geo<NT>::WP, CS = kPipeChunk;
   auto nv_of = [&](int c) { return min(CS, n_tok - c * CS); };
@@ -439,7 +458,158 @@ __device__ __forceinline__ void pipe_producer(PipeSmem<NT, READOUT>& sm, const _
     __syncthreads();
     if (c + 2 < nch) __syncthreads();
   }
-  if (dst && l < SP::RK && row < W) dst[(long long)W * kDV + row] = sm.z[nch & 1][row];
+  if (dst && l < SP::RK && row < W) {
+    put_state<COH>(dst + (long long)W * kDV + row, sm.z[nch & 1][row]);
+    if (keep) keep[W * kDV + row] = sm.z[nch & 1][row];
+  }
+}
+
+// Consumer wave w (value columns 16w..16w+15) over one piece: the running state starts from src
+// (null: zero; a generic pointer, so it may sit in LDS), the outputs go to o (READOUT), and the state
+// at the piece's end goes to dst (null: not written; `pad`: dst is a final state, whose padding after
+// z is zeroed too).  Executes exactly 2 + nch barriers, like the producers.
+template <int NT, bool READOUT, bool CENT, bool COH = false>
+__device__ __forceinline__ void pipe_consumer(PipeSmem<NT, READOUT>& sm, const SeqPiece& pc, const float* src,
+                                              float* dst, bool pad, float* __restrict__ o, long long stride,
+                                              int w, int tid, float* keep = nullptr) {
+  constexpr int W = Geo<NT>::W, NAT = Geo<NT>::NAT, NKB = Geo<NT>::NKB;
+  constexpr int CS = kPipeChunk, NIT = CS / 16;
+  const int l = tid & 63, l16 = l & 15, lg = l >> 4;
+  const int nch = (pc.n + CS - 1) / CS;
+
+  // ---- consumers: wave w owns value columns 16w..16w+15 ----
+  f32x4 Srun[NAT];
+#pragma unroll
+  for (int t = 0; t < NAT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int a = 16 * t + 4 * lg + r;
+      Srun[t][r] = (src && a < W) ? src[(long long)a * kDV + 16 * w + l16] : 0.f;
+    }
+  __syncthreads();
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int b = c & 1;
+    const int nv = min(CS, pc.n - c * CS);
+    const long long tok0 = pc.tok + (long long)c * CS;
+    const float srow0 = Srun[0][0];  // S_{<c}[0][16w + l16] on lanes 0..15 (CENT)
+    f32x4 O[READOUT ? NIT : 1];
+    if constexpr (READOUT) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // readout with S_{<c} = hi + lo, one 32-feature k-block at a time
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        bf16x2 h[4], lw[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const f32x4& src = Srun[2 * kb + (r >> 1)];
+          split_bf16x2(src[2 * (r & 1)], src[2 * (r & 1) + 1], h[r], lw[r]);
+        }
+        const bf16x8 hi = {h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
+        const bf16x8 lo = {lw[0][0], lw[0][1], lw[1][0], lw[1][1], lw[2][0], lw[2][1], lw[3][0], lw[3][1]};
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[b][16 * it + l16][32 * kb + 8 * lg]);
+          O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, O[it], 0, 0, 0);
+          O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, O[it], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight (register budget)
+      }
+      // intra-chunk V^T x scores (weights as hi + lo)
+#pragma unroll
+      for (int it = 0; it < NIT; ++it)
+#pragma unroll
+        for (int jt = 0; jt <= it; ++jt) {
+          const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.vt[b][16 * w + l16][16 * jt + 4 * lg]);
+          const bf16x4 bh = sm.a[b][pair_index(jt, it)][l];
+          const bf16x4 bl = sm.alo[b][pair_index(jt, it)][l];
+          // V^T (hi + lo) as one 16x16x32 MFMA: the halves of k pair av with bh and av with bl
+          O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(av, av, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                         __builtin_shufflevector(bh, bl, 0, 1, 2, 3, 4, 5, 6, 7), O[it],
+                                                         0, 0, 0);
+        }
+    }
+    // state update
+#pragma unroll
+    for (int jb = 0; jb < CS / 32; ++jb) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[b][16 * w + l16][32 * jb + 8 * lg]);
+#pragma unroll
+      for (int t = 0; t < NAT; ++t) {
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.phikt[b][16 * t + l16][32 * jb + 8 * lg]);
+        Srun[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bv, Srun[t], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (READOUT) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int i = 16 * it + l16;
+        float d = 1.f;  // the expanded-softmax readout has no normaliser
+        if constexpr (!CENT) {
+          d = 0.f;
+#pragma unroll
+          for (int pp = 0; pp < kPipeProducers; ++pp) d += sm.den_part[b][pp][i];
+#pragma unroll
+          for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][pair_index(jt, it)][l16];
+        } else {
+          // + gamma_0(i) S_{<c}[0][16w + 4lg + r]: row 0 of columns 16w + 4lg .. lives on lanes 4lg ..
+          const float g0 = sm.den_part[b][0][i];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[it][r] = fmaf(g0, __shfl(srow0, 4 * lg + r), O[it][r]);
+        }
+        if (i < nv) {
+          const float inv = CENT ? 1.0f : __builtin_amdgcn_rcpf(d);
+          const f32x4 r = O[it];
+          *reinterpret_cast<f32x4*>(o + (tok0 + i) * kDV + 16 * w + 4 * lg) =
+              f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (dst) {
+#pragma unroll
+    for (int t = 0; t < NAT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int a = 16 * t + 4 * lg + r;
+        if (a < W) {
+          put_state<COH>(dst + (long long)a * kDV + 16 * w + l16, Srun[t][r]);
+          if (keep) keep[a * kDV + 16 * w + l16] = Srun[t][r];
+        }
+      }
+    if (pad && w == 0)  // the padding after z
+      for (long long e = (long long)W * (kDV + 1) + l; e < stride; e += 64) dst[e] = 0.f;
+  }
+}
+
+// The producer waves (w >= kPipeConsumers) over one piece, each on its own compile-time role.
+template <int NT, bool READOUT, bool CENT, bool COH = false>
+__device__ __forceinline__ void pipe_producers(PipeSmem<NT, READOUT>& sm, int w, const __bf16* q, const __bf16* k,
+                                               const __bf16* v, const float* cf, const float* src, float* dst,
+                                               float* zc0, long long tok, int n, int l, float scale,
+                                               float* keep = nullptr) {
+  const int nch = (n + kPipeChunk - 1) / kPipeChunk;
+  static_assert(kPipeProducers <= 8, "dispatch below lists up to 8 producers");
+#define TAYLOR_PRODUCER(G_)                                                                              \
+  case G_:                                                                                             \
+    if constexpr (G_ < kPipeProducers)                                                                 \
+      pipe_producer<NT, READOUT, CENT, G_, COH>(sm, q, k, v, cf, src, dst, zc0, tok, n, nch, l, scale, keep); \
+    break;
+  switch (w - kPipeConsumers) {
+    TAYLOR_PRODUCER(0)
+    TAYLOR_PRODUCER(1)
+    TAYLOR_PRODUCER(2)
+    TAYLOR_PRODUCER(3)
+    TAYLOR_PRODUCER(4)
+    TAYLOR_PRODUCER(5)
+    TAYLOR_PRODUCER(6)
+    TAYLOR_PRODUCER(7)
+    default: break;
+  }
+#undef TAYLOR_PRODUCER
 }
 
 template <int NT, bool READOUT, bool PACKED, bool CENT>
@@ -453,8 +623,7 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
                                                                     long long nslot, long long stride, float scale) {
   using G = Geo<NT>;
   using SM = PipeSmem<NT, READOUT>;
-  constexpr int W = G::W, NAT = G::NAT, NKB = G::NKB;
-  constexpr int CS = kPipeChunk, NIT = CS / 16;
+  constexpr int W = G::W;
   __shared__ SM sm;
 
   // The role is taken from a wave-uniform scalar so each wave runs only its own loops; both roles
@@ -462,7 +631,7 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
   // another in LDS without an extra barrier: a piece's last barrier orders every read of its
   // buffers before the next piece's first writes, and the z rows each producer rewrites at a
   // piece's start are its own.
-  const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long bx = blockIdx.x, by = blockIdx.y;
   // Where a piece's state starts and ends.  Segments: the readout pass starts from its prefix slot and
@@ -524,141 +693,180 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
     }
   };
   if (w >= kPipeConsumers) {
-    static_assert(kPipeProducers <= 8, "dispatch below lists up to 8 producers");
-#define TAYLOR_PRODUCER(G_)                                                                           \
-  case G_:                                                                                          \
-    if constexpr (G_ < kPipeProducers)                                                              \
-      walk(false, [&](const SeqPiece& pc) __attribute__((always_inline)) {                          \
-        pipe_producer<NT, READOUT, CENT, G_>(sm, q, k, v, cf, state_src(pc), state_dst(pc),         \
-                                             zc ? zc + seq.chunk_index(pc, 0, CS) * W : nullptr,    \
-                                             pc.tok, pc.n,                                          \
-                                       (pc.n + CS - 1) / CS, l, scale);                             \
-      });                                                                                           \
-    break;
-    switch (w - kPipeConsumers) {
-      TAYLOR_PRODUCER(0)
-      TAYLOR_PRODUCER(1)
-      TAYLOR_PRODUCER(2)
-      TAYLOR_PRODUCER(3)
-      TAYLOR_PRODUCER(4)
-      TAYLOR_PRODUCER(5)
-      TAYLOR_PRODUCER(6)
-      TAYLOR_PRODUCER(7)
-      default: break;
-    }
-#undef TAYLOR_PRODUCER
+    walk(false, [&](const SeqPiece& pc) __attribute__((always_inline)) {
+      pipe_producers<NT, READOUT, CENT>(sm, w, q, k, v, cf, state_src(pc), state_dst(pc),
+                                        zc ? zc + seq.chunk_index(pc, 0, kPipeChunk) * W : nullptr, pc.tok, pc.n, l,
+                                        scale);
+    });
     return;
   }
 
   walk(true, [&](const SeqPiece& pc) __attribute__((always_inline)) {
-    const int nch = (pc.n + CS - 1) / CS;
-    const float* src = state_src(pc);
-    float* dst = state_dst(pc);
-
-    // ---- consumers: wave w owns value columns 16w..16w+15 ----
-    f32x4 Srun[NAT];
-#pragma unroll
-    for (int t = 0; t < NAT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int a = 16 * t + 4 * lg + r;
-        Srun[t][r] = (src && a < W) ? src[(long long)a * kDV + 16 * w + l16] : 0.f;
-      }
-    __syncthreads();
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      const int b = c & 1;
-      const int nv = min(CS, pc.n - c * CS);
-      const long long tok0 = pc.tok + (long long)c * CS;
-      const float srow0 = Srun[0][0];  // S_{<c}[0][16w + l16] on lanes 0..15 (CENT)
-      f32x4 O[READOUT ? NIT : 1];
-      if constexpr (READOUT) {
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // readout with S_{<c} = hi + lo, one 32-feature k-block at a time
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          bf16x2 h[4], lw[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const f32x4& src = Srun[2 * kb + (r >> 1)];
-            split_bf16x2(src[2 * (r & 1)], src[2 * (r & 1) + 1], h[r], lw[r]);
-          }
-          const bf16x8 hi = {h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
-          const bf16x8 lo = {lw[0][0], lw[0][1], lw[1][0], lw[1][1], lw[2][0], lw[2][1], lw[3][0], lw[3][1]};
-#pragma unroll
-          for (int it = 0; it < NIT; ++it) {
-            const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[b][16 * it + l16][32 * kb + 8 * lg]);
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, O[it], 0, 0, 0);
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, O[it], 0, 0, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight (register budget)
-        }
-        // intra-chunk V^T x scores (weights as hi + lo)
-#pragma unroll
-        for (int it = 0; it < NIT; ++it)
-#pragma unroll
-          for (int jt = 0; jt <= it; ++jt) {
-            const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.vt[b][16 * w + l16][16 * jt + 4 * lg]);
-            const bf16x4 bh = sm.a[b][pair_index(jt, it)][l];
-            const bf16x4 bl = sm.alo[b][pair_index(jt, it)][l];
-            // V^T (hi + lo) as one 16x16x32 MFMA: the halves of k pair av with bh and av with bl
-            O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(av, av, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                           __builtin_shufflevector(bh, bl, 0, 1, 2, 3, 4, 5, 6, 7), O[it],
-                                                           0, 0, 0);
-          }
-      }
-      // state update
-#pragma unroll
-      for (int jb = 0; jb < CS / 32; ++jb) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[b][16 * w + l16][32 * jb + 8 * lg]);
-#pragma unroll
-        for (int t = 0; t < NAT; ++t) {
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.phikt[b][16 * t + l16][32 * jb + 8 * lg]);
-          Srun[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bv, Srun[t], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (READOUT) {
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const int i = 16 * it + l16;
-          float d = 1.f;  // the expanded-softmax readout has no normaliser
-          if constexpr (!CENT) {
-            d = 0.f;
-#pragma unroll
-            for (int pp = 0; pp < kPipeProducers; ++pp) d += sm.den_part[b][pp][i];
-#pragma unroll
-            for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][pair_index(jt, it)][l16];
-          } else {
-            // + gamma_0(i) S_{<c}[0][16w + 4lg + r]: row 0 of columns 16w + 4lg .. lives on lanes 4lg ..
-            const float g0 = sm.den_part[b][0][i];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) O[it][r] = fmaf(g0, __shfl(srow0, 4 * lg + r), O[it][r]);
-          }
-          if (i < nv) {
-            const float inv = CENT ? 1.0f : __builtin_amdgcn_rcpf(d);
-            const f32x4 r = O[it];
-            *reinterpret_cast<f32x4*>(o + (tok0 + i) * kDV + 16 * w + 4 * lg) =
-                f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
-          }
-        }
-      }
-      __syncthreads();
-    }
-
-    if (dst) {
-#pragma unroll
-      for (int t = 0; t < NAT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int a = 16 * t + 4 * lg + r;
-          if (a < W) dst[(long long)a * kDV + 16 * w + l16] = Srun[t][r];
-        }
-      if (direct && w == 0)  // the padding after z
-        for (long long e = (long long)W * (kDV + 1) + l; e < stride; e += 64) dst[e] = 0.f;
-    }
+    pipe_consumer<NT, READOUT, CENT>(sm, pc, state_src(pc), state_dst(pc), direct != 0, o, stride, w, tid);
   });
+}
+
+// ------------------------------------------------------------------------------------------------
+// Single-pass prefill over segments (equal lengths, the truncated-kernel readout): the state pass,
+// the scan and the readout pass of the split form in one launch, with a decoupled look-back between
+// the segments of a (sequence, head) pair ("Expanding Attention", Abstract: the states add across
+// chunks, so prefill admits a parallel scan).  Workgroup (x, pair) walks segment x:
+//   1. its state sum over the segment, written to its slot and published at once with a flag
+//      (segment 0 starts from the incoming state, so its sum is already the inclusive prefix);
+//   2. the exclusive prefix: the flags of segments x-1, x-2, ... are read back until an inclusive one
+//      is found, and the published sums from there on are added in segment order; the inclusive
+//      prefix (exclusive + its own sum) is then published in turn, so later segments stop at this one;
+//   3. the readout walk from the exclusive prefix (staged in LDS); the last segment writes the final
+//      state at its end and needs no state sum of its own (nobody reads it).
+// A flag is the call's tag (bits 2..63) plus kFlagAgg or kFlagIncl: a flag from an earlier call, or
+// whatever the workspace held, carries another tag and reads as not yet published.  Eager calls take
+// a fresh nonzero tag each; a call recorded into a HIP graph (replayed with the same arguments) uses
+// tag 0 and clears its flags first with a fill kernel.  Waits are only on lower segments of the same
+// pair, i.e. on workgroups with lower linear ids, which the hardware dispatches first, and the form is
+// used only where the whole grid is one round (at most one workgroup per CU).  Every wait is also
+// bounded: after kSpinLimit polls the prefix is taken as NaN (outputs NaN, nothing hangs).
+// ------------------------------------------------------------------------------------------------
+constexpr unsigned long long kFlagAgg = 1, kFlagIncl = 2, kFlagMask = 3;
+constexpr int kSpinLimit = 1 << 20;
+constexpr int kFusedMaxGrid = 256;
+
+// This thread's elements e = tid + 512 i of a state block (S rows then z).
+template <int NT>
+struct StateSlice {
+  static constexpr long long E = (long long)Geo<NT>::W * (kDV + 1);
+  static constexpr int K = (int)((E + kPipeThreads - 1) / kPipeThreads);
+};
+
+template <int NT>
+__global__ __launch_bounds__(kPipeThreads) void prefill_pipe_fused_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v, float* __restrict__ o,
+    float* __restrict__ agg, float* __restrict__ incl, unsigned long long* flags, const float* sin, float* sout,
+    int N, int L, long long stride, float scale, unsigned long long tag) {
+  using SM1 = PipeSmem<NT, true>;
+  using SM0 = PipeSmem<NT, false>;
+  using SL = StateSlice<NT>;
+  static_assert(sizeof(SM0) <= sizeof(SM1), "the state walk's LDS fits in the readout's");
+  static_assert(SL::E * sizeof(float) <= sizeof(SM1::phiq), "the starting state fits where phi(sQ) goes");
+  __shared__ SM1 sm;
+  __shared__ unsigned long long seen;
+  SM0& sm0 = *reinterpret_cast<SM0*>(&sm);
+  float* pre = reinterpret_cast<float*>(&sm.phiq[0][0][0]);  // the segment's starting state, between phases
+  // the segment's own sum, kept in LDS at the end of the state walk (where V^T and phi(K)^T were; only
+  // the producers' z rows, further on, are still read then)
+  float* own = reinterpret_cast<float*>(&sm);
+  static_assert(SL::E * sizeof(float) <= offsetof(SM0, phiq), "the kept sum lies before the walk's z rows");
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int x = blockIdx.x, nseg = gridDim.x;
+  const long long pair = blockIdx.y, slot = pair * nseg + x;
+  const SeqPiece pc{pair * N + (long long)x * L, min(L, N - x * L), slot, pair};
+  const bool last = x == nseg - 1;
+  const float* sin_p = sin ? sin + pair * stride : nullptr;
+
+  // 1. the segment's state sum (not needed from the last segment)
+  if (!last) {
+    const float* src = x == 0 ? sin_p : nullptr;
+    float* dst = (x == 0 ? incl : agg) + slot * stride;
+    if (w >= kPipeConsumers)
+      pipe_producers<NT, false, false, true>(sm0, w, q, k, v, nullptr, src, dst, nullptr, pc.tok, pc.n, l, scale,
+                                             own);
+    else
+      pipe_consumer<NT, false, false, true>(sm0, pc, src, dst, false, nullptr, stride, w, tid, own);
+  }
+  // The sum of a middle segment is published at once, so later segments need not wait for its
+  // look-back.  Publishing: the sums were stored through to the point of coherence (agent-scope
+  // stores); every wave waits until its stores are acknowledged, then, after the barrier, one thread
+  // stores the flag.  Readers load the flag and then the sums from the point of coherence too, so no
+  // cache is written back or invalidated on either side.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // also: the state walk's last LDS reads (z rows for dst) are done before `pre` is written
+  if (x > 0 && !last && tid == 0)
+    __hip_atomic_store(flags + slot, tag | kFlagAgg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // 2. the exclusive prefix into `pre`, and the inclusive one published
+  if (x == 0) {
+    for (long long e = tid; e < SL::E; e += kPipeThreads) pre[e] = sin_p ? sin_p[e] : 0.f;
+  } else {
+    // thread 0 walks the flags back to the nearest inclusive prefix j (every flag on the way is a
+    // published sum); the prefix is then summed forward from j, incl[j] + agg[j+1] + ... + agg[x-1],
+    // which is the left-to-right sum the inclusive chain itself computes, so the result does not
+    // depend on which segments had published when (the output is bitwise repeatable)
+    if (tid == 0) {
+      long long j = slot - 1;
+      for (;; --j) {
+        unsigned long long f = 0;
+        for (int spin = 0;; ++spin) {
+          f = __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((f & ~kFlagMask) == tag && (f & kFlagMask) != 0) break;
+          if (spin >= kSpinLimit) {
+            f = 0;  // never published: give up
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (f == 0) {
+          j = -1;
+          break;
+        }
+        if ((f & kFlagMask) == kFlagIncl) break;
+      }
+      seen = (unsigned long long)j;
+    }
+    __syncthreads();
+    const long long j0 = (long long)seen;
+    float acc[SL::K];
+    const float* first = incl + (j0 < 0 ? slot : j0) * stride;  // (not read when j0 < 0)
+#pragma unroll
+    for (int i = 0; i < SL::K; ++i) {
+      const long long e = tid + (long long)kPipeThreads * i;
+      acc[i] = j0 < 0 ? __builtin_nanf("") : (e < SL::E ? get_published(first + e) : 0.f);
+    }
+    // up to three published sums at a time: all their loads are issued before the first add
+    for (long long m = j0 + 1; j0 >= 0 && m < slot; m += 3) {
+      const int cnt = (int)min(3LL, slot - m);
+      float t[3][SL::K];
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+#pragma unroll
+        for (int i = 0; i < SL::K; ++i) {
+          const long long e = tid + (long long)kPipeThreads * i;
+          t[u][i] = (u < cnt && e < SL::E) ? get_published(agg + (m + u) * stride + e) : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+        if (u < cnt)
+#pragma unroll
+          for (int i = 0; i < SL::K; ++i) acc[i] += t[u][i];  // in segment order
+    }
+    float* inc = incl + slot * stride;
+#pragma unroll
+    for (int i = 0; i < SL::K; ++i) {
+      const long long e = tid + (long long)kPipeThreads * i;
+      if (e < SL::E) {
+        pre[e] = acc[i];
+        if (!last) put_state<true>(inc + e, acc[i] + own[e]);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores acknowledged (as above)
+  __syncthreads();
+  if (!last && tid == 0)
+    __hip_atomic_store(flags + slot, tag | kFlagIncl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // 3. the readout walk from `pre` (a generic pointer into LDS; every read of it precedes the walk's
+  // first barrier, after which the pipeline reuses that LDS)
+  float* dst = last && sout ? sout + pair * stride : nullptr;
+  if (w >= kPipeConsumers)
+    pipe_producers<NT, true, false>(sm, w, q, k, v, nullptr, pre, dst, nullptr, pc.tok, pc.n, l, scale);
+  else
+    pipe_consumer<NT, true, false>(sm, pc, pre, dst, dst != nullptr, o, stride, w, tid);
+}
+
+// Clears the flags of a call recorded into a graph (tag 0), before its single-pass kernel.
+__global__ void clear_flags_kernel(unsigned long long* flags, long long n) {
+  const long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x;
+  if (i < n) flags[i] = 0;
 }
 
 int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -743,6 +951,22 @@ auto pipe_kernel_for(bool packed, bool cent) {
   return packed ? prefill_pipe_kernel<NT, READOUT, true, false> : prefill_pipe_kernel<NT, READOUT, false, false>;
 }
 
+// The single-pass form applies to equal lengths split into segments, with the truncated-kernel
+// readout, where the whole grid is one round of one workgroup per CU.
+bool fused_form(const PipePlan& p, const SeqMap& seq, int BH, int readout) {
+  const long long nseg = seq.grid_x(p.L);
+  return !p.direct && !seq.packed && readout != 1 && nseg > 1 && nseg * BH <= kFusedMaxGrid;
+}
+
+// A fresh nonzero tag (bits 2..63) per eager single-pass call, from a process-wide counter started at
+// a time-derived value.
+unsigned long long next_tag() {
+  static std::atomic<unsigned long long> counter{
+      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9e3779b97f4a7c15ull};
+  unsigned long long t = counter.fetch_add(1, std::memory_order_relaxed) & ((1ull << 62) - 1);
+  return (t ? t : 1) << 2;
+}
+
 template <int NT>
 int run_pipe(const PrefillArgs& a) {
   const PipePlan p = pipe_plan(a.BH, a.seq, a.s.readout != 1);
@@ -769,6 +993,24 @@ int run_pipe(const PrefillArgs& a) {
       pipe_kernel_for<NT, false>(a.seq.packed, false)<<<grid, block, 0, a.stream>>>(
           q, k, v, nullptr, nullptr, ws, nullptr, a.state_in, a.state, p.longest_first ? 3 : 1, a.seq, p.L,
           p.nslot, a.s.stride, a.s.scale);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+  }
+  if (a.o && fused_form(p, a.seq, a.BH, a.s.readout)) {
+    // single pass: state sums, look-back and readout in one launch (slots: sums | inclusive | flags)
+    const long long slots = (long long)grid.x * grid.y;
+    float* incl = ws + round_up(slots * a.s.stride, 64);
+    unsigned long long* flags = reinterpret_cast<unsigned long long*>(incl + round_up(slots * a.s.stride, 64));
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const bool recorded = hipStreamIsCapturing(a.stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
+    unsigned long long tag = 0;
+    if (recorded) {
+      clear_flags_kernel<<<dim3((unsigned)cdiv(slots, 256)), dim3(256), 0, a.stream>>>(flags, slots);
+      if (hipGetLastError() != hipSuccess) return -3;
+    } else {
+      tag = next_tag();
+    }
+    prefill_pipe_fused_kernel<NT><<<grid, block, 0, a.stream>>>(q, k, v, a.o, ws, incl, flags, a.state_in, a.state,
+                                                                 a.seq.N, p.L, a.s.stride, a.s.scale, tag);
     return hipGetLastError() == hipSuccess ? 0 : -3;
   }
   pipe_kernel_for<NT, false>(a.seq.packed, cent)<<<grid, block, 0, a.stream>>>(
@@ -801,6 +1043,7 @@ bool prefill_mfma_has(int nt, int dk, int dv, int dtype) { return dk == kDK && d
 long long prefill_mfma_ws_bytes(const Shape& s, int BH, const SeqMap& seq) {
   const PipePlan p = pipe_plan(BH, seq, s.readout != 1);
   const long long slots = round_up(seq.rows(BH) * p.nslot * s.stride, 64);
+  if (fused_form(p, seq, BH, s.readout)) return (2 * slots + seq.rows(BH) * p.nslot * 2) * 4;  // + 8-byte flags
   if (s.readout != 1) return slots * 4;
   return (slots + round_up(4 * seq.tokens(BH), 64) + seq.chunk_count(BH, kPipeChunk) * s.W) * 4;
 }
