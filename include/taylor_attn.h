@@ -36,7 +36,9 @@
  *   nothing has been enqueued (TAYLOR_ERR_HIP: a launch failed; earlier
  *   kernels of the same call may already be queued).  No C++ exception crosses
  *   this boundary.  Calls are re-entrant; the only global state is the
- *   address of taylor_attn_prefill_into_static's workspace on each device.
+ *   address of taylor_attn_prefill_into_static's workspace on each device and
+ *   a process-wide counter that tags the single-pass prefill's flags per call
+ *   (so a workspace's prior contents never read as this call's).
  *
  * State layout (per head, float32): the "packed" block of
  * W*(d_v+1) values the Abstract counts (9,945 at n=3, d_k=16, d_v=64),

@@ -3,9 +3,9 @@
 // Everything here is host logic.  Validation happens before any HIP call, so
 // an invalid call returns its status without touching the device (and without
 // needing one).  The library never allocates, frees or synchronises device
-// memory; its one piece of global state is the per-device address of the
-// static workspace array of taylor_attn_prefill_into_static (set once per
-// device under a mutex).
+// memory; its global state is the per-device address of the static workspace
+// array of taylor_attn_prefill_into_static (set once per device under a mutex)
+// and the single-pass prefill's per-call tag counter (prefill_mfma.hip).
 #include <cmath>
 #include <cstdint>
 #include <cstring>
