@@ -118,7 +118,21 @@ __global__ __launch_bounds__(kThreads) void seg_scan_kernel(float* __restrict__ 
   seq.pair_slots(bh, nslot, L, first, n);
   float run = seed ? seed[bh * stride + e] : 0.f;
   float* w = ws + first * stride + e;
-  for (int s = 0; s < n; ++s) {
+  // eight slots at a time: their loads are all in flight before the first add (the walk over a pair's
+  // slots is otherwise one memory round trip per slot); the sums stay in slot order
+  constexpr int kBatch = 8;
+  int s = 0;
+  for (; s + kBatch <= n; s += kBatch) {
+    float t[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) t[u] = w[(s + u) * stride];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (write_prefix) w[(s + u) * stride] = run;
+      run += t[u];
+    }
+  }
+  for (; s < n; ++s) {
     const float t = w[s * stride];
     if (write_prefix) w[s * stride] = run;
     run += t;
