@@ -203,6 +203,28 @@ def accuracy(o, ref):
             "row_rel_l2_median": float(rr.median()), "rel_frobenius": float(diff.norm() / ref.norm())}
 
 
+def prefill_into_call(rs, torch, q, k, v, o, state_in, state_out, ws, cfg):
+    """A closure making the taylor_attn_prefill_into C-ABI call with fixed raw arguments, for timed loops.
+    The binding function is called once first, so its argument checks run; the closure then skips them
+    (they cost tens of microseconds of host time per call, as much as the smallest prefills take on the
+    GPU, which would otherwise time the host)."""
+    import ctypes
+
+    rs.taylor_attn_prefill_into(q, k, v, o, state_in, state_out, ws, cfg)
+    B, H, N = k.shape[:3]
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())
+    args = (ptr(q), ptr(k), ptr(v), ptr(o), ptr(state_in), ptr(state_out), ptr(ws), B, H, N, ctypes.byref(cfg),
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    f = rs.lib().taylor_attn_prefill_into
+
+    def call():
+        rc = f(*args)
+        if rc:
+            raise rs.TaylorError(rc, "taylor_attn_prefill_into")
+
+    return call
+
+
 def timed_us(torch, fn, reps):
     fn()
     torch.cuda.synchronize()
@@ -240,7 +262,7 @@ def order_sweep(rs, synth, torch, dev, reps=3, rows_per_head=256):
             chunk = rs.taylor_prefill_chunk(cfg)
             st = torch.empty((B, H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
             ws = rs.new_workspace(cfg, B, H, N, dev)
-            us = timed_us(torch, lambda: rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg), reps)
+            us = timed_us(torch, prefill_into_call(rs, torch, q, k, v, o, None, st, ws, cfg), reps)
             w = rs.taylor_feature_width(n, DK)
             flops = B * H * N * prefill_flops_per_token_head(w, chunk)
             out[f"n{n}"] = {"W": w, "chunk": chunk, "us": us, "tok_s": B * N / us * 1e6, "TFLOPs": flops / us / 1e6,
@@ -265,7 +287,7 @@ def prefill_f32_config(rs, synth, torch, dev, reps=20):
     o = torch.empty((B, H, N, DV), dtype=torch.float32, device=dev)
     st = torch.empty((B, H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
     ws = rs.new_workspace(cfg, B, H, N, dev)
-    us = timed_us(torch, lambda: rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg), reps)
+    us = timed_us(torch, prefill_into_call(rs, torch, q, k, v, o, None, st, ws, cfg), reps)
     w = rs.taylor_feature_width(n, DK)
     flops = B * H * N * prefill_flops_per_token_head(w, chunk)
     nbytes = B * H * N * 4 * (DK + DK + DV + DV)
@@ -319,8 +341,7 @@ def centered_prefill(rs, torch, dev, q, k, v, reps=5):
         st = torch.empty((B, H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
         ws = rs.new_workspace(cfg, B, H, N, dev)
 
-        def step():
-            rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg)
+        step = prefill_into_call(rs, torch, q, k, v, o, None, st, ws, cfg)
 
         step()
         torch.cuda.synchronize()
@@ -405,7 +426,7 @@ def softmax_crossover(rs, synth, torch, dev, reps=5):
         o = torch.empty((B, H, N, DV), dtype=torch.float32, device=dev)
         st = torch.empty((B, H, rs.taylor_state_stride(cfg)), dtype=torch.float32, device=dev)
         ws = rs.new_workspace(cfg, B, H, N, dev)
-        t_us = timed(lambda: rs.taylor_attn_prefill_into(q, k, v, o, None, st, ws, cfg))
+        t_us = timed(prefill_into_call(rs, torch, q, k, v, o, None, st, ws, cfg))
         qp = torch.nn.functional.pad(q, (0, DV - DK)).contiguous()
         kp = torch.nn.functional.pad(k, (0, DV - DK)).contiguous()
         s_us, err = None, None
@@ -534,10 +555,12 @@ def main():
         torch.cuda.synchronize()
         log("decode graph captured")
 
+    prefill_step = prefill_into_call(rs, torch, pq, pk, pv, po, None, pstate, pws, pcfg)
+
     def step(evs):
         cur = torch.cuda.current_stream()
         evs[0].record(cur)
-        rs.taylor_attn_prefill_into(pq, pk, pv, po, None, pstate, pws, pcfg)
+        prefill_step()
         evs[1].record(cur)
         if graph is not None:
             graph.replay()

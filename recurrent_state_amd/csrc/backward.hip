@@ -42,6 +42,7 @@
 // coefficient (x_c0 x_c1 has at most 16 significant bits).  S += phi(K)^T V (state pass, pass A) then runs
 // as two 16x16x16 bfloat16 MFMAs per 16 tokens with the same float32 products, the coefficient applied
 // once (pass A keeps S_f / cf_f in its accumulators); G v (pass B) takes G as three bfloat16 terms
+// (hi and mid in one 16x16x32 MFMA, lo in a second)
 // (24 significant bits) against exact v.
 #include <type_traits>
 #include <utility>
@@ -107,9 +108,6 @@ __device__ __forceinline__ void split3(const f32x4& x, bf16x4& h, bf16x4& m, bf1
   h = bf16x4{hh[0][0], hh[0][1], hh[1][0], hh[1][1]};
   m = bf16x4{mm[0][0], mm[0][1], mm[1][0], mm[1][1]};
   l = bf16x4{ll[0][0], ll[0][1], ll[1][0], ll[1][1]};
-}
-__device__ __forceinline__ f32x4 mfma_bf16(i16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
 }
 
 // c + a0 b0 + a1 b1 as one 16x16x32 MFMA: lane group g supplies k = 8g..8g+7 of both operands, so the
@@ -871,11 +869,14 @@ __global__ __launch_bounds__(kThreads) void bwd_dkv_kernel(const E* __restrict__
 #pragma unroll
               for (int jt = 0; jt < 4; ++jt) {
                 const bf16x4 vv = *reinterpret_cast<const bf16x4*>(&sm.vb[16 * jt + l16][16 * dt + 4 * lg]);
+                // (hi, mid) and (lo, 0) as the k-halves of two 16x16x32 MFMAs against (v, v): only
+                // 16x16x32s chain on zt (a 16x16x16 reading a 16x16x32 result right after it is a
+                // pairing that gives wrong sums on gfx950)
 #pragma unroll
-                for (int u = 0; u < NA; ++u)
-#pragma unroll
-                  for (int e = 0; e < 3; ++e)
-                    zt[u][jt] = mfma_bf16(__builtin_bit_cast(i16x4, gs3[u][e]), vv, zt[u][jt]);
+                for (int u = 0; u < NA; ++u) {
+                  zt[u][jt] = mfma_bf16_pair(gs3[u][0], gs3[u][1], vv, vv, zt[u][jt]);
+                  zt[u][jt] = mfma_bf16_pair(gs3[u][2], bf16x4{}, vv, vv, zt[u][jt]);
+                }
               }
             }
 #pragma unroll

@@ -8,7 +8,7 @@
 // At n = 4, 5 the state (W x 65 floats per head, up to 1.26 MB) fits neither registers nor LDS.  But
 // each feature row of S evolves on its own (S_f += phi_f(K_c)^T V1_c involves only features f), and the
 // readout phi(sQ) S_{<c} = sum_f phi_f(sQ) S_{f,<c} is a sum over feature blocks f.  So the work is split
-// over (segment, head, block of FB features; FB = 64 at n = 4, 128 at n = 5), one workgroup of 8
+// over (segment, head, block of FB features; FB = 64 at n = 4, 160 at n = 5), one workgroup of 8
 // wavefronts each:
 //   * waves 0..3 ("consumers") own value columns 16w..16w+15 of the block's state slice, kept in MFMA
 //     accumulator registers, and run only float32 16x16x4 MFMAs on chunk c: the readout with S_{<c}, the
@@ -51,11 +51,12 @@ static_assert(kPairs <= kProd, "one score tile per producer");
 
 // Features per block: one block holds all features at n <= 3 (16, 32, 160 for W = 1, 17, 153: the
 // outputs are then final and written directly); 64 at n = 4 (16 blocks: enough (head, block)
-// workgroups at few heads without a state pass); 128 at n = 5 (38 blocks; half the partial-output
-// traffic of 64).
+// workgroups at few heads without a state pass); 160 at n = 5 (31 blocks: 16 heads make 496
+// workgroups, two rounds of one per CU, where 128-feature blocks made 608, three rounds; 20% less
+// partial-output traffic too).
 template <int NT>
 constexpr int block_features() {
-  return NT == 1 ? 16 : NT == 2 ? 32 : NT == 3 ? 160 : NT == 4 ? 64 : 128;
+  return NT == 1 ? 16 : NT == 2 ? 32 : NT == 3 ? 160 : NT == 4 ? 64 : 160;
 }
 template <int NT>
 constexpr int n_blocks() {
@@ -497,7 +498,24 @@ __global__ __launch_bounds__(256) void wide_reduce_kernel(const float* __restric
   if (tok >= tokens) return;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float d = 0.f;
-  for (int b = 0; b < nb; ++b) {
+  // eight blocks at a time: their loads are in flight together; the sums stay in block order
+  constexpr int kBatch = 8;
+  int b = 0;
+  for (; b + kBatch <= nb; b += kBatch) {
+    f32x4 x[kBatch];
+    float y[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      x[u] = *reinterpret_cast<const f32x4*>(num + ((long long)(b + u) * tokens + tok) * kDV + 4 * g);
+      y[u] = den[(long long)(b + u) * tokens + tok];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      acc = acc + x[u];
+      d += y[u];
+    }
+  }
+  for (; b < nb; ++b) {
     const f32x4 x = *reinterpret_cast<const f32x4*>(num + ((long long)b * tokens + tok) * kDV + 4 * g);
     acc = acc + x;
     d += den[(long long)b * tokens + tok];
