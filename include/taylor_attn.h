@@ -283,7 +283,9 @@ int64_t taylor_prefill_backward_workspace_bytes(const taylor_config* cfg, int B,
  *   workspace : taylor_prefill_backward_workspace_bytes(cfg, B, H, N) bytes.
  * So a sequence prefilled in pieces is differentiated piece by piece in reverse,
  * passing dstate along.  Compiled for cfg->readout = TAYLOR_READOUT_KERNEL,
- * n_terms = 1..3, d_k = 16, d_v = 64, either input type (float32 arithmetic);
+ * n_terms = 1..5, d_k = 16, d_v = 64, either input type (float32 arithmetic;
+ * n = 4, 5 on feature blocks, whose per-block partial gradients make the
+ * workspace 5,456 (n = 4) or 12,584 (n = 5) bytes per token and head);
  * otherwise TAYLOR_ERR_UNSUPPORTED.  B*H == 0 or N == 0 is a no-op (dstate
  * unchanged).  Calls sharing a workspace must not overlap. */
 int taylor_attn_prefill_backward(const void* q, const void* k, const void* v, const float* o, const float* g,

@@ -538,5 +538,5 @@ def taylor_attention(q, k, v, cfg, state=None):
     bfloat16 as cfg says): the forward is taylor_attn_prefill_into from `state` (a float32 [B, H,
     stride] incoming state, or None for an empty history), the backward taylor_attn_prefill_backward;
     returns o [B, H, N, d_v] float32.  q, k, v and `state` receive gradients when they require them
-    (the truncated-kernel readout at n = 1..3, d_k = 16, d_v = 64)."""
+    (the truncated-kernel readout at n = 1..5, d_k = 16, d_v = 64)."""
     return _autograd_fn().apply(q, k, v, state, cfg)

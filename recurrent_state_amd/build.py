@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(LIBDIR, "libtaylor_attn.so")
 
-SOURCES = ["api.cpp", "decode.hip", "prefill_generic.hip", "prefill_mfma.hip", "prefill_wide.hip", "centered.hip", "backward.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill_generic.hip", "prefill_mfma.hip", "prefill_wide.hip", "centered.hip", "backward.hip", "backward_wide.hip"]
 ARCH = "gfx950"
 
 

@@ -14,7 +14,8 @@
 // (the gradient of the state at that point) give
 //     dv_j += G_S^T phi(k_j),   dk_j += J_phi(k_j)^T (G_S v_j + G_z).
 // G at the start of the call is the incoming state's gradient; a gradient for the final state seeds
-// G at the end.  J_phi is the Jacobian of the monomial features (orders <= 2 here: n <= 3).
+// G at the end.  J_phi is the Jacobian of the monomial features (orders <= 2 here: n <= 3; n = 4, 5
+// run on feature blocks in backward_wide.hip).
 //
 // Passes over segments of L tokens (one workgroup of 8 wavefronts per segment, 64-token chunks):
 //   1. state pass: the S, z increments of each segment;
@@ -1098,9 +1099,10 @@ int bwd_run(const BwdArgs& a) {
 
 }  // namespace
 
-bool backward_has(int nt, int dk, int dv) { return dk == kDK && dv == kDV && nt >= 1 && nt <= 3; }
+bool backward_has(int nt, int dk, int dv) { return dk == kDK && dv == kDV && nt >= 1 && nt <= 5; }
 
 long long backward_ws_bytes(const Shape& s, int BH, int N) {
+  if (s.nt >= 4) return backward_wide_ws_bytes(s, BH, N);
   if (BH == 0 || N == 0) return 0;
   const BwdPlan p = plan_for(BH, N);
   return (2 * (long long)BH * p.nseg * s.stride + (long long)BH * N * (kDV + 1)) * 4;
@@ -1108,6 +1110,7 @@ long long backward_ws_bytes(const Shape& s, int BH, int N) {
 
 int backward_launch(const BwdArgs& a) {
   if (!backward_has(a.s.nt, a.s.dk, a.s.dv)) return -2;
+  if (a.s.nt >= 4) return backward_wide_launch(a);
   switch (a.s.nt) {
     case 1: return a.s.dtype == 0 ? bwd_run<1, float>(a) : bwd_run<1, uint16_t>(a);
     case 2: return a.s.dtype == 0 ? bwd_run<2, float>(a) : bwd_run<2, uint16_t>(a);

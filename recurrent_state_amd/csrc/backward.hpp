@@ -1,4 +1,4 @@
-// Backward of truncated-kernel causal attention (d_k = 16, d_v = 64, n = 1..3).
+// Backward of truncated-kernel causal attention (d_k = 16, d_v = 64, n = 1..5).
 #pragma once
 
 #include "launch.hpp"
@@ -24,5 +24,9 @@ struct BwdPlan {
 bool backward_has(int nt, int dk, int dv);
 long long backward_ws_bytes(const Shape& s, int BH, int N);
 int backward_launch(const BwdArgs& a);
+
+// n = 4, 5 (backward_wide.hip): feature blocks with per-block partial gradients.
+long long backward_wide_ws_bytes(const Shape& s, int BH, int N);
+int backward_wide_launch(const BwdArgs& a);
 
 }  // namespace taylor

@@ -275,9 +275,12 @@ def test_varlen_validation():
 
 def test_backward_queries_and_validation():
     L = rs.lib()
-    for n in (1, 2, 3):
+    for n in (1, 2, 3, 4, 5):
         for dt in (rs.TAYLOR_F32, rs.TAYLOR_BF16):
             assert rs.taylor_prefill_backward_workspace_bytes(rs.config(n, 16, 64, 0, 1.0, dt), 4, 16, 8192) > 0
+    # n = 4, 5: gh and delta (68 floats) plus per feature block a den, 16 dq / dk and 64 dv floats per token
+    for n, blocks in ((4, 16), (5, 38)):
+        assert rs.taylor_prefill_backward_workspace_bytes(rs.config(n, 16, 64), 2, 3, 100) == 600 * 4 * (68 + 81 * blocks)
     cfg = rs.config(3, 16, 64)
     assert rs.taylor_prefill_backward_workspace_bytes(cfg, 0, 16, 8192) == 0
     assert rs.taylor_prefill_backward_workspace_bytes(cfg, 4, 16, 0) == 0
@@ -287,7 +290,7 @@ def test_backward_queries_and_validation():
     def wsb(c, B=1, H=1, N=64):
         return L.taylor_prefill_backward_workspace_bytes(ctypes.byref(c) if c else None, B, H, N)
 
-    assert wsb(rs.config(4, 16, 64)) == U
+    assert wsb(rs.config(6, 16, 64)) == U
     assert wsb(rs.config(3, 8, 32)) == U
     assert wsb(rs.config(3, 16, 64, 0, 1.0, 0, rs.TAYLOR_READOUT_CENTERED)) == U
     assert wsb(None) == E
@@ -311,7 +314,9 @@ def test_backward_queries_and_validation():
     a[10] = None
     assert bwd(a) == E  # workspace required
     assert bwd(ok, c=None) == E
-    assert bwd(ok, c=rs.config(4, 16, 64)) == U
+    assert bwd(ok, c=rs.config(6, 16, 64)) == U
+    assert bwd(ok, c=rs.config(3, 16, 64, 0, 1.0, 0, rs.TAYLOR_READOUT_CENTERED)) == U
+    assert bwd(ok, c=rs.config(4, 8, 32)) == U
     # documented no-ops: no pairs, no tokens
     assert bwd([None] * 11, B=0) == rs.TAYLOR_OK
     assert bwd([None] * 11, N=0) == rs.TAYLOR_OK

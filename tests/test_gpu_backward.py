@@ -74,7 +74,7 @@ def _check(got, x, g, n, scale, tol=TOL_F32, label=""):
                 assert r <= 1.0, f"{label} {name} ({b}, {h}): {r:.2f} x the per-row bar"
 
 
-@pytest.mark.parametrize("n", [1, 2, 3])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_backward_matches_oracle(n, dtype):
     x = synth.make_qkv(110 + n, 2, 2, 333, DK, DV, dtype)
@@ -93,6 +93,29 @@ def test_backward_short_lengths(N):
     announce("backward-lengths", N)
     o = _oracle_fwd(x, 3, 1.0).astype(np.float32)
     _check(_run(x, g, o, cfg), x, g, 3, 1.0, label=f"N={N}")
+
+
+@pytest.mark.parametrize("n", [4, 5])
+@pytest.mark.parametrize("N", [1, 31, 32, 33, 64, 97])
+def test_backward_feature_blocks_short_lengths(n, N):
+    # n = 4, 5 walk 32-token chunks over feature blocks: lengths at and around chunk edges
+    x = synth.make_qkv(130 + n, 1, 3, N, DK, DV)
+    g = _grad_inputs(x, 1300 + N)
+    cfg = _cfg(n, "f32")
+    announce("backward-blocks-lengths", n, N)
+    o = _oracle_fwd(x, n, 1.0).astype(np.float32)
+    _check(_run(x, g, o, cfg), x, g, n, 1.0, label=f"n={n} N={N}")
+
+
+@pytest.mark.parametrize("n", [4, 5])
+def test_backward_feature_blocks_raw_scores_and_many_heads(n):
+    # raw Gaussian q, k at sigma = 1/4 (large, cancelling terms), bf16 inputs, 2 x 5 heads
+    x = synth.make_qkv(135 + n, 2, 5, 200, DK, DV, "bf16", unit_norm=False)
+    g = _grad_inputs(x, 1350 + n)
+    cfg = _cfg(n, "bf16", 0.25)
+    announce("backward-blocks-raw", n)
+    o = _oracle_fwd(x, n, 0.25).astype(np.float32)
+    _check(_run(x, g, o, cfg), x, g, n, 0.25, label=f"raw n={n}")
 
 
 def test_backward_raw_scores():
@@ -130,14 +153,14 @@ def test_backward_with_the_library_forward():
     _check(_run(x, g, o.cpu().numpy(), cfg), x, g, n, 1.0, label="e2e")
 
 
-@pytest.mark.parametrize("N", [300, 50])
+@pytest.mark.parametrize("n,N", [(3, 300), (3, 50), (4, 300), (5, 77)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_from_a_state_and_its_gradient(dtype, N):
-    # the forward continued from an incoming state: gradients of q, k, v and of that state (N = 50:
-    # one segment, where no state pass runs)
+def test_backward_from_a_state_and_its_gradient(dtype, n, N):
+    # the forward continued from an incoming state: gradients of q, k, v and of that state (n = 3,
+    # N = 50: one segment, where no state pass runs; n = 4, 5: the feature-block kernels)
     import torch
 
-    n, H, N0 = 3, 2, 200
+    H, N0 = 2, 200
     x0 = synth.make_qkv(118, 1, H, N0, DK, DV, dtype)
     x = synth.make_qkv(119, 1, H, N, DK, DV, dtype)
     g = _grad_inputs(x, 1190)
@@ -169,12 +192,13 @@ def test_backward_from_a_state_and_its_gradient(dtype, N):
         assert _rel(gs, want) <= 1e-5, f"dstate head {h}: {_rel(gs, want):.3e}"
 
 
-def test_backward_in_pieces_passes_the_state_gradient():
+@pytest.mark.parametrize("n", [3, 4, 5])
+def test_backward_in_pieces_passes_the_state_gradient(n):
     # A sequence prefilled in two calls is differentiated in reverse: the second call's backward
     # returns dL/d(state between the calls), which seeds the first call's backward.
     import torch
 
-    n, H, N1, N2 = 3, 2, 400, 250
+    H, N1, N2 = 2, 400, 250
     x = synth.make_qkv(120, 1, H, N1 + N2, DK, DV)
     g = _grad_inputs(x, 1200)
     cfg = _cfg(n, "f32")
