@@ -397,6 +397,63 @@ def backward_prefill(rs, torch, dev, q, k, v, reps=3):
             "floor_us_at_peaks": floor_us, "frac_mixed_peak": floor_us / us}
 
 
+def backward_flops_per_token_head(w, chunk):
+    """Algorithmic flops of the backward per token-head in the factorised form: forward walk S g_i
+    (2*W*d_v) and S, z += phi(k)^T [v | 1] (2*W*(d_v + 1)) and the normaliser part (2*W); reverse walk
+    G_S^T phi(k_j), G_S v_j (2*W*d_v each) and G += phi(a)^T [gh | -delta] (2*W*(d_v + 1)); intra-chunk
+    products over the causal half of a chunk ((C + 1) / 2 keys per query): scores twice (2*d_k each),
+    g.v and gh.v (2*d_v each), dv (2*d_v), dq and dk (2*d_k each)."""
+    return 2 * w * (5 * DV + 3) + (chunk + 1) / 2 * (8 * DK + 6 * DV)
+
+
+def backward_orders(rs, synth, torch, dev, reps=2):
+    """taylor_attn_prefill_backward at the order-sweep shape (B1 x H16 x N16384, float32, unit-norm q, k)
+    for n = 3, 4, 5, with the library's float32 forward outputs and a seeded upstream gradient, HIP events
+    around raw C-ABI calls; algorithmic flops (backward_flops_per_token_head at the chunk each kernel
+    walks: 64 at n = 3, 32 at n = 4, 5) against the float32 matrix peak, and the time over the forward's."""
+    import ctypes
+
+    B, H, N = 1, 16, 16384
+    x = synth.make_qkv(5, B, H, N, DK, DV, synth.F32)
+    q, k, v = x.torch(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(78)
+    g = torch.randn((B, H, N, DV), generator=gen, device=dev)
+    o = torch.empty((B, H, N, DV), dtype=torch.float32, device=dev)
+    dq = torch.empty((B, H, N, DK), device=dev)
+    dk = torch.empty_like(dq)
+    dv = torch.empty_like(o)
+    res = {}
+    for n in (3, 4, 5):
+        cfg = rs.config(n, DK, DV, 0, 1.0, rs.TAYLOR_F32)
+        fwd = prefill_into_call(rs, torch, q, k, v, o, None, None, rs.new_workspace(cfg, B, H, N, dev), cfg)
+        fwd_us = timed_us(torch, fwd, reps)
+        ws = rs.new_backward_workspace(cfg, B, H, N, dev)
+        rs.taylor_attn_prefill_backward(q, k, v, o, g, None, None, dq, dk, dv, ws, cfg)
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+        args = (ptr(q), ptr(k), ptr(v), ptr(o), ptr(g), None, None, ptr(dq), ptr(dk), ptr(dv),
+                None if ws is None else ptr(ws), B, H, N, ctypes.byref(cfg),
+                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        f = rs.lib().taylor_attn_prefill_backward
+
+        def call():
+            rc = f(*args)
+            if rc:
+                raise rs.TaylorError(rc, "taylor_attn_prefill_backward")
+
+        us = timed_us(torch, call, reps)
+        w = rs.taylor_feature_width(n, DK)
+        chunk = 64 if n <= 3 else 32
+        flops = B * H * N * backward_flops_per_token_head(w, chunk)
+        res["n%d" % n] = {"W": w, "chunk": chunk, "us": us, "tok_s": B * N / us * 1e6, "forward_us": fwd_us,
+                          "over_forward": us / fwd_us, "alg_flops": flops, "TFLOPs": flops / us / 1e6,
+                          "frac_fp32_mfma": flops / us / 1e6 / FP32_PEAK_TFLOPS,
+                          "workspace_MB": (0 if ws is None else ws.numel()) / 1e6}
+        del ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def softmax_crossover(rs, synth, torch, dev, reps=5):
     """Context: exact causal softmax attention (torch's fused flash kernel, bfloat16, scale 1) against the
     bfloat16 prefill (n = 3, from an empty history, final state written) at B = 4, H = 16 for N = 128 ..
@@ -473,6 +530,7 @@ def main():
     ap.add_argument("--no-centered", action="store_true", help="skip the expanded-softmax readout timing")
     ap.add_argument("--no-softmax", action="store_true", help="skip the exact softmax attention comparison")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-backward-orders", action="store_true", help="skip the backward timing at n = 3, 4, 5")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (scale reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -658,6 +716,9 @@ def main():
     if not args.no_backward:
         log("backward (gradients of the prefill)")
         out["backward_bf16_B4xH16xN8192"] = backward_prefill(rs, torch, dev, pq, pk, pv)
+    if not args.no_backward_orders:
+        log("backward at n = 3, 4, 5 (float32, B1 H16 N16384)")
+        out["backward_f32_B1xH16xN16384"] = backward_orders(rs, synth, torch, dev)
     if not args.no_varlen:
         log("ragged-batch prefill (32 prompts, 16 heads, bf16)")
         out["prefill_varlen_bf16_32seqs_H16"] = varlen_prefill(rs, synth, torch, dev)

@@ -1,4 +1,5 @@
-"""GPU parity of taylor_attn_prefill_backward against the float64 oracle's gradients.
+"""GPU parity of taylor_attn_prefill_backward against the float64 oracle's gradients (n = 1..3 on the
+segment kernels, n = 4, 5 on the feature-block kernels).
 
 The oracle's gradients are pinned by finite differences of the forward definition
 (tests/test_oracle_backward.py).  The kernels compute in float32 from the same
@@ -262,6 +263,44 @@ def test_backward_full_size_properties():
         mag = oracle.attention_backward_dq_magnitude_rows(*args)
         r = rows_within(dqn[b, h, rows], ref, mag, TOL_F32)
         assert r <= 1.0, f"dq rows ({b}, {h}): {r:.2f} x the per-row bar"
+
+
+@pytest.mark.parametrize("n", [4, 5])
+def test_backward_feature_blocks_full_size_properties(n):
+    # the order-sweep shape B1 x H16 x N16384 (float32) on the feature-block kernels: finite gradients,
+    # the sum rule of dv and sampled rows of dq against the oracle
+    import torch
+
+    B, H, N = 1, 16, 16384
+    x = synth.make_qkv(5, B, H, N, DK, DV)
+    cfg = _cfg(n, "f32")
+    announce("backward-blocks-full", n, B, H, N)
+    q, k, v = x.torch(DEV)
+    o = torch.empty((B, H, N, DV), device=DEV)
+    rs.taylor_attn_prefill(q, k, v, o, None, rs.new_workspace(cfg, B, H, N, DEV), cfg)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1220 + n)
+    g = torch.randn((B, H, N, DV), generator=gen, device=DEV)
+    dq = torch.empty((B, H, N, DK), device=DEV)
+    dk = torch.empty((B, H, N, DK), device=DEV)
+    dv = torch.empty((B, H, N, DV), device=DEV)
+    rs.taylor_attn_prefill_backward(q, k, v, o, g, None, None, dq, dk, dv, rs.new_backward_workspace(cfg, B, H, N, DEV),
+                                    cfg)
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    sdv = dv.double().sum(dim=2)
+    sg = g.double().sum(dim=2)
+    assert float((sdv - sg).abs().max()) <= 1e-3 * float(sg.abs().max())
+    gn = g.cpu().numpy()
+    dqn = dq.cpu().numpy()
+    rng = np.random.default_rng(1230 + n)
+    for h in (0, 7, 15):
+        rows = np.unique(np.concatenate([[0, 1, 31, 32, 33, N - 1], rng.integers(1, N, 4)]))
+        args = (x.q64[0, h], x.k64[0, h], x.v64[0, h], gn[0, h], n, rows)
+        ref = oracle.attention_backward_dq_rows(*args)
+        mag = oracle.attention_backward_dq_magnitude_rows(*args)
+        r = rows_within(dqn[0, h, rows], ref, mag, TOL_F32)
+        assert r <= 1.0, f"dq rows head {h}: {r:.2f} x the per-row bar"
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
