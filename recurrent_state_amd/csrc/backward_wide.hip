@@ -39,7 +39,6 @@ constexpr int kC = 32;  // tokens per chunk
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLX = 20;      // a, k rows (16 coordinates; 16-byte aligned, 20 mod 64 banks)
-constexpr int kLV = 68;      // v, g rows and state rows
 constexpr int kLY = kC + 4;  // feature-major rows of Y
 constexpr int kLG = 68;      // gh (64), delta, padding per token in the workspace
 
@@ -53,15 +52,24 @@ struct WB {
   static constexpr int LP = FB + 4;              // token-major feature rows
 };
 
-template <int NT>
+// Row strides are chosen per pass so that the MFMA operand reads of each pass's main products hit 64
+// distinct banks or at most two lanes per bank: an operand read [16 x + lane % 16][4 s + lane / 16]
+// wants a stride of 4 mod 64, a read [4 s + lane / 16][16 x + lane % 16] one of 16 mod 64 (8 mod 64
+// serves both at two lanes per bank).
+template <int NT, bool A>
 struct WBSmem {
   using P = WB<NT>;
-  alignas(16) float pk[kC][P::LP];  // phi_f(k_t) of the block's features
-  alignas(16) float pa[kC][P::LP];  // phi_f(a_t)
-  alignas(16) float st[P::FB][kLV];  // S rows (pass A) or G_S rows (pass B) of the block
+  static constexpr int LPK = P::FB + (A ? 16 : 4);  // pass A reads phi(K) by token rows, pass B by feature
+  static constexpr int LPA = P::FB + (A ? 4 : 16);
+  static constexpr int LST = A ? 68 : 72;
+  static constexpr int LVV = A ? 80 : 68;
+  static constexpr int LGG = A ? 68 : 80;
+  alignas(16) float pk[kC][LPK];   // phi_f(k_t) of the block's features
+  alignas(16) float pa[kC][LPA];   // phi_f(a_t)
+  alignas(16) float st[P::FB][LST];  // S rows (pass A) or G_S rows (pass B) of the block
   alignas(16) float y[P::FB][kLY];   // per feature and token: the vector the Jacobian contracts
-  alignas(16) float v[kC][kLV];      // v rows
-  alignas(16) float gg[kC][kLV];     // g rows (pass A) or gh rows (pass B)
+  alignas(16) float v[kC][LVV];      // v rows
+  alignas(16) float gg[kC][LGG];     // g rows (pass A) or gh rows (pass B)
   alignas(16) float xa[kC][kLX];     // a = sigma q
   alignas(16) float xk[kC][kLX];     // k
   float part[kWaves + 1][kC][kDK + 1];  // per-wavefront Jacobian rows; [kWaves]: intra-chunk rows
@@ -90,26 +98,80 @@ __device__ __forceinline__ float ldx(const void* p, long long i, bool bf16) {
   return bf16 ? __uint_as_float((uint32_t)(static_cast<const uint16_t*>(p)[i]) << 16) : static_cast<const float*>(p)[i];
 }
 
-// The chunk's a, k and v rows (tokens tok0 .. tok0 + nv - 1; rows past nv are zero).  Thread
-// (t = tid / 16, c = tid % 16): coordinate c of a and k, value columns 4c .. 4c + 3.
-template <int NT>
-__device__ __forceinline__ void load_akv(WBSmem<NT>& sm, const void* q, const void* k, const void* v, long long tok0,
-                                         int nv, float scale, bool bf16, int tid) {
+// One thread's share of a chunk's inputs, loaded a chunk ahead into registers (thread t = tid / 16,
+// c = tid % 16: coordinate c of q and k, value columns 4c .. 4c + 3 of v and of g, o (pass A) or gh
+// (pass B, with delta in o4[0])).  Rows past the end of the pair are zero.
+struct ChunkIn {
+  float q1, k1;
+  f32x4 v4, g4, o4;
+};
+
+__device__ __forceinline__ f32x4 ld4(const void* p, long long i, bool bf16) {
+  if (bf16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+    return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                 __uint_as_float(u.y & 0xffff0000u)};
+  }
+  return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+}
+
+// pass A: q, k, v, g, o of tokens tok0 .. tok0 + nv - 1
+__device__ __forceinline__ void load_a(ChunkIn& in, const void* q, const void* k, const void* v, const float* g,
+                                       const float* o, long long tok0, int nv, bool bf16, int tid) {
   const int t = tid >> 4, c = tid & 15;
-  const bool ok = t < nv;
-  const long long r = tok0 + t;
-  sm.xa[t][c] = ok ? scale * ldx(q, r * kDK + c, bf16) : 0.f;
-  sm.xk[t][c] = ok ? ldx(k, r * kDK + c, bf16) : 0.f;
-  f32x4 vv;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) vv[e] = ok ? ldx(v, r * kDV + 4 * c + e, bf16) : 0.f;
-  *reinterpret_cast<f32x4*>(&sm.v[t][4 * c]) = vv;
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  in = ChunkIn{0.f, 0.f, z4, z4, z4};
+  if (t < nv) {
+    const long long r = tok0 + t;
+    in.q1 = ldx(q, r * kDK + c, bf16);
+    in.k1 = ldx(k, r * kDK + c, bf16);
+    in.v4 = ld4(v, r * kDV + 4 * c, bf16);
+    in.g4 = *reinterpret_cast<const f32x4*>(g + r * kDV + 4 * c);
+    in.o4 = *reinterpret_cast<const f32x4*>(o + r * kDV + 4 * c);
+  }
+}
+
+// pass B: q, k, v and gh, delta of tokens tok0 .. tok0 + nv - 1
+__device__ __forceinline__ void load_b(ChunkIn& in, const void* q, const void* k, const void* v, const float* ghd,
+                                       long long tok0, int nv, bool bf16, int tid) {
+  const int t = tid >> 4, c = tid & 15;
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  in = ChunkIn{0.f, 0.f, z4, z4, z4};
+  if (t < nv) {
+    const long long r = tok0 + t;
+    in.q1 = ldx(q, r * kDK + c, bf16);
+    in.k1 = ldx(k, r * kDK + c, bf16);
+    in.v4 = ld4(v, r * kDV + 4 * c, bf16);
+    in.g4 = *reinterpret_cast<const f32x4*>(ghd + r * kLG + 4 * c);
+    if (c == 0) in.o4[0] = ghd[r * kLG + kDV];
+  }
+}
+
+// The chunk's rows into LDS: a = sigma q, k, v, g (or gh); go = g . o per token (pass A, a sum over
+// the 16 lanes of the token) or delta (pass B).
+template <bool PASS_A, class SM>
+__device__ __forceinline__ void store_chunk(SM& sm, const ChunkIn& in, float scale, int tid) {
+  const int t = tid >> 4, c = tid & 15;
+  sm.xa[t][c] = scale * in.q1;
+  sm.xk[t][c] = in.k1;
+  *reinterpret_cast<f32x4*>(&sm.v[t][4 * c]) = in.v4;
+  *reinterpret_cast<f32x4*>(&sm.gg[t][4 * c]) = in.g4;
+  if constexpr (PASS_A) {
+    float p = (in.g4[0] * in.o4[0] + in.g4[1] * in.o4[1]) + (in.g4[2] * in.o4[2] + in.g4[3] * in.o4[3]);
+    p += __shfl_xor(p, 8, 16);
+    p += __shfl_xor(p, 4, 16);
+    p += __shfl_xor(p, 2, 16);
+    p += __shfl_xor(p, 1, 16);
+    if (c == 0) sm.go[t] = p;
+  } else {
+    if (c == 0) sm.go[t] = in.o4[0];
+  }
 }
 
 // Features F0 .. F0 + FW - 1 of the chunk's tokens: lanes 0..31 from k into pk, lanes 32..63 from a
 // into pa (token l % 32).  A token past the end has zero rows, so only its constant feature is masked.
-template <int NT, int F0>
-__device__ __forceinline__ void expand_w(WBSmem<NT>& sm, int l, int nv) {
+template <int NT, int F0, class SM>
+__device__ __forceinline__ void expand_w(SM& sm, int l, int nv) {
   using P = WB<NT>;
   constexpr int L0 = F0 % P::FB;
   const int t = l & 31;
@@ -166,8 +228,8 @@ __device__ __forceinline__ void feature_vjp(const float (&x)[kDK], float y, floa
 
 // One lane per token t (< 32): J_phi(x_t)^T y[., t] over the wavefront's features F0 .. F0 + FW - 1,
 // into its row of part.
-template <int NT, int F0>
-__device__ __forceinline__ void jacobian_w(WBSmem<NT>& sm, int w, int t, bool of_a) {
+template <int NT, int F0, class SM>
+__device__ __forceinline__ void jacobian_w(SM& sm, int w, int t, bool of_a) {
   using P = WB<NT>;
   constexpr int L0 = F0 % P::FB;
   const float* xr = of_a ? &sm.xa[t][0] : &sm.xk[t][0];
@@ -188,8 +250,8 @@ __device__ __forceinline__ void jacobian_w(WBSmem<NT>& sm, int w, int t, bool of
 
 // Block 0, intra-chunk: wm[i][j] = K_n(s_ij), dm[i][j] = (gg_i . v_j - go_i) K_{n-1}(s_ij) for key
 // j <= query i (zero above the diagonal).  Waves 0..3 take the four 16x16 tiles.
-template <int NT>
-__device__ __forceinline__ void intra_weights(WBSmem<NT>& sm, int w, int i16, int lg) {
+template <int NT, class SM>
+__device__ __forceinline__ void intra_weights(SM& sm, int w, int i16, int lg) {
   if (w >= 4) return;
   const int it = w >> 1, jt = w & 1;
   f32x4 sc = {0.f, 0.f, 0.f, 0.f}, gv = {0.f, 0.f, 0.f, 0.f};
@@ -221,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void bwdw_a_kernel(const void* __restrict
                                                           long long T) {
   using P = WB<NT>;
   constexpr int FB = P::FB, NFT = P::NFT, W = P::W;
-  __shared__ WBSmem<NT> sm;
+  __shared__ WBSmem<NT, true> sm;
   const int tid = threadIdx.x, l = tid & 63, i16 = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fb = blockIdx.x;
@@ -234,26 +296,15 @@ __global__ __launch_bounds__(kThreads) void bwdw_a_kernel(const void* __restrict
   for (int f = tid; f < FB; f += kThreads)
     sm.zz[f] = (state && f0 + f < W) ? state[bh * stride + (long long)W * kDV + f0 + f] : 0.f;
   const int nch = (N + kC - 1) / kC;
+  const bool bf = bf16 != 0;
+  ChunkIn in;
+  load_a(in, q, k, v, g, o, bh * N, min(kC, N), bf, tid);
   for (int c = 0; c < nch; ++c) {
     const int nv = min(kC, N - c * kC);
     const long long tok0 = bh * N + (long long)c * kC;
     __syncthreads();  // the previous chunk's readers are done
-    load_akv(sm, q, k, v, tok0, nv, scale, bf16 != 0, tid);
-    {
-      const int t = tid >> 4, cc = tid & 15;
-      const bool ok = t < nv;
-      const long long r = tok0 + t;
-      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 gv = ok ? *reinterpret_cast<const f32x4*>(g + r * kDV + 4 * cc) : z4;
-      const f32x4 ov = ok ? *reinterpret_cast<const f32x4*>(o + r * kDV + 4 * cc) : z4;
-      *reinterpret_cast<f32x4*>(&sm.gg[t][4 * cc]) = gv;
-      float p = (gv[0] * ov[0] + gv[1] * ov[1]) + (gv[2] * ov[2] + gv[3] * ov[3]);
-      p += __shfl_xor(p, 8, 16);
-      p += __shfl_xor(p, 4, 16);
-      p += __shfl_xor(p, 2, 16);
-      p += __shfl_xor(p, 1, 16);
-      if (cc == 0) sm.go[t] = p;
-    }
+    store_chunk<true>(sm, in, scale, tid);
+    if (c + 1 < nch) load_a(in, q, k, v, g, o, tok0 + kC, min(kC, N - (c + 1) * kC), bf, tid);
     __syncthreads();
     dispatch_index<0, P::NB * kWaves>(slot_of(fb, w), [&](auto I) { expand_w<NT, decltype(I)::value * P::FW>(sm, l, nv); });
     __syncthreads();
@@ -299,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void bwdw_a_kernel(const void* __restrict
       dispatch_index<0, P::NB * kWaves>(slot_of(fb, w), [&](auto I) { jacobian_w<NT, decltype(I)::value * P::FW>(sm, w, l, true); });
     __syncthreads();
     if (fb == 0) {
-      intra_weights(sm, w, i16, lg);
+      intra_weights<NT>(sm, w, i16, lg);
       __syncthreads();
       if (w < 2) {
         // sum_j dm[i][j] k_j over the chunk: rows 16 w .. 16 w + 15
@@ -371,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void bwdw_b_kernel(const void* __restrict
                                                           float scale, int bf16, long long T) {
   using P = WB<NT>;
   constexpr int FB = P::FB, NFT = P::NFT, W = P::W;
-  __shared__ WBSmem<NT> sm;
+  __shared__ WBSmem<NT, false> sm;
   const int tid = threadIdx.x, l = tid & 63, i16 = l & 15, lg = l >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fb = blockIdx.x;
@@ -385,19 +436,15 @@ __global__ __launch_bounds__(kThreads) void bwdw_b_kernel(const void* __restrict
     sm.zz[f] = (dstate && f0 + f < W) ? dstate[bh * stride + (long long)W * kDV + f0 + f] : 0.f;
   const int nch = (N + kC - 1) / kC;
   const int tt = w >> 2, dt = w & 3;  // this wavefront's 16x16 tile of the chunk's dv
+  const bool bf = bf16 != 0;
+  ChunkIn in;
+  load_b(in, q, k, v, ghd, bh * N + (long long)(nch - 1) * kC, N - (nch - 1) * kC, bf, tid);
   for (int c = nch - 1; c >= 0; --c) {
     const int nv = min(kC, N - c * kC);
     const long long tok0 = bh * N + (long long)c * kC;
     __syncthreads();
-    load_akv(sm, q, k, v, tok0, nv, scale, bf16 != 0, tid);
-    {
-      const int t = tid >> 4, cc = tid & 15;
-      const bool ok = t < nv;
-      const long long r = tok0 + t;
-      const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4*>(&sm.gg[t][4 * cc]) = ok ? *reinterpret_cast<const f32x4*>(ghd + r * kLG + 4 * cc) : z4;
-      if (cc == 0) sm.go[t] = ok ? ghd[r * kLG + kDV] : 0.f;
-    }
+    store_chunk<false>(sm, in, scale, tid);
+    if (c > 0) load_b(in, q, k, v, ghd, tok0 - kC, kC, bf, tid);
     __syncthreads();
     dispatch_index<0, P::NB * kWaves>(slot_of(fb, w), [&](auto I) { expand_w<NT, decltype(I)::value * P::FW>(sm, l, nv); });
     __syncthreads();
@@ -438,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void bwdw_b_kernel(const void* __restrict
       dispatch_index<0, P::NB * kWaves>(slot_of(fb, w), [&](auto I) { jacobian_w<NT, decltype(I)::value * P::FW>(sm, w, l, false); });
     __syncthreads();
     if (fb == 0) {
-      intra_weights(sm, w, i16, lg);
+      intra_weights<NT>(sm, w, i16, lg);
       __syncthreads();
       // dv_j += sum_i wm[i][j] gh_i (the same tile as dva); dk_j += sum_i dm[i][j] a_i (waves 0, 1)
 #pragma unroll
