@@ -41,7 +41,7 @@ def _inputs(seed, N=7, d=3, dv=2):
     return q, k, v, g
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 def test_gradients_match_finite_differences(n):
     q, k, v, g = _inputs(10 + n)
     scale = 0.7
@@ -51,7 +51,7 @@ def test_gradients_match_finite_differences(n):
     np.testing.assert_allclose(dv, _fd(lambda x: _loss(q, k, x, g, n, scale), v), rtol=1e-6, atol=1e-8)
 
 
-@pytest.mark.parametrize("n", [2, 3])
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
 def test_gradients_with_an_incoming_state(n):
     # the recursion continued from a state (states add across chunks): gradients of q, k, v and of
     # the state itself against finite differences of the forward recursion
@@ -109,7 +109,7 @@ def test_dq_rows_form_matches_full():
                                atol=1e-14)
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
 @pytest.mark.parametrize("with_state", [False, True])
 def test_magnitudes_bound_the_gradients(n, with_state):
     # the magnitudes are sums of absolute values of the gradients' terms, so they dominate the
