@@ -27,6 +27,7 @@
 
 #include "centered.hpp"
 #include "features.hpp"
+#include "lookback.hpp"
 #include "prefill_mfma.hpp"
 
 namespace taylor {
@@ -75,22 +76,6 @@ __host__ __device__ constexpr int slot_feature_bf16(int s) {
 }
 
 __device__ __forceinline__ int pair_index(int jt, int it) { return it * (it + 1) / 2 + jt; }
-
-// A state value that other workgroups of the same launch read (the single-pass form's published sums,
-// COH): stored through to the device's point of coherence (an agent-scope store), so that publishing
-// needs no write-back of the XCD's L2, which would also flush every other workgroup's pending outputs.
-template <bool COH>
-__device__ __forceinline__ void put_state(float* p, float v) {
-  if constexpr (COH)
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else
-    *p = v;
-}
-
-// A value another workgroup of the same launch published (read from the point of coherence).
-__device__ __forceinline__ float get_published(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // x where ok holds, else zero, selected word by word (a select of the whole vector would take the
 // operands' addresses and move them to scratch memory).
@@ -718,23 +703,13 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_kernel(const __bf16
 //      prefix (exclusive + its own sum) is then published in turn, so later segments stop at this one;
 //   3. the readout walk from the exclusive prefix (staged in LDS); the last segment writes the final
 //      state at its end and needs no state sum of its own (nobody reads it).
-// A flag is the call's tag (bits 2..63) plus kFlagAgg or kFlagIncl: a flag from an earlier call, or
-// whatever the workspace held, carries another tag and reads as not yet published.  Eager calls take
-// a fresh nonzero tag each; a call recorded into a HIP graph (replayed with the same arguments) uses
-// tag 0 and clears its flags first with a fill kernel.  Waits are only on lower segments of the same
-// pair, i.e. on workgroups with lower linear ids, which the hardware dispatches first, and the form is
-// used only where the whole grid is one round (at most one workgroup per CU).  Every wait is also
-// bounded: after kSpinLimit polls the prefix is taken as NaN (outputs NaN, nothing hangs).
+// Flags, tags and the bounded waits are those of lookback.hpp.
 // ------------------------------------------------------------------------------------------------
-constexpr unsigned long long kFlagAgg = 1, kFlagIncl = 2, kFlagMask = 3;
-constexpr int kSpinLimit = 1 << 20;
-constexpr int kFusedMaxGrid = 256;
 
-// This thread's elements e = tid + 512 i of a state block (S rows then z).
+// The elements of a state block (S rows then z).
 template <int NT>
 struct StateSlice {
   static constexpr long long E = (long long)Geo<NT>::W * (kDV + 1);
-  static constexpr int K = (int)((E + kPipeThreads - 1) / kPipeThreads);
 };
 
 template <int NT>
@@ -785,74 +760,7 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_fused_kernel(
     __hip_atomic_store(flags + slot, tag | kFlagAgg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // 2. the exclusive prefix into `pre`, and the inclusive one published
-  if (x == 0) {
-    for (long long e = tid; e < SL::E; e += kPipeThreads) pre[e] = sin_p ? sin_p[e] : 0.f;
-  } else {
-    // thread 0 walks the flags back to the nearest inclusive prefix j (every flag on the way is a
-    // published sum); the prefix is then summed forward from j, incl[j] + agg[j+1] + ... + agg[x-1],
-    // which is the left-to-right sum the inclusive chain itself computes, so the result does not
-    // depend on which segments had published when (the output is bitwise repeatable)
-    if (tid == 0) {
-      long long j = slot - 1;
-      for (;; --j) {
-        unsigned long long f = 0;
-        for (int spin = 0;; ++spin) {
-          f = __hip_atomic_load(flags + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if ((f & ~kFlagMask) == tag && (f & kFlagMask) != 0) break;
-          if (spin >= kSpinLimit) {
-            f = 0;  // never published: give up
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        if (f == 0) {
-          j = -1;
-          break;
-        }
-        if ((f & kFlagMask) == kFlagIncl) break;
-      }
-      seen = (unsigned long long)j;
-    }
-    __syncthreads();
-    const long long j0 = (long long)seen;
-    float acc[SL::K];
-    const float* first = incl + (j0 < 0 ? slot : j0) * stride;  // (not read when j0 < 0)
-#pragma unroll
-    for (int i = 0; i < SL::K; ++i) {
-      const long long e = tid + (long long)kPipeThreads * i;
-      acc[i] = j0 < 0 ? __builtin_nanf("") : (e < SL::E ? get_published(first + e) : 0.f);
-    }
-    // up to three published sums at a time: all their loads are issued before the first add
-    for (long long m = j0 + 1; j0 >= 0 && m < slot; m += 3) {
-      const int cnt = (int)min(3LL, slot - m);
-      float t[3][SL::K];
-#pragma unroll
-      for (int u = 0; u < 3; ++u)
-#pragma unroll
-        for (int i = 0; i < SL::K; ++i) {
-          const long long e = tid + (long long)kPipeThreads * i;
-          t[u][i] = (u < cnt && e < SL::E) ? get_published(agg + (m + u) * stride + e) : 0.f;
-        }
-#pragma unroll
-      for (int u = 0; u < 3; ++u)
-        if (u < cnt)
-#pragma unroll
-          for (int i = 0; i < SL::K; ++i) acc[i] += t[u][i];  // in segment order
-    }
-    float* inc = incl + slot * stride;
-#pragma unroll
-    for (int i = 0; i < SL::K; ++i) {
-      const long long e = tid + (long long)kPipeThreads * i;
-      if (e < SL::E) {
-        pre[e] = acc[i];
-        if (!last) put_state<true>(inc + e, acc[i] + own[e]);
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores acknowledged (as above)
-  __syncthreads();
-  if (!last && tid == 0)
-    __hip_atomic_store(flags + slot, tag | kFlagIncl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lookback_prefix<SL::E, kPipeThreads>(pre, own, sin_p, agg, incl, flags, slot, x, last, stride, tag, seen, tid);
 
   // 3. the readout walk from `pre` (a generic pointer into LDS; every read of it precedes the walk's
   // first barrier, after which the pipeline reuses that LDS)
@@ -958,15 +866,6 @@ bool fused_form(const PipePlan& p, const SeqMap& seq, int BH, int readout) {
   return !p.direct && !seq.packed && readout != 1 && nseg > 1 && nseg * BH <= kFusedMaxGrid;
 }
 
-// A fresh nonzero tag (bits 2..63) per eager single-pass call, from a process-wide counter started at
-// a time-derived value.
-unsigned long long next_tag() {
-  static std::atomic<unsigned long long> counter{
-      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9e3779b97f4a7c15ull};
-  unsigned long long t = counter.fetch_add(1, std::memory_order_relaxed) & ((1ull << 62) - 1);
-  return (t ? t : 1) << 2;
-}
-
 template <int NT>
 int run_pipe(const PrefillArgs& a) {
   const PipePlan p = pipe_plan(a.BH, a.seq, a.s.readout != 1);
@@ -1000,14 +899,12 @@ int run_pipe(const PrefillArgs& a) {
     const long long slots = (long long)grid.x * grid.y;
     float* incl = ws + round_up(slots * a.s.stride, 64);
     unsigned long long* flags = reinterpret_cast<unsigned long long*>(incl + round_up(slots * a.s.stride, 64));
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    const bool recorded = hipStreamIsCapturing(a.stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone;
     unsigned long long tag = 0;
-    if (recorded) {
+    if (stream_recording(a.stream)) {
       clear_flags_kernel<<<dim3((unsigned)cdiv(slots, 256)), dim3(256), 0, a.stream>>>(flags, slots);
       if (hipGetLastError() != hipSuccess) return -3;
     } else {
-      tag = next_tag();
+      tag = lookback_tag();
     }
     prefill_pipe_fused_kernel<NT><<<grid, block, 0, a.stream>>>(q, k, v, a.o, ws, incl, flags, a.state_in, a.state,
                                                                  a.seq.N, p.L, a.s.stride, a.s.scale, tag);
@@ -1035,6 +932,15 @@ int run_pipe(const PrefillArgs& a) {
 }
 
 }  // namespace
+
+// Tags of the single-pass kernels (lookback.hpp): one process-wide counter, started at a time-derived
+// value.
+unsigned long long lookback_tag() {
+  static std::atomic<unsigned long long> counter{
+      (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9e3779b97f4a7c15ull};
+  unsigned long long t = counter.fetch_add(1, std::memory_order_relaxed) & ((1ull << 62) - 1);
+  return (t ? t : 1) << 2;
+}
 
 // bfloat16 inputs at d_k = 16, d_v = 64, n = 1..3.  The kernel walks 64-token chunks whatever the
 // configured chunk (64 or 128); the outputs do not depend on the chunk length beyond rounding.

@@ -216,7 +216,7 @@ __device__ __forceinline__ void expand_rows(WideSmem<READOUT, FB>& sm, int b, in
 }
 
 // Producer g prepares the chunk in buffer b from its inputs.
-template <int NT, typename E, bool READOUT, bool CENT>
+template <int NT, typename E, bool READOUT, bool CENT, bool OPAQUE>
 __device__ __forceinline__ void wide_produce(WideSmem<READOUT, block_features<NT>()>& sm, const WideIn<E, CENT>& in,
                                              int b, int fb, int g, int l, int nv, float scale, float* zrow) {
   constexpr int NB = n_blocks<NT>(), FB = block_features<NT>(), FP = FB / kProd;
@@ -234,7 +234,12 @@ __device__ __forceinline__ void wide_produce(WideSmem<READOUT, block_features<NT
     const float sx = (READOUT && h) ? scale : (valid ? 1.0f : 0.0f);
 #pragma unroll
     for (int d = 0; d < kDK; ++d) x[d] = sx * in.row.get(d);
-    dispatch_index<0, NB * kProd>(fb * kProd + g, [&](auto I) {
+    // OPAQUE: the slot is opaque to the optimiser here: otherwise the comparisons of the dispatch
+    // tree are hoisted out of the chunk loop, and their results occupy scalar registers that spill
+    // (for the ragged kernels, whose piece loop surrounds the chunk loop, hoisting them costs less)
+    int slot = fb * kProd + g;
+    if constexpr (OPAQUE) asm volatile("" : "+s"(slot));
+    dispatch_index<0, NB * kProd>(slot, [&](auto I) {
       expand_rows<NT, READOUT, CENT, FB, decltype(I)::value * FP>(sm, b, g, l, x, valid, in.cq);
     });
   }
@@ -301,190 +306,204 @@ __device__ __forceinline__ void piece_state(const WideIO& io, const SeqPiece& pc
     dst = io.state + pc.pair * io.stride;
 }
 
+// Producer wave g's walk over one piece of block fb: z starts from init (null: zero) and ends in dst
+// (null: not written).  Executes exactly 2 + nch barriers, like the consumers.
+template <int NT, typename E, bool READOUT, bool CENT, bool OPAQUE>
+__device__ __forceinline__ void wide_producer_piece(WideSmem<READOUT, block_features<NT>()>& sm, const WideIO& io,
+                                                    const SeqMap& seq, const SeqPiece& pc, const float* init,
+                                                    float* dst, const E* q, const E* k, const E* v, int fb, int g,
+                                                    int l, float scale) {
+  constexpr int W = FeatureTable<NT, kDK>::W;
+  constexpr int FB = block_features<NT>(), FP = FB / kProd;
+  const int f0 = fb * FB;
+  const int nch = (pc.n + kCS - 1) / kCS;
+  auto nv_of = [&](int c) { return min(kCS, pc.n - c * kCS); };
+  auto tok_of = [&](int c) { return pc.tok + (long long)c * kCS; };
+  auto zrow = [&](int c) {
+    return CENT && !READOUT && c % 2 == 0
+               ? io.zc + (seq.chunk_index(pc, 0, 2 * kCS) + c / 2) * FeatureTable<NT, kDK>::W
+               : nullptr;
+  };
+  if (l < FP) {
+    const int a = f0 + FP * g + l;
+    sm.z[FP * g + l] = (init && a < W) ? init[(long long)W * kDV + a] : 0.f;
+  }
+  WideIn<E, CENT> pa, pb;
+  pa.load(q, k, v, io.coef, tok_of(0), nv_of(0), l, g, READOUT);
+  __syncthreads();
+  if (nch > 1) pb.load(q, k, v, io.coef, tok_of(1), nv_of(1), l, g, READOUT);
+  wide_produce<NT, E, READOUT, CENT, OPAQUE>(sm, pa, 0, fb, g, l, nv_of(0), scale, zrow(0));
+  __syncthreads();  // chunk 0 ready
+  int c = 0;
+  for (; c + 3 < nch; c += 2) {
+    pa.load(q, k, v, io.coef, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
+    wide_produce<NT, E, READOUT, CENT, OPAQUE>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale, zrow(c + 1));
+    __syncthreads();
+    pb.load(q, k, v, io.coef, tok_of(c + 3), nv_of(c + 3), l, g, READOUT);
+    wide_produce<NT, E, READOUT, CENT, OPAQUE>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale, zrow(c + 2));
+    __syncthreads();
+  }
+  // nch - c phases remain (1 to 3); chunks c+1 and c+2 may still need preparing
+  if (c + 2 < nch) pa.load(q, k, v, io.coef, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
+  if (c + 1 < nch) wide_produce<NT, E, READOUT, CENT, OPAQUE>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale, zrow(c + 1));
+  __syncthreads();
+  if (c + 1 < nch) {
+    if (c + 2 < nch) wide_produce<NT, E, READOUT, CENT, OPAQUE>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale, zrow(c + 2));
+    __syncthreads();
+    if (c + 2 < nch) __syncthreads();
+  }
+  if (dst && l < FP) {
+    const int a = f0 + FP * g + l;
+    if (a < W) dst[(long long)W * kDV + a] = sm.z[FP * g + l];
+  }
+  // the padding after S and z: zero, whatever the array held before
+  if (dst && fb == 0 && g == 0 && l < io.stride - (long long)W * (kDV + 1)) dst[(long long)W * (kDV + 1) + l] = 0.f;
+}
+
+// Consumer wave w's walk over one piece of block fb (value columns 16w..16w+15): the running state
+// starts from init and ends in dst as for the producers; the outputs (READOUT) go to io.out (one
+// block) or to the block's partial numerators and denominators.
+template <int NT, typename E, bool READOUT, bool CENT>
+__device__ __forceinline__ void wide_consumer_piece(WideSmem<READOUT, block_features<NT>()>& sm, const WideIO& io,
+                                                    const SeqPiece& pc, const float* init, float* dst, int fb,
+                                                    int w, int tid) {
+  constexpr int W = FeatureTable<NT, kDK>::W;
+  constexpr int FB = block_features<NT>(), NAT = FB / 16;
+  const int l = tid & 63, l16 = l & 15, lg = l >> 4;
+  const int f0 = fb * FB;
+  const int nch = (pc.n + kCS - 1) / kCS;
+  auto nv_of = [&](int c) { return min(kCS, pc.n - c * kCS); };
+  auto tok_of = [&](int c) { return pc.tok + (long long)c * kCS; };
+
+  // ---- consumers: wave w owns value columns 16w..16w+15 ----
+  const int col = 16 * w + l16;
+  const bool intra = READOUT && fb == 0;  // block 0 also carries the intra-chunk term
+  f32x4 Srun[NAT];
+#pragma unroll
+  for (int t = 0; t < NAT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int a = f0 + 16 * t + 4 * lg + r;
+      Srun[t][r] = (init && a < W) ? init[(long long)a * kDV + col] : 0.f;
+    }
+  __syncthreads();
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int b = c & 1;
+    const int nv = nv_of(c);
+    const long long tok0 = tok_of(c);
+    f32x4 O[READOUT ? kNIT : 1];
+    if constexpr (READOUT) {
+#pragma unroll
+      for (int it = 0; it < kNIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // readout: O[it][r] = (phi_f(sQ) S_{f,<c})[token 16it + l16][column 16w + 4lg + r]
+#pragma unroll
+      for (int t = 0; t < NAT; ++t)
+#pragma unroll
+        for (int it = 0; it < kNIT; ++it) {
+          const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[b][16 * it + l16][16 * t + 4 * lg]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], O[it], 0, 0, 0);
+        }
+      if (intra) {
+#pragma unroll
+        for (int it = 0; it < kNIT; ++it)
+#pragma unroll
+          for (int jt = 0; jt <= it; ++jt) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jt + 4 * lg]);
+            const f32x4 bw = sm.a[b][it * (it + 1) / 2 + jt][l];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bw[r], O[it], 0, 0, 0);
+          }
+      }
+    }
+    // state update: Srun[t] += phi_f(K)^T[16t.., chunk] V[chunk, columns]
+#pragma unroll
+    for (int jb = 0; jb < kCS / 16; ++jb) {
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jb + 4 * lg]);
+#pragma unroll
+      for (int t = 0; t < NAT; ++t) {
+        const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[b][16 * t + l16][16 * jb + 4 * lg]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
+      }
+    }
+    if constexpr (READOUT && n_blocks<NT>() == 1) {
+      // a single block: the outputs are final (columns 16w + 4lg .. + 3 of token 16it + l16); the
+      // expanded-softmax readout has no normaliser (its weights already sum to one)
+#pragma unroll
+      for (int it = 0; it < kNIT; ++it) {
+        const int i = 16 * it + l16;
+        float d = 1.f;
+        if constexpr (!CENT) {
+          d = 0.f;
+#pragma unroll
+          for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
+          for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][it * (it + 1) / 2 + jt][l16];
+        }
+        if (i < nv) {
+          const float inv = CENT ? 1.0f : 1.0f / d;
+          const f32x4 r = O[it];
+          *reinterpret_cast<f32x4*>(io.out + (tok0 + i) * kDV + 16 * w + 4 * lg) =
+              f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
+        }
+      }
+    } else if constexpr (READOUT) {
+      // partial numerators of this block (columns 16w + 4lg .. + 3 of token 16it + l16)
+      float* pn = io.part_num + ((long long)fb * io.tokens + tok0) * kDV;
+#pragma unroll
+      for (int it = 0; it < kNIT; ++it) {
+        const int i = 16 * it + l16;
+        if (i < nv) *reinterpret_cast<f32x4*>(pn + (long long)i * kDV + 16 * w + 4 * lg) = O[it];
+      }
+      // partial denominators: consumer w < kNIT writes tokens 16w .. 16w + 15
+      if (w < kNIT && lg == 0) {
+        const int i = 16 * w + l16;
+        float d = 0.f;
+#pragma unroll
+        for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
+        if (intra)
+          for (int jt = 0; jt <= w; ++jt) d += sm.den_intra[b][w * (w + 1) / 2 + jt][l16];
+        if (i < nv) io.part_den[(long long)fb * io.tokens + tok0 + i] = d;
+      }
+    }
+    __syncthreads();
+  }
+
+  if (dst) {
+#pragma unroll
+    for (int t = 0; t < NAT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int a = f0 + 16 * t + 4 * lg + r;
+        if (a < W) dst[(long long)a * kDV + col] = Srun[t][r];
+      }
+  }
+}
+
 // The pieces of one workgroup (see SeqMap: a segment of one pair, or the pieces of one token
 // range of one head), one feature block; grid = (segments or ranges, pairs or heads, blocks).
 template <int NT, typename E, bool READOUT, bool PACKED, bool CENT>
 __global__ __launch_bounds__(kThreads) void prefill_wide_kernel(const E* __restrict__ q, const E* __restrict__ k,
                                                                 const E* __restrict__ v, WideIO io, SeqMap seq,
                                                                 int L, float scale) {
-  constexpr int W = FeatureTable<NT, kDK>::W;
-  constexpr int FB = block_features<NT>(), FP = FB / kProd, NAT = FB / 16;
-  __shared__ WideSmem<READOUT, FB> sm;
-
-  const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, lg = l >> 4;
+  __shared__ WideSmem<READOUT, block_features<NT>()> sm;
+  const int tid = threadIdx.x, l = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fb = blockIdx.z;
   const long long bx = blockIdx.x, by = blockIdx.y;
-  const int f0 = fb * FB;
   // Both roles walk the same pieces and execute exactly 2 + nch barriers per piece.  Pieces follow
   // one another in LDS without an extra barrier: a piece's last barrier orders every read of its
   // buffers before the next piece's first writes, and each producer rewrites only its own z rows
   // at a piece's start.
-  if (w >= kCons) {
-    // ---- producers ----
-    for_each_piece<PACKED>(seq, bx, by, L, io.nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
-      const int nch = (pc.n + kCS - 1) / kCS;
-      auto nv_of = [&](int c) { return min(kCS, pc.n - c * kCS); };
-      auto tok_of = [&](int c) { return pc.tok + (long long)c * kCS; };
-      auto zrow = [&](int c) {
-        return CENT && !READOUT && c % 2 == 0
-                   ? io.zc + (seq.chunk_index(pc, 0, 2 * kCS) + c / 2) * FeatureTable<NT, kDK>::W
-                   : nullptr;
-      };
-      const float* init;
-      float* dst;
-      piece_state<READOUT>(io, pc, init, dst);
-      const int g = w - kCons;
-      if (l < FP) {
-        const int a = f0 + FP * g + l;
-        sm.z[FP * g + l] = (init && a < W) ? init[(long long)W * kDV + a] : 0.f;
-      }
-      WideIn<E, CENT> pa, pb;
-      pa.load(q, k, v, io.coef, tok_of(0), nv_of(0), l, g, READOUT);
-      __syncthreads();
-      if (nch > 1) pb.load(q, k, v, io.coef, tok_of(1), nv_of(1), l, g, READOUT);
-      wide_produce<NT, E, READOUT, CENT>(sm, pa, 0, fb, g, l, nv_of(0), scale, zrow(0));
-      __syncthreads();  // chunk 0 ready
-      int c = 0;
-      for (; c + 3 < nch; c += 2) {
-        pa.load(q, k, v, io.coef, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
-        wide_produce<NT, E, READOUT, CENT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale, zrow(c + 1));
-        __syncthreads();
-        pb.load(q, k, v, io.coef, tok_of(c + 3), nv_of(c + 3), l, g, READOUT);
-        wide_produce<NT, E, READOUT, CENT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale, zrow(c + 2));
-        __syncthreads();
-      }
-      // nch - c phases remain (1 to 3); chunks c+1 and c+2 may still need preparing
-      if (c + 2 < nch) pa.load(q, k, v, io.coef, tok_of(c + 2), nv_of(c + 2), l, g, READOUT);
-      if (c + 1 < nch) wide_produce<NT, E, READOUT, CENT>(sm, pb, (c + 1) & 1, fb, g, l, nv_of(c + 1), scale, zrow(c + 1));
-      __syncthreads();
-      if (c + 1 < nch) {
-        if (c + 2 < nch) wide_produce<NT, E, READOUT, CENT>(sm, pa, c & 1, fb, g, l, nv_of(c + 2), scale, zrow(c + 2));
-        __syncthreads();
-        if (c + 2 < nch) __syncthreads();
-      }
-      if (dst && l < FP) {
-        const int a = f0 + FP * g + l;
-        if (a < W) dst[(long long)W * kDV + a] = sm.z[FP * g + l];
-      }
-      // the padding after S and z: zero, whatever the array held before
-      if (dst && fb == 0 && g == 0 && l < io.stride - (long long)W * (kDV + 1)) dst[(long long)W * (kDV + 1) + l] = 0.f;
-    });
-    return;
-  }
-
   for_each_piece<PACKED>(seq, bx, by, L, io.nslot, [&](const SeqPiece& pc) __attribute__((always_inline)) {
-    const int nch = (pc.n + kCS - 1) / kCS;
-    auto nv_of = [&](int c) { return min(kCS, pc.n - c * kCS); };
-    auto tok_of = [&](int c) { return pc.tok + (long long)c * kCS; };
     const float* init;
     float* dst;
     piece_state<READOUT>(io, pc, init, dst);
-
-    // ---- consumers: wave w owns value columns 16w..16w+15 ----
-    const int col = 16 * w + l16;
-    const bool intra = READOUT && fb == 0;  // block 0 also carries the intra-chunk term
-    f32x4 Srun[NAT];
-#pragma unroll
-    for (int t = 0; t < NAT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int a = f0 + 16 * t + 4 * lg + r;
-        Srun[t][r] = (init && a < W) ? init[(long long)a * kDV + col] : 0.f;
-      }
-    __syncthreads();
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      const int b = c & 1;
-      const int nv = nv_of(c);
-      const long long tok0 = tok_of(c);
-      f32x4 O[READOUT ? kNIT : 1];
-      if constexpr (READOUT) {
-#pragma unroll
-        for (int it = 0; it < kNIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // readout: O[it][r] = (phi_f(sQ) S_{f,<c})[token 16it + l16][column 16w + 4lg + r]
-#pragma unroll
-        for (int t = 0; t < NAT; ++t)
-#pragma unroll
-          for (int it = 0; it < kNIT; ++it) {
-            const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[b][16 * it + l16][16 * t + 4 * lg]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], O[it], 0, 0, 0);
-          }
-        if (intra) {
-#pragma unroll
-          for (int it = 0; it < kNIT; ++it)
-#pragma unroll
-            for (int jt = 0; jt <= it; ++jt) {
-              const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jt + 4 * lg]);
-              const f32x4 bw = sm.a[b][it * (it + 1) / 2 + jt][l];
-#pragma unroll
-              for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bw[r], O[it], 0, 0, 0);
-            }
-        }
-      }
-      // state update: Srun[t] += phi_f(K)^T[16t.., chunk] V[chunk, columns]
-#pragma unroll
-      for (int jb = 0; jb < kCS / 16; ++jb) {
-        const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jb + 4 * lg]);
-#pragma unroll
-        for (int t = 0; t < NAT; ++t) {
-          const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[b][16 * t + l16][16 * jb + 4 * lg]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
-        }
-      }
-      if constexpr (READOUT && n_blocks<NT>() == 1) {
-        // a single block: the outputs are final (columns 16w + 4lg .. + 3 of token 16it + l16); the
-        // expanded-softmax readout has no normaliser (its weights already sum to one)
-#pragma unroll
-        for (int it = 0; it < kNIT; ++it) {
-          const int i = 16 * it + l16;
-          float d = 1.f;
-          if constexpr (!CENT) {
-            d = 0.f;
-#pragma unroll
-            for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
-            for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][it * (it + 1) / 2 + jt][l16];
-          }
-          if (i < nv) {
-            const float inv = CENT ? 1.0f : 1.0f / d;
-            const f32x4 r = O[it];
-            *reinterpret_cast<f32x4*>(io.out + (tok0 + i) * kDV + 16 * w + 4 * lg) =
-                f32x4{r[0] * inv, r[1] * inv, r[2] * inv, r[3] * inv};
-          }
-        }
-      } else if constexpr (READOUT) {
-        // partial numerators of this block (columns 16w + 4lg .. + 3 of token 16it + l16)
-        float* pn = io.part_num + ((long long)fb * io.tokens + tok0) * kDV;
-#pragma unroll
-        for (int it = 0; it < kNIT; ++it) {
-          const int i = 16 * it + l16;
-          if (i < nv) *reinterpret_cast<f32x4*>(pn + (long long)i * kDV + 16 * w + 4 * lg) = O[it];
-        }
-        // partial denominators: consumer w < kNIT writes tokens 16w .. 16w + 15
-        if (w < kNIT && lg == 0) {
-          const int i = 16 * w + l16;
-          float d = 0.f;
-#pragma unroll
-          for (int p = 0; p < kProd; ++p) d += sm.den_part[b][p][i];
-          if (intra)
-            for (int jt = 0; jt <= w; ++jt) d += sm.den_intra[b][w * (w + 1) / 2 + jt][l16];
-          if (i < nv) io.part_den[(long long)fb * io.tokens + tok0 + i] = d;
-        }
-      }
-      __syncthreads();
-    }
-
-    if (dst) {
-#pragma unroll
-      for (int t = 0; t < NAT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int a = f0 + 16 * t + 4 * lg + r;
-          if (a < W) dst[(long long)a * kDV + col] = Srun[t][r];
-        }
-    }
+    if (w >= kCons)
+      wide_producer_piece<NT, E, READOUT, CENT, !PACKED>(sm, io, seq, pc, init, dst, q, k, v, fb, w - kCons, l, scale);
+    else
+      wide_consumer_piece<NT, E, READOUT, CENT>(sm, io, pc, init, dst, fb, w, tid);
   });
 }
 
@@ -545,6 +564,8 @@ int wide_segments(int BH, int nb, int nchunk, bool outputs) {
   return best;
 }
 
+long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
+
 struct WideLayout {
   int L;  // piece (segment or range) length
   long long gx, nslot, slot_floats, part_floats, coef_floats, zc_floats;
@@ -589,8 +610,6 @@ auto wide_kernel_for(bool packed, bool cent) {
   }
   return packed ? prefill_wide_kernel<NT, E, READOUT, true, false> : prefill_wide_kernel<NT, E, READOUT, false, false>;
 }
-
-long long round_up(long long x, long long m) { return (x + m - 1) / m * m; }
 
 template <int NT, typename E>
 int wide_run(const PrefillArgs& a) {
