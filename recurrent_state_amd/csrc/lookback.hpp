@@ -64,8 +64,19 @@ __device__ __forceinline__ void lookback_prefix(float* pre, const float* own, co
                                                 unsigned long long& seen, int tid) {
   constexpr int K = (int)((E + THREADS - 1) / THREADS);
   if (x == 0) {
-    // segment 0's walk started from the incoming state, so it wrote its inclusive prefix itself
-    for (long long e = tid; e < E; e += THREADS) pre[e] = sin_p ? sin_p[e] : 0.f;
+    // segment 0's walk started from the incoming state, so it wrote its inclusive prefix itself; all
+    // loads are issued before the first store (a load between stores would wait for each of them)
+    float t[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const long long e = tid + (long long)THREADS * i;
+      t[i] = sin_p && e < E ? sin_p[e] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const long long e = tid + (long long)THREADS * i;
+      if (e < E) pre[e] = t[i];
+    }
   } else {
     if (tid == 0) {
       long long j = slot - 1;
