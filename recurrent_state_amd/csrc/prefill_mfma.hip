@@ -110,13 +110,13 @@ constexpr int kPipePairs = 10;  // (key tile <= query tile) pairs of 16-token ti
 template <int NT, bool READOUT>
 struct PipeSmem {
   static constexpr int WP = Geo<NT>::WP;
-  static constexpr int LQ = WP + 8;           // phi(sQ) row stride (bf16)
-  static constexpr int LK = kPipeChunk + 8;   // phi(K)^T and V^T row stride (bf16)
+  // Unpadded rows, 16-byte slots swizzled within each row (swz_kv, swz_q): every access of the three
+  // tiles below is free of LDS bank conflicts.
   static constexpr int RQ = READOUT ? kPipeChunk : 1;
   static constexpr int RP = READOUT ? kPipePairs : 1;
-  alignas(16) __bf16 vt[2][kDV][LK];
-  alignas(16) __bf16 phikt[2][WP][LK];
-  alignas(16) __bf16 phiq[2][RQ][LQ];
+  alignas(16) __bf16 vt[2][kDV][kPipeChunk];
+  alignas(16) __bf16 phikt[2][WP][kPipeChunk];
+  alignas(16) __bf16 phiq[2][RQ][WP];
   alignas(16) bf16x4 a[2][RP][64];    // score tiles, high bfloat16 part
   alignas(16) bf16x4 alo[2][RP][64];  // score tiles, low part (w - hi), so hi + lo keeps float32 accuracy
   float den_part[2][kPipeProducers][RQ];
@@ -136,21 +136,41 @@ struct PipeSplit {
   static constexpr int VC = kDV / kPipeProducers;
 };
 
-// Transposed bfloat16 tiles ([row][token], `stride` elements per row) are written two rows at a time
-// as whole dwords: lane j holds (row r, row r+1) of token j; lanes j and j^1 swap those pairs (a quad
-// permutation), then the even lane stores row r of tokens j, j+1 and the odd lane row r+1 of tokens
-// j-1, j.  `base` is the lane's byte address for row 0; a row pair adds r * stride * 2 bytes.
+// LDS layout of the bfloat16 tiles.  Bank rule (measured on gfx950 with one pair of active lanes at a
+// time): reads see 64 four-byte banks, writes 32; a 16-byte read serves 16 lanes per cycle (those with
+// the same lane bit 5 and the same parity of lane bits 2..4), an 8-byte read 32 consecutive lanes, a
+// 16-byte write 8, a 4-byte write 32.  Padding alone cannot satisfy both sides of a tile (the phi(sQ)
+// rows, for one, are conflict-free to read for 16-byte-slot strides of 2 mod 4 and to write for odd
+// ones), so the rows are unpadded and the 16-byte slots of each row are permuted by an XOR with bits
+// of the row index; the swizzles below make every read and write of these tiles conflict-free.
+//
+// phi(K)^T and V^T: 128-byte rows (64 tokens), slot s of row r at slot s ^ swz_kv(r).
+__host__ __device__ constexpr int swz_kv(int r) { return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2); }
+// phi(sQ): one row per token, slot s of row r at slot s ^ swz_q(r) (within its aligned group of 4).
+__host__ __device__ constexpr int swz_q(int r) { return (r >> 1) & 3; }
+// Byte offset of token t in row r of a phi(K)^T or V^T tile.
+static_assert(kPipeChunk == 64, "phi(K)^T and V^T rows are 128 bytes: 8 slots of 8 tokens");
+__device__ __forceinline__ int kv_off(int r, int t) { return r * 128 + 16 * ((t >> 3) ^ swz_kv(r)) + 2 * (t & 7); }
+
+// phi(K)^T rows are written two rows at a time as whole dwords: lane j holds (row r, row r+1) of
+// token j; lanes j and j^1 swap those pairs (a quad permutation), then the even lane stores row r of
+// tokens j, j+1 and the odd lane row r+1 of tokens j-1, j.  For even r, swz_kv(r + 1) = swz_kv(r) ^ 4,
+// so the odd lanes flip bit 2 of their slot once, here.
 struct PairStore {
-  char* base;
+  char* base;    // the lane's row (r or r + 1) and dword within its slot
+  int slot;      // the lane's slot before the row's swizzle
   uint32_t sel;  // v_perm_b32(partner, own) bytes: even -> (own.lo, partner.lo), odd -> (partner.hi, own.hi)
-  __device__ __forceinline__ PairStore(__bf16* tile, int stride, int j) {
+  __device__ __forceinline__ PairStore(__bf16* tile, int j) {
     const bool odd = j & 1;
-    base = reinterpret_cast<char*>(tile) + (odd ? stride * 2 + (j - 1) * 2 : j * 2);
+    base = reinterpret_cast<char*>(tile) + (odd ? 128 : 0) + 4 * ((j >> 1) & 3);
+    slot = (j >> 3) ^ (odd ? 4 : 0);
     sel = odd ? 0x03020706u : 0x05040100u;
   }
-  __device__ __forceinline__ void store(int row_bytes, uint32_t own) const {
+  template <int R>  // even row of the pair
+  __device__ __forceinline__ void store(uint32_t own) const {
+    static_assert(R % 2 == 0, "rows are written in pairs from an even row");
     const uint32_t partner = (uint32_t)__builtin_amdgcn_mov_dpp((int)own, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
-    *reinterpret_cast<uint32_t*>(base + row_bytes) = __builtin_amdgcn_perm(partner, own, sel);
+    *reinterpret_cast<uint32_t*>(base + R * 128 + 16 * (slot ^ swz_kv(R))) = __builtin_amdgcn_perm(partner, own, sel);
   }
 };
 
@@ -159,9 +179,8 @@ template <int NT, bool READOUT, int G>
 __device__ __forceinline__ void pipe_phik_rows(PipeSmem<NT, READOUT>& sm, int b, int j, const float (&x)[kDK],
                                                bool valid) {
   using SP = PipeSplit<NT>;
-  using SM = PipeSmem<NT, READOUT>;
   static_assert(SP::RK % 2 == 0, "rows are written in pairs");
-  const PairStore ps(&sm.phikt[b][0][0], SM::LK, j);
+  const PairStore ps(&sm.phikt[b][0][0], j);
   [&]<int... I>(std::integer_sequence<int, I...>) {
     (([&] {
        constexpr int r0 = G * SP::RK + 2 * I, r1 = r0 + 1;
@@ -171,7 +190,7 @@ __device__ __forceinline__ void pipe_phik_rows(PipeSmem<NT, READOUT>& sm, int b,
            f0 = valid ? 1.f : 0.f;
          else
            f0 = feat<NT, r0>(x);
-         ps.store(r0 * SM::LK * 2, __builtin_bit_cast(uint32_t, to_bf16x2(f0, feat<NT, r1>(x))));
+         ps.store<r0>(__builtin_bit_cast(uint32_t, to_bf16x2(f0, feat<NT, r1>(x))));
        }
      }()),
      ...);
@@ -226,7 +245,8 @@ __device__ __forceinline__ float pipe_phiq_groups(PipeSmem<NT, READOUT>& sm, int
               ...);
            }
          }(std::make_integer_sequence<int, 4>{});
-         *reinterpret_cast<uint4*>(&sm.phiq[b][j][s0]) = make_uint4(v[0], v[1], v[2], v[3]);
+         *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&sm.phiq[b][j][0]) + 16 * (grp ^ swz_q(j))) =
+             make_uint4(v[0], v[1], v[2], v[3]);
        }
      }()),
      ...);
@@ -337,8 +357,10 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
     const uint32_t w[4] = {in.v[u].x, in.v[u].y, in.v[u].z, in.v[u].w};
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      sm.vt[b][SP::VC * G + 8 * u + 2 * h][l] = __builtin_bit_cast(__bf16, (uint16_t)(w[h] & 0xffffu));
-      sm.vt[b][SP::VC * G + 8 * u + 2 * h + 1][l] = __builtin_bit_cast(__bf16, (uint16_t)(w[h] >> 16));
+      const int c = SP::VC * G + 8 * u + 2 * h;
+      char* vt = reinterpret_cast<char*>(&sm.vt[b][0][0]);
+      *reinterpret_cast<uint16_t*>(vt + kv_off(c, l)) = (uint16_t)(w[h] & 0xffffu);
+      *reinterpret_cast<uint16_t*>(vt + kv_off(c + 1, l)) = (uint16_t)(w[h] >> 16);
     }
   }
   if constexpr (READOUT) {
@@ -392,7 +414,7 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int t = 0; t < kPipeChunk; t += 8) {
-      const bf16x8 x8 = *reinterpret_cast<const bf16x8*>(&sm.phikt[b][row][t]);
+      const bf16x8 x8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(&sm.phikt[b][0][0]) + kv_off(row, t));
 #pragma unroll
       for (int h = 0; h < 4; ++h) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x8[2 * h], x8[2 * h + 1]}, ones, acc, false);
     }
@@ -495,7 +517,8 @@ __device__ __forceinline__ void pipe_consumer(PipeSmem<NT, READOUT>& sm, const S
         const bf16x8 lo = {lw[0][0], lw[0][1], lw[1][0], lw[1][1], lw[2][0], lw[2][1], lw[3][0], lw[3][1]};
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(&sm.phiq[b][16 * it + l16][32 * kb + 8 * lg]);
+          const bf16x8 bq = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(&sm.phiq[b][16 * it + l16][0]) +
+                                                             64 * kb + 16 * (lg ^ swz_q(l16)));
           O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, O[it], 0, 0, 0);
           O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, O[it], 0, 0, 0);
         }
@@ -506,7 +529,8 @@ __device__ __forceinline__ void pipe_consumer(PipeSmem<NT, READOUT>& sm, const S
       for (int it = 0; it < NIT; ++it)
 #pragma unroll
         for (int jt = 0; jt <= it; ++jt) {
-          const bf16x4 av = *reinterpret_cast<const bf16x4*>(&sm.vt[b][16 * w + l16][16 * jt + 4 * lg]);
+          const bf16x4 av = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const char*>(&sm.vt[b][0][0]) +
+                                                             kv_off(16 * w + l16, 16 * jt + 4 * lg));
           const bf16x4 bh = sm.a[b][pair_index(jt, it)][l];
           const bf16x4 bl = sm.alo[b][pair_index(jt, it)][l];
           // V^T (hi + lo) as one 16x16x32 MFMA: the halves of k pair av with bh and av with bl
@@ -518,10 +542,12 @@ __device__ __forceinline__ void pipe_consumer(PipeSmem<NT, READOUT>& sm, const S
     // state update
 #pragma unroll
     for (int jb = 0; jb < CS / 32; ++jb) {
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sm.vt[b][16 * w + l16][32 * jb + 8 * lg]);
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(&sm.vt[b][0][0]) +
+                                                         kv_off(16 * w + l16, 32 * jb + 8 * lg));
 #pragma unroll
       for (int t = 0; t < NAT; ++t) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&sm.phikt[b][16 * t + l16][32 * jb + 8 * lg]);
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(&sm.phikt[b][0][0]) +
+                                                           kv_off(16 * t + l16, 32 * jb + 8 * lg));
         Srun[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bv, Srun[t], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
