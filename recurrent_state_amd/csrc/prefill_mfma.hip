@@ -27,6 +27,7 @@
 
 #include "centered.hpp"
 #include "features.hpp"
+#include "lds_layout.hpp"
 #include "lookback.hpp"
 #include "prefill_mfma.hpp"
 
@@ -75,6 +76,12 @@ __host__ __device__ constexpr int slot_feature_bf16(int s) {
   return 32 * kb + (r < 4 ? g * 4 + r : 16 + g * 4 + (r - 4));
 }
 
+// The slot of feature f in a phi(sQ) row (the inverse of slot_feature_bf16).
+__host__ __device__ constexpr int feature_slot_bf16(int f) {
+  const int kb = f / 32, f32 = f % 32, hi = f32 >= 16, u = f32 % 16;
+  return 32 * kb + 8 * (u / 4) + 4 * hi + u % 4;
+}
+
 __device__ __forceinline__ int pair_index(int jt, int it) { return it * (it + 1) / 2 + jt; }
 
 // x where ok holds, else zero, selected word by word (a select of the whole vector would take the
@@ -88,13 +95,14 @@ __device__ __forceinline__ uint4 keep_if(bool ok, uint4 x) {
 //
 // Waves 0..3 ("consumers") own value columns 16w..16w+15 and run the MFMAs of chunk c:
 // the readout phi(sQ_c) S_{<c} (state kept in accumulator registers, split hi + lo), the
+// denominators phi(sQ_c) z_{<c} (z as hi + lo, one more product per readout operand), the
 // intra-chunk product V^T tril(K_n(s K Q^T)), the state update phi(K_c)^T V_c, and the
 // output division.  Waves 4..7 ("producers") meanwhile prepare chunk c+1 in the other half
 // of a double-buffered LDS area: phi(K)^T rows, phi(sQ) rows (slot-permuted), V^T, the
 // intra-chunk score tiles (16x16x16 MFMA + Horner + causal mask, stored as bfloat16 hi + lo
-// so the intra-chunk weights keep float32 accuracy) and the two denominator parts:
-// phi(sq_i) . z_{<c+1} (z kept in LDS, each producer owning a quarter of the features) and
-// the row sums of the score tiles.  Producers read their inputs straight
+// so the intra-chunk weights keep float32 accuracy) with their row sums (the intra-chunk
+// denominator part), and z_{<c+1} (kept in LDS in float32, each producer owning a quarter of the
+// features, and handed to the consumers as hi + lo).  Producers read their inputs straight
 // from global memory, issued a whole chunk ahead.  The single barrier per chunk both hands
 // buffer c+1 to the consumers and returns buffer c to the producers.  The feature work per
 // token (vector ALU) and the LDS traffic of the operands bound this kernel; the matrix work
@@ -110,8 +118,8 @@ constexpr int kPipePairs = 10;  // (key tile <= query tile) pairs of 16-token ti
 template <int NT, bool READOUT>
 struct PipeSmem {
   static constexpr int WP = Geo<NT>::WP;
-  // Unpadded rows, 16-byte slots swizzled within each row (swz_kv, swz_q): every access of the three
-  // tiles below is free of LDS bank conflicts.
+  // Unpadded rows, 16-byte slots swizzled within each row (swz_kv, swz_q): every access the kernels
+  // make of the three tiles below is free of LDS bank conflicts.
   static constexpr int RQ = READOUT ? kPipeChunk : 1;
   static constexpr int RP = READOUT ? kPipePairs : 1;
   alignas(16) __bf16 vt[2][kDV][kPipeChunk];
@@ -119,7 +127,10 @@ struct PipeSmem {
   alignas(16) __bf16 phiq[2][RQ][WP];
   alignas(16) bf16x4 a[2][RP][64];    // score tiles, high bfloat16 part
   alignas(16) bf16x4 alo[2][RP][64];  // score tiles, low part (w - hi), so hi + lo keeps float32 accuracy
-  float den_part[2][kPipeProducers][RQ];
+  // z_{<c} as bfloat16 hi (row 0) and lo (row 1) in phi(sQ) slot order: the A operand of the
+  // denominator phi(sQ) z, one more matrix-core product of the readout (truncated-kernel readout)
+  alignas(16) __bf16 zop[2][2][READOUT ? WP : 8];
+  float den_part[2][kPipeProducers][RQ];  // expanded-softmax readout: gamma_0 of each token
   float den_intra[2][RP][16];
   float z[2][WP];  // z_{<c} for chunk parity c & 1, natural feature order
 };
@@ -136,21 +147,11 @@ struct PipeSplit {
   static constexpr int VC = kDV / kPipeProducers;
 };
 
-// LDS layout of the bfloat16 tiles.  Bank rule (measured on gfx950 with one pair of active lanes at a
-// time): reads see 64 four-byte banks, writes 32; a 16-byte read serves 16 lanes per cycle (those with
-// the same lane bit 5 and the same parity of lane bits 2..4), an 8-byte read 32 consecutive lanes, a
-// 16-byte write 8, a 4-byte write 32.  Padding alone cannot satisfy both sides of a tile (the phi(sQ)
-// rows, for one, are conflict-free to read for 16-byte-slot strides of 2 mod 4 and to write for odd
-// ones), so the rows are unpadded and the 16-byte slots of each row are permuted by an XOR with bits
-// of the row index; the swizzles below make every read and write of these tiles conflict-free.
-//
-// phi(K)^T and V^T: 128-byte rows (64 tokens), slot s of row r at slot s ^ swz_kv(r).
-__host__ __device__ constexpr int swz_kv(int r) { return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | (((r ^ (r >> 3)) & 1) << 2); }
-// phi(sQ): one row per token, slot s of row r at slot s ^ swz_q(r) (within its aligned group of 4).
-__host__ __device__ constexpr int swz_q(int r) { return (r >> 1) & 3; }
-// Byte offset of token t in row r of a phi(K)^T or V^T tile.
+// LDS layout of the bfloat16 tiles (lds_layout.hpp): unpadded rows, 16-byte slots swizzled by row.
 static_assert(kPipeChunk == 64, "phi(K)^T and V^T rows are 128 bytes: 8 slots of 8 tokens");
-__device__ __forceinline__ int kv_off(int r, int t) { return r * 128 + 16 * ((t >> 3) ^ swz_kv(r)) + 2 * (t & 7); }
+__device__ __forceinline__ int kv_bf16(int r, int t) { return kv_off<2>(r, t); }
+template <int NT>
+__device__ __forceinline__ int swz_q(int r) { return swz_tok<Geo<NT>::WP / 8>(r); }
 
 // phi(K)^T rows are written two rows at a time as whole dwords: lane j holds (row r, row r+1) of
 // token j; lanes j and j^1 swap those pairs (a quad permutation), then the even lane stores row r of
@@ -221,13 +222,12 @@ __device__ __forceinline__ float qfeat(const float (&x)[kDK], const f32x4& cq) {
     return feat<NT, A>(x);
 }
 
-// Writes this wave's phi(sQ) groups of token j and returns their part of phi(sq_j) . z (CENT: the
-// features scaled by the token's coefficients gamma_m, and no denominator part).
+// Writes this wave's phi(sQ) groups of token j (CENT: the features scaled by the token's coefficients
+// gamma_m).
 template <int NT, bool READOUT, bool CENT, int G>
-__device__ __forceinline__ float pipe_phiq_groups(PipeSmem<NT, READOUT>& sm, int b, int zb, int j,
-                                                  const float (&x)[kDK], const f32x4& cq) {
+__device__ __forceinline__ void pipe_phiq_groups(PipeSmem<NT, READOUT>& sm, int b, int j, const float (&x)[kDK],
+                                                 const f32x4& cq) {
   using SP = PipeSplit<NT>;
-  float acc = 0.f;
   [&]<int... P>(std::integer_sequence<int, P...>) {
     (([&] {
        constexpr int grp = G * SP::RG + P;
@@ -239,19 +239,13 @@ __device__ __forceinline__ float pipe_phiq_groups(PipeSmem<NT, READOUT>& sm, int
                                        to_bf16x2(qfeat<NT, CENT, slot_feature_bf16(s0 + 2 * R)>(x, cq),
                                                  qfeat<NT, CENT, slot_feature_bf16(s0 + 2 * R + 1)>(x, cq)))),
             ...);
-           if constexpr (!CENT) {
-             ((acc = fmaf(__uint_as_float(v[R] << 16), sm.z[zb][slot_feature_bf16(s0 + 2 * R)], acc)), ...);
-             ((acc = fmaf(__uint_as_float(v[R] & 0xffff0000u), sm.z[zb][slot_feature_bf16(s0 + 2 * R + 1)], acc)),
-              ...);
-           }
          }(std::make_integer_sequence<int, 4>{});
-         *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&sm.phiq[b][j][0]) + 16 * (grp ^ swz_q(j))) =
+         *reinterpret_cast<uint4*>(reinterpret_cast<char*>(&sm.phiq[b][j][0]) + 16 * (grp ^ swz_q<NT>(j))) =
              make_uint4(v[0], v[1], v[2], v[3]);
        }
      }()),
      ...);
   }(std::make_integer_sequence<int, SP::RG>{});
-  return acc;
 }
 
 // Query tile and key tile of intra-chunk score pair p (pairs ordered by query tile, then key tile).
@@ -341,13 +335,23 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
     unpack_row16(kr, x, 1.0f);
     pipe_phik_rows<NT, READOUT, G>(sm, b, l, x, valid);
   }
+  if constexpr (READOUT && !CENT) {
+    // z_{<chunk} of this wave's rows (written by the same lanes in the previous phase) as the
+    // consumers' denominator operand: hi + lo keeps about 16 significant bits
+    const int row = G * SP::RK + l;
+    if (l < SP::RK && row < WP) {
+      const float zr = sm.z[b][row];
+      const __bf16 hi = (__bf16)zr;
+      const int s = feature_slot_bf16(row);
+      sm.zop[b][0][s] = hi;
+      sm.zop[b][1][s] = (__bf16)(zr - (float)hi);
+    }
+  }
   if constexpr (READOUT) {
     float x[kDK];
     unpack_row16(in.q, x, scale);
-    const float dp = pipe_phiq_groups<NT, READOUT, CENT, G>(sm, b, b, l, x, in.cq);
-    if constexpr (!CENT)
-      sm.den_part[b][G][l] = dp;
-    else if constexpr (G == 0)
+    pipe_phiq_groups<NT, READOUT, CENT, G>(sm, b, l, x, in.cq);
+    if constexpr (CENT && G == 0)
       sm.den_part[b][0][l] = in.cq[0];  // gamma_0 of token l, for the consumers' constant-feature term
   }
   // V^T: this producer's value columns of token l (16-bit stores: the dword pairing measured no
@@ -359,8 +363,8 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
     for (int h = 0; h < 4; ++h) {
       const int c = SP::VC * G + 8 * u + 2 * h;
       char* vt = reinterpret_cast<char*>(&sm.vt[b][0][0]);
-      *reinterpret_cast<uint16_t*>(vt + kv_off(c, l)) = (uint16_t)(w[h] & 0xffffu);
-      *reinterpret_cast<uint16_t*>(vt + kv_off(c + 1, l)) = (uint16_t)(w[h] >> 16);
+      *reinterpret_cast<uint16_t*>(vt + kv_bf16(c, l)) = (uint16_t)(w[h] & 0xffffu);
+      *reinterpret_cast<uint16_t*>(vt + kv_bf16(c + 1, l)) = (uint16_t)(w[h] >> 16);
     }
   }
   if constexpr (READOUT) {
@@ -414,7 +418,7 @@ __device__ __forceinline__ void pipe_produce(PipeSmem<NT, READOUT>& sm, const Pi
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int t = 0; t < kPipeChunk; t += 8) {
-      const bf16x8 x8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(&sm.phikt[b][0][0]) + kv_off(row, t));
+      const bf16x8 x8 = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(&sm.phikt[b][0][0]) + kv_bf16(row, t));
 #pragma unroll
       for (int h = 0; h < 4; ++h) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{x8[2 * h], x8[2 * h + 1]}, ones, acc, false);
     }
@@ -501,9 +505,16 @@ __device__ __forceinline__ void pipe_consumer(PipeSmem<NT, READOUT>& sm, const S
     const long long tok0 = pc.tok + (long long)c * CS;
     const float srow0 = Srun[0][0];  // S_{<c}[0][16w + l16] on lanes 0..15 (CENT)
     f32x4 O[READOUT ? NIT : 1];
+    // denominators phi(sQ) z_{<c}: operand rows 0..7 carry z hi, rows 8..15 z lo, so result rows 0..7
+    // (lanes 0..31) hold the hi part and rows 8..15 (lanes 32..63) the lo part of each token's sum
+    constexpr bool DEN = READOUT && !CENT;
+    f32x4 Dz[DEN ? NIT : 1];
     if constexpr (READOUT) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (DEN)
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) Dz[it] = f32x4{0.f, 0.f, 0.f, 0.f};
       // readout with S_{<c} = hi + lo, one 32-feature k-block at a time
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
@@ -515,12 +526,15 @@ __device__ __forceinline__ void pipe_consumer(PipeSmem<NT, READOUT>& sm, const S
         }
         const bf16x8 hi = {h[0][0], h[0][1], h[1][0], h[1][1], h[2][0], h[2][1], h[3][0], h[3][1]};
         const bf16x8 lo = {lw[0][0], lw[0][1], lw[1][0], lw[1][1], lw[2][0], lw[2][1], lw[3][0], lw[3][1]};
+        bf16x8 za;
+        if constexpr (DEN) za = *reinterpret_cast<const bf16x8*>(&sm.zop[b][l16 >> 3][32 * kb + 8 * lg]);
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
           const bf16x8 bq = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(&sm.phiq[b][16 * it + l16][0]) +
-                                                             64 * kb + 16 * (lg ^ swz_q(l16)));
+                                                             64 * kb + 16 * (lg ^ swz_q<NT>(l16)));
           O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bq, O[it], 0, 0, 0);
           O[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bq, O[it], 0, 0, 0);
+          if constexpr (DEN) Dz[it] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(za, bq, Dz[it], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);  // bound the operands in flight (register budget)
       }
@@ -530,7 +544,7 @@ __device__ __forceinline__ void pipe_consumer(PipeSmem<NT, READOUT>& sm, const S
 #pragma unroll
         for (int jt = 0; jt <= it; ++jt) {
           const bf16x4 av = *reinterpret_cast<const bf16x4*>(reinterpret_cast<const char*>(&sm.vt[b][0][0]) +
-                                                             kv_off(16 * w + l16, 16 * jt + 4 * lg));
+                                                             kv_bf16(16 * w + l16, 16 * jt + 4 * lg));
           const bf16x4 bh = sm.a[b][pair_index(jt, it)][l];
           const bf16x4 bl = sm.alo[b][pair_index(jt, it)][l];
           // V^T (hi + lo) as one 16x16x32 MFMA: the halves of k pair av with bh and av with bl
@@ -543,11 +557,11 @@ __device__ __forceinline__ void pipe_consumer(PipeSmem<NT, READOUT>& sm, const S
 #pragma unroll
     for (int jb = 0; jb < CS / 32; ++jb) {
       const bf16x8 bv = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(&sm.vt[b][0][0]) +
-                                                         kv_off(16 * w + l16, 32 * jb + 8 * lg));
+                                                         kv_bf16(16 * w + l16, 32 * jb + 8 * lg));
 #pragma unroll
       for (int t = 0; t < NAT; ++t) {
         const bf16x8 ak = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(&sm.phikt[b][0][0]) +
-                                                           kv_off(16 * t + l16, 32 * jb + 8 * lg));
+                                                           kv_bf16(16 * t + l16, 32 * jb + 8 * lg));
         Srun[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, bv, Srun[t], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -558,9 +572,7 @@ __device__ __forceinline__ void pipe_consumer(PipeSmem<NT, READOUT>& sm, const S
         const int i = 16 * it + l16;
         float d = 1.f;  // the expanded-softmax readout has no normaliser
         if constexpr (!CENT) {
-          d = 0.f;
-#pragma unroll
-          for (int pp = 0; pp < kPipeProducers; ++pp) d += sm.den_part[b][pp][i];
+          d = Dz[it][0] + __shfl_xor(Dz[it][0], 32);  // hi part + lo part of the token's phi(sq) . z
 #pragma unroll
           for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][pair_index(jt, it)][l16];
         } else {
