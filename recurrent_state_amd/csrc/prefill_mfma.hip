@@ -787,15 +787,15 @@ __global__ __launch_bounds__(kPipeThreads) void prefill_pipe_fused_kernel(
     else
       pipe_consumer<NT, false, false, true>(sm0, pc, src, dst, false, nullptr, stride, w, tid, own);
   }
-  // The sum of a middle segment is published at once, so later segments need not wait for its
-  // look-back.  Publishing: the sums were stored through to the point of coherence (agent-scope
+  // The sum of a middle segment is published at once (segment 0's as its inclusive prefix), so later
+  // segments need not wait for its look-back.  Publishing: the sums were stored through to the point of coherence (agent-scope
   // stores); every wave waits until its stores are acknowledged, then, after the barrier, one thread
   // stores the flag.  Readers load the flag and then the sums from the point of coherence too, so no
   // cache is written back or invalidated on either side.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // also: the state walk's last LDS reads (z rows for dst) are done before `pre` is written
-  if (x > 0 && !last && tid == 0)
-    __hip_atomic_store(flags + slot, tag | kFlagAgg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!last && tid == 0)  // segment 0's sum is already its inclusive prefix
+    __hip_atomic_store(flags + slot, tag | (x == 0 ? kFlagIncl : kFlagAgg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // 2. the exclusive prefix into `pre`, and the inclusive one published
   lookback_prefix<SL::E, kPipeThreads>(pre, own, sin_p, agg, incl, flags, slot, x, last, stride, tag, seen, tid);
