@@ -4,7 +4,7 @@
 admits a parallel scan; here the scan is a decoupled look-back between the segments of each
 (sequence, head) pair.  Equal-length bfloat16 calls that split pairs into segments take this form.
 Checked: the oracle at the segmented shapes (64 and 96 pairs of 8,192 tokens; 8 pairs of 777 tokens
-cut into many one-chunk segments), continuation from a state in place and out of place, a workspace
+cut into many one-chunk segments; 2 pairs of 16,384 and one of 65,536 tokens in 128 and 256 segments), continuation from a state in place and out of place, a workspace
 reused by calls of other shapes or holding arbitrary bytes (a flag from another call must read as
 unpublished), and graph replays (the recorded form clears its flags first) interleaved with eager
 calls on the same workspace.
@@ -50,7 +50,9 @@ def _check_oracle(x, o, st, heads, n=3, full=False):
         assert np.all(np.abs(got - want) <= bound), f"state ({b}, {h})"
 
 
-@pytest.mark.parametrize("B,H,N", [(4, 16, 8192), (6, 16, 8192), (2, 4, 777)])
+# (2, 1, 16384) and (1, 1, 65536): 128 and 256 segments per pair, so the look-back of segments past the
+# 64th reads its flags in more than one window of 64
+@pytest.mark.parametrize("B,H,N", [(4, 16, 8192), (6, 16, 8192), (2, 4, 777), (2, 1, 16384), (1, 1, 65536)])
 def test_segmented_shapes_against_the_oracle(B, H, N):
     import torch
 
