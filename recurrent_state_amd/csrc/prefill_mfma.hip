@@ -572,7 +572,12 @@ __device__ __forceinline__ void pipe_consumer(PipeSmem<NT, READOUT>& sm, const S
         const int i = 16 * it + l16;
         float d = 1.f;  // the expanded-softmax readout has no normaliser
         if constexpr (!CENT) {
-          d = Dz[it][0] + __shfl_xor(Dz[it][0], 32);  // hi part + lo part of the token's phi(sq) . z
+          // hi part (lanes 0..31) + lo part (lanes 32..63) of the token's phi(sq) . z: after the swap one
+          // register holds lanes 0..31's values in both halves and the other lanes 32..63's, so their
+          // sum is the same in lanes l and l ^ 32 (v_permlane32_swap: no LDS round trip)
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(Dz[it][0]), __float_as_uint(Dz[it][0]),
+                                                           false, false);
+          d = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 #pragma unroll
           for (int jt = 0; jt <= it; ++jt) d += sm.den_intra[b][pair_index(jt, it)][l16];
         } else {
