@@ -12,12 +12,12 @@
 // wavefronts each:
 //   * waves 0..3 ("consumers") own value columns 16w..16w+15 of the block's state slice, kept in MFMA
 //     accumulator registers, and run only float32 16x16x4 MFMAs on chunk c: the readout with S_{<c}, the
-//     intra-chunk PV (block 0), the state update;
+//     intra-chunk PV (the last block, whose padding tiles past W are skipped), the state update;
 //   * waves 4..7 ("producers") meanwhile prepare chunk c+1 in the other half of a double-buffered LDS
 //     area: producer g expands features g*FB/4 .. of the block for the chunk's 32 tokens (lanes 0..31
 //     from k into phi(K)^T, lanes 32..63 from sq into phi(sQ), the same compile-time code on both
 //     halves), writes its V^T columns, its part of the denominators phi_f(sq) . z_{f,<c} and updates the
-//     block's z rows it owns; for block 0 producers 0..2 also build the three intra-chunk score tiles and
+//     block's z rows it owns; for the last block producers 0..2 also build the three intra-chunk score tiles and
 //     their column sums.  Their inputs are global loads issued a chunk ahead, in two alternating register
 //     sets;
 //   * one barrier per chunk; each block writes partial numerators and denominators per token to a
@@ -61,6 +61,19 @@ constexpr int block_features() {
 template <int NT>
 constexpr int n_blocks() {
   return (FeatureTable<NT, kDK>::W + block_features<NT>() - 1) / block_features<NT>();
+}
+// The block that also carries the intra-chunk term (score tiles, their PV and column sums): the last
+// one, whose features past W are padding (9 of 64 real at n = 4, 45 of 160 at n = 5), so that its
+// consumers run only the 16-feature tiles holding real features and the extra term lands on the
+// lightest block instead of adding to a full one.
+template <int NT>
+constexpr int intra_block() {
+  return n_blocks<NT>() - 1;
+}
+// 16-feature tiles of the last block that hold real features (all of them at n <= 3: one block).
+template <int NT>
+constexpr int last_block_tiles() {
+  return (FeatureTable<NT, kDK>::W - intra_block<NT>() * block_features<NT>() + 15) / 16;
 }
 
 constexpr int pair_it(int p) {
@@ -247,7 +260,7 @@ __device__ __forceinline__ void wide_produce(WideSmem<READOUT, block_features<NT
 #pragma unroll
   for (int c = 0; c < 8; ++c) sm.vt[b][16 * g + 8 * h + c][tk] = valid ? in.v.get(c) : 0.f;
   if constexpr (READOUT) {
-    if (fb == 0 && g < kPairs) {
+    if (fb == intra_block<NT>() && g < kPairs) {
       // score tile of pair g and its column sums (16 keys per query column)
       const int it = pair_it(g), jt = pair_jt(g);
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -377,7 +390,10 @@ __device__ __forceinline__ void wide_consumer_piece(WideSmem<READOUT, block_feat
 
   // ---- consumers: wave w owns value columns 16w..16w+15 ----
   const int col = 16 * w + l16;
-  const bool intra = READOUT && fb == 0;  // block 0 also carries the intra-chunk term
+  const bool intra = READOUT && fb == intra_block<NT>();  // the last block also carries the intra-chunk term
+  // the last block's tiles past W hold zero features and a zero state: it runs only the others
+  constexpr int NLAST = last_block_tiles<NT>();
+  const bool short_block = NLAST < NAT && fb == intra_block<NT>();
   f32x4 Srun[NAT];
 #pragma unroll
   for (int t = 0; t < NAT; ++t)
@@ -393,41 +409,49 @@ __device__ __forceinline__ void wide_consumer_piece(WideSmem<READOUT, block_feat
     const int nv = nv_of(c);
     const long long tok0 = tok_of(c);
     f32x4 O[READOUT ? kNIT : 1];
-    if constexpr (READOUT) {
+    // the chunk's matrix work over the first NTL feature tiles of the block
+    auto chunk_mfma = [&](auto ntl) __attribute__((always_inline)) {
+      constexpr int NTL = decltype(ntl)::value;
+      if constexpr (READOUT) {
 #pragma unroll
-      for (int it = 0; it < kNIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // readout: O[it][r] = (phi_f(sQ) S_{f,<c})[token 16it + l16][column 16w + 4lg + r]
+        for (int it = 0; it < kNIT; ++it) O[it] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // readout: O[it][r] = (phi_f(sQ) S_{f,<c})[token 16it + l16][column 16w + 4lg + r]
 #pragma unroll
-      for (int t = 0; t < NAT; ++t)
+        for (int t = 0; t < NTL; ++t)
 #pragma unroll
-        for (int it = 0; it < kNIT; ++it) {
-          const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[b][16 * it + l16][16 * t + 4 * lg]);
+          for (int it = 0; it < kNIT; ++it) {
+            const f32x4 bq = *reinterpret_cast<const f32x4*>(&sm.phiq[b][16 * it + l16][16 * t + 4 * lg]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], O[it], 0, 0, 0);
-        }
-      if (intra) {
-#pragma unroll
-        for (int it = 0; it < kNIT; ++it)
-#pragma unroll
-          for (int jt = 0; jt <= it; ++jt) {
-            const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jt + 4 * lg]);
-            const f32x4 bw = sm.a[b][it * (it + 1) / 2 + jt][l];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bw[r], O[it], 0, 0, 0);
+            for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(Srun[t][r], bq[r], O[it], 0, 0, 0);
           }
+        if (intra) {
+#pragma unroll
+          for (int it = 0; it < kNIT; ++it)
+#pragma unroll
+            for (int jt = 0; jt <= it; ++jt) {
+              const f32x4 av = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jt + 4 * lg]);
+              const f32x4 bw = sm.a[b][it * (it + 1) / 2 + jt][l];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) O[it] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[r], bw[r], O[it], 0, 0, 0);
+            }
+        }
       }
-    }
-    // state update: Srun[t] += phi_f(K)^T[16t.., chunk] V[chunk, columns]
+      // state update: Srun[t] += phi_f(K)^T[16t.., chunk] V[chunk, columns]
 #pragma unroll
-    for (int jb = 0; jb < kCS / 16; ++jb) {
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jb + 4 * lg]);
+      for (int jb = 0; jb < kCS / 16; ++jb) {
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(&sm.vt[b][col][16 * jb + 4 * lg]);
 #pragma unroll
-      for (int t = 0; t < NAT; ++t) {
-        const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[b][16 * t + l16][16 * jb + 4 * lg]);
+        for (int t = 0; t < NTL; ++t) {
+          const f32x4 ak = *reinterpret_cast<const f32x4*>(&sm.phikt[b][16 * t + l16][16 * jb + 4 * lg]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
+          for (int r = 0; r < 4; ++r) Srun[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(ak[r], bv[r], Srun[t], 0, 0, 0);
+        }
       }
-    }
+    };
+    if (short_block)
+      chunk_mfma(std::integral_constant<int, NLAST>{});
+    else
+      chunk_mfma(std::integral_constant<int, NAT>{});
     if constexpr (READOUT && n_blocks<NT>() == 1) {
       // a single block: the outputs are final (columns 16w + 4lg .. + 3 of token 16it + l16); the
       // expanded-softmax readout has no normaliser (its weights already sum to one)
