@@ -13,9 +13,9 @@
 // gh exists; but every term of dq carries the factor 1 / den_i, so the forward walk computes den's
 // block parts and dq * den together and the first reduction divides:
 //   pass A (chunks in order): den parts phi_B(a_i) . z_B, and J_phi_B(a_i)^T (S_B g_i - z_B (g_i . o_i));
-//          block 0 adds the intra-chunk parts;
+//          the last block adds the intra-chunk parts;
 //   reduce 1: den, dq = sigma sum / den, gh and delta per token;
-//   pass B (chunks in reverse; G seeded with the final state's gradient): dv and dk parts; block 0
+//   pass B (chunks in reverse; G seeded with the final state's gradient): dv and dk parts; the last block
 //          adds the intra-chunk parts; the block's G at the start is the incoming state's gradient;
 //   reduce 2: dk, dv.
 // Wavefront w owns the block's 16-feature tile w: it keeps that tile of S (pass A) or
@@ -26,7 +26,7 @@
 // Jacobian (one lane per token).  Only two things cross wavefronts: the per-token sums of the eight
 // tiles' Jacobian rows and den parts, and in pass B dv, a product over all the block's features, for
 // which each wavefront leaves its G tile in LDS once per chunk.  Barriers per chunk: two in pass A,
-// three in pass B (plus two in block 0 for the intra-chunk terms).  All products run as float32
+// three in pass B (plus two in the last block for the intra-chunk terms).  All products run as float32
 // 16x16x4 MFMAs; LDS row strides keep each product's operand reads on distinct banks.
 #include <type_traits>
 #include <utility>
@@ -74,10 +74,10 @@ struct SmemA {
   alignas(16) float pk[kC][LS];    // phi_f(k_t), the block's features (wavefront w: columns 16w..)
   alignas(16) float pa[kC][LS];    // phi_f(a_t)
   alignas(16) float dred[NW][kC];  // per-tile den parts
-  alignas(16) float dintra[kC];        // intra-chunk den (block 0)
-  float part[NW + 1][kC][kDK + 1];  // per-tile Jacobian rows; [NW]: intra-chunk rows (block 0)
-  float wm[kC][kC + 1];            // intra-chunk weights [query][key] (block 0)
-  float dm[kC][kC + 1];            // intra-chunk score gradients times den (block 0)
+  alignas(16) float dintra[kC];        // intra-chunk den (last block)
+  float part[NW + 1][kC][kDK + 1];  // per-tile Jacobian rows; [NW]: intra-chunk rows (last block)
+  float wm[kC][kC + 1];            // intra-chunk weights [query][key] (last block)
+  float dm[kC][kC + 1];            // intra-chunk score gradients times den (last block)
   alignas(16) float v[kC][kLR];    // v rows
   alignas(16) float gt[kDV][kLT];  // g^T
 };
@@ -277,7 +277,7 @@ __device__ __forceinline__ void jacobian_tile(SM& sm, int w, int t, const float*
   for (int c = 0; c < kDK; ++c) sm.part[w][t][c] = d[c];
 }
 
-// Block 0, intra-chunk: wm[i][j] = K_n(s_ij), dm[i][j] = (u_i . v_j - go_i) K_{n-1}(s_ij) for key
+// The last block, intra-chunk: wm[i][j] = K_n(s_ij), dm[i][j] = (u_i . v_j - go_i) K_{n-1}(s_ij) for key
 // j <= query i (zero above the diagonal), u = g (pass A) or gh (pass B).  Waves 0..3 take the four
 // 16x16 tiles; u_i . v_j from u rows given as [d][i] (pass A: g^T) or [i][d] (pass B: gh) and v as
 // [j][d] (pass A) or [d][j] (pass B).
@@ -308,7 +308,7 @@ __device__ __forceinline__ void intra_weights(SM& sm, int w, int i16, int lg) {
 }
 
 // Pass A: one workgroup per (block, pair), chunks in order.  Writes per token: den_part[block] and
-// p16[block] = sigma J_phi_B(a)^T (S_B g - z_B (g . o)) (block 0: plus the intra-chunk parts).
+// p16[block] = sigma J_phi_B(a)^T (S_B g - z_B (g . o)) (the last block: plus the intra-chunk parts).
 template <int NT>
 __global__ __launch_bounds__(WB<NT>::TH) void bwdw_a_kernel(const void* __restrict__ q, const void* __restrict__ k,
                                                             const void* __restrict__ v, const float* __restrict__ g,
@@ -326,6 +326,8 @@ __global__ __launch_bounds__(WB<NT>::TH) void bwdw_a_kernel(const void* __restri
   const long long bh = blockIdx.y;
   const int f0 = fb * P::FB + 16 * w;  // the wavefront's first feature
   const int t0 = tid >> 4, c16 = tid & 15;  // the thread's token group (rounds of 4 NW tokens) and coordinate
+  const bool intra = fb == NB - 1;          // the block that adds the intra-chunk parts
+  const bool real = f0 < W;                 // the tile holds real features (else S, y stay unused zeros)
   // S^T tile: lane holds S[f0 + i16][16 dt + 4 lg + r] in Sa[dt][r]
   f32x4 Sa[4];
   {
@@ -358,18 +360,20 @@ __global__ __launch_bounds__(WB<NT>::TH) void bwdw_a_kernel(const void* __restri
     dispatch_index<0, NB * NW>(slot_of<NW>(fb, w), [&](auto I) { expand_tile<NT, decltype(I)::value * 16>(sm, l, nv); });
     wave_fence();
     // y = S g - z (g . o) over the tile's features (S, z before this chunk)
+    if (real) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int tt = 0; tt < 2; ++tt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc = mfma(Sa[dt][r], sm.gt[16 * dt + 4 * lg + r][16 * tt + i16], acc);
-      // acc[r]: feature 16 w + 4 lg + r, token 16 tt + i16
+          for (int r = 0; r < 4; ++r) acc = mfma(Sa[dt][r], sm.gt[16 * dt + 4 * lg + r][16 * tt + i16], acc);
+        // acc[r]: feature 16 w + 4 lg + r, token 16 tt + i16
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int f = 16 * w + 4 * lg + r, t = 16 * tt + i16;
-        sm.y[f][t] = acc[r] - sm.zz[f] * sm.go[t];
+        for (int r = 0; r < 4; ++r) {
+          const int f = 16 * w + 4 * lg + r, t = 16 * tt + i16;
+          sm.y[f][t] = acc[r] - sm.zz[f] * sm.go[t];
+        }
       }
     }
     if (l < kC) {
@@ -388,10 +392,12 @@ __global__ __launch_bounds__(WB<NT>::TH) void bwdw_a_kernel(const void* __restri
     }
     wave_fence();
     // S^T += V^T phi(K) over the tile's features, z += phi(K)^T 1
+    if (real) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int s = 0; s < kC / 4; ++s) Sa[dt] = mfma(sm.v[4 * s + lg][16 * dt + i16], sm.pk[4 * s + lg][16 * w + i16], Sa[dt]);
+        for (int s = 0; s < kC / 4; ++s) Sa[dt] = mfma(sm.v[4 * s + lg][16 * dt + i16], sm.pk[4 * s + lg][16 * w + i16], Sa[dt]);
+    }
     if (l < 16) {
       float acc = 0.f;
 #pragma unroll
@@ -400,7 +406,7 @@ __global__ __launch_bounds__(WB<NT>::TH) void bwdw_a_kernel(const void* __restri
     }
     if (l < kC)
       dispatch_index<0, NB * NW>(slot_of<NW>(fb, w), [&](auto I) { jacobian_tile<NT, decltype(I)::value * 16>(sm, w, l, &sm.xa[l][0]); });
-    if (fb == 0) {
+    if (intra) {
       intra_weights<NT, true>(sm, w, i16, lg);
       __syncthreads();
       if (w < 2) {
@@ -425,13 +431,13 @@ __global__ __launch_bounds__(WB<NT>::TH) void bwdw_a_kernel(const void* __restri
         float s = 0.f;
 #pragma unroll
         for (int x = 0; x < NW; ++x) s += sm.part[x][t][c16];
-        if (fb == 0) s += sm.part[NW][t][c16];
+        if (intra) s += sm.part[NW][t][c16];
         p16[((long long)fb * T + tok0 + t) * kDK + c16] = scale * s;
         if (c16 == 0) {
           float dn = 0.f;
 #pragma unroll
           for (int x = 0; x < NW; ++x) dn += sm.dred[x][t];
-          if (fb == 0) dn += sm.dintra[t];
+          if (intra) dn += sm.dintra[t];
           den_part[(long long)fb * T + tok0 + t] = dn;
         }
       }
@@ -503,7 +509,7 @@ __global__ __launch_bounds__(256) void bwdw_r1_kernel(const float* __restrict__ 
 }
 
 // Pass B: one workgroup per (block, pair), chunks in reverse.  Writes per token the dv and dk parts of
-// the block (block 0: plus the intra-chunk parts), and the block's rows of the incoming state's
+// the block (the last block: plus the intra-chunk parts), and the block's rows of the incoming state's
 // gradient.
 template <int NT>
 __global__ __launch_bounds__(WB<NT>::TH) void bwdw_b_kernel(const void* __restrict__ q, const void* __restrict__ k,
@@ -521,6 +527,10 @@ __global__ __launch_bounds__(WB<NT>::TH) void bwdw_b_kernel(const void* __restri
   const long long bh = blockIdx.y;
   const int f0 = fb * FB + 16 * w;
   const int t0 = tid >> 4, c16 = tid & 15;
+  const bool intra = fb == NB - 1;  // the block that adds the intra-chunk parts
+  const bool real = f0 < W;         // the tile holds real features (else G_S, y stay unused zeros)
+  // steps of 4 features of the last block with a real one among them (its padding is zero in pk)
+  constexpr int kLastSteps = (W - (NB - 1) * FB + 3) / 4;
   // G_S^T tile: lane holds G_S[f0 + i16][16 dt + 4 lg + r] in Ga[dt][r]
   f32x4 Ga[4];
   {
@@ -560,35 +570,46 @@ __global__ __launch_bounds__(WB<NT>::TH) void bwdw_b_kernel(const void* __restri
     // dv parts = phi_B(K) G_S (G of the later tokens) over all the block's features: the wavefront's
     // tiles u = w, w + NW of the eight (token tile u / 4, column tile u % 4)
     f32x4 dva[ND];
+    auto dv_parts = [&](auto nsteps) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < ND; ++e) {
-      const int u = w + NW * e, tt = u >> 2, dt = u & 3;
-      dva[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < ND; ++e) {
+        const int u = w + NW * e, tt = u >> 2, dt = u & 3;
+        dva[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-      for (int s = 0; s < FB / 4; ++s) dva[e] = mfma(sm.pk[16 * tt + i16][4 * s + lg], sm.gs[4 * s + lg][16 * dt + i16], dva[e]);
-    }
+        for (int s = 0; s < decltype(nsteps)::value; ++s)
+          dva[e] = mfma(sm.pk[16 * tt + i16][4 * s + lg], sm.gs[4 * s + lg][16 * dt + i16], dva[e]);
+      }
+    };
+    if (intra)
+      dv_parts(std::integral_constant<int, kLastSteps>{});
+    else
+      dv_parts(std::integral_constant<int, FB / 4>{});
     __builtin_amdgcn_sched_barrier(0);
     // y = G_S v + G_z over the tile's features
+    if (real) {
 #pragma unroll
-    for (int ut = 0; ut < 2; ++ut) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int ut = 0; ut < 2; ++ut) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc = mfma(Ga[dt][r], sm.vt[16 * dt + 4 * lg + r][16 * ut + i16], acc);
+          for (int r = 0; r < 4; ++r) acc = mfma(Ga[dt][r], sm.vt[16 * dt + 4 * lg + r][16 * ut + i16], acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int f = 16 * w + 4 * lg + r;
-        sm.y[f][16 * ut + i16] = acc[r] + sm.zz[f];
+        for (int r = 0; r < 4; ++r) {
+          const int f = 16 * w + 4 * lg + r;
+          sm.y[f][16 * ut + i16] = acc[r] + sm.zz[f];
+        }
       }
     }
     wave_fence();
     __builtin_amdgcn_sched_barrier(0);
     // G_S^T += gh^T phi(A), G_z -= phi(A)^T delta over the tile's features
+    if (real) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int s = 0; s < kC / 4; ++s) Ga[dt] = mfma(sm.gh[4 * s + lg][16 * dt + i16], sm.pa[4 * s + lg][16 * w + i16], Ga[dt]);
+        for (int s = 0; s < kC / 4; ++s) Ga[dt] = mfma(sm.gh[4 * s + lg][16 * dt + i16], sm.pa[4 * s + lg][16 * w + i16], Ga[dt]);
+    }
     if (l < 16) {
       float acc = 0.f;
 #pragma unroll
@@ -598,7 +619,7 @@ __global__ __launch_bounds__(WB<NT>::TH) void bwdw_b_kernel(const void* __restri
     __builtin_amdgcn_sched_barrier(0);
     if (l < kC)
       dispatch_index<0, NB * NW>(slot_of<NW>(fb, w), [&](auto I) { jacobian_tile<NT, decltype(I)::value * 16>(sm, w, l, &sm.xk[l][0]); });
-    if (fb == 0) {
+    if (intra) {
       intra_weights<NT, false>(sm, w, i16, lg);
       __syncthreads();
       // dv_j += sum_i wm[i][j] gh_i (the wavefront's dv tiles); dk_j += sum_i dm[i][j] a_i (waves 0, 1)
@@ -633,7 +654,7 @@ __global__ __launch_bounds__(WB<NT>::TH) void bwdw_b_kernel(const void* __restri
         float s = 0.f;
 #pragma unroll
         for (int x = 0; x < NW; ++x) s += sm.part[x][t][c16];
-        if (fb == 0) s += sm.part[NW][t][c16];
+        if (intra) s += sm.part[NW][t][c16];
         p16[((long long)fb * T + tok0 + t) * kDK + c16] = s;
       }
     }
