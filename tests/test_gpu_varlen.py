@@ -90,7 +90,7 @@ def test_varlen_orders(n, dtype):
             _check_state(st, b, h, ks[h], vs[h], n, dtype, cfg)
 
 
-@pytest.mark.parametrize("n,dtype", [(3, "bf16"), (3, "f32"), (5, "f32"), (2, "bf16")])
+@pytest.mark.parametrize("n,dtype", [(3, "bf16"), (3, "f32"), (5, "f32"), (2, "bf16"), (4, "bf16"), (4, "f32")])
 def test_varlen_equal_lengths_agree_with_the_batched_call(n, dtype):
     # Equal lengths through the ragged entry point ([H][B*N] layout, cut into token ranges) against
     # taylor_attn_prefill over [B, H, N] (cut into per-sequence segments): the same values up to
@@ -158,7 +158,7 @@ def test_varlen_resume(dtype):
             _check_state(st, b, h, ks[h], vs[h], n, dtype, cfg)
 
 
-@pytest.mark.parametrize("n,dtype", [(3, "bf16"), (5, "f32")])
+@pytest.mark.parametrize("n,dtype", [(3, "bf16"), (5, "f32"), (4, "bf16")])
 def test_varlen_one_long_many_short(n, dtype):
     # Workgroups take equal ranges of the packed token axis: the long sequence spans many ranges
     # (its pieces chain through the scan) while single ranges hold many short sequences.
