@@ -119,6 +119,20 @@ def test_backward_feature_blocks_raw_scores_and_many_heads(n):
     _check(_run(x, g, o, cfg), x, g, n, 0.25, label=f"raw n={n}")
 
 
+@pytest.mark.parametrize("n", [4, 5])
+def test_backward_feature_blocks_bitwise_repeatable(n):
+    # per-block gradient parts summed in block order (the last block adds the intra-chunk parts): two
+    # calls on the same inputs give the same bits
+    x = synth.make_qkv(140 + n, 1, 3, 333, DK, DV)
+    g = _grad_inputs(x, 1400 + n)
+    cfg = _cfg(n, "f32")
+    announce("backward-blocks-repeat", n)
+    o = _oracle_fwd(x, n, 1.0).astype(np.float32)
+    first, second = _run(x, g, o, cfg), _run(x, g, o, cfg)
+    for name, a, b in zip(("dq", "dk", "dv"), first, second):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{name} not bitwise repeatable"
+
+
 def test_backward_raw_scores():
     x = synth.make_qkv(116, 1, 2, 300, DK, DV, unit_norm=False)
     g = _grad_inputs(x, 1160)

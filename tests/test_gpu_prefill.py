@@ -195,6 +195,24 @@ def test_chunk_size_invariance_and_repeatability():
     assert err <= 1e-5
 
 
+@pytest.mark.parametrize("n", [4, 5])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_feature_blocks_bitwise_repeatable(n, dtype):
+    # n = 4, 5: per-block partial outputs summed in block order (the last block also carries the
+    # intra-chunk term), over several segments per pair (state pass and scan): two calls on the same
+    # inputs give the same bits, outputs and final state
+    x = synth.make_qkv(64 + n, 1, 3, 700, 16, 64, dtype)
+    cfg = rs.config(n, 16, 64, 0, 1.0, rs.TAYLOR_BF16 if dtype == "bf16" else rs.TAYLOR_F32)
+    announce("blocks-repeat", n, dtype)
+    runs = []
+    for _ in range(2):
+        st = rs.new_state(1, 3, cfg, DEV)
+        o, _ = run_prefill(x, cfg, DEV, state=st)
+        runs.append((o.cpu().numpy(), st.cpu().numpy()))
+    for a, b in zip(*runs):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "not bitwise repeatable"
+
+
 def test_noop_calls_leave_memory_untouched():
     import torch
 
